@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-layer hot path on one MI355X.
+
+Headline (the JSON line's `value`): prefill throughput in tokens/s of one MoE
+layer at T=2048 tokens with Zipf-skewed routing (H=2048, I=512, 256 experts,
+top-8 + shared expert, 4-bit affine g=64 weights), one step = moe_route +
+moe_expert_gemm_q4 + moe_down_combine on a batch already resident in HBM.
+Consecutive steps rotate over independently seeded weight sets (distinct
+layers) so that no step finds its weights in the 256 MB last-level cache.
+
+Also reported: the gate/up GEMM kernel's MFMA roofline fraction (HIP events
+around its launch inside the timed loop), the batch-1 decode path's HBM
+bandwidth, and the CPU oracle's throughput on a bounded token sample.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer prefill tokens/s @T=2048 (MFMA %); T=1 decode HBM GB/s (% of peak)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+T, H, I, E, K_TOP = 2048, 2048, 512, 256, 8
+ZIPF_S = 1.1
+SEED_PREFILL = 4000
+SEED_DECODE = 2000
+
+
+def expert_bytes(H, I):
+    """Packed bytes of one expert: codes (0.5 B/weight) + bf16 scale and bias per 64 weights."""
+    return 3 * H * I // 2 + 3 * H * (I // 64) * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=6, help="weight sets rotated in the prefill loop")
+    ap.add_argument("--decode-sets", type=int, default=32)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the MoE layer on one GPU only; the expert-parallel "
+              "split across GPUs is a design note, not implemented. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_expert_top_amd as moe
+    from synth.device import make_layer_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape = moe.Shape(T=T, H=H, I=I, E=E, top_k=K_TOP)
+
+    def device_layer(d):
+        proj = {n: d[n] for n in moe.DeviceLayer.NAMES}
+        return moe.DeviceLayer(proj, d["router_wt"], d["router_bias"], device=dev)
+
+    # ---------------- prefill: T=2048, Zipf-skewed routing ----------------
+    print(f"[bench] generating {args.sets} prefill weight sets", file=sys.stderr, flush=True)
+    raw0 = make_layer_device(SEED_PREFILL, T, H, I, E, zipf_s=ZIPF_S, device=dev)
+    x = raw0["x"]
+    sets = [device_layer(raw0)]
+    for s in range(1, args.sets):
+        sets.append(device_layer(make_layer_device(SEED_PREFILL + 100 * s, T, H, I, E,
+                                                   zipf_s=ZIPF_S, device=dev, with_x=False)))
+    r = moe.Routing(shape, dev, with_logits=False)
+    ws = moe.workspace(shape, dev)
+    h = torch.empty((T * K_TOP + T, I), dtype=torch.int16, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def step(w):
+        moe.moe_route(shape, x, w, r, ws)
+        moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
+        moe.moe_down_combine(shape, h, w, r, y, ws)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(K):
+        w = sets[s % len(sets)]
+        e0, e1, e2, e3 = ev[s]
+        e0.record()
+        moe.moe_route(shape, x, w, r, ws)
+        e1.record()
+        moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
+        e2.record()
+        moe.moe_down_combine(shape, h, w, r, y, ws)
+        e3.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / K
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    gateup_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    down_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+
+    rows = T * K_TOP + T
+    flops_gateup = 2.0 * rows * (2 * I) * H
+    flops_down = 2.0 * rows * I * H
+    tok_s = T / (ms_step * 1e-3)
+    gateup_tflops = flops_gateup / (gateup_ms * 1e-3) / 1e12
+    layer_mfma_frac = (flops_gateup + flops_down) / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+
+    # ---------------- decode: T=1 ----------------
+    print(f"[bench] prefill {ms_step * 1e3:.1f} us/step; decode with {args.decode_sets} weight sets",
+          file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    dshape = moe.Shape(T=1, H=H, I=I, E=E, top_k=K_TOP)
+    dsets = []
+    for s in range(args.decode_sets):
+        d = make_layer_device(SEED_DECODE + s, 1, H, I, E, zipf_s=None, device=dev)
+        dsets.append((d["x"], device_layer(d)))
+    dws = moe.workspace(dshape, dev)
+    ids = torch.empty(K_TOP, dtype=torch.int32, device=dev)
+    tw = torch.empty(K_TOP, dtype=torch.float32, device=dev)
+    yd = torch.empty(H, dtype=torch.float32, device=dev)
+    for i in range(10):
+        xd, wd = dsets[i % len(dsets)]
+        moe.moe_decode(dshape, xd, wd, ids, tw, yd, dws)
+    torch.cuda.synchronize()
+    DK = args.decode_steps
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(DK)]
+    for s in range(DK):
+        xd, wd = dsets[s % len(dsets)]
+        dev_ev[s][0].record()
+        moe.moe_decode(dshape, xd, wd, ids, tw, yd, dws)
+        dev_ev[s][1].record()
+    torch.cuda.synchronize()
+    dec_us = sum(a.elapsed_time(b) for a, b in dev_ev) / DK * 1e3
+    dec_bytes = 9 * expert_bytes(H, I) + E * H * 2 + H * 2 + H * 4 + K_TOP * 8
+    dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
+    del dsets
+    torch.cuda.empty_cache()
+
+    # ---------------- CPU oracle baseline (rank 0, N=1) ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        from synth.device import to_host_inputs
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        inp = to_host_inputs(raw0, T, H, I, E, K_TOP)
+        L = oracle.Layer(inp)
+        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        L.tokens(list(range(cores)))                       # calibration
+        per_tok = (time.perf_counter() - t0) / cores
+        n = int(max(cores, min(T, args.cpu_seconds / max(per_tok, 1e-6))))
+        rng = np.random.default_rng(0)
+        toks = sorted(rng.choice(T, size=n, replace=False).tolist())
+        t0 = time.perf_counter()
+        L.tokens(toks)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"{n} of the {T} tokens of the same layer (weight set 0), full per-token "
+                         f"path: router over 256 experts, top-8, 9 SwiGLU experts in float64; "
+                         f"{dt:.1f} s wall"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill2048_zipf: one MoE layer, T=2048 tokens, H=2048, I=512, "
+                               "256 experts top-8 + shared expert, 4-bit affine g=64 weights, "
+                               "Zipf(1.1) router bias",
+                   "T": T, "H": H, "I": I, "E": E, "top_k": K_TOP, "weight_sets": args.sets,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "q4_gemm_kernel<0> (gate/up + SwiGLU)",
+                     "achieved": round(gateup_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gateup_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_us": round(gateup_ms * 1e3, 2),
+                     "flops_per_launch": flops_gateup},
+        "layer_mfma_frac": round(layer_mfma_frac, 4),
+        "phase_us": {"route": round(route_ms * 1e3, 2), "gateup": round(gateup_ms * 1e3, 2),
+                     "down_combine": round(down_ms * 1e3, 2)},
+        "wall_s": round(wall, 3),
+        "decode": {"metric": "T=1 decode HBM GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
+                   "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(dec_us, 2),
+                   "bytes_per_call": dec_bytes, "weight_sets": args.decode_sets},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

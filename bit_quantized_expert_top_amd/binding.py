@@ -1,0 +1,242 @@
+"""ctypes binding of libmoeq4.so: argument marshalling only."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeq4.so")
+
+P = C.c_void_p
+i32 = C.c_int32
+
+
+class _Shape(C.Structure):
+    _fields_ = [("T", i32), ("H", i32), ("I", i32), ("E", i32), ("top_k", i32), ("group", i32),
+                ("bits", i32)]
+
+
+class _Q4(C.Structure):
+    _fields_ = [("q", P), ("scale", P), ("bias", P)]
+
+
+class _Weights(C.Structure):
+    _fields_ = [("gate", _Q4), ("up", _Q4), ("down", _Q4), ("sh_gate", _Q4), ("sh_up", _Q4),
+                ("sh_down", _Q4), ("router_wt", P), ("router_bias", P)]
+
+
+class _Routing(C.Structure):
+    _fields_ = [("logits", P), ("topk_ids", P), ("topk_w", P), ("counts", P), ("offsets", P),
+                ("row_token", P), ("tok_row", P), ("row_w", P), ("blocks", P),
+                ("num_blocks", P)]
+
+
+_lib = None
+
+# every entry point of include/moe_q4.h with its ctypes signature
+_SIGS = {
+    "moe_query": ([C.POINTER(_Shape), C.POINTER(C.c_size_t), C.POINTER(i32), C.POINTER(i32)], i32),
+    "moe_route": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, C.c_size_t,
+                   P], i32),
+    "moe_expert_gemm_q4": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P,
+                            C.c_size_t, P], i32),
+    "moe_down_combine": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P,
+                          C.c_size_t, P], i32),
+    "moe_layer": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P, P,
+                   C.c_size_t, P], i32),
+    "moe_decode": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, P, P, P, C.c_size_t, P], i32),
+    "moe_rmsnorm_residual": ([i32, i32, C.c_float, P, P, P, P], i32),
+    "moe_dequant_q4": ([C.POINTER(_Q4), i32, i32, P, P], i32),
+    "moe_status_str": ([i32], C.c_char_p),
+}
+
+
+def lib():
+    """Load libmoeq4.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m bit_quantized_expert_top_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_str(status)} ({status})")
+
+
+def moe_status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor], dtypes=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+_B16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U32 = (torch.int32, torch.uint32)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+@dataclass
+class Shape:
+    T: int
+    H: int
+    I: int
+    E: int = 256
+    top_k: int = 8
+    group: int = 64
+    bits: int = 4
+
+    def c(self) -> _Shape:
+        return _Shape(self.T, self.H, self.I, self.E, self.top_k, self.group, self.bits)
+
+
+def moe_query(shape: Shape):
+    """(workspace_bytes, max_blocks, block_rows) for `shape`."""
+    ws = C.c_size_t()
+    mb = i32()
+    br = i32()
+    _check(lib().moe_query(C.byref(shape.c()), C.byref(ws), C.byref(mb), C.byref(br)), "moe_query")
+    return ws.value, mb.value, br.value
+
+
+def workspace(shape: Shape, device="cuda") -> torch.Tensor:
+    nbytes, _, _ = moe_query(shape)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+class Routing:
+    """Device buffers of moe_routing, allocated for one shape."""
+
+    def __init__(self, shape: Shape, device="cuda", with_logits: bool = True):
+        _, max_blocks, _ = moe_query(shape)
+        T, E, k = shape.T, shape.E, shape.top_k
+        dev = torch.device(device)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if with_logits else None
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.row_token = torch.empty(T * k, dtype=torch.int32, device=dev)
+        self.tok_row = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.row_w = torch.empty(T * k, dtype=torch.float32, device=dev)
+        self.blocks = torch.empty((max_blocks, 3), dtype=torch.int32, device=dev)
+        self.num_blocks = torch.empty(1, dtype=torch.int32, device=dev)
+        self.max_blocks = max_blocks
+
+    def c(self) -> _Routing:
+        return _Routing(_ptr(self.logits, _F32, "logits"), _ptr(self.topk_ids, _I32, "topk_ids"),
+                        _ptr(self.topk_w, _F32, "topk_w"), _ptr(self.counts, _I32, "counts"),
+                        _ptr(self.offsets, _I32, "offsets"), _ptr(self.row_token, _I32, "row_token"),
+                        _ptr(self.tok_row, _I32, "tok_row"), _ptr(self.row_w, _F32, "row_w"),
+                        _ptr(self.blocks, _I32, "blocks"), _ptr(self.num_blocks, _I32, "num_blocks"))
+
+
+def _to_dev(a, device, dtype):
+    t = torch.from_numpy(a) if not isinstance(a, torch.Tensor) else a
+    return t.contiguous().view(dtype).to(device)
+
+
+class DeviceLayer:
+    """The layer's weights on the device (moe_weights).
+
+    Each projection is given as (codes uint32, scale bf16-bits, bias bf16-bits)
+    arrays, numpy or torch; routed ones stacked [E][N][...].
+    """
+
+    NAMES = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
+
+    def __init__(self, projections: dict, router_wt, router_bias=None, device="cuda"):
+        self.t = {}
+        for n in self.NAMES:
+            q, s, b = projections[n]
+            self.t[n] = (_to_dev(q, device, torch.int32), _to_dev(s, device, torch.int16),
+                         _to_dev(b, device, torch.int16))
+        self.router_wt = _to_dev(router_wt, device, torch.int16)
+        self.router_bias = None if router_bias is None else _to_dev(router_bias, device, torch.float32)
+
+    def c(self) -> _Weights:
+        q4 = {n: _Q4(*(_ptr(x, None, n) for x in self.t[n])) for n in self.NAMES}
+        return _Weights(q4["gate"], q4["up"], q4["down"], q4["sh_gate"], q4["sh_up"], q4["sh_down"],
+                        _ptr(self.router_wt, _B16, "router_wt"),
+                        _ptr(self.router_bias, _F32, "router_bias"))
+
+
+def moe_route(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, ws: torch.Tensor,
+              stream=None):
+    _check(lib().moe_route(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()), C.byref(r.c()),
+                           _ptr(ws, None, "ws"), ws.numel(), _stream(stream)), "moe_route")
+
+
+def moe_expert_gemm_q4(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,
+                       ws: torch.Tensor, stream=None):
+    _check(lib().moe_expert_gemm_q4(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
+                                    C.byref(r.c()), _ptr(h, _B16, "h"), _ptr(ws, None, "ws"),
+                                    ws.numel(), _stream(stream)), "moe_expert_gemm_q4")
+
+
+def moe_down_combine(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing, y: torch.Tensor,
+                     ws: torch.Tensor, stream=None):
+    _check(lib().moe_down_combine(C.byref(shape.c()), _ptr(h, _B16, "h"), C.byref(w.c()),
+                                  C.byref(r.c()), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
+                                  ws.numel(), _stream(stream)), "moe_down_combine")
+
+
+def moe_layer(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,
+              y: torch.Tensor, ws: torch.Tensor, stream=None):
+    _check(lib().moe_layer(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()), C.byref(r.c()),
+                           _ptr(h, _B16, "h"), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
+                           ws.numel(), _stream(stream)), "moe_layer")
+
+
+def moe_decode(shape: Shape, x: torch.Tensor, w: DeviceLayer, ids: torch.Tensor, tw: torch.Tensor,
+               y: torch.Tensor, ws: torch.Tensor, stream=None):
+    _check(lib().moe_decode(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
+                            _ptr(ids, _I32, "ids"), _ptr(tw, _F32, "topk_w"), _ptr(y, _F32, "y"),
+                            _ptr(ws, None, "ws"), ws.numel(), _stream(stream)), "moe_decode")
+
+
+def moe_rmsnorm_residual(T: int, H: int, eps: float, r: torch.Tensor, y: torch.Tensor,
+                         u: torch.Tensor, stream=None):
+    _check(lib().moe_rmsnorm_residual(T, H, eps, _ptr(r, _F32, "r"), _ptr(y, _F32, "y"),
+                                      _ptr(u, _B16, "u"), _stream(stream)), "moe_rmsnorm_residual")
+
+
+def moe_dequant_q4(q: torch.Tensor, s: torch.Tensor, b: torch.Tensor, N: int, K: int,
+                   out: torch.Tensor, stream=None):
+    p = _Q4(_ptr(q, None, "q"), _ptr(s, _B16, "scale"), _ptr(b, _B16, "bias"))
+    _check(lib().moe_dequant_q4(C.byref(p), N, K, _ptr(out, _B16, "out"), _stream(stream)),
+           "moe_dequant_q4")

@@ -1,0 +1,231 @@
+// Host side of libmoeq4: argument validation, workspace layout and launch
+// order.  Every check runs before the first launch, so an error return
+// means nothing was enqueued.
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int max_blocks_for(int T, int E, int k) {
+    const int rows = T * k;
+    return (rows + kBM - 1) / kBM + (rows < E ? rows : E);
+}
+
+size_t decode_scratch_bytes(int I, int k);
+
+WsLayout ws_layout(int T, int H, int I, int E, int k) {
+    WsLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t nTB = (size_t)(T + 63) / 64;
+    L.logits = take((size_t)T * E * 4);
+    L.xsum = take((size_t)T * (H / 64) * 4);
+    L.hsum = take((size_t)(T * k + T) * (I / 64) * 4);
+    L.blk_cnt = take(nTB * E * 4);
+    L.lrank = take((size_t)T * k * 4);
+    L.dec = take(T == 1 ? decode_scratch_bytes(I, k) : 0);
+    L.total = off;
+    return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+bool aligned(const void *p) { return p && (((uintptr_t)p) & 15u) == 0; }
+
+moe_status check_shape(const moe_shape *s) {
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->T < 1 || s->H < 1 || s->I < 1 || s->E < 1 || s->top_k < 1) return MOE_ERR_INVALID_ARG;
+    if (s->bits != 4 || s->group != 64) return MOE_ERR_UNSUPPORTED;
+    if (s->E != 256 || s->top_k != 8) return MOE_ERR_UNSUPPORTED;
+    if (s->H % 256 != 0 || s->H > 4096) return MOE_ERR_UNSUPPORTED;
+    if (s->I % 128 != 0 || s->I > 4096) return MOE_ERR_UNSUPPORTED;
+    if (s->T > 65536) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+bool q4_ok(const moe_q4 &p) { return aligned(p.q) && aligned(p.scale) && aligned(p.bias); }
+
+moe_status check_weights(const moe_weights *w, bool need_router, bool need_gu, bool need_down) {
+    if (!w) return MOE_ERR_INVALID_ARG;
+    if (need_router) {
+        if (!aligned(w->router_wt)) return MOE_ERR_INVALID_ARG;
+        if (w->router_bias && !aligned(w->router_bias)) return MOE_ERR_INVALID_ARG;
+    }
+    if (need_gu && !(q4_ok(w->gate) && q4_ok(w->up) && q4_ok(w->sh_gate) && q4_ok(w->sh_up)))
+        return MOE_ERR_INVALID_ARG;
+    if (need_down && !(q4_ok(w->down) && q4_ok(w->sh_down))) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_routing(const moe_routing *r) {
+    if (!r) return MOE_ERR_INVALID_ARG;
+    if (r->logits && !aligned(r->logits)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(r->topk_ids) || !aligned(r->topk_w) || !aligned(r->counts) ||
+        !aligned(r->offsets) || !aligned(r->row_token) || !aligned(r->tok_row) ||
+        !aligned(r->row_w) || !aligned(r->blocks) || !aligned(r->num_blocks))
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_shape *s, void *ws, size_t ws_bytes) {
+    const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
+    if (!ws || (((uintptr_t)ws) & 255u) != 0 || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+GemmProj gp(const moe_q4 &p) { return GemmProj{p.q, p.scale, p.bias}; }
+
+#define MOE_TRY(x)                      \
+    do {                                \
+        const moe_status st_ = (x);     \
+        if (st_ != MOE_OK) return st_;  \
+    } while (0)
+
+moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weights *w,
+                         const moe_routing *r, char *ws, hipStream_t st) {
+    const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
+    float *logits = r->logits ? r->logits : (float *)(ws + L.logits);
+    int32_t *blk_cnt = (int32_t *)(ws + L.blk_cnt);
+    int32_t *lrank = (int32_t *)(ws + L.lrank);
+    launch_router_logits(x, w->router_wt, w->router_bias, s->T, s->H, s->E, logits, st);
+    launch_group_sums(x, s->T, s->H, (float *)(ws + L.xsum), st);
+    launch_topk_local(logits, s->T, s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank, st);
+    launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, lrank, s->T, s->E, s->top_k, kBM,
+                        max_blocks_for(s->T, s->E, s->top_k), r->counts, r->offsets, r->row_token,
+                        r->tok_row, r->row_w, r->blocks, r->num_blocks, st);
+    return launched();
+}
+
+moe_status enqueue_gateup(const moe_shape *s, const uint16_t *x, const moe_weights *w,
+                          const moe_routing *r, uint16_t *h, char *ws, hipStream_t st) {
+    const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
+    launch_gateup(*s, x, (const float *)(ws + L.xsum), gp(w->gate), gp(w->up), gp(w->sh_gate),
+                  gp(w->sh_up), r->blocks, r->num_blocks, max_blocks_for(s->T, s->E, s->top_k),
+                  r->row_token, h, st);
+    return launched();
+}
+
+moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights *w,
+                        const moe_routing *r, float *y, char *ws, hipStream_t st) {
+    const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
+    float *hsum = (float *)(ws + L.hsum);
+    launch_group_sums(h, s->T * s->top_k + s->T, s->I, hsum, st);
+    launch_down(*s, h, hsum, gp(w->down), gp(w->sh_down), r->blocks, r->num_blocks,
+                max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, y, st);
+    return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_query(const moe_shape *shape, size_t *workspace_bytes, int32_t *max_blocks,
+                     int32_t *block_rows) {
+    MOE_TRY(check_shape(shape));
+    const WsLayout L = ws_layout(shape->T, shape->H, shape->I, shape->E, shape->top_k);
+    if (workspace_bytes) *workspace_bytes = L.total;
+    if (max_blocks) *max_blocks = max_blocks_for(shape->T, shape->E, shape->top_k);
+    if (block_rows) *block_rows = kBM;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                     const moe_routing *r, void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(x)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, true, false, false));
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    return enqueue_route(shape, x, w, r, (char *)ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_gemm_q4(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                              const moe_routing *r, uint16_t *h, void *ws, size_t ws_bytes,
+                              void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(x) || !aligned(h)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, false, true, false));
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    return enqueue_gateup(shape, x, w, r, h, (char *)ws, (hipStream_t)stream);
+}
+
+moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe_weights *w,
+                            const moe_routing *r, float *y, void *ws, size_t ws_bytes,
+                            void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(h) || !aligned(y)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, false, false, true));
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    return enqueue_down(shape, h, w, r, y, (char *)ws, (hipStream_t)stream);
+}
+
+moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                     const moe_routing *r, uint16_t *h, float *y, void *ws, size_t ws_bytes,
+                     void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(x) || !aligned(h) || !aligned(y)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, true, true, true));
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY(enqueue_route(shape, x, w, r, (char *)ws, st));
+    MOE_TRY(enqueue_gateup(shape, x, w, r, h, (char *)ws, st));
+    return enqueue_down(shape, h, w, r, y, (char *)ws, st);
+}
+
+moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                      int32_t *topk_ids, float *topk_w, float *y, void *ws, size_t ws_bytes,
+                      void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (shape->T != 1) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(topk_ids) || !aligned(topk_w) || !aligned(y))
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, true, true, true));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(1, shape->H, shape->I, shape->E, shape->top_k);
+    launch_decode(*shape, x, *w, topk_ids, topk_w, y, (char *)ws + L.dec, (hipStream_t)stream);
+    return launched();
+}
+
+moe_status moe_rmsnorm_residual(int32_t T, int32_t H, float eps, float *r, const float *y,
+                                uint16_t *u, void *stream) {
+    if (T < 1 || H < 4 || H % 4 != 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(r) || !aligned(y) || !aligned(u)) return MOE_ERR_INVALID_ARG;
+    launch_rmsnorm_residual(T, H, eps, r, y, u, (hipStream_t)stream);
+    return launched();
+}
+
+moe_status moe_dequant_q4(const moe_q4 *p, int32_t N, int32_t K, uint16_t *out, void *stream) {
+    if (!p || N < 1 || K < 64 || K % 64 != 0) return MOE_ERR_INVALID_ARG;
+    if (!q4_ok(*p) || !aligned(out)) return MOE_ERR_INVALID_ARG;
+    launch_dequant(gp(*p), N, K, out, (hipStream_t)stream);
+    return launched();
+}
+
+const char *moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer or bad size)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported format or shape";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Shared device helpers and internal launcher declarations of libmoeq4.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_q4.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;      // quantisation group along K
+constexpr int kBM = 128;        // rows per routing block (GEMM M tile)
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
+}
+
+// Workspace layout (byte offsets), shared by route/gemm/decode.  All host-known.
+struct WsLayout {
+    size_t logits;      // fp32 [T][E]            (used when routing.logits == NULL)
+    size_t xsum;        // fp32 [T][H/64]         group sums of x
+    size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h
+    size_t blk_cnt;     // int32 [nTB][E]         per token-block expert counts
+    size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
+    size_t dec;         // decode scratch
+    size_t total;
+};
+
+WsLayout ws_layout(int T, int H, int I, int E, int k);
+int max_blocks_for(int T, int E, int k);
+
+// ---- launchers (defined in the .hip files; all asynchronous) ----
+void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *bias, int T, int H,
+                          int E, float *logits, hipStream_t s);
+void launch_topk_local(const float *logits, int T, int E, int k, int32_t *ids, float *w,
+                       int32_t *blk_cnt, int32_t *lrank, hipStream_t s);
+void launch_scan_scatter(const int32_t *ids, const float *w, const int32_t *blk_cnt,
+                         const int32_t *lrank, int T, int E, int k, int BM, int max_blocks,
+                         int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
+                         float *row_w, int32_t *blocks, int32_t *num_blocks, hipStream_t s);
+void launch_group_sums(const uint16_t *a, int rows, int K, float *out, hipStream_t s);
+
+struct GemmProj {
+    const uint32_t *q;
+    const uint16_t *s;
+    const uint16_t *b;
+};
+
+void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum, GemmProj gate,
+                   GemmProj up, GemmProj sgate, GemmProj sup, const int32_t *blocks,
+                   const int32_t *num_blocks, int max_blocks, const int32_t *row_token,
+                   uint16_t *h, hipStream_t s);
+void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
+                 GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks, int max_blocks,
+                 const int32_t *row_token, const float *row_w, float *y, hipStream_t s);
+
+void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w, int32_t *ids,
+                   float *tw, float *y, void *scratch, hipStream_t s);
+
+void launch_rmsnorm_residual(int T, int H, float eps, float *r, const float *y, uint16_t *u,
+                             hipStream_t s);
+void launch_dequant(const GemmProj &p, int N, int K, uint16_t *out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,162 @@
+/*
+ * moe_q4.h -- C ABI of the MI355X (gfx950) mixture-of-experts layer with
+ * 4-bit affine expert weights.
+ *
+ * The layer (Lily pages: lefilia.fr article body; mechatronicstore.cl
+ * article, sections "Tres formas de carga" and "Prefill: pesos comprimidos y
+ * enrutamiento en la GPU"; neuro-ai.ru article, "Пять приёмов"):
+ *   router logits over E = 256 experts, top-8 per token, plus one shared
+ *   expert that every token uses; GPU-resident routing (expert histogram,
+ *   prefix scan, token scatter, block map) with no host synchronisation;
+ *   a grouped SwiGLU expert GEMM that reads the 4-bit weights directly and
+ *   accumulates in FP32; a routing-weighted combine.  Batch-1 decode is a
+ *   separate weight-streaming path (mechatronicstore.cl, "Decode: mover menos
+ *   bytes por token"; neuro-ai.ru, "Спекулятивное декодирование не взлетело").
+ *
+ * Conventions common to every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory)
+ *     unless marked "host".  Every pointer must be 16-byte aligned.
+ *   - bf16 values are passed as their uint16_t bit patterns.
+ *   - A 4-bit projection W[N][K] is { q, scale, bias }: q holds uint32 words
+ *     [N][K/8], code k of row n in word k/8 at bits 4*(k%8)..+3 (low nibble
+ *     first); scale and bias are bf16 [N][K/64]; w[n][k] = q*scale + bias
+ *     with group k/64.  Routed experts stack E projections: [E][N][...].
+ *     gate and up have N = I, K = H; down has N = H, K = I.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     only ENQUEUES work on `stream`; none synchronises or copies
+ *     device->host.  The caller owns every buffer; the library never
+ *     allocates, frees or caches device memory and keeps no global state,
+ *     so calls on different streams are independent.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a call that returns an error has enqueued nothing.
+ *     MOE_ERR_INVALID_ARG: NULL or misaligned pointer, T < 1, bad sizes.
+ *     MOE_ERR_UNSUPPORTED: bits != 4, group != 64, E != 256, top_k != 8,
+ *       H not a multiple of 256 or above 4096, I not a multiple of 128 or
+ *       above 4096, T > 65536 (the checkpoint-format validation that
+ *       refuses every other format).
+ *     MOE_ERR_WORKSPACE: workspace NULL, not 256-byte aligned, or smaller
+ *       than moe_query reports.
+ *     MOE_ERR_HIP: a launch failed (hipGetLastError after the launch).
+ */
+#ifndef MOE_Q4_H
+#define MOE_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,
+    MOE_ERR_UNSUPPORTED = -2,
+    MOE_ERR_WORKSPACE = -3,
+    MOE_ERR_HIP = -4
+} moe_status;
+
+/* host struct; group must be 64 and bits 4 */
+typedef struct {
+    int32_t T, H, I, E, top_k, group, bits;
+} moe_shape;
+
+/* one 4-bit projection (device pointers) */
+typedef struct {
+    const uint32_t *q;
+    const uint16_t *scale;
+    const uint16_t *bias;
+} moe_q4;
+
+/* the layer's weights (host struct holding device pointers) */
+typedef struct {
+    moe_q4 gate, up, down;          /* routed experts, stacked [E][...]      */
+    moe_q4 sh_gate, sh_up, sh_down; /* the shared expert                     */
+    const uint16_t *router_wt;      /* bf16 [E][H]: router weight, row/expert */
+    const float *router_bias;       /* fp32 [E] additive logit bias, or NULL  */
+} moe_weights;
+
+/* Routing outputs (host struct holding device pointers).  Row r of the
+ * routed part of h is one (token, pick) pair; rows are ordered by expert,
+ * then token.  row_w[r] is the routing weight of row r.  blocks[b] =
+ * {expert, first row, row count} tiles the rows of each expert in blocks of
+ * at most block_rows rows (moe_query); *num_blocks stays on the device. */
+typedef struct {
+    float *logits;      /* fp32 [T][E] router logits, or NULL (then kept in ws) */
+    int32_t *topk_ids;  /* [T][top_k], by logit descending, index ascending    */
+    float *topk_w;      /* [T][top_k], softmax restricted to the picks          */
+    int32_t *counts;    /* [E]                                                   */
+    int32_t *offsets;   /* [E+1], exclusive scan of counts, offsets[E] = T*top_k */
+    int32_t *row_token; /* [T*top_k]                                             */
+    int32_t *tok_row;   /* [T][top_k]                                            */
+    float *row_w;       /* [T*top_k]                                             */
+    int32_t *blocks;    /* [max_blocks][3]                                        */
+    int32_t *num_blocks;/* [1]                                                    */
+} moe_routing;
+
+/* Host only.  Workspace bytes needed by every call below for `shape`, the
+ * capacity max_blocks of routing.blocks, and the rows per block (BM). */
+moe_status moe_query(const moe_shape *shape, size_t *workspace_bytes, int32_t *max_blocks,
+                     int32_t *block_rows);
+
+/* Router and routing (the pages' "histogram, prefix scan, scatter and block
+ * map in one GPU command buffer", mechatronicstore.cl "Prefill: ...").
+ * x: bf16 [T][H].  Logits are float32 in a fixed order (within each chunk
+ * of 64 inputs a sequential sum from the chunk's first product, then a
+ * sequential sum over chunks, then + bias), so routing is reproducible bit
+ * for bit.  Also fills the workspace's group sums of x used by
+ * moe_expert_gemm_q4. */
+moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                     const moe_routing *r, void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped gate/up GEMM over the routed rows and the shared expert, reading
+ * 4-bit codes directly (mechatronicstore.cl "Prefill: ...": weights rebuilt
+ * tile by tile inside the grouped GEMM, FP32 accumulation), with the SwiGLU
+ * epilogue h = silu(W_gate x) * (W_up x).
+ * h: bf16 [T*top_k + T][I]; rows 0..T*top_k-1 follow routing order, row
+ * T*top_k + t is the shared expert of token t.  Needs moe_route's outputs
+ * and workspace. */
+moe_status moe_expert_gemm_q4(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                              const moe_routing *r, uint16_t *h, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* Down GEMM plus routing-weighted combine:
+ * y[t] = sum_j topk_w[t][j] * W_down[ids[t][j]] h[tok_row[t][j]] + W_sh_down h[T*top_k + t].
+ * y: fp32 [T][H] (overwritten).  Summation order of the eight routed terms
+ * is not fixed (device atomics), so y is reproducible to rounding only. */
+moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe_weights *w,
+                            const moe_routing *r, float *y, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* The whole layer: moe_route, moe_expert_gemm_q4, moe_down_combine. */
+moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                     const moe_routing *r, uint16_t *h, float *y, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Batch-1 decode (T must be 1): router, top-8 and weights, then the eight
+ * routed experts and the shared expert as weight-streaming GEMVs that read
+ * only the selected experts' packed weights (mechatronicstore.cl "Decode:
+ * mover menos bytes por token"; neuro-ai.ru "Спекулятивное ...": batch-1
+ * decode is bound by weight bandwidth).  topk_ids [top_k], topk_w [top_k],
+ * y fp32 [H] (overwritten). */
+moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                      int32_t *topk_ids, float *topk_w, float *y, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Between stacked layers: r <- r + y (fp32), u = bf16(r / sqrt(mean(r^2) + eps))
+ * (unit RMSNorm weight).  r, y: fp32 [T][H]; u: bf16 [T][H]. */
+moe_status moe_rmsnorm_residual(int32_t T, int32_t H, float eps, float *r, const float *y,
+                                uint16_t *u, void *stream);
+
+/* Test hook: dequantise one projection to bf16, out[n][k] =
+ * bf16_round_nearest_even(fp32 fma(code, scale, bias)).  out: bf16 [N][K]. */
+moe_status moe_dequant_q4(const moe_q4 *p, int32_t N, int32_t K, uint16_t *out, void *stream);
+
+/* Static string for a status code. */
+const char *moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_Q4_H */

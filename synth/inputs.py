@@ -13,8 +13,9 @@ PACK = 8            # 4-bit codes per uint32 word
 def f32_to_bf16_bits(a) -> np.ndarray:
     """Round float32 values to bf16 (round to nearest, ties to even); return uint16 bits."""
     f = np.ascontiguousarray(a, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    # finite inputs only: u + 0x8000 cannot wrap below 0xFF800000
+    u = (u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16
     return u.astype(np.uint16)
 
 

@@ -1,0 +1,88 @@
+"""Helpers shared by the GPU tests: upload a synthetic layer and run the C ABI."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import bit_quantized_expert_top_amd as moe
+
+TOL = 2e-2     # max |y - y_oracle| <= TOL * RMS(y_oracle)
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def shape_of(inp) -> moe.Shape:
+    return moe.Shape(T=inp.T, H=inp.H, I=inp.I, E=inp.E, top_k=inp.top_k)
+
+
+def upload(inp, dev=None) -> moe.DeviceLayer:
+    dev = dev or device()
+    proj = {n: (getattr(inp, n).q, getattr(inp, n).scale, getattr(inp, n).bias)
+            for n in moe.DeviceLayer.NAMES}
+    return moe.DeviceLayer(proj, inp.router_wt, inp.router_bias, device=dev)
+
+
+def x_dev(inp, dev=None):
+    return torch.from_numpy(inp.x).view(torch.int16).to(dev or device())
+
+
+class LayerRun:
+    """Buffers and results of one moe_layer call."""
+
+    def __init__(self, inp, w: moe.DeviceLayer = None, dev=None):
+        dev = dev or device()
+        self.inp = inp
+        self.shape = shape_of(inp)
+        self.w = w or upload(inp, dev)
+        self.x = x_dev(inp, dev)
+        self.r = moe.Routing(self.shape, dev)
+        self.ws = moe.workspace(self.shape, dev)
+        rows = inp.T * inp.top_k + inp.T
+        self.h = torch.zeros((rows, inp.I), dtype=torch.int16, device=dev)
+        self.y = torch.zeros((inp.T, inp.H), dtype=torch.float32, device=dev)
+
+    def route(self):
+        moe.moe_route(self.shape, self.x, self.w, self.r, self.ws)
+        return self
+
+    def gemm(self):
+        moe.moe_expert_gemm_q4(self.shape, self.x, self.w, self.r, self.h, self.ws)
+        return self
+
+    def down(self):
+        moe.moe_down_combine(self.shape, self.h, self.w, self.r, self.y, self.ws)
+        return self
+
+    def layer(self):
+        moe.moe_layer(self.shape, self.x, self.w, self.r, self.h, self.y, self.ws)
+        return self
+
+    def sync(self):
+        torch.cuda.synchronize()
+        return self
+
+    def routing_np(self):
+        r = self.r
+        nb = int(r.num_blocks.cpu()[0])
+        return dict(logits=r.logits.cpu().numpy(), ids=r.topk_ids.cpu().numpy(),
+                    w=r.topk_w.cpu().numpy(), counts=r.counts.cpu().numpy(),
+                    offsets=r.offsets.cpu().numpy(), row_token=r.row_token.cpu().numpy(),
+                    tok_row=r.tok_row.cpu().numpy(), row_w=r.row_w.cpu().numpy(),
+                    blocks=r.blocks.cpu().numpy()[:nb], num_blocks=nb)
+
+
+def bf16_np(t: torch.Tensor) -> np.ndarray:
+    """int16/bf16 device tensor of bf16 bits -> float32 numpy."""
+    u = t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32)
+
+
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float = TOL):
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    err = float(np.max(np.abs(y_gpu.astype(np.float64) - y_ref)))
+    assert np.all(np.isfinite(y_gpu)), "non-finite output"
+    assert err <= tol * rms, f"max err {err:.4g} > {tol} * rms {rms:.4g} (ratio {err / rms:.4g})"
+    return err / rms

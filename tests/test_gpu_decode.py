@@ -1,0 +1,55 @@
+"""Batch-1 decode path against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_expert_top_amd as moe
+import oracle
+from synth import make_layer
+from moe_case import LayerRun, check_y, device, shape_of, upload, x_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(inp, w=None):
+    dev = device()
+    w = w or upload(inp, dev)
+    sh = shape_of(inp)
+    ids = torch.empty(inp.top_k, dtype=torch.int32, device=dev)
+    tw = torch.empty(inp.top_k, dtype=torch.float32, device=dev)
+    y = torch.empty(inp.H, dtype=torch.float32, device=dev)
+    ws = moe.workspace(sh, dev)
+    moe.moe_decode(sh, x_dev(inp, dev), w, ids, tw, y, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), tw.cpu().numpy(), y.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed", [2000, 2001, 2002, 2003])
+def test_decode_matches_oracle(seed):
+    print(f"[decode] seed={seed}", flush=True)
+    inp = make_layer(seed, T=1, H=2048, I=512)
+    ids, tw, y = run_decode(inp)
+    y_ref, ids_ref, w_ref = oracle.Layer(inp).tokens([0])
+    np.testing.assert_array_equal(ids, ids_ref[0])
+    np.testing.assert_allclose(tw, w_ref[0], rtol=2e-6, atol=2e-7)
+    ratio = check_y(y[None, :], y_ref)
+    print(f"  max err / rms = {ratio:.4g}", flush=True)
+
+
+def test_decode_tiny_and_zipf():
+    for kw, seed in ((dict(T=1, H=512, I=128), 1030), (dict(T=1, H=2048, I=512, zipf_s=1.1), 4010)):
+        inp = make_layer(seed, **kw)
+        ids, tw, y = run_decode(inp)
+        y_ref, ids_ref, _ = oracle.Layer(inp).tokens([0])
+        np.testing.assert_array_equal(ids, ids_ref[0])
+        check_y(y[None, :], y_ref)
+
+
+def test_decode_equals_prefill_path_at_t1():
+    inp = make_layer(2005, T=1, H=2048, I=512)
+    w = upload(inp)
+    ids, tw, y = run_decode(inp, w)
+    run = LayerRun(inp, w=w).layer().sync()
+    np.testing.assert_array_equal(run.r.topk_ids.cpu().numpy()[0], ids)
+    y2 = run.y.cpu().numpy()[0]
+    assert np.max(np.abs(y2 - y)) <= 1e-2 * np.sqrt(np.mean(y ** 2))

@@ -1,0 +1,107 @@
+"""The whole layer (route -> gate/up GEMM -> down + combine) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_layer
+from moe_case import LayerRun, bf16_np, check_y
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_tokens(T, n, seed):
+    if T <= n:
+        return list(range(T))
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=n - 3, replace=False).tolist()) | {0, T - 1, T // 2}
+    return sorted(pick)
+
+
+CASES = [
+    ("tiny", dict(T=32, H=512, I=128), 1000, 32),
+    ("tiny_zipf", dict(T=32, H=512, I=128, zipf_s=1.1), 1001, 32),
+    ("ragged129", dict(T=129, H=512, I=128, zipf_s=1.1), 1003, 129),
+    ("T1_prefill_path", dict(T=1, H=2048, I=512), 2001, 1),
+    ("prefill512", dict(T=512, H=2048, I=512), 3000, 40),
+    ("prefill2048_zipf", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4000, 40),
+]
+
+
+@pytest.mark.parametrize("name,kw,seed,nsamp", CASES, ids=[c[0] for c in CASES])
+def test_layer_matches_oracle(name, kw, seed, nsamp):
+    print(f"[layer] {name} seed={seed} {kw}", flush=True)
+    inp = make_layer(seed, **kw)
+    run = LayerRun(inp).layer().sync()
+    y = run.y.cpu().numpy()
+    toks = sample_tokens(inp.T, nsamp, seed)
+    y_ref, ids_ref, _ = oracle.Layer(inp).tokens(toks)
+    got = run.routing_np()
+    np.testing.assert_array_equal(got["ids"][toks], ids_ref)
+    ratio = check_y(y[toks], y_ref)
+    print(f"  max err / rms = {ratio:.4g}", flush=True)
+
+
+def test_hidden_rows_match_oracle():
+    """h rows (SwiGLU activations) of routed and shared rows against the oracle's.
+
+    h is stored in bf16, so each element may differ from the float64 value by
+    half a bf16 ulp (at most 2^-8 relative); the fp32 arithmetic before the
+    rounding adds at most a small fraction of the row's RMS."""
+    inp = make_layer(4000, T=2048, H=2048, I=512, zipf_s=1.1)
+    run = LayerRun(inp).route().gemm().sync()
+    got = run.routing_np()
+    h = bf16_np(run.h)
+    L = oracle.Layer(inp)
+    T, k = inp.T, inp.top_k
+    rng = np.random.default_rng(5)
+    checks = [(int(t), int(j)) for t, j in zip(rng.integers(0, T, 12), rng.integers(0, k, 12))]
+    for t, j in checks:
+        e = int(got["ids"][t, j])
+        a = L.expert_act(e, t)
+        r = int(got["tok_row"][t, j])
+        bound = 2.0 ** -8 * np.abs(a) + 1e-3 * np.sqrt(np.mean(a ** 2))
+        assert np.all(np.abs(h[r] - a) <= bound), (t, j, e, np.max(np.abs(h[r] - a) - bound))
+    for t in (0, 1000, T - 1):
+        a = L.expert_act(inp.E, t)
+        bound = 2.0 ** -8 * np.abs(a) + 1e-3 * np.sqrt(np.mean(a ** 2))
+        assert np.all(np.abs(h[T * k + t] - a) <= bound), t
+
+
+def test_layer_zero_experts_and_single_live_expert():
+    inp = make_layer(1020, T=64, H=512, I=128)
+    for p in (inp.gate, inp.up, inp.down):
+        p.q[...] = np.uint32(0x88888888)           # code 8 with bias -8*scale: zero weight
+    live = 5
+    rng = np.random.default_rng(3)
+    for p in (inp.gate, inp.up, inp.down):
+        p.q[live] = rng.integers(0, 2 ** 32, size=p.q[live].shape, dtype=np.uint32)
+    run = LayerRun(inp).layer().sync()
+    y_ref, _, _ = oracle.Layer(inp).tokens(range(inp.T))
+    check_y(run.y.cpu().numpy(), y_ref)
+
+
+def test_layer_all_tokens_one_expert_set():
+    """Every token on the same 8 experts: 8 groups of T rows, blocks of exactly 128 and a ragged tail."""
+    inp = make_layer(1021, T=300, H=512, I=128)
+    inp.router_bias = np.zeros(inp.E, np.float32)
+    inp.router_bias[[3, 50, 99, 120, 180, 201, 230, 255]] = 50.0
+    run = LayerRun(inp).layer().sync()
+    got = run.routing_np()
+    assert got["num_blocks"] == 8 * 3
+    toks = sample_tokens(inp.T, 60, 1)
+    y_ref, _, _ = oracle.Layer(inp).tokens(toks)
+    check_y(run.y.cpu().numpy()[toks], y_ref)
+
+
+def test_layer_repeat_stable():
+    """Two runs agree to rounding (the routed combine uses device atomics)."""
+    inp = make_layer(3001, T=512, H=2048, I=512)
+    run = LayerRun(inp)
+    run.layer().sync()
+    y1 = run.y.clone()
+    h1 = run.h.clone()
+    run.layer().sync()
+    assert torch.equal(run.h, h1)
+    d = (run.y - y1).abs().max().item()
+    assert d <= 1e-5 * y1.abs().max().item()

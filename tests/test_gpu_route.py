@@ -1,0 +1,74 @@
+"""GPU routing vs the oracle: logits, ids, counts, offsets, scatter and block map bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_layer
+from moe_case import LayerRun
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("tiny", dict(T=32, H=512, I=128), 1000),
+    ("tiny_zipf", dict(T=32, H=512, I=128, zipf_s=1.1), 1001),
+    ("ragged33", dict(T=33, H=512, I=128), 1002),
+    ("ragged129", dict(T=129, H=512, I=128, zipf_s=1.1), 1003),
+    ("decode_shape", dict(T=1, H=2048, I=512), 2000),
+    ("prefill512", dict(T=512, H=2048, I=512), 3000),
+    ("prefill2048_zipf", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4000),
+    ("prefill2048_zipf_s1", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4001),
+]
+
+
+def compare_routing(inp, got):
+    l_ref = oracle.router_logits(inp.x, inp.router_wt, inp.router_bias)
+    np.testing.assert_array_equal(got["logits"].view(np.uint32), l_ref.view(np.uint32))
+    ids_ref, w_ref = oracle.topk(l_ref, inp.top_k)
+    np.testing.assert_array_equal(got["ids"], ids_ref)
+    # weights: float32 on the GPU, float64 in the oracle
+    np.testing.assert_allclose(got["w"], w_ref, rtol=2e-6, atol=2e-7)
+    assert np.all(np.abs(got["w"].astype(np.float64).sum(axis=1) - 1.0) <= 1e-6)
+    _, _, BM = 0, 0, 128
+    ref = oracle.routing(ids_ref, inp.E, BM)
+    for key in ("counts", "offsets", "row_token", "tok_row"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    assert got["num_blocks"] == ref["num_blocks"]
+    np.testing.assert_array_equal(got["blocks"], ref["blocks"])
+    # row weights are the pick weights moved to their rows, bit for bit
+    np.testing.assert_array_equal(got["row_w"][got["tok_row"].ravel()], got["w"].ravel())
+
+
+@pytest.mark.parametrize("name,kw,seed", CASES, ids=[c[0] for c in CASES])
+def test_route_matches_oracle(name, kw, seed):
+    print(f"[route] {name} seed={seed} {kw}", flush=True)
+    inp = make_layer(seed, **kw)
+    run = LayerRun(inp).route().sync()
+    compare_routing(inp, run.routing_np())
+
+
+def test_route_forced_ties_and_hot_experts():
+    """Duplicate router rows (exact ties) and a bias that sends every token to experts 0..7."""
+    inp = make_layer(1010, T=100, H=512, I=128)
+    inp.router_wt[7] = inp.router_wt[200]        # experts 7 and 200 always tie
+    inp.router_wt[3] = inp.router_wt[4]
+    inp.router_bias = np.zeros(inp.E, np.float32)
+    inp.router_bias[:8] = 40.0
+    run = LayerRun(inp).route().sync()
+    got = run.routing_np()
+    compare_routing(inp, got)
+    assert set(np.unique(got["ids"]).tolist()) == set(range(8))
+    assert got["num_blocks"] == 8
+
+
+def test_route_deterministic_repeats():
+    inp = make_layer(4002, T=2048, H=2048, I=512, zipf_s=1.1)
+    run = LayerRun(inp)
+    first = None
+    for _ in range(5):
+        run.route().sync()
+        got = run.routing_np()
+        if first is None:
+            first = got
+            continue
+        for k in ("logits", "ids", "w", "row_token", "tok_row", "blocks", "counts"):
+            np.testing.assert_array_equal(got[k], first[k])
