@@ -27,7 +27,9 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     const size_t nTB = (size_t)(T + 63) / 64;
     L.logits = take((size_t)T * E * 4);
     L.xsum = take((size_t)T * (H / 64) * 4);
+    L.xp = take((size_t)T * H * 2);
     L.hsum = take((size_t)(T * k + T) * (I / 64) * 4);
+    L.stage = take((size_t)T * k * H * 4);
     L.blk_cnt = take(nTB * E * 4);
     L.lrank = take((size_t)T * k * 4);
     L.dec = take(T == 1 ? decode_scratch_bytes(I, k) : 0);
@@ -48,8 +50,8 @@ moe_status check_shape(const moe_shape *s) {
     if (s->T < 1 || s->H < 1 || s->I < 1 || s->E < 1 || s->top_k < 1) return MOE_ERR_INVALID_ARG;
     if (s->bits != 4 || s->group != 64) return MOE_ERR_UNSUPPORTED;
     if (s->E != 256 || s->top_k != 8) return MOE_ERR_UNSUPPORTED;
-    if (s->H % 256 != 0 || s->H > 4096) return MOE_ERR_UNSUPPORTED;
-    if (s->I % 128 != 0 || s->I > 4096) return MOE_ERR_UNSUPPORTED;
+    if (s->H % 256 != 0 || s->H > 2048) return MOE_ERR_UNSUPPORTED;
+    if (s->I % 128 != 0 || s->I > 2048) return MOE_ERR_UNSUPPORTED;
     if (s->T > 65536) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -101,7 +103,7 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
     int32_t *blk_cnt = (int32_t *)(ws + L.blk_cnt);
     int32_t *lrank = (int32_t *)(ws + L.lrank);
     launch_router_logits(x, w->router_wt, w->router_bias, s->T, s->H, s->E, logits, st);
-    launch_group_sums(x, s->T, s->H, (float *)(ws + L.xsum), st);
+    launch_prep_act(x, s->T, s->H, (uint16_t *)(ws + L.xp), (float *)(ws + L.xsum), st);
     launch_topk_local(logits, s->T, s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank, st);
     launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, lrank, s->T, s->E, s->top_k, kBM,
                         max_blocks_for(s->T, s->E, s->top_k), r->counts, r->offsets, r->row_token,
@@ -112,7 +114,8 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
 moe_status enqueue_gateup(const moe_shape *s, const uint16_t *x, const moe_weights *w,
                           const moe_routing *r, uint16_t *h, char *ws, hipStream_t st) {
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
-    launch_gateup(*s, x, (const float *)(ws + L.xsum), gp(w->gate), gp(w->up), gp(w->sh_gate),
+    (void)x;
+    launch_gateup(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum), gp(w->gate), gp(w->up), gp(w->sh_gate),
                   gp(w->sh_up), r->blocks, r->num_blocks, max_blocks_for(s->T, s->E, s->top_k),
                   r->row_token, h, st);
     return launched();
@@ -124,7 +127,8 @@ moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights
     float *hsum = (float *)(ws + L.hsum);
     launch_group_sums(h, s->T * s->top_k + s->T, s->I, hsum, st);
     launch_down(*s, h, hsum, gp(w->down), gp(w->sh_down), r->blocks, r->num_blocks,
-                max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, y, st);
+                max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
+                (float *)(ws + L.stage), y, st);
     return launched();
 }
 

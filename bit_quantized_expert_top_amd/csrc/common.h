@@ -35,11 +35,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
+// Activations enter the GEMMs with every 8-column block stored in the order
+// (0,4,1,5,2,6,3,7), matching the pair order in which 4-bit codes unpack.
+// Position of column `col` in that storage.
+__host__ __device__ __forceinline__ int perm_pos(int col) {
+    const int p = col & 7;
+    return (col & ~7) | ((p & 3) << 1) | (p >> 2);
+}
+
 // Workspace layout (byte offsets), shared by route/gemm/decode.  All host-known.
 struct WsLayout {
     size_t logits;      // fp32 [T][E]            (used when routing.logits == NULL)
     size_t xsum;        // fp32 [T][H/64]         group sums of x
+    size_t xp;          // bf16 [T][H]            x with 8-blocks in the permuted order
     size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h
+    size_t stage;       // fp32 [T*k][H]          routed down outputs times routing weight
     size_t blk_cnt;     // int32 [nTB][E]         per token-block expert counts
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
     size_t dec;         // decode scratch
@@ -59,6 +69,7 @@ void launch_scan_scatter(const int32_t *ids, const float *w, const int32_t *blk_
                          int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
                          float *row_w, int32_t *blocks, int32_t *num_blocks, hipStream_t s);
 void launch_group_sums(const uint16_t *a, int rows, int K, float *out, hipStream_t s);
+void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, hipStream_t s);
 
 struct GemmProj {
     const uint32_t *q;
@@ -72,7 +83,8 @@ void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum, Ge
                    uint16_t *h, hipStream_t s);
 void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
                  GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks, int max_blocks,
-                 const int32_t *row_token, const float *row_w, float *y, hipStream_t s);
+                 const int32_t *row_token, const float *row_w, const int32_t *tok_row,
+                 float *stage, float *y, hipStream_t s);
 
 void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w, int32_t *ids,
                    float *tw, float *y, void *scratch, hipStream_t s);

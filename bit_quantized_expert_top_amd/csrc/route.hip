@@ -325,6 +325,40 @@ __global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *__restr
     out[i] = s;
 }
 
+// Activation preparation for the GEMM: the 8-block permutation (0,4,1,5,2,6,3,7)
+// of every row plus the group sums, one thread per (row, group of 64).
+__global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restrict__ x, int rows,
+                                                       int K, uint16_t *__restrict__ xp,
+                                                       float *__restrict__ out) {
+    const int G = K / 64;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)rows * G) return;
+    const size_t r = i / G, g = i % G;
+    const u32x4 *p = (const u32x4 *)(x + r * K + g * 64);
+    u32x4 *q = (u32x4 *)(xp + r * K + g * 64);
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const u32x4 v = p[j];
+        s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
+             bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+        u32x4 o;
+        o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+        o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+        o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+        o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+        q[j] = o;
+    }
+    out[i] = s;
+}
+
+void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, hipStream_t s) {
+    const size_t n = (size_t)rows * (K / 64);
+    if (n == 0) return;
+    hipLaunchKernelGGL(prep_act_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, rows,
+                       K, xp, xsum);
+}
+
 void launch_group_sums(const uint16_t *a, int rows, int K, float *out, hipStream_t s) {
     const size_t n = (size_t)rows * (K / 64);
     if (n == 0) return;

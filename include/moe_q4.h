@@ -31,8 +31,8 @@
  *     enqueued; a call that returns an error has enqueued nothing.
  *     MOE_ERR_INVALID_ARG: NULL or misaligned pointer, T < 1, bad sizes.
  *     MOE_ERR_UNSUPPORTED: bits != 4, group != 64, E != 256, top_k != 8,
- *       H not a multiple of 256 or above 4096, I not a multiple of 128 or
- *       above 4096, T > 65536 (the checkpoint-format validation that
+ *       H not a multiple of 256 or above 2048, I not a multiple of 128 or
+ *       above 2048, T > 65536 (the checkpoint-format validation that
  *       refuses every other format).
  *     MOE_ERR_WORKSPACE: workspace NULL, not 256-byte aligned, or smaller
  *       than moe_query reports.
@@ -114,16 +114,19 @@ moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weight
  * tile by tile inside the grouped GEMM, FP32 accumulation), with the SwiGLU
  * epilogue h = silu(W_gate x) * (W_up x).
  * h: bf16 [T*top_k + T][I]; rows 0..T*top_k-1 follow routing order, row
- * T*top_k + t is the shared expert of token t.  Needs moe_route's outputs
- * and workspace. */
+ * T*top_k + t is the shared expert of token t.  Within each row, every block
+ * of 8 consecutive columns is stored in the order 0,4,1,5,2,6,3,7 (the
+ * order in which the down GEMM consumes it).  Needs moe_route's outputs and
+ * workspace. */
 moe_status moe_expert_gemm_q4(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                               const moe_routing *r, uint16_t *h, void *ws, size_t ws_bytes,
                               void *stream);
 
 /* Down GEMM plus routing-weighted combine:
  * y[t] = sum_j topk_w[t][j] * W_down[ids[t][j]] h[tok_row[t][j]] + W_sh_down h[T*top_k + t].
- * y: fp32 [T][H] (overwritten).  Summation order of the eight routed terms
- * is not fixed (device atomics), so y is reproducible to rounding only. */
+ * y: fp32 [T][H] (overwritten).  Each routed row's weighted output goes to a
+ * workspace staging row and every token then adds its eight rows in pick
+ * order, so y is reproducible bit for bit. */
 moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe_weights *w,
                             const moe_routing *r, float *y, void *ws, size_t ws_bytes,
                             void *stream);

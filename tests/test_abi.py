@@ -60,7 +60,7 @@ def test_query_sizes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(bits=8), UNSUP), (dict(group=32), UNSUP), (dict(E=128), UNSUP), (dict(top_k=4), UNSUP),
-    (dict(H=2048 + 64), UNSUP), (dict(I=512 + 64), UNSUP), (dict(H=8192), UNSUP),
+    (dict(H=2048 + 64), UNSUP), (dict(I=512 + 64), UNSUP), (dict(H=4096), UNSUP), (dict(I=4096), UNSUP),
     (dict(T=0), INVALID), (dict(T=-3), INVALID), (dict(T=70000), UNSUP), (dict(I=0), INVALID),
 ])
 def test_query_rejects(kw, code):
