@@ -48,9 +48,12 @@ struct WsLayout {
     size_t logits;      // fp32 [T][E]            (used when routing.logits == NULL)
     size_t xsum;        // fp32 [T][H/64]         group sums of x
     size_t xp;          // bf16 [T][H]            x with 8-blocks in the permuted order
+    size_t xsq;         // fp32 [T][H/64]         group sums of x^2
+    size_t part;        // fp32 [4][T][E]         K-split approximate router logits
+    size_t wn2;         // fp32 [E]               squared norms of the router rows
     size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h
     size_t stage;       // fp32 [T*k][H]          routed down outputs times routing weight
-    size_t blk_cnt;     // int32 [nTB][E]         per token-block expert counts
+    size_t blk_cnt;     // int32 [T/16][E]        per token-block expert counts / bases
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
     size_t dec;         // decode scratch
     size_t total;
@@ -62,14 +65,19 @@ int max_blocks_for(int T, int E, int k);
 // ---- launchers (defined in the .hip files; all asynchronous) ----
 void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *bias, int T, int H,
                           int E, float *logits, hipStream_t s);
-void launch_topk_local(const float *logits, int T, int E, int k, int32_t *ids, float *w,
-                       int32_t *blk_cnt, int32_t *lrank, hipStream_t s);
-void launch_scan_scatter(const int32_t *ids, const float *w, const int32_t *blk_cnt,
-                         const int32_t *lrank, int T, int E, int k, int BM, int max_blocks,
-                         int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
-                         float *row_w, int32_t *blocks, int32_t *num_blocks, hipStream_t s);
+void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
+                        float *wn2, hipStream_t s);
+void launch_route_select(const float *part, const float *exact, const float *xsq,
+                         const float *wn2, const float *bias, const uint16_t *x,
+                         const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,
+                         int32_t *blk_cnt, int32_t *lrank, hipStream_t s);
+void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
+                         const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
+                         int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
+                         int32_t *blocks, int32_t *num_blocks, hipStream_t s);
 void launch_group_sums(const uint16_t *a, int rows, int K, float *out, hipStream_t s);
-void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, hipStream_t s);
+void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
+                     hipStream_t s);
 
 struct GemmProj {
     const uint32_t *q;

@@ -106,15 +106,25 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
                    float *tw, float *y, void *scratch, hipStream_t s) {
     const int H = sh.H, I = sh.I, E = sh.E, k = sh.top_k;
     char *p = (char *)scratch;
-    float *logits = (float *)p;
+    float *part = (float *)p;           // [4][1][E]
     p += 4096;
-    int32_t *blk_cnt = (int32_t *)p;
-    p += 4096;
-    int32_t *lrank = (int32_t *)p;
-    p += 4096;
-    float *hbuf = (float *)p;
-    launch_router_logits(x, w.router_wt, w.router_bias, 1, H, E, logits, s);
-    launch_topk_local(logits, 1, E, k, ids, tw, blk_cnt, lrank, s);
+    float *wn2 = (float *)p;            // [E]
+    p += 1024;
+    float *xsum = (float *)p;           // [H/64]
+    p += 256;
+    float *xsq = (float *)p;            // [H/64]
+    p += 256;
+    int32_t *blk_cnt = (int32_t *)p;    // [1][E]
+    p += 1024;
+    int32_t *lrank = (int32_t *)p;      // [k]
+    p += 256;
+    uint16_t *xp = (uint16_t *)p;       // [H]
+    p += 2 * 2048;
+    float *hbuf = (float *)p;           // [k+1][I]
+    launch_prep_act(x, 1, H, xp, xsum, xsq, s);
+    launch_router_fast(x, w.router_wt, 1, H, E, part, wn2, s);
+    launch_route_select(part, nullptr, xsq, wn2, w.router_bias, x, w.router_wt, 1, H, E, k, ids,
+                        tw, blk_cnt, lrank, s);
     const GemmProj gate{w.gate.q, w.gate.scale, w.gate.bias}, up{w.up.q, w.up.scale, w.up.bias};
     const GemmProj sgate{w.sh_gate.q, w.sh_gate.scale, w.sh_gate.bias};
     const GemmProj sup{w.sh_up.q, w.sh_up.scale, w.sh_up.bias};
@@ -127,6 +137,6 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
                        tw, k, down, sdown, y);
 }
 
-size_t decode_scratch_bytes(int I, int k) { return 3 * 4096 + (size_t)(k + 1) * I * 4; }
+size_t decode_scratch_bytes(int I, int k) { return 16384 + (size_t)(k + 1) * I * 4; }
 
 }  // namespace moe

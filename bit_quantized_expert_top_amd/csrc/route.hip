@@ -116,19 +116,32 @@ void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *
 }
 
 // ---------------------------------------------------------------------------
-// Top-k per token (one wave per token) and the per-token-block half of the
-// routing: each workgroup takes 64 consecutive tokens, records for every
-// expert the set of its tokens that picked it as a 64-bit lane mask in LDS
-// (an OR is order independent, so the masks are deterministic), and from
-// the masks writes the block's expert histogram and the rank of each
-// (token, pick) among the block's tokens of that expert (popcount of the
-// lower mask bits).  Ranks in token order make the scatter stable.
+// Fast certified routing.
+//
+// 1. router_mfma: approximate logits on the matrix cores, split over K into S
+//    partial sums (each 64-wide chunk is one 4-step MFMA chain from zero,
+//    chunks added in fp32).  Whatever order or rounding the hardware uses
+//    inside a chain, |approx - exact| <= (2*63 + 32) u (sum|x_k w_k| + |b|)
+//    with u = 2^-24, and the fixed-order logit is within 95 u of the same
+//    quantity, so every approximate logit lies within
+//        delta = 2^-16 (||x|| ||w|| + |b|)  (+ a denormal guard)
+//    of the fixed-order logit (Cauchy-Schwarz bounds sum|x_k w_k|).
+// 2. route_select (one wave per token): the top-8 by approximate logits is
+//    accepted as is when the 8 intervals are disjoint and no other expert's
+//    interval reaches the lowest of them; otherwise the fixed-order logits of
+//    every candidate that might belong to the top-8 are recomputed exactly
+//    (same order as router_logits) and the top-8 is taken from those.  Either
+//    way the ids equal those of the fixed-order logits, bit for bit.
 // ---------------------------------------------------------------------------
-constexpr int TB = 64;   // tokens per routing block
+constexpr int TB = 16;            // tokens per routing block (one wave each)
+constexpr int RS_SPLIT = 4;       // K splits of the approximate router
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
     uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 ranks with +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t kh) {
+    return __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
@@ -141,166 +154,386 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
-__global__ __launch_bounds__(256) void topk_local_kernel(const float *__restrict__ logits, int T,
-                                                         int E, int k, int32_t *__restrict__ ids,
-                                                         float *__restrict__ tw,
-                                                         int32_t *__restrict__ blk_cnt,
-                                                         int32_t *__restrict__ lrank) {
-    __shared__ unsigned long long mask[256];
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// squared L2 norm of each router row (one wave per expert)
+__global__ __launch_bounds__(256) void wnorm_kernel(const uint16_t *__restrict__ wr, int E, int H,
+                                                    float *__restrict__ wn2) {
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (e >= E) return;
+    float s = 0.0f;
+    for (int k = lane * 8; k < H; k += 512) {
+        const u32x4 v = *(const u32x4 *)(wr + (size_t)e * H + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = bf16_lo(v[q]), b = bf16_hi(v[q]);
+            s = __builtin_fmaf(a, a, s);
+            s = __builtin_fmaf(b, b, s);
+        }
+    }
+    s = wave_sum_f(s);
+    if (lane == 0) wn2[e] = s;
+}
+
+// approximate logits (no bias), partial over K range s: part[s][t][e]
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ wr, int T,
+                                                          int H, int E, int S,
+                                                          float *__restrict__ part) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l32 = lane & 31, gg = lane >> 5;
+    const int t0 = blockIdx.x * 64 + 32 * (wave & 1), e0 = blockIdx.y * 64 + 32 * (wave >> 1);
+    const int sp = blockIdx.z, klen = H / S, kbeg = sp * klen;
+    const int trow = min(t0 + l32, T - 1);
+    const uint16_t *pa = x + (size_t)trow * H + kbeg + 8 * gg;
+    const uint16_t *pb = wr + (size_t)(e0 + l32) * H + kbeg + 8 * gg;
+    floatx16 tot;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot[i] = 0.0f;
+    const floatx16 zero = {};
+    const int nch = klen / 64;
+    u32x4 av[4], bv[4], an[4], bn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        av[j] = *(const u32x4 *)(pa + 16 * j);
+        bv[j] = *(const u32x4 *)(pb + 16 * j);
+    }
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                an[j] = *(const u32x4 *)(pa + 64 * (c + 1) + 16 * j);
+                bn[j] = *(const u32x4 *)(pb + 64 * (c + 1) + 16 * j);
+            }
+        }
+        floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, av[0]), __builtin_bit_cast(bf16x8, bv[0]), zero, 0, 0, 0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j)
+            p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]),
+                                                        __builtin_bit_cast(bf16x8, bv[j]), p, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tot[i] += p[i];
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                av[j] = an[j];
+                bv[j] = bn[j];
+            }
+        }
+    }
+    float *out = part + (size_t)sp * T * E;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = t0 + 8 * (i >> 2) + 4 * gg + (i & 3);
+        if (t < T) out[(size_t)t * E + e0 + l32] = tot[i];
+    }
+}
+
+// Fixed-order logit of token row xr and expert row wrow for the half-wave
+// `half` (lanes 32*half .. +31): lane c computes chunk c sequentially from its
+// first product, then the chunk partials are added in chunk order and the
+// bias once.  Must be called by the whole wave (uses shuffles); the result is
+// returned in every lane of the half.
+__device__ float canon_logit_half(const uint16_t *xr, const uint16_t *wrow, int H, float bias_e,
+                                  int lane) {
+    const int half = lane >> 5, c = lane & 31, nch = H / 64;
+    float part = 0.0f;
+    if (c < nch && wrow) {
+        const u32x4 *px = (const u32x4 *)(xr + 64 * c);
+        const u32x4 *pw = (const u32x4 *)(wrow + 64 * c);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const u32x4 xv = px[q], wv = pw[q];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (q == 0 && r == 0)
+                    part = bf16_lo(xv[0]) * bf16_lo(wv[0]);
+                else
+                    part = __builtin_fmaf(bf16_lo(xv[r]), bf16_lo(wv[r]), part);
+                part = __builtin_fmaf(bf16_hi(xv[r]), bf16_hi(wv[r]), part);
+            }
+        }
+    }
+    float total = __shfl(part, 32 * half);
+    for (int cc = 1; cc < nch; ++cc) {
+        const float v = __shfl(part, 32 * half + cc);
+        total = total + v;
+    }
+    return total + bias_e;
+}
+
+__global__ __launch_bounds__(64 * TB) void route_select_kernel(
+    const float *__restrict__ part, int S, const float *__restrict__ exact,
+    const float *__restrict__ xsq, int G, const float *__restrict__ wn2,
+    const float *__restrict__ bias, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ wr, int T, int H, int E, int k, int32_t *__restrict__ ids,
+    float *__restrict__ tw, int32_t *__restrict__ blk_cnt, int32_t *__restrict__ lrank) {
+    __shared__ uint32_t mask[256];
     __shared__ int32_t sid[TB][8];
+    __shared__ uint32_t cand_e[TB][256];
+    __shared__ float cand_l[TB][256];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tb0 = blockIdx.x * TB;
-    mask[tid] = 0ull;
+    const int tl = wave, t = blockIdx.x * TB + tl;
+    if (tid < 256) mask[tid] = 0u;
     __syncthreads();
-    for (int tl = wave; tl < TB; tl += 4) {
-        const int t = tb0 + tl;
-        if (t >= T) break;
-        const float *l = logits + (size_t)t * E;
-        uint64_t key[4];
+    if (t < T) {
+        // ---- logits (approximate or exact) and their error radius
+        float lt[4], dl[4];
+        float nx = 0.0f;
+        if (!exact) {
+            float ss = (lane < G) ? xsq[(size_t)t * G + lane] : 0.0f;
+            nx = sqrtf(wave_sum_f(ss));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane + 64 * j;
-            key[j] = ((uint64_t)ordered_key(l[e]) << 32) | (uint32_t)(0xffffu - e);
-        }
-        int my_pick = -1;
-        float my_logit = 0.0f;
-        for (int p = 0; p < k; ++p) {
-            uint64_t best = key[0];
-#pragma unroll
-            for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
-            best = wave_max_u64(best);
-            const int e = 0xffff - (int)(best & 0xffffu);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (lane + 64 * j == e) key[j] = 0ull;
-            if (lane == p) {
-                // the winning key carries the logit: invert the order-preserving map
-                const uint32_t kh = (uint32_t)(best >> 32);
-                my_pick = e;
-                my_logit = __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
+            const float b = bias ? bias[e] : 0.0f;
+            if (exact) {
+                lt[j] = exact[(size_t)t * E + e];
+                dl[j] = 0.0f;
+            } else {
+                float v = part[(size_t)t * E + e];
+                for (int sp = 1; sp < S; ++sp) v += part[((size_t)sp * T + t) * E + e];
+                lt[j] = v + b;
+                dl[j] = 0x1p-16f * (sqrtf(wn2[e]) * nx * 1.001f + fabsf(b)) + 0x1p-100f;
             }
         }
-        // renormalised softmax over the k picks: exp(l_j - l_0) / sum
-        const float lmax = __shfl(my_logit, 0);
-        float pj = (lane < k) ? expf(my_logit - lmax) : 0.0f;
-        float sum = pj;
+        // ---- top-k by the (approximate) logits, ties to the lower index
+        uint64_t key[4];
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        for (int j = 0; j < 4; ++j)
+            key[j] = ((uint64_t)ordered_key(lt[j]) << 32) | (uint32_t)(0xffffu - (lane + 64 * j));
+        int my_pick = -1;
+        float my_l = 0.0f, my_lb = 0.0f, my_ub = 0.0f;
+        bool taken[4] = {false, false, false, false};
+        for (int p = 0; p < k; ++p) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!taken[j] && key[j] > best) best = key[j];
+            best = wave_max_u64(best);
+            const int e = 0xffff - (int)(best & 0xffffu);
+            float lb = 0.0f, ub = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (lane + 64 * j == e) {
+                    taken[j] = true;
+                    lb = lt[j] - dl[j];
+                    ub = lt[j] + dl[j];
+                }
+            lb = __shfl(lb, e & 63);
+            ub = __shfl(ub, e & 63);
+            if (lane == p) {
+                my_pick = e;
+                my_l = key_to_float((uint32_t)(best >> 32));
+                my_lb = lb;
+                my_ub = ub;
+            }
+        }
+        // ---- certification: disjoint intervals in rank order, nothing else reaching the 8th
+        float m8 = (lane < k) ? my_lb : INFINITY;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m8 = fminf(m8, __shfl_xor(m8, off));
+        const float next_ub = __shfl(my_ub, (lane + 1) & 63);
+        const bool pair_ok = (lane >= k - 1) || (my_lb > next_ub);
+        bool extra = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (!taken[j] && lt[j] + dl[j] >= m8) extra = true;
+        const bool certified = __all(pair_ok) && !__any(extra);
+        float wl = my_l;   // logit used for the weights (lanes < k)
+        if (!certified) {
+            // candidates: every expert whose interval reaches m8 (includes the k picks)
+            const uint16_t *xr = x + (size_t)t * H;
+            int nc = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool c = taken[j] || (lt[j] + dl[j] >= m8);
+                const uint64_t bal = __ballot(c);
+                const int pos = nc + (int)__popcll(bal & ((1ull << lane) - 1ull));
+                if (c) cand_e[tl][pos] = lane + 64 * j;
+                nc += (int)__popcll(bal);
+            }
+            __builtin_amdgcn_wave_barrier();
+            for (int c0 = 0; c0 < nc; c0 += 2) {
+                const int ci = c0 + (lane >> 5);
+                const int e = ci < nc ? (int)cand_e[tl][ci] : -1;
+                const float b = (e >= 0 && bias) ? bias[e] : 0.0f;
+                const float L = canon_logit_half(xr, e >= 0 ? wr + (size_t)e * H : nullptr, H, b,
+                                                 lane);
+                if ((lane & 31) == 0 && ci < nc) cand_l[tl][ci] = L;
+            }
+            __builtin_amdgcn_wave_barrier();
+            // top-k among the candidates by the exact logits
+            uint64_t ck[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ci = lane + 64 * j;
+                ck[j] = ci < nc ? (((uint64_t)ordered_key(cand_l[tl][ci]) << 32) |
+                                   (uint32_t)(0xffffu - cand_e[tl][ci]))
+                                : 0ull;
+            }
+            for (int p = 0; p < k; ++p) {
+                uint64_t best = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (ck[j] > best) best = ck[j];
+                best = wave_max_u64(best);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (ck[j] == best) ck[j] = 0ull;
+                if (lane == p) {
+                    my_pick = 0xffff - (int)(best & 0xffffu);
+                    wl = key_to_float((uint32_t)(best >> 32));
+                }
+            }
+        }
+        // ---- renormalised softmax over the k picks
+        const float lmax = __shfl(wl, 0);
+        const float pj = (lane < k) ? expf(wl - lmax) : 0.0f;
+        const float sum = wave_sum_f(pj);
         if (lane < k) {
             ids[(size_t)t * k + lane] = my_pick;
             tw[(size_t)t * k + lane] = pj / sum;
             sid[tl][lane] = my_pick;
-            atomicOr(&mask[my_pick], 1ull << tl);
+            atomicOr(&mask[my_pick], 1u << tl);
         }
     }
     __syncthreads();
-    blk_cnt[(size_t)blockIdx.x * E + tid] = __popcll(mask[tid]);
-    for (int idx = tid; idx < TB * k; idx += 256) {
-        const int tl = idx / k, j = idx % k;
-        const int t = tb0 + tl;
-        if (t < T) {
-            const int e = sid[tl][j];
-            lrank[(size_t)t * k + j] = __popcll(mask[e] & ((1ull << tl) - 1ull));
+    if (tid < 256) blk_cnt[(size_t)blockIdx.x * E + tid] = __popc(mask[tid]);
+    if (tid < TB * k) {
+        const int tl2 = tid / k, j = tid % k;
+        const int t2 = blockIdx.x * TB + tl2;
+        if (t2 < T) {
+            const int e = sid[tl2][j];
+            lrank[(size_t)t2 * k + j] = __popc(mask[e] & ((1u << tl2) - 1u));
         }
     }
 }
 
-void launch_topk_local(const float *logits, int T, int E, int k, int32_t *ids, float *w,
-                       int32_t *blk_cnt, int32_t *lrank, hipStream_t s) {
-    hipLaunchKernelGGL(topk_local_kernel, dim3((T + TB - 1) / TB), dim3(256), 0, s, logits, T, E,
-                       k, ids, w, blk_cnt, lrank);
+void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
+                        float *wn2, hipStream_t s) {
+    const int S = min(RS_SPLIT, H / 64);
+    hipLaunchKernelGGL(wnorm_kernel, dim3((E + 3) / 4), dim3(256), 0, s, wr, E, H, wn2);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 63) / 64, E / 64, S), dim3(256), 0, s, x, wr,
+                       T, H, E, S, part);
+}
+
+void launch_route_select(const float *part, const float *exact, const float *xsq,
+                         const float *wn2, const float *bias, const uint16_t *x,
+                         const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,
+                         int32_t *blk_cnt, int32_t *lrank, hipStream_t s) {
+    const int S = min(RS_SPLIT, H / 64);
+    hipLaunchKernelGGL(route_select_kernel, dim3((T + TB - 1) / TB), dim3(64 * TB), 0, s, part, S,
+                       exact, xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank);
 }
 
 // ---------------------------------------------------------------------------
-// Prefix scans, block map and stable scatter in one workgroup: per expert an
-// exclusive scan of the token-block counts (written back in place), the
-// expert histogram, its exclusive scan (offsets), the block map (blocks of at
-// most BM consecutive rows of one expert, in expert order), and finally the
-// scatter row = offsets[e] + block_base[b][e] + rank.
+// Routing structures from the per-block counts: per expert an exclusive scan
+// over token blocks (one workgroup per expert), then expert offsets and the
+// block map (one workgroup), then the stable scatter (one thread per pick):
+// row = offsets[e] + block_base[b][e] + rank, which orders rows by expert,
+// then token.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void scan_scatter_kernel(
-    const int32_t *__restrict__ ids, const float *__restrict__ tw, int32_t *__restrict__ blk_cnt,
-    const int32_t *__restrict__ lrank, int T, int E, int k, int BM, int max_blocks,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ row_token,
-    int32_t *__restrict__ tok_row, float *__restrict__ row_w, int32_t *__restrict__ blocks,
-    int32_t *__restrict__ num_blocks) {
+__global__ __launch_bounds__(256) void scan_experts_kernel(int32_t *__restrict__ blk_cnt, int nTB,
+                                                           int E, int32_t *__restrict__ counts) {
     __shared__ int tmp[256];
-    __shared__ int s_off[257];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    int run = 0;
+    for (int b0 = 0; b0 < nTB; b0 += 256) {
+        const int b = b0 + tid;
+        const int v = b < nTB ? blk_cnt[(size_t)b * E + e] : 0;
+        tmp[tid] = v;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const int a = tid >= o ? tmp[tid - o] : 0;
+            __syncthreads();
+            tmp[tid] += a;
+            __syncthreads();
+        }
+        if (b < nTB) blk_cnt[(size_t)b * E + e] = run + tmp[tid] - v;
+        run += tmp[255];
+        __syncthreads();
+    }
+    if (tid == 0) counts[e] = run;
+}
+
+__global__ __launch_bounds__(256) void scan_offsets_kernel(const int32_t *__restrict__ counts,
+                                                           int BM, int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ blocks,
+                                                           int32_t *__restrict__ num_blocks) {
+    __shared__ int tmp[256];
     const int tid = threadIdx.x;
-    const int nTB = (T + TB - 1) / TB;
-    int cnt = 0, nblk = 0;
-    if (tid < 256) {
-        int run = 0;
-        for (int b = 0; b < nTB; ++b) {
-            const int c = blk_cnt[(size_t)b * E + tid];
-            blk_cnt[(size_t)b * E + tid] = run;
-            run += c;
-        }
-        cnt = run;
-        counts[tid] = cnt;
-        nblk = (cnt + BM - 1) / BM;
-    }
-    // the scans use the first 256 threads; the others wait at the barriers
-    int off = 0, bstart = 0;
-    {
-        // expert offsets
-        if (tid < 256) tmp[tid] = cnt;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            int a = 0;
-            if (tid < 256 && tid >= o) a = tmp[tid - o];
-            __syncthreads();
-            if (tid < 256) tmp[tid] += a;
-            __syncthreads();
-        }
-        if (tid < 256) off = tmp[tid] - cnt;
-        __syncthreads();
-        // block starts
-        if (tid < 256) tmp[tid] = nblk;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            int a = 0;
-            if (tid < 256 && tid >= o) a = tmp[tid - o];
-            __syncthreads();
-            if (tid < 256) tmp[tid] += a;
-            __syncthreads();
-        }
-        if (tid < 256) bstart = tmp[tid] - nblk;
-    }
-    if (tid < 256) {
-        s_off[tid] = off;
-        offsets[tid] = off;
-        if (tid == 255) {
-            offsets[256] = off + cnt;
-            num_blocks[0] = bstart + nblk;
-        }
-        for (int i = 0; i < nblk; ++i) {
-            int32_t *bp = blocks + 3 * (size_t)(bstart + i);
-            bp[0] = tid;
-            bp[1] = off + i * BM;
-            bp[2] = min(BM, cnt - i * BM);
-        }
-    }
+    const int cnt = counts[tid];
+    const int nblk = (cnt + BM - 1) / BM;
+    int off, bstart;
+    tmp[tid] = cnt;
     __syncthreads();
-    for (int idx = tid; idx < T * k; idx += 1024) {
-        const int t = idx / k;
-        const int e = ids[idx];
-        if (e < 0 || e >= E) continue;
-        const int r = s_off[e] + blk_cnt[(size_t)(t / TB) * E + e] + lrank[idx];
-        if (r < 0 || r >= T * k) continue;
-        row_token[r] = t;
-        tok_row[idx] = r;
-        row_w[r] = tw[idx];
+    for (int o = 1; o < 256; o <<= 1) {
+        const int a = tid >= o ? tmp[tid - o] : 0;
+        __syncthreads();
+        tmp[tid] += a;
+        __syncthreads();
+    }
+    off = tmp[tid] - cnt;
+    __syncthreads();
+    tmp[tid] = nblk;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int a = tid >= o ? tmp[tid - o] : 0;
+        __syncthreads();
+        tmp[tid] += a;
+        __syncthreads();
+    }
+    bstart = tmp[tid] - nblk;
+    offsets[tid] = off;
+    if (tid == 255) {
+        offsets[256] = off + cnt;
+        num_blocks[0] = bstart + nblk;
+    }
+    for (int i = 0; i < nblk; ++i) {
+        int32_t *bp = blocks + 3 * (size_t)(bstart + i);
+        bp[0] = tid;
+        bp[1] = off + i * BM;
+        bp[2] = min(BM, cnt - i * BM);
     }
 }
 
-void launch_scan_scatter(const int32_t *ids, const float *w, const int32_t *blk_cnt,
-                         const int32_t *lrank, int T, int E, int k, int BM, int max_blocks,
-                         int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
-                         float *row_w, int32_t *blocks, int32_t *num_blocks, hipStream_t s) {
-    hipLaunchKernelGGL(scan_scatter_kernel, dim3(1), dim3(1024), 0, s, ids, w,
-                       const_cast<int32_t *>(blk_cnt), lrank, T, E, k, BM, max_blocks, counts,
-                       offsets, row_token, tok_row, row_w, blocks, num_blocks);
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ ids,
+                                                      const float *__restrict__ tw,
+                                                      const int32_t *__restrict__ blk_base,
+                                                      const int32_t *__restrict__ lrank,
+                                                      const int32_t *__restrict__ offsets, int T,
+                                                      int E, int k, int32_t *__restrict__ row_token,
+                                                      int32_t *__restrict__ tok_row,
+                                                      float *__restrict__ row_w) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * k) return;
+    const int t = idx / k;
+    const int e = ids[idx];
+    if (e < 0 || e >= E) return;
+    const int r = offsets[e] + blk_base[(size_t)(t / TB) * E + e] + lrank[idx];
+    if (r < 0 || r >= T * k) return;
+    row_token[r] = t;
+    tok_row[idx] = r;
+    row_w[r] = tw[idx];
+}
+
+void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
+                         const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
+                         int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
+                         int32_t *blocks, int32_t *num_blocks, hipStream_t s) {
+    const int nTB = (T + TB - 1) / TB;
+    hipLaunchKernelGGL(scan_experts_kernel, dim3(E), dim3(256), 0, s, blk_cnt, nTB, E, counts);
+    hipLaunchKernelGGL(scan_offsets_kernel, dim3(1), dim3(256), 0, s, counts, BM, offsets, blocks,
+                       num_blocks);
+    hipLaunchKernelGGL(scatter_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w, blk_cnt,
+                       lrank, offsets, T, E, k, row_token, tok_row, row_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -329,19 +562,25 @@ __global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *__restr
 // of every row plus the group sums, one thread per (row, group of 64).
 __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restrict__ x, int rows,
                                                        int K, uint16_t *__restrict__ xp,
-                                                       float *__restrict__ out) {
+                                                       float *__restrict__ out,
+                                                       float *__restrict__ sq) {
     const int G = K / 64;
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (size_t)rows * G) return;
     const size_t r = i / G, g = i % G;
     const u32x4 *p = (const u32x4 *)(x + r * K + g * 64);
     u32x4 *q = (u32x4 *)(xp + r * K + g * 64);
-    float s = 0.0f;
+    float s = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const u32x4 v = p[j];
         s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
              bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s2 = __builtin_fmaf(bf16_lo(v[q]), bf16_lo(v[q]), s2);
+            s2 = __builtin_fmaf(bf16_hi(v[q]), bf16_hi(v[q]), s2);
+        }
         u32x4 o;
         o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
         o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
@@ -350,13 +589,15 @@ __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restric
         q[j] = o;
     }
     out[i] = s;
+    if (sq) sq[i] = s2;
 }
 
-void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, hipStream_t s) {
+void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
+                     hipStream_t s) {
     const size_t n = (size_t)rows * (K / 64);
     if (n == 0) return;
     hipLaunchKernelGGL(prep_act_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, rows,
-                       K, xp, xsum);
+                       K, xp, xsum, xsq);
 }
 
 void launch_group_sums(const uint16_t *a, int rows, int K, float *out, hipStream_t s) {

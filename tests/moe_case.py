@@ -32,13 +32,15 @@ def x_dev(inp, dev=None):
 class LayerRun:
     """Buffers and results of one moe_layer call."""
 
-    def __init__(self, inp, w: moe.DeviceLayer = None, dev=None):
+    def __init__(self, inp, w: moe.DeviceLayer = None, dev=None, logits: bool = False):
+        """logits=False runs the production routing (certified fast router); logits=True also
+        computes every router logit in the fixed order and selects on those."""
         dev = dev or device()
         self.inp = inp
         self.shape = shape_of(inp)
         self.w = w or upload(inp, dev)
         self.x = x_dev(inp, dev)
-        self.r = moe.Routing(self.shape, dev)
+        self.r = moe.Routing(self.shape, dev, with_logits=logits)
         self.ws = moe.workspace(self.shape, dev)
         rows = inp.T * inp.top_k + inp.T
         self.h = torch.zeros((rows, inp.I), dtype=torch.int16, device=dev)
@@ -67,7 +69,8 @@ class LayerRun:
     def routing_np(self):
         r = self.r
         nb = int(r.num_blocks.cpu()[0])
-        return dict(logits=r.logits.cpu().numpy(), ids=r.topk_ids.cpu().numpy(),
+        return dict(logits=None if r.logits is None else r.logits.cpu().numpy(),
+                    ids=r.topk_ids.cpu().numpy(),
                     w=r.topk_w.cpu().numpy(), counts=r.counts.cpu().numpy(),
                     offsets=r.offsets.cpu().numpy(), row_token=r.row_token.cpu().numpy(),
                     tok_row=r.tok_row.cpu().numpy(), row_w=r.row_w.cpu().numpy(),

@@ -31,7 +31,7 @@ def test_decode_matches_oracle(seed):
     ids, tw, y = run_decode(inp)
     y_ref, ids_ref, w_ref = oracle.Layer(inp).tokens([0])
     np.testing.assert_array_equal(ids, ids_ref[0])
-    np.testing.assert_allclose(tw, w_ref[0], rtol=2e-6, atol=2e-7)
+    np.testing.assert_allclose(tw, w_ref[0], rtol=2e-5, atol=2e-7)
     ratio = check_y(y[None, :], y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)
 
