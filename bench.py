@@ -90,12 +90,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # per-phase timing (eager launches, HIP events on the launch stream)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
     for s in range(K):
         w = sets[s % len(sets)]
         e0, e1, e2, e3 = ev[s]
@@ -106,14 +102,34 @@ def main():
         e2.record()
         moe.moe_down_combine(shape, h, w, r, y, ws)
         e3.record()
+    torch.cuda.synchronize()
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    gateup_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    down_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+
+    # throughput: the layer steps captured once in a HIP graph (one step per weight
+    # set), replayed so that exactly K steps run between the two events
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for w in sets:
+            step(w)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, K // len(sets))
+    K = reps * len(sets)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(reps):
+        graph.replay()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / K
-    route_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    gateup_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    down_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    del graph
 
     rows = T * K_TOP + T
     flops_gateup = 2.0 * rows * (2 * I) * H
@@ -140,16 +156,23 @@ def main():
         xd, wd = dsets[i % len(dsets)]
         moe.moe_decode(dshape, xd, wd, ids, tw, yd, dws)
     torch.cuda.synchronize()
-    DK = args.decode_steps
-    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(DK)]
-    for s in range(DK):
-        xd, wd = dsets[s % len(dsets)]
-        dev_ev[s][0].record()
-        moe.moe_decode(dshape, xd, wd, ids, tw, yd, dws)
-        dev_ev[s][1].record()
+    # one HIP graph holding one decode per weight set, replayed
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dgraph):
+        for xd, wd in dsets:
+            moe.moe_decode(dshape, xd, wd, ids, tw, yd, dws)
+    dgraph.replay()
     torch.cuda.synchronize()
-    dec_us = sum(a.elapsed_time(b) for a, b in dev_ev) / DK * 1e3
+    dreps = max(1, args.decode_steps // len(dsets))
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(dreps):
+        dgraph.replay()
+    d1.record()
+    torch.cuda.synchronize()
+    dec_us = d0.elapsed_time(d1) / (dreps * len(dsets)) * 1e3
+    del dgraph
     dec_bytes = 9 * expert_bytes(H, I) + E * H * 2 + H * 2 + H * 4 + K_TOP * 8
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
     del dsets

@@ -30,7 +30,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.xp = take((size_t)T * H * 2);
     L.xsq = take((size_t)T * (H / 64) * 4);
     L.part = take((size_t)4 * T * E * 4);
-    L.wn2 = take((size_t)E * 4);
+    L.wn2 = take((size_t)4 * E * 4);
     L.hsum = take((size_t)(T * k + T) * (I / 64) * 4);
     L.stage = take((size_t)T * k * H * 4);
     L.blk_cnt = take(nTB * E * 4);
@@ -105,15 +105,16 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
     int32_t *blk_cnt = (int32_t *)(ws + L.blk_cnt);
     int32_t *lrank = (int32_t *)(ws + L.lrank);
     float *xsq = (float *)(ws + L.xsq);
-    launch_prep_act(x, s->T, s->H, (uint16_t *)(ws + L.xp), (float *)(ws + L.xsum), xsq, st);
     if (r->logits) {
+        launch_prep_act(x, s->T, s->H, (uint16_t *)(ws + L.xp), (float *)(ws + L.xsum), xsq, st);
         // every logit requested: compute them all in the fixed order, select on them directly
         launch_router_logits(x, w->router_wt, w->router_bias, s->T, s->H, s->E, r->logits, st);
         launch_route_select(nullptr, r->logits, xsq, nullptr, w->router_bias, x, w->router_wt,
                             s->T, s->H, s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank, st);
     } else {
         float *part = (float *)(ws + L.part), *wn2 = (float *)(ws + L.wn2);
-        launch_router_fast(x, w->router_wt, s->T, s->H, s->E, part, wn2, st);
+        launch_router_fast(x, w->router_wt, s->T, s->H, s->E, part, wn2, (uint16_t *)(ws + L.xp),
+                           (float *)(ws + L.xsum), xsq, st);
         launch_route_select(part, nullptr, xsq, wn2, w->router_bias, x, w->router_wt, s->T, s->H,
                             s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank, st);
     }

@@ -50,7 +50,7 @@ struct WsLayout {
     size_t xp;          // bf16 [T][H]            x with 8-blocks in the permuted order
     size_t xsq;         // fp32 [T][H/64]         group sums of x^2
     size_t part;        // fp32 [4][T][E]         K-split approximate router logits
-    size_t wn2;         // fp32 [E]               squared norms of the router rows
+    size_t wn2;         // fp32 [4][E]            squared norms of the router rows, per K split
     size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h
     size_t stage;       // fp32 [T*k][H]          routed down outputs times routing weight
     size_t blk_cnt;     // int32 [T/16][E]        per token-block expert counts / bases
@@ -66,7 +66,7 @@ int max_blocks_for(int T, int E, int k);
 void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *bias, int T, int H,
                           int E, float *logits, hipStream_t s);
 void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
-                        float *wn2, hipStream_t s);
+                        float *wn2part, uint16_t *xp, float *xsum, float *xsq, hipStream_t s);
 void launch_route_select(const float *part, const float *exact, const float *xsq,
                          const float *wn2, const float *bias, const uint16_t *x,
                          const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,

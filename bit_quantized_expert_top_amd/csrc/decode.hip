@@ -108,8 +108,8 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     char *p = (char *)scratch;
     float *part = (float *)p;           // [4][1][E]
     p += 4096;
-    float *wn2 = (float *)p;            // [E]
-    p += 1024;
+    float *wn2 = (float *)p;            // [4][E]
+    p += 4096;
     float *xsum = (float *)p;           // [H/64]
     p += 256;
     float *xsq = (float *)p;            // [H/64]
@@ -121,8 +121,7 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     uint16_t *xp = (uint16_t *)p;       // [H]
     p += 2 * 2048;
     float *hbuf = (float *)p;           // [k+1][I]
-    launch_prep_act(x, 1, H, xp, xsum, xsq, s);
-    launch_router_fast(x, w.router_wt, 1, H, E, part, wn2, s);
+    launch_router_fast(x, w.router_wt, 1, H, E, part, wn2, xp, xsum, xsq, s);
     launch_route_select(part, nullptr, xsq, wn2, w.router_bias, x, w.router_wt, 1, H, E, k, ids,
                         tw, blk_cnt, lrank, s);
     const GemmProj gate{w.gate.q, w.gate.scale, w.gate.bias}, up{w.up.q, w.up.scale, w.up.bias};
@@ -137,6 +136,6 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
                        tw, k, down, sdown, y);
 }
 
-size_t decode_scratch_bytes(int I, int k) { return 16384 + (size_t)(k + 1) * I * 4; }
+size_t decode_scratch_bytes(int I, int k) { return 20480 + (size_t)(k + 1) * I * 4; }
 
 }  // namespace moe

@@ -144,15 +144,6 @@ __device__ __forceinline__ float key_to_float(uint32_t kh) {
     return __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
 
 __device__ __forceinline__ float wave_sum_f(float v) {
 #pragma unroll
@@ -160,35 +151,60 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     return v;
 }
 
-// squared L2 norm of each router row (one wave per expert)
-__global__ __launch_bounds__(256) void wnorm_kernel(const uint16_t *__restrict__ wr, int E, int H,
-                                                    float *__restrict__ wn2) {
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (e >= E) return;
-    float s = 0.0f;
-    for (int k = lane * 8; k < H; k += 512) {
-        const u32x4 v = *(const u32x4 *)(wr + (size_t)e * H + k);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float a = bf16_lo(v[q]), b = bf16_hi(v[q]);
-            s = __builtin_fmaf(a, a, s);
-            s = __builtin_fmaf(b, b, s);
-        }
-    }
-    s = wave_sum_f(s);
-    if (lane == 0) wn2[e] = s;
+// Wave-wide unsigned max, returned in every lane: DPP steps inside each row of
+// 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row
+// results read as scalars.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+    v = dpp_umax<0xB1>(v);
+    v = dpp_umax<0x4E>(v);
+    v = dpp_umax<0x141>(v);
+    v = dpp_umax<0x140>(v);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
 }
 
-// approximate logits (no bias), partial over K range s: part[s][t][e]
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ wr, int T,
-                                                          int H, int E, int S,
-                                                          float *__restrict__ part) {
+// Largest key among 4 per lane (key[j] belongs to expert lane + 64 j; taken
+// entries excluded), ties to the lowest expert index.  Returns the expert.
+__device__ __forceinline__ int wave_argmax4(const uint32_t (&key)[4], const bool (&taken)[4],
+                                            uint32_t *kmax) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (!taken[j] && key[j] > m) m = key[j];
+    m = wave_umax(m);
+    *kmax = m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t b = __ballot(!taken[j] && key[j] == m);
+        if (b) return 64 * j + __builtin_ctzll(b);
+    }
+    return -1;
+}
+
+// Approximate logits (no bias), partial over K range s: part[s][t][e].  The
+// same pass also prepares x for the expert GEMM (workgroups of expert tile 0:
+// the 8-block permutation (0,4,1,5,2,6,3,7), and per group of 64 the sum and
+// the sum of squares), and the squared norms of the router rows per K range
+// (workgroups of token tile 0).
+__global__ __launch_bounds__(256) void router_mfma_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int H, int E, int S,
+    float *__restrict__ part, uint16_t *__restrict__ xp, float *__restrict__ xsum,
+    float *__restrict__ xsq, float *__restrict__ wn2part) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, gg = lane >> 5;
     const int t0 = blockIdx.x * 64 + 32 * (wave & 1), e0 = blockIdx.y * 64 + 32 * (wave >> 1);
     const int sp = blockIdx.z, klen = H / S, kbeg = sp * klen;
     const int trow = min(t0 + l32, T - 1);
+    const bool do_prep = blockIdx.y == 0 && (wave >> 1) == 0 && t0 + l32 < T;
+    const bool do_norm = blockIdx.x == 0 && (wave & 1) == 0;
+    const int G = H / 64;
     const uint16_t *pa = x + (size_t)trow * H + kbeg + 8 * gg;
     const uint16_t *pb = wr + (size_t)(e0 + l32) * H + kbeg + 8 * gg;
     floatx16 tot;
@@ -196,6 +212,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__rest
     for (int i = 0; i < 16; ++i) tot[i] = 0.0f;
     const floatx16 zero = {};
     const int nch = klen / 64;
+    float wsq = 0.0f;
     u32x4 av[4], bv[4], an[4], bn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -218,6 +235,43 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__rest
                                                         __builtin_bit_cast(bf16x8, bv[j]), p, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) tot[i] += p[i];
+        if (do_prep) {
+            // this lane holds k = 16j + 8gg + 0..7 of the chunk's group
+            float s1 = 0.0f, s2 = 0.0f;
+            uint16_t *q = xp + (size_t)(t0 + l32) * H + kbeg + 64 * c + 8 * gg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 v = av[j];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s1 += bf16_lo(v[r]) + bf16_hi(v[r]);
+                    s2 = __builtin_fmaf(bf16_lo(v[r]), bf16_lo(v[r]), s2);
+                    s2 = __builtin_fmaf(bf16_hi(v[r]), bf16_hi(v[r]), s2);
+                }
+                u32x4 o;
+                o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+                o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+                o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+                o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+                *(u32x4 *)(q + 16 * j) = o;
+            }
+            s1 += __shfl_xor(s1, 32);
+            s2 += __shfl_xor(s2, 32);
+            if (gg == 0) {
+                const size_t gi = (size_t)(t0 + l32) * G + kbeg / 64 + c;
+                xsum[gi] = s1;
+                xsq[gi] = s2;
+            }
+        }
+        if (do_norm) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    wsq = __builtin_fmaf(bf16_lo(bv[j][r]), bf16_lo(bv[j][r]), wsq);
+                    wsq = __builtin_fmaf(bf16_hi(bv[j][r]), bf16_hi(bv[j][r]), wsq);
+                }
+        }
         if (c + 1 < nch) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -225,6 +279,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__rest
                 bv[j] = bn[j];
             }
         }
+    }
+    if (do_norm) {
+        wsq += __shfl_xor(wsq, 32);
+        if (gg == 0) wn2part[(size_t)sp * E + e0 + l32] = wsq;
     }
     float *out = part + (size_t)sp * T * E;
 #pragma unroll
@@ -234,37 +292,49 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__rest
     }
 }
 
-// Fixed-order logit of token row xr and expert row wrow for the half-wave
-// `half` (lanes 32*half .. +31): lane c computes chunk c sequentially from its
-// first product, then the chunk partials are added in chunk order and the
-// bias once.  Must be called by the whole wave (uses shuffles); the result is
-// returned in every lane of the half.
-__device__ float canon_logit_half(const uint16_t *xr, const uint16_t *wrow, int H, float bias_e,
-                                  int lane) {
-    const int half = lane >> 5, c = lane & 31, nch = H / 64;
+// Fixed-order logit of one expert row for the half-wave `half` (lanes
+// 32*half .. +31): lane c computes chunk c sequentially from its first product
+// (xv: the token's 64 inputs of chunk c, already in registers); the chunk
+// partials go through LDS (scratch: 64 floats for the wave) and the first lane
+// of each half adds them in chunk order, then the bias.  Called by the whole
+// wave; the result is valid in lanes 0 (half 0) and 32 (half 1).
+__device__ float canon_logit_half(const u32x4 (&xv)[8], const uint16_t *wrow, int H, float bias_e,
+                                  int lane, float *scratch) {
+    const int c = lane & 31, nch = H / 64;
     float part = 0.0f;
     if (c < nch && wrow) {
-        const u32x4 *px = (const u32x4 *)(xr + 64 * c);
         const u32x4 *pw = (const u32x4 *)(wrow + 64 * c);
+        u32x4 wv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wv[q] = pw[q];      // all loads in flight before use
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const u32x4 xv = px[q], wv = pw[q];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if (q == 0 && r == 0)
-                    part = bf16_lo(xv[0]) * bf16_lo(wv[0]);
+                    part = bf16_lo(xv[0][0]) * bf16_lo(wv[0][0]);
                 else
-                    part = __builtin_fmaf(bf16_lo(xv[r]), bf16_lo(wv[r]), part);
-                part = __builtin_fmaf(bf16_hi(xv[r]), bf16_hi(wv[r]), part);
+                    part = __builtin_fmaf(bf16_lo(xv[q][r]), bf16_lo(wv[q][r]), part);
+                part = __builtin_fmaf(bf16_hi(xv[q][r]), bf16_hi(wv[q][r]), part);
             }
         }
     }
-    float total = __shfl(part, 32 * half);
-    for (int cc = 1; cc < nch; ++cc) {
-        const float v = __shfl(part, 32 * half + cc);
-        total = total + v;
+    scratch[lane] = part;
+    __builtin_amdgcn_wave_barrier();
+    float total = 0.0f;
+    if (c == 0) {
+        const float *ps = scratch + lane;
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) v[q] = ps[q];
+        total = v[0];
+#pragma unroll
+        for (int q = 1; q < 32; ++q)
+            if (q < nch) total = total + v[q];
+        total = total + bias_e;
     }
-    return total + bias_e;
+    __builtin_amdgcn_wave_barrier();
+    return total;
 }
 
 __global__ __launch_bounds__(64 * TB) void route_select_kernel(
@@ -277,6 +347,7 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     __shared__ int32_t sid[TB][8];
     __shared__ uint32_t cand_e[TB][256];
     __shared__ float cand_l[TB][256];
+    __shared__ float scr[TB][64];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int tl = wave, t = blockIdx.x * TB + tl;
     if (tid < 256) mask[tid] = 0u;
@@ -300,24 +371,21 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 float v = part[(size_t)t * E + e];
                 for (int sp = 1; sp < S; ++sp) v += part[((size_t)sp * T + t) * E + e];
                 lt[j] = v + b;
-                dl[j] = 0x1p-16f * (sqrtf(wn2[e]) * nx * 1.001f + fabsf(b)) + 0x1p-100f;
+                float w2 = wn2[e];
+                for (int sp = 1; sp < S; ++sp) w2 += wn2[(size_t)sp * E + e];
+                dl[j] = 0x1p-16f * (sqrtf(w2) * nx * 1.001f + fabsf(b)) + 0x1p-100f;
             }
         }
         // ---- top-k by the (approximate) logits, ties to the lower index
-        uint64_t key[4];
+        uint32_t key[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            key[j] = ((uint64_t)ordered_key(lt[j]) << 32) | (uint32_t)(0xffffu - (lane + 64 * j));
+        for (int j = 0; j < 4; ++j) key[j] = ordered_key(lt[j]);
+        bool taken[4] = {false, false, false, false};
         int my_pick = -1;
         float my_l = 0.0f, my_lb = 0.0f, my_ub = 0.0f;
-        bool taken[4] = {false, false, false, false};
         for (int p = 0; p < k; ++p) {
-            uint64_t best = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (!taken[j] && key[j] > best) best = key[j];
-            best = wave_max_u64(best);
-            const int e = 0xffff - (int)(best & 0xffffu);
+            uint32_t km;
+            const int e = wave_argmax4(key, taken, &km);
             float lb = 0.0f, ub = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -326,20 +394,25 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                     lb = lt[j] - dl[j];
                     ub = lt[j] + dl[j];
                 }
-            lb = __shfl(lb, e & 63);
-            ub = __shfl(ub, e & 63);
+            const float lbe = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lb), e & 63));
+            const float ube = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ub), e & 63));
             if (lane == p) {
                 my_pick = e;
-                my_l = key_to_float((uint32_t)(best >> 32));
-                my_lb = lb;
-                my_ub = ub;
+                my_l = key_to_float(km);
+                my_lb = lbe;
+                my_ub = ube;
             }
         }
         // ---- certification: disjoint intervals in rank order, nothing else reaching the 8th
-        float m8 = (lane < k) ? my_lb : INFINITY;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m8 = fminf(m8, __shfl_xor(m8, off));
-        const float next_ub = __shfl(my_ub, (lane + 1) & 63);
+        float m8 = INFINITY;
+        for (int p = 0; p < k; ++p)
+            m8 = fminf(m8, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_lb), p)));
+        // lane p < k-1 compares its lower bound with the upper bound of pick p+1
+        float next_ub = 0.0f;
+        for (int p = 0; p + 1 < k; ++p) {
+            const float nu = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ub), p + 1));
+            if (lane == p) next_ub = nu;
+        }
         const bool pair_ok = (lane >= k - 1) || (my_lb > next_ub);
         bool extra = false;
 #pragma unroll
@@ -350,6 +423,11 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
         if (!certified) {
             // candidates: every expert whose interval reaches m8 (includes the k picks)
             const uint16_t *xr = x + (size_t)t * H;
+            u32x4 xv[8];
+            if ((lane & 31) < H / 64) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) xv[q] = ((const u32x4 *)(xr + 64 * (lane & 31)))[q];
+            }
             int nc = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -364,32 +442,41 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 const int ci = c0 + (lane >> 5);
                 const int e = ci < nc ? (int)cand_e[tl][ci] : -1;
                 const float b = (e >= 0 && bias) ? bias[e] : 0.0f;
-                const float L = canon_logit_half(xr, e >= 0 ? wr + (size_t)e * H : nullptr, H, b,
-                                                 lane);
+                const float L = canon_logit_half(xv, e >= 0 ? wr + (size_t)e * H : nullptr, H, b,
+                                                 lane, scr[tl]);
                 if ((lane & 31) == 0 && ci < nc) cand_l[tl][ci] = L;
             }
             __builtin_amdgcn_wave_barrier();
-            // top-k among the candidates by the exact logits
-            uint64_t ck[4];
+            // top-k among the candidates by the exact logits (ties to the lower index)
+            uint32_t ck[4];
+            bool gone[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int ci = lane + 64 * j;
-                ck[j] = ci < nc ? (((uint64_t)ordered_key(cand_l[tl][ci]) << 32) |
-                                   (uint32_t)(0xffffu - cand_e[tl][ci]))
-                                : 0ull;
+                gone[j] = ci >= nc;
+                ck[j] = gone[j] ? 0u : ordered_key(cand_l[tl][ci]);
             }
             for (int p = 0; p < k; ++p) {
-                uint64_t best = 0;
+                uint32_t m = 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (ck[j] > best) best = ck[j];
-                best = wave_max_u64(best);
+                    if (!gone[j] && ck[j] > m) m = ck[j];
+                m = wave_umax(m);
+                // among the candidates holding the max key, the lowest expert index
+                uint32_t emin = 0xffffffffu;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (ck[j] == best) ck[j] = 0ull;
+                    if (!gone[j] && ck[j] == m) {
+                        const uint32_t ee = cand_e[tl][lane + 64 * j];
+                        emin = ee < emin ? ee : emin;
+                    }
+                emin = ~wave_umax(~emin);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (!gone[j] && ck[j] == m && cand_e[tl][lane + 64 * j] == emin) gone[j] = true;
                 if (lane == p) {
-                    my_pick = 0xffff - (int)(best & 0xffffu);
-                    wl = key_to_float((uint32_t)(best >> 32));
+                    my_pick = (int)emin;
+                    wl = key_to_float(m);
                 }
             }
         }
@@ -417,11 +504,10 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
 }
 
 void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
-                        float *wn2, hipStream_t s) {
+                        float *wn2part, uint16_t *xp, float *xsum, float *xsq, hipStream_t s) {
     const int S = min(RS_SPLIT, H / 64);
-    hipLaunchKernelGGL(wnorm_kernel, dim3((E + 3) / 4), dim3(256), 0, s, wr, E, H, wn2);
     hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 63) / 64, E / 64, S), dim3(256), 0, s, x, wr,
-                       T, H, E, S, part);
+                       T, H, E, S, part, xp, xsum, xsq, wn2part);
 }
 
 void launch_route_select(const float *part, const float *exact, const float *xsq,
@@ -463,15 +549,19 @@ __global__ __launch_bounds__(256) void scan_experts_kernel(int32_t *__restrict__
     if (tid == 0) counts[e] = run;
 }
 
-__global__ __launch_bounds__(256) void scan_offsets_kernel(const int32_t *__restrict__ counts,
-                                                           int BM, int32_t *__restrict__ offsets,
-                                                           int32_t *__restrict__ blocks,
-                                                           int32_t *__restrict__ num_blocks) {
+// Every workgroup scans the expert counts itself (256 values) to get the
+// offsets; workgroup 0 also publishes offsets, the block map and its size.
+// Then one thread per pick: row = offsets[e] + block_base[b][e] + rank.
+__global__ __launch_bounds__(256) void scatter_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ tw,
+    const int32_t *__restrict__ blk_base, const int32_t *__restrict__ lrank,
+    const int32_t *__restrict__ counts, int T, int E, int k, int BM,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ blocks, int32_t *__restrict__ num_blocks,
+    int32_t *__restrict__ row_token, int32_t *__restrict__ tok_row, float *__restrict__ row_w) {
     __shared__ int tmp[256];
+    __shared__ int s_off[256];
     const int tid = threadIdx.x;
     const int cnt = counts[tid];
-    const int nblk = (cnt + BM - 1) / BM;
-    int off, bstart;
     tmp[tid] = cnt;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
@@ -480,44 +570,39 @@ __global__ __launch_bounds__(256) void scan_offsets_kernel(const int32_t *__rest
         tmp[tid] += a;
         __syncthreads();
     }
-    off = tmp[tid] - cnt;
-    __syncthreads();
-    tmp[tid] = nblk;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int a = tid >= o ? tmp[tid - o] : 0;
+    const int off = tmp[tid] - cnt;
+    s_off[tid] = off;
+    if (blockIdx.x == 0) {
+        const int nblk = (cnt + BM - 1) / BM;
         __syncthreads();
-        tmp[tid] += a;
+        tmp[tid] = nblk;
         __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const int a = tid >= o ? tmp[tid - o] : 0;
+            __syncthreads();
+            tmp[tid] += a;
+            __syncthreads();
+        }
+        const int bstart = tmp[tid] - nblk;
+        offsets[tid] = off;
+        if (tid == 255) {
+            offsets[256] = off + cnt;
+            num_blocks[0] = bstart + nblk;
+        }
+        for (int i = 0; i < nblk; ++i) {
+            int32_t *bp = blocks + 3 * (size_t)(bstart + i);
+            bp[0] = tid;
+            bp[1] = off + i * BM;
+            bp[2] = min(BM, cnt - i * BM);
+        }
     }
-    bstart = tmp[tid] - nblk;
-    offsets[tid] = off;
-    if (tid == 255) {
-        offsets[256] = off + cnt;
-        num_blocks[0] = bstart + nblk;
-    }
-    for (int i = 0; i < nblk; ++i) {
-        int32_t *bp = blocks + 3 * (size_t)(bstart + i);
-        bp[0] = tid;
-        bp[1] = off + i * BM;
-        bp[2] = min(BM, cnt - i * BM);
-    }
-}
-
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ ids,
-                                                      const float *__restrict__ tw,
-                                                      const int32_t *__restrict__ blk_base,
-                                                      const int32_t *__restrict__ lrank,
-                                                      const int32_t *__restrict__ offsets, int T,
-                                                      int E, int k, int32_t *__restrict__ row_token,
-                                                      int32_t *__restrict__ tok_row,
-                                                      float *__restrict__ row_w) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
+    __syncthreads();
+    const int idx = blockIdx.x * 256 + tid;
     if (idx >= T * k) return;
     const int t = idx / k;
     const int e = ids[idx];
     if (e < 0 || e >= E) return;
-    const int r = offsets[e] + blk_base[(size_t)(t / TB) * E + e] + lrank[idx];
+    const int r = s_off[e] + blk_base[(size_t)(t / TB) * E + e] + lrank[idx];
     if (r < 0 || r >= T * k) return;
     row_token[r] = t;
     tok_row[idx] = r;
@@ -530,10 +615,9 @@ void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          int32_t *blocks, int32_t *num_blocks, hipStream_t s) {
     const int nTB = (T + TB - 1) / TB;
     hipLaunchKernelGGL(scan_experts_kernel, dim3(E), dim3(256), 0, s, blk_cnt, nTB, E, counts);
-    hipLaunchKernelGGL(scan_offsets_kernel, dim3(1), dim3(256), 0, s, counts, BM, offsets, blocks,
-                       num_blocks);
     hipLaunchKernelGGL(scatter_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w, blk_cnt,
-                       lrank, offsets, T, E, k, row_token, tok_row, row_w);
+                       lrank, counts, T, E, k, BM, offsets, blocks, num_blocks, row_token,
+                       tok_row, row_w);
 }
 
 // ---------------------------------------------------------------------------
