@@ -47,6 +47,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device-to-device copies of MIB MiB (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -61,6 +64,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
     shape = moe.Shape(T=T, H=H, I=I, E=E, top_k=K_TOP)
 
     def device_layer(d):
