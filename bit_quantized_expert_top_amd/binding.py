@@ -99,6 +99,7 @@ def _ptr(t: Optional[torch.Tensor], dtypes=None, name="tensor") -> Optional[int]
 
 
 _B16 = (torch.bfloat16, torch.int16, torch.uint16)
+_H16 = (torch.float16, torch.int16, torch.uint16)      # h: fp16 bits
 _U32 = (torch.int32, torch.uint32)
 _I32 = (torch.int32,)
 _F32 = (torch.float32,)
@@ -204,13 +205,13 @@ def moe_route(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, ws: tor
 def moe_expert_gemm_q4(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,
                        ws: torch.Tensor, stream=None):
     _check(lib().moe_expert_gemm_q4(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
-                                    C.byref(r.c()), _ptr(h, _B16, "h"), _ptr(ws, None, "ws"),
+                                    C.byref(r.c()), _ptr(h, _H16, "h"), _ptr(ws, None, "ws"),
                                     ws.numel(), _stream(stream)), "moe_expert_gemm_q4")
 
 
 def moe_down_combine(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing, y: torch.Tensor,
                      ws: torch.Tensor, stream=None):
-    _check(lib().moe_down_combine(C.byref(shape.c()), _ptr(h, _B16, "h"), C.byref(w.c()),
+    _check(lib().moe_down_combine(C.byref(shape.c()), _ptr(h, _H16, "h"), C.byref(w.c()),
                                   C.byref(r.c()), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
                                   ws.numel(), _stream(stream)), "moe_down_combine")
 
@@ -218,7 +219,7 @@ def moe_down_combine(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing, 
 def moe_layer(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,
               y: torch.Tensor, ws: torch.Tensor, stream=None):
     _check(lib().moe_layer(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()), C.byref(r.c()),
-                           _ptr(h, _B16, "h"), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
+                           _ptr(h, _H16, "h"), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
                            ws.numel(), _stream(stream)), "moe_layer")
 
 

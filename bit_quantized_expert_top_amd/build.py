@@ -15,7 +15,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed fp32 arithmetic in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs: the GEMM scales them with VALU right away
+    # MFMA results in VGPRs: the router sums its partial products with VALU
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]

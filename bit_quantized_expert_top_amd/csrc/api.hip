@@ -130,15 +130,15 @@ moe_status enqueue_gateup(const moe_shape *s, const uint16_t *x, const moe_weigh
     (void)x;
     launch_gateup(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum), gp(w->gate), gp(w->up), gp(w->sh_gate),
                   gp(w->sh_up), r->blocks, r->num_blocks, max_blocks_for(s->T, s->E, s->top_k),
-                  r->row_token, h, st);
+                  r->row_token, h, (float *)(ws + L.hsum), st);
     return launched();
 }
 
 moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights *w,
                         const moe_routing *r, float *y, char *ws, hipStream_t st) {
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
-    float *hsum = (float *)(ws + L.hsum);
-    launch_group_sums(h, s->T * s->top_k + s->T, s->I, hsum, st);
+    // group sums of h: left in the workspace by the gate/up pass
+    const float *hsum = (const float *)(ws + L.hsum);
     launch_down(*s, h, hsum, gp(w->down), gp(w->sh_down), r->blocks, r->num_blocks,
                 max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
                 (float *)(ws + L.stage), y, st);

@@ -10,6 +10,8 @@
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -35,6 +37,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
+// fp32 -> fp16 bits, round to nearest even
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+    return (float)__builtin_bit_cast(f16x2, v)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+    return (float)__builtin_bit_cast(f16x2, v)[1];
+}
+
 // Activations enter the GEMMs with every 8-column block stored in the order
 // (0,4,1,5,2,6,3,7), matching the pair order in which 4-bit codes unpack.
 // Position of column `col` in that storage.
@@ -47,11 +66,11 @@ __host__ __device__ __forceinline__ int perm_pos(int col) {
 struct WsLayout {
     size_t logits;      // fp32 [T][E]            (used when routing.logits == NULL)
     size_t xsum;        // fp32 [T][H/64]         group sums of x
-    size_t xp;          // bf16 [T][H]            x with 8-blocks in the permuted order
+    size_t xp;          // fp16 [T][H]            x in fp16, 8-blocks in the permuted order
     size_t xsq;         // fp32 [T][H/64]         group sums of x^2
     size_t part;        // fp32 [4][T][E]         K-split approximate router logits
     size_t wn2;         // fp32 [4][E]            squared norms of the router rows, per K split
-    size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h
+    size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h (fp16 values)
     size_t stage;       // fp32 [T*k][H]          routed down outputs times routing weight
     size_t blk_cnt;     // int32 [T/16][E]        per token-block expert counts / bases
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
@@ -75,7 +94,6 @@ void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
                          int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
                          int32_t *blocks, int32_t *num_blocks, hipStream_t s);
-void launch_group_sums(const uint16_t *a, int rows, int K, float *out, hipStream_t s);
 void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
                      hipStream_t s);
 
@@ -88,7 +106,7 @@ struct GemmProj {
 void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum, GemmProj gate,
                    GemmProj up, GemmProj sgate, GemmProj sup, const int32_t *blocks,
                    const int32_t *num_blocks, int max_blocks, const int32_t *row_token,
-                   uint16_t *h, hipStream_t s);
+                   uint16_t *h, float *hsum, hipStream_t s);
 void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
                  GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,

@@ -1,62 +1,65 @@
-// Grouped expert GEMMs over 4-bit affine weights on bf16 MFMA (gfx950).
+// Grouped expert GEMMs over 4-bit affine weights on fp16 MFMA (gfx950).
 //
-// The pages' design rebuilds bf16 weights tile by tile inside the grouped
-// GEMM and accumulates in FP32 (mechatronicstore.cl, "Prefill: pesos
-// comprimidos y enrutamiento en la GPU").  Rounding q*scale+bias to bf16
-// loses up to 4 significant bits per weight, which on these layers leaves
-// almost no margin under the output tolerance, so this kernel feeds the
-// MFMA the exact codes instead and applies scale and bias in FP32:
+// The pages rebuild 16-bit weights tile by tile inside the grouped GEMM and
+// accumulate in FP32 (mechatronicstore.cl, "Prefill: pesos comprimidos y
+// enrutamiento en la GPU").  Here the rebuilt weight is exact: with a bf16
+// scale s (8 significant bits) and a code q in 0..15, (q - 8) * s needs at
+// most 11 significant bits, so it is an fp16 number.  Splitting
 //
-//   sum_k x_k w_k = sum_g s_g * P_g  +  sum_g c_g * xs_g,
-//   P_g = sum_{k in g} x_k (128 + q_k),   c_g = b_g - 128 s_g,   xs_g = sum_{k in g} x_k
+//   w = q s + b = (q - 8) s + c,        c = b + 8 s   (per group, fp32),
 //
-//  * a code word becomes four bf16 pairs 128+q with one and-or each (the
-//    nibble drops into the mantissa of 128.0): exact, 7 VALU ops per 8 codes;
-//  * P_g comes from four 32x32x16 MFMA k-steps started from zero;
-//  * the FP32 accumulator takes acc += s_g * P_g once per group;
-//  * the rank-G term sum_g c_g xs_g is a small MFMA pass with K = 3G over
-//    bf16 hi/lo splits: c_hi xs_hi + c_hi xs_lo + c_lo xs_hi.
+// the contraction becomes
 //
-// Element order: the code pairs come out as k = (0,4), (1,5), (2,6), (3,7) of
-// each 8-block, so the activations are stored with every 8-block permuted to
-// (0,4,1,5,2,6,3,7): x by the preparation pass, h by the gate/up epilogue.
+//   sum_k x_k w_k = sum_k x_k [(q_k - 8) s_g]  +  sum_g c_g xs_g,   xs_g = sum_{k in g} x_k
 //
-// Tiles: a workgroup takes one routing block (up to 128 rows of one expert)
-// and a slice of output columns; each of its 4 waves owns 64 output columns
-// (gate/up: 32 gate + the 32 matching up columns, so SwiGLU is local to a
-// lane) for all rows.  The activation rows of a 128-wide K chunk are copied
-// global->LDS directly (no registers), double buffered, XOR-swizzled so the
-// MFMA operand reads are bank-conflict free; the codes go straight from
-// global memory to registers, each word used by exactly one wave.
+//  * each code word turns into four fp16 pairs (q - 8) s: one and-or drops a
+//    nibble pair into the mantissa of 1024.0, one packed add removes 1032,
+//    one packed multiply applies the scale, all exact;
+//  * the activations enter the MFMA in fp16 (x is converted once, exactly for
+//    |x| in the fp16 normal range; h is written in fp16 by the gate/up pass);
+//  * the 32x32x16 fp16 MFMA accumulates straight into the fp32 result, so no
+//    per-group rescaling is left on the vector ALU;
+//  * the rank-G term sum_g c_g xs_g is zero whenever b = -8 s (the format's
+//    symmetric case); otherwise a wave adds it with a small MFMA pass over
+//    K = 3G of fp16 hi/lo splits: c_hi xs_hi + c_hi xs_lo + c_lo xs_hi.
+//
+// Element order: code pairs come out as k = (0,4), (1,5), (2,6), (3,7) of each
+// 8-block, so activations are stored with every 8-block permuted to
+// (0,4,1,5,2,6,3,7): x by the router's preparation pass, h by the gate/up
+// epilogue.
+//
+// Tiles: a workgroup (4 waves) takes one routing block (up to 128 rows of one
+// expert) and 256 weight columns: gate/up takes 128 columns of I from both
+// projections (wave w owns gate and up columns 32w..32w+31, so SwiGLU stays
+// inside a lane), down takes 256 columns of H.  Each wave computes all rows x
+// its 64 columns.  Per 64-wide K step (one quantisation group) the activation
+// rows, the code words, the scales and the biases are copied global->LDS by
+// DMA (no registers) into a 3-deep ring, swizzled so that every MFMA operand
+// read is free of bank conflicts.  Two workgroups share a CU.
 #include "common.h"
 
 namespace moe {
 
-constexpr int KC = 128;                 // K per chunk: two quantisation groups
-constexpr int A_ROW = 2 * KC;           // LDS bytes per staged activation row
-constexpr int MAXG = 32;                // K <= 2048
-constexpr int KB3_MAX = 3 * MAXG;       // K'' of the bias pass
-constexpr int AB_LD = KB3_MAX + 8;      // bf16 per row of the bias-pass A operand
-constexpr int NRING = 3;                // code/scale ring depth (chunks in flight)
-constexpr int NWAVE = 8;                // waves per workgroup: 2 row halves x 4 column quarters
-constexpr int B_NQ = 4096;              // bytes of codes per column quarter per chunk
-constexpr int S_NQ = 256;               // bytes of scales per column quarter per chunk
-
-// LDS map (bytes)
-constexpr int L_A = 0;                                   // [2][128 rows][256 B] swizzled
-constexpr int L_B = L_A + 2 * kBM * A_ROW;               // [NRING][4 nq][2 nt][2 groups][64 lanes][16 B]
-constexpr int L_S = L_B + NRING * 4 * B_NQ;              // [NRING][4 nq][64 lanes][4 B]
-constexpr int L_AB = L_S + NRING * 4 * S_NQ;             // [128 rows][AB_LD] bf16
-constexpr int L_TOK = L_AB + kBM * AB_LD * 2;            // [128] int32 source rows
-constexpr int L_TOTAL = L_TOK + kBM * 4;
+constexpr int NW = 4;                        // waves per workgroup
+constexpr int NTHR = 64 * NW;
+constexpr int KC = 64;                       // K per stage: one quantisation group
+constexpr int NSTAGE = 3;
+constexpr int A_BYTES = kBM * KC * 2;        // [128 rows][8 x 16 B], 16 B slots XOR-swizzled
+constexpr int B_BYTES = 256 * 32;            // [256 columns][2 x 16 B halves], halves swizzled
+constexpr int S_BYTES = 256 * 4;             // one dword per column (bf16 in the low half)
+constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;   // + the group's bias per column
+constexpr int L_TOTAL = NSTAGE * STAGE;      // 79872: two workgroups per CU
+constexpr int HS_LD = 272;                   // epilogue h tile row stride (bytes)
+constexpr int YS_LD = 1056;                  // epilogue y tile row stride (bytes)
+static_assert(kBM * HS_LD <= L_TOTAL && 32 * YS_LD <= L_TOTAL, "epilogue tiles fit the ring");
 
 struct GemmArgs {
-    const uint16_t *A;     // permuted activations: x [T][H] (gate/up) or h [rows][I] (down)
+    const uint16_t *A;     // fp16 permuted activations: x [T][H] (gate/up) or h [rows][I] (down)
     const float *Asum;     // group sums of A rows: by token [T][G] or by row [rows][G]
     int K, G;
+    int N;                 // rows of one projection: I (gate/up) or H (down)
     GemmProj p0, p1;       // routed projections: gate, up  |  down, -
     GemmProj s0, s1;       // the shared expert's
-    int N;                 // rows per projection: I (gate/up) or H (down)
     const int32_t *blocks;
     const int32_t *num_blocks;
     int max_blocks;
@@ -65,369 +68,350 @@ struct GemmArgs {
     int T, topk, E;
     int n_tiles;
     int n_shared;          // shared-expert M blocks (scheduled first)
-    uint16_t *h;
+    uint16_t *h;           // gate/up output, fp16 [T*topk + T][I]
+    float *hsum;           // gate/up output, group sums of h [T*topk + T][I/64]
     float *y;
     float *stage;          // routed down outputs times their routing weight [T*topk][H]
-    int ldo;               // output row stride: I (h) or H (y)
 };
 
-// 8 codes of one word -> 8 bf16 values 128+q, element order (0,4,1,5,2,6,3,7):
-// one v_and_or_b32 per pair (both constants in VGPRs, so no literal limits apply)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
     uint32_t r;
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
     return r;
 }
-__device__ __forceinline__ bf16x8 codes_to_bf16x8(uint32_t w, uint32_t M, uint32_t C) {
+
+// 8 codes of one word -> 8 fp16 weights (q - 8) * s, element order (0,4,1,5,2,6,3,7)
+__device__ __forceinline__ f16x8 rebuild8(uint32_t w, uint32_t M, uint32_t C, f16x2 m1032,
+                                          f16x2 ss) {
+    const f16x2 p0 = (__builtin_bit_cast(f16x2, and_or(w, M, C)) + m1032) * ss;
+    const f16x2 p1 = (__builtin_bit_cast(f16x2, and_or(w >> 4, M, C)) + m1032) * ss;
+    const f16x2 p2 = (__builtin_bit_cast(f16x2, and_or(w >> 8, M, C)) + m1032) * ss;
+    const f16x2 p3 = (__builtin_bit_cast(f16x2, and_or(w >> 12, M, C)) + m1032) * ss;
     u32x4 v;
-    v.x = and_or(w, M, C);
-    v.y = and_or(w >> 4, M, C);
-    v.z = and_or(w >> 8, M, C);
-    v.w = and_or(w >> 12, M, C);
-    return __builtin_bit_cast(bf16x8, v);
+    v.x = __builtin_bit_cast(uint32_t, p0);
+    v.y = __builtin_bit_cast(uint32_t, p1);
+    v.z = __builtin_bit_cast(uint32_t, p2);
+    v.w = __builtin_bit_cast(uint32_t, p3);
+    return __builtin_bit_cast(f16x8, v);
 }
 
-__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ floatx16 mfma16(f16x8 a, f16x8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Asynchronous global->LDS copies.  Lane i of the wave writes LDS bytes
-// [lds + 16 i, lds + 16 i + 16) (dword form: 4 i).  Issued through inline
-// assembly so that the compiler does not wait for them before every LDS read;
-// completion is awaited explicitly (s_waitcnt vmcnt) before the barrier that
-// publishes a chunk.
+// [lds + 16 i, +16) (ushort form: the value zero-extended to the dword at
+// lds + 4 i).  Issued through inline assembly so that the compiler does not
+// wait for them before every LDS read; completion is awaited explicitly
+// (s_waitcnt vmcnt) before the barrier that publishes a stage.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+__device__ __forceinline__ void dma2(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
 
-template <int MODE>   // 0: gate/up + SwiGLU -> h ; 1: down -> y (shared) / staging (routed)
-__global__ __launch_bounds__(512, 1) void q4_gemm_kernel(GemmArgs a) {
-    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    uint8_t *As = smem + L_A;
-    uint16_t *abias = (uint16_t *)(smem + L_AB);
-    int32_t *s_src = (int32_t *)(smem + L_TOK);
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
+// One tile: a routing block (or a shared-expert block) times 256 weight columns.
+struct Tile {
+    bool shared;
+    int e, r0, nrows, ntile;
+};
 
+// activation source row of tile row m (rows past nrows repeat row 0)
+template <int MODE>
+__device__ __forceinline__ int src_row(const GemmArgs &a, const Tile &t, int m) {
+    const int mm = m < t.nrows ? m : 0;
+    if (MODE == 0) {
+        const int tok = t.shared ? (t.r0 - a.T * a.topk + mm) : a.row_token[t.r0 + mm];
+        return (tok >= 0 && tok < a.T) ? tok : 0;
+    }
+    return t.r0 + mm;
+}
+
+// projection and row of weight column bc (0..255) of the tile
+template <int MODE>
+__device__ __forceinline__ void column_of(const GemmArgs &a, const Tile &t, int bc, GemmProj &p,
+                                          size_t &row) {
+    const int w = bc >> 6, nt = (bc >> 5) & 1, l = bc & 31;
+    int n;
+    if (MODE == 0) {
+        p = t.shared ? (nt ? a.s1 : a.s0) : (nt ? a.p1 : a.p0);
+        n = t.ntile * 128 + 32 * w + l;
+    } else {
+        p = t.shared ? a.s0 : a.p0;
+        n = t.ntile * 256 + 64 * w + 32 * nt + l;
+    }
+    row = (t.shared ? 0 : (size_t)t.e * a.N) + n;
+}
+
+template <int MODE, int MT>
+__device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nq = wave & 3, mh = wave >> 2;       // column quarter, row half
     const int l32 = lane & 31, gg = lane >> 5;
-    const int bid = (int)blockIdx.x / a.n_tiles;
-    const int nt = (int)blockIdx.x % a.n_tiles;
-    // shared-expert blocks first (full tiles), then the routed block map
-    const bool shared = bid < a.n_shared;
-    int e = 0, r0, nrows;
-    if (!shared) {
-        const int mb = bid - a.n_shared;
-        if (mb >= a.num_blocks[0] || mb >= a.max_blocks) return;
-        e = a.blocks[3 * mb];
-        r0 = a.blocks[3 * mb + 1];
-        nrows = a.blocks[3 * mb + 2];
-        // a malformed block map turns into a no-op, never an out-of-bounds access
-        if (e < 0 || e >= a.E || r0 < 0 || nrows < 1 || nrows > kBM || r0 + nrows > a.T * a.topk)
-            return;
-    } else {
-        r0 = a.T * a.topk + bid * kBM;
-        nrows = min(kBM, a.T - bid * kBM);
-    }
-    const int K = a.K, G = a.G;
-    const int Trk = a.T * a.topk;
-    const int nchunks = K / KC;
+    const int K = a.K, G = a.G, nch = K / KC;
 
-    // ---- this wave's two projection rows (one per 32-column n-tile)
-    const GemmProj P0 = shared ? a.s0 : a.p0;
-    const GemmProj P1 = shared ? (MODE == 0 ? a.s1 : a.s0) : (MODE == 0 ? a.p1 : a.p0);
-    const size_t eoff = shared ? 0 : (size_t)e * a.N;
-    int nrow[2];
-    if (MODE == 0) {
-        nrow[0] = nrow[1] = nt * 128 + 32 * nq + l32;
-    } else {
-        nrow[0] = nt * 256 + 64 * nq + l32;
-        nrow[1] = nrow[0] + 32;
-    }
-    const uint32_t *qrow[2];
-    const uint16_t *srow[2], *brow[2];
-    {
-        const GemmProj pp[2] = {P0, P1};
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const size_t rr = eoff + nrow[q];
-            qrow[q] = pp[q].q + rr * (K / 8) + 4 * gg;
-            srow[q] = pp[q].s + rr * G;
-            brow[q] = pp[q].b + rr * G;
-        }
-    }
-    // codes of chunk c for column quarter nq: this wave copies n-tile mh (2 copies);
-    // both waves copy the (identical) scales
-    const uint32_t lB = lds0 + L_B + nq * B_NQ, lS = lds0 + L_S + nq * S_NQ;
-    const uint32_t *my_q = mh ? qrow[1] : qrow[0];
-    const uint16_t *my_srow = gg ? srow[1] : srow[0];     // lane L copies column (L>>5, L&31)
-    auto copy_codes = [&](int c) {
-        const int slot = c % NRING;
-#pragma unroll
-        for (int gm = 0; gm < 2; ++gm)
-            dma16(my_q + c * 16 + gm * 8, lB + slot * 4 * B_NQ + (2 * mh + gm) * 1024);
-        dma4(my_srow + 2 * c, lS + slot * 4 * S_NQ);
-    };
-
-    // ---- source rows of the tile (clamped: rows past nrows repeat row 0)
-    if (tid < kBM) {
-        const int mm = tid < nrows ? tid : 0;
-        int src;
-        if (MODE == 0) {
-            const int t = shared ? (r0 - Trk + mm) : a.row_token[r0 + mm];
-            src = (t >= 0 && t < a.T) ? t : 0;
-        } else {
-            src = r0 + mm;
-        }
-        s_src[tid] = src;
-    }
-    copy_codes(0);
-    __syncthreads();
-
-    // ---- activation chunk copies: wave w covers rows 16w .. 16w+15 in 4 copies of
-    // 4 rows; lane L fills 16-byte slot L&15 of row L>>4, holding segment (L&15)^(row&15)
+    // ---- DMA sources of this thread
+    // A: rows 32i + tid/8 (i = 0..3); 16 B slot tid&7 of a row holds its
+    // segment slot ^ ((row >> 1) & 7)
     uint32_t aoff[4];
+    {
+        const int seg = (tid & 7) ^ ((tid >> 4) & 7);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * i + (lane >> 4);
-        const int segd = (lane & 15) ^ (row & 15);
-        aoff[i] = (uint32_t)s_src[row] * (uint32_t)K + (uint32_t)(segd * 8);
+        for (int i = 0; i < 4; ++i) {
+            const int m = 32 * i + (tid >> 3);
+            aoff[i] = (uint32_t)src_row<MODE>(a, t, m) * (uint32_t)K + (uint32_t)(8 * seg);
+        }
     }
-    auto copy_act = [&](int c, int buf) {
+    // B: columns 128i + tid/2 (i = 0, 1); LDS half tid&1 holds code words
+    // 4 * ((tid&1) ^ ((col >> 3) & 1)) .. +3 of the group
+    const uint32_t *qsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        GemmProj p;
+        size_t row;
+        column_of<MODE>(a, t, 128 * i + (tid >> 1), p, row);
+        qsrc[i] = p.q + row * (size_t)(K / 8) + 4 * ((tid & 1) ^ ((tid >> 4) & 1));
+    }
+    // scale and bias of column tid
+    const uint16_t *ssrc, *bsrc;
+    {
+        GemmProj p;
+        size_t row;
+        column_of<MODE>(a, t, tid, p, row);
+        ssrc = p.s + row * (size_t)G;
+        bsrc = p.b + row * (size_t)G;
+    }
+    auto issue = [&](int c) {
+        const uint32_t base = lds0 + (uint32_t)((c % NSTAGE) * STAGE);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dma16(a.A + (size_t)aoff[i] + c * KC,
-                  lds0 + L_A + buf * kBM * A_ROW + (16 * wave + 4 * i) * A_ROW);
+            dma16(a.A + (size_t)aoff[i] + c * KC, base + (uint32_t)((i * 256 + wave * 64) * 16));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            dma16(qsrc[i] + c * 8, base + (uint32_t)(A_BYTES + (i * 256 + wave * 64) * 16));
+        dma2(ssrc + c, base + (uint32_t)(A_BYTES + B_BYTES + wave * 64 * 4));
+        dma2(bsrc + c, base + (uint32_t)(A_BYTES + B_BYTES + S_BYTES + wave * 64 * 4));
     };
-    copy_act(0, 0);
-    // issued last, so that "all but the newest 3 copies" below means chunk 0 complete
-    if (nchunks > 1) copy_codes(1);
+    // 8 copies per thread per stage: "all but the newest 8" = all of the older stage
 
-    // ---- group sums -> bias-pass A operand: [xs_hi | xs_lo | xs_hi | 0 pad].
-    // Thread t owns a quarter row (G/4 <= 8 sums): all loads issued before use.
-    const int KB3 = (3 * G + 15) & ~15;
-    {
-        const int m = tid >> 2, qt = tid & 3, qg = G >> 2, rem = G & 3;
-        // quarters of G (G is even; the last quarter takes the remainder)
-        const int g0 = qt * qg, cnt = qg + (qt == 3 ? rem : 0);
-        const float *src = a.Asum + (size_t)s_src[m] * G + g0;
-        float sv[10];
-#pragma unroll
-        for (int i = 0; i < 10; ++i)
-            if (i < cnt) sv[i] = src[i];
-        uint16_t *dst = abias + m * AB_LD + g0;
-#pragma unroll
-        for (int g = 0; g < 10; ++g) {
-            if (g < cnt) {
-                const uint16_t hi = f32_to_bf16(sv[g]);
-                dst[g] = hi;
-                dst[G + g] = f32_to_bf16(sv[g] - bf16_to_f32(hi));
-                dst[2 * G + g] = hi;
-            }
-        }
-        for (int c = 3 * G + qt; c < KB3; c += 4) abias[m * AB_LD + c] = 0;
-    }
+    issue(0);
+    if (nch > 1) issue(1);
 
-    // rows of this wave: 64*mh + 32*mt + ..., mt < MT
-    const int MT = max(0, min(2, (nrows - 64 * mh + 31) >> 5));
-    floatx16 acc[2][2];
+    floatx16 acc[MT][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mt][q][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) acc[mt][0][i] = acc[mt][1][i] = 0.0f;
 
-    // chunk 0 (activations + codes) and chunk 1 codes are in flight; wait for chunk 0
-    if (nchunks > 1)
-        asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    uint32_t cM = 0x000F000Fu, cC = 0x64006400u;
+    asm volatile("" : "+v"(cM), "+v"(cC));       // keep the unpack constants in VGPRs
+    const f16x2 m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const int sw = (l32 >> 1) & 7;
+    const int swb = (l32 >> 3) & 1;
+    bool nz = false;                             // any group with b != -8 s in my columns
 
-    const floatx16 zero = {};
-    uint32_t cM = 0x000F000Fu, cC = 0x43004300u;
-    asm volatile("" : "+v"(cM), "+v"(cC));   // keep the unpack constants in VGPRs
-    for (int c = 0; c < nchunks; ++c) {
-        const int cur = c & 1, slot = c % NRING;
-        if (c + 1 < nchunks) copy_act(c + 1, cur ^ 1);
-        if (c + 2 < nchunks) copy_codes(c + 2);
-        const uint8_t *bsl = smem + L_B + slot * 4 * B_NQ + nq * B_NQ + lane * 16;
-        const uint32_t *ssl = (const uint32_t *)(smem + L_S + slot * 4 * S_NQ + nq * S_NQ);
-        const uint32_t sc0 = ssl[l32], sc1 = ssl[32 + l32];
-        if (MT > 0) {
-#pragma unroll
-            for (int gm = 0; gm < 2; ++gm) {
-                const float s0 = gm ? bf16_hi(sc0) : bf16_lo(sc0);
-                const float s1 = gm ? bf16_hi(sc1) : bf16_lo(sc1);
-                const u32x4 w0 = *(const u32x4 *)(bsl + (0 + gm) * 1024);
-                const u32x4 w1 = *(const u32x4 *)(bsl + (2 + gm) * 1024);
-                bf16x8 bfr[2][4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bfr[0][j] = codes_to_bf16x8(w0[j], cM, cC);
-                    bfr[1][j] = codes_to_bf16x8(w1[j], cM, cC);
-                }
-                const uint8_t *abase = As + cur * kBM * A_ROW + (64 * mh + l32) * A_ROW;
-                const int sw = l32 & 15;
-                floatx16 p[2][2];
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    if (mt < MT) {
-                        bf16x8 af[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            af[j] = *(const bf16x8 *)(abase + mt * 32 * A_ROW +
-                                                      (((8 * gm + 4 * gg + j) ^ sw) << 4));
-                        p[mt][0] = mfma32(af[0], bfr[0][0], zero);
-                        p[mt][1] = mfma32(af[0], bfr[1][0], zero);
-#pragma unroll
-                        for (int j = 1; j < 4; ++j) {
-                            p[mt][0] = mfma32(af[j], bfr[0][j], p[mt][0]);
-                            p[mt][1] = mfma32(af[j], bfr[1][j], p[mt][1]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    if (mt < MT) {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            acc[mt][0][i] = __builtin_fmaf(s0, p[mt][0][i], acc[mt][0][i]);
-                            acc[mt][1][i] = __builtin_fmaf(s1, p[mt][1][i], acc[mt][1][i]);
-                        }
-                    }
-                }
-            }
-        }
-        // publish chunk c+1: its activations and codes must have landed (the
-        // codes of chunk c+2, issued last, may still be in flight)
-        if (c + 2 < nchunks)
-            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch)
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        __syncthreads();                         // stage c visible; stage c-1 no longer read
+        if (c + 2 < nch) issue(c + 2);
+
+        const uint8_t *sb = smem + (c % NSTAGE) * STAGE;
+        u32x4 wq[2];
+        f16x2 ss[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int bc = 64 * wave + 32 * nt + l32;
+            wq[nt] = *(const u32x4 *)(sb + A_BYTES + bc * 32 + 16 * (gg ^ swb));
+            const uint32_t sv = *(const uint32_t *)(sb + A_BYTES + B_BYTES + bc * 4);
+            const uint32_t bv = *(const uint32_t *)(sb + A_BYTES + B_BYTES + S_BYTES + bc * 4);
+            const float sf = bf16_lo(sv);
+            nz |= bf16_lo(bv) != -8.0f * sf;
+            const _Float16 sh = (_Float16)sf;
+            ss[nt] = f16x2{sh, sh};
+        }
+        const uint8_t *arow = sb + l32 * (KC * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f16x8 b0 = rebuild8(wq[0][j], cM, cC, m1032, ss[0]);
+            const f16x8 b1 = rebuild8(wq[1][j], cM, cC, m1032, ss[1]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f16x8 af =
+                    *(const f16x8 *)(arow + mt * 32 * (KC * 2) + 16 * ((4 * gg + j) ^ sw));
+                acc[mt][0] = mfma16(af, b0, acc[mt][0]);
+                acc[mt][1] = mfma16(af, b1, acc[mt][1]);
+            }
+        }
     }
 
-    // ---- rank-G term: sum_g c[n][g] * xs[m][g], c = b - 128 s, as MFMA over
-    // K'' = 3G with A'' = [xs_hi | xs_lo | xs_hi] and B'' = [c_hi | c_hi | c_lo].
-    // Scales and biases of this wave's 64 columns are staged in the (now free)
-    // activation buffer: lane L holds column (L>>5, L&31).
-    uint16_t *sb_s = (uint16_t *)(As + wave * 64 * 2 * MAXG * 2);
-    uint16_t *sb_b = sb_s + 64 * MAXG;
-    {
-        const uint16_t *ps = gg ? srow[1] : srow[0];
-        const uint16_t *pb = gg ? brow[1] : brow[0];
-        if ((G & 7) == 0) {
-            u32x4 vs[4], vb[4];
+    // ---- rank-G term for groups whose bias is not -8 s (none for symmetric codes)
+    if (__any(nz)) {
+        const int K3 = 3 * G;
+        int srcr[MT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (8 * i < G) {
-                    vs[i] = *(const u32x4 *)(ps + 8 * i);
-                    vb[i] = *(const u32x4 *)(pb + 8 * i);
-                }
+        for (int mt = 0; mt < MT; ++mt) srcr[mt] = src_row<MODE>(a, t, 32 * mt + l32);
+        const uint16_t *cs[2], *cb[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (8 * i < G) {
-                    *(u32x4 *)(sb_s + lane * MAXG + 8 * i) = vs[i];
-                    *(u32x4 *)(sb_b + lane * MAXG + 8 * i) = vb[i];
-                }
-        } else {
-            for (int g = 0; g < G; ++g) {
-                sb_s[lane * MAXG + g] = ps[g];
-                sb_b[lane * MAXG + g] = pb[g];
-            }
+        for (int nt = 0; nt < 2; ++nt) {
+            GemmProj p;
+            size_t row;
+            column_of<MODE>(a, t, 64 * wave + 32 * nt + l32, p, row);
+            cs[nt] = p.s + row * (size_t)G;
+            cb[nt] = p.b + row * (size_t)G;
         }
-    }
-    __syncthreads();
-    for (int j3 = 0; j3 < KB3 / 16; ++j3) {
-        bf16x8 bb[2];
-        const int kap0 = 16 * j3 + 8 * gg;
+        for (int j3 = 0; j3 < (K3 + 15) / 16; ++j3) {
+            uint32_t bw[2][4], aw[MT][4];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int col = q * 32 + l32;
-            u32x4 pk = {0u, 0u, 0u, 0u};
-            if ((G & 7) == 0) {
-                // the 8 slots share one term tau and run over groups gam0 .. gam0+7
-                const int tau = kap0 / G, gam0 = kap0 - tau * G;
-                if (tau < 3) {
-                    const u32x4 vs = *(const u32x4 *)(sb_s + col * MAXG + gam0);
-                    const u32x4 vb = *(const u32x4 *)(sb_b + col * MAXG + gam0);
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float bvals[2][2], avals[MT][2];
 #pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) {
-                        const float c0 = bf16_lo(vb[w2]) - 128.0f * bf16_lo(vs[w2]);
-                        const float c1 = bf16_hi(vb[w2]) - 128.0f * bf16_hi(vs[w2]);
-                        const uint32_t hi = pack_bf16x2(c0, c1);
-                        pk[w2] = tau < 2 ? hi : pack_bf16x2(c0 - bf16_lo(hi), c1 - bf16_hi(hi));
+                for (int hh = 0; hh < 2; ++hh) {
+                    // operand slot k'' = 16 j3 + 8 gg + 2 e2 + hh: term tau, group g
+                    const int kk = 16 * j3 + 8 * gg + 2 * e2 + hh;
+                    const int tau = kk / G, g = kk - tau * G;
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        float v = 0.0f;
+                        if (tau < 3) {
+                            const float cf = bf16_to_f32(cb[nt][g]) + 8.0f * bf16_to_f32(cs[nt][g]);
+                            const float hi = (float)(_Float16)cf;
+                            v = tau < 2 ? hi : (float)(_Float16)(cf - hi);
+                        }
+                        bvals[nt][hh] = v;
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        float v = 0.0f;
+                        if (tau < 3) {
+                            const float xs = a.Asum[(size_t)srcr[mt] * G + g];
+                            const float hi = (float)(_Float16)xs;
+                            v = tau == 1 ? (float)(_Float16)(xs - hi) : hi;
+                        }
+                        avals[mt][hh] = v;
                     }
                 }
-            } else {
-                uint16_t v[8];
 #pragma unroll
-                for (int el = 0; el < 8; ++el) {
-                    const int kap = kap0 + el;
-                    const int tau = kap / G, gam = kap - tau * G;
-                    uint16_t val = 0;
-                    if (tau < 3) {
-                        const float cf = bf16_to_f32(sb_b[col * MAXG + gam]) -
-                                         128.0f * bf16_to_f32(sb_s[col * MAXG + gam]);
-                        const uint16_t chi = f32_to_bf16(cf);
-                        val = tau < 2 ? chi : f32_to_bf16(cf - bf16_to_f32(chi));
-                    }
-                    v[el] = val;
-                }
-                pk.x = v[0] | ((uint32_t)v[1] << 16);
-                pk.y = v[2] | ((uint32_t)v[3] << 16);
-                pk.z = v[4] | ((uint32_t)v[5] << 16);
-                pk.w = v[6] | ((uint32_t)v[7] << 16);
+                for (int nt = 0; nt < 2; ++nt) bw[nt][e2] = pack_f16x2(bvals[nt][0], bvals[nt][1]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) aw[mt][e2] = pack_f16x2(avals[mt][0], avals[mt][1]);
             }
-            bb[q] = __builtin_bit_cast(bf16x8, pk);
-        }
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            if (mt < MT) {
-                const bf16x8 af = *(const bf16x8 *)&abias[(64 * mh + 32 * mt + l32) * AB_LD +
-                                                          16 * j3 + 8 * gg];
-                acc[mt][0] = mfma32(af, bb[0], acc[mt][0]);
-                acc[mt][1] = mfma32(af, bb[1], acc[mt][1]);
+            for (int mt = 0; mt < MT; ++mt) {
+                const u32x4 av = {aw[mt][0], aw[mt][1], aw[mt][2], aw[mt][3]};
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const u32x4 bv = {bw[nt][0], bw[nt][1], bw[nt][2], bw[nt][3]};
+                    acc[mt][nt] = mfma16(__builtin_bit_cast(f16x8, av),
+                                         __builtin_bit_cast(f16x8, bv), acc[mt][nt]);
+                }
             }
         }
     }
 
     // ---- epilogue.  Accumulator element i of lane (l32, gg) is row
-    // 8*(i/4) + 4*gg + i%4 of the 32-row tile, column l32.
-    const int hcol = perm_pos(nrow[0]);
+    // 8*(i/4) + 4*gg + i%4 of its 32-row tile, column l32 of the wave's n-tile.
+    __syncthreads();                             // every wave is done with the ring
+    if (MODE == 0) {
+        // SwiGLU -> fp16 h tile in LDS [128 rows][128 columns], columns permuted
+        const int pc = perm_pos(32 * wave + l32);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        if (mt >= MT) continue;
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 64 * mh + 32 * mt + 8 * (i >> 2) + 4 * gg + (i & 3);
-            if (row >= nrows) continue;
-            if (MODE == 0) {
+            for (int i = 0; i < 16; ++i) {
+                const int row = 32 * mt + 8 * (i >> 2) + 4 * gg + (i & 3);
                 const float g = acc[mt][0][i], u = acc[mt][1][i];
                 const float hv = __fdividef(g, 1.0f + __expf(-g)) * u;
-                a.h[(size_t)(r0 + row) * a.ldo + hcol] = f32_to_bf16(hv);
-            } else {
-                if (shared) {
-                    const size_t t = (size_t)(r0 - Trk + row);
-                    a.y[t * a.ldo + nrow[0]] = acc[mt][0][i];
-                    a.y[t * a.ldo + nrow[1]] = acc[mt][1][i];
+                *(uint16_t *)(smem + row * HS_LD + 2 * pc) = f32_to_f16(hv);
+            }
+        __syncthreads();
+        // thread: row tid/2, 64-column half tid&1 -> 128 B of h and one group sum
+        const int row = tid >> 1, half = tid & 1;
+        if (row < t.nrows) {
+            const uint8_t *src = smem + row * HS_LD + half * 128;
+            uint16_t *dst = a.h + (size_t)(t.r0 + row) * a.N + t.ntile * 128 + half * 64;
+            float sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const u32x4 v = *(const u32x4 *)(src + 16 * q);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sum += f16_lo(v[r]) + f16_hi(v[r]);
+                *(u32x4 *)(dst + 8 * q) = v;
+            }
+            a.hsum[(size_t)(t.r0 + row) * (a.N / 64) + t.ntile * 2 + half] = sum;
+        }
+    } else {
+        const int Trk = a.T * a.topk;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (mt > 0) __syncthreads();
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rr = 8 * (i >> 2) + 4 * gg + (i & 3);
+                    *(float *)(smem + rr * YS_LD + 4 * (64 * wave + 32 * nt + l32)) = acc[mt][nt][i];
+                }
+            __syncthreads();
+            // thread: row tid/8 of the 32-row tile, 32 columns from (tid&7)*32
+            const int rr = tid >> 3, seg = tid & 7;
+            const int row = 32 * mt + rr;
+            if (row < t.nrows) {
+                const uint8_t *src = smem + rr * YS_LD + seg * 128;
+                float *dst;
+                float wr = 1.0f;
+                if (t.shared) {
+                    dst = a.y + (size_t)(t.r0 - Trk + row) * a.N;
                 } else {
-                    // routing-weighted output of routed row r0+row, combined later
-                    const float wr = a.row_w[r0 + row];
-                    float *o = a.stage + (size_t)(r0 + row) * a.ldo;
-                    o[nrow[0]] = wr * acc[mt][0][i];
-                    o[nrow[1]] = wr * acc[mt][1][i];
+                    dst = a.stage + (size_t)(t.r0 + row) * a.N;
+                    wr = a.row_w[t.r0 + row];
+                }
+                dst += t.ntile * 256 + seg * 32;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    floatx4 v = *(const floatx4 *)(src + 16 * q);
+                    v *= wr;
+                    *(floatx4 *)(dst + 4 * q) = v;
                 }
             }
         }
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    Tile t;
+    const int bid = (int)blockIdx.x / a.n_tiles;
+    t.ntile = (int)blockIdx.x % a.n_tiles;
+    // shared-expert blocks first (full tiles), then the routed block map
+    t.shared = bid < a.n_shared;
+    t.e = 0;
+    if (!t.shared) {
+        const int mb = bid - a.n_shared;
+        if (mb >= a.num_blocks[0] || mb >= a.max_blocks) return;
+        t.e = a.blocks[3 * mb];
+        t.r0 = a.blocks[3 * mb + 1];
+        t.nrows = a.blocks[3 * mb + 2];
+        // a malformed block map turns into a no-op, never an out-of-bounds access
+        if (t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
+            t.r0 + t.nrows > a.T * a.topk)
+            return;
+    } else {
+        t.r0 = a.T * a.topk + bid * kBM;
+        t.nrows = min(kBM, a.T - bid * kBM);
+    }
+    switch ((t.nrows + 31) >> 5) {
+        case 1: gemm_tile<MODE, 1>(a, t, smem); break;
+        case 2: gemm_tile<MODE, 2>(a, t, smem); break;
+        case 3: gemm_tile<MODE, 3>(a, t, smem); break;
+        default: gemm_tile<MODE, 4>(a, t, smem); break;
     }
 }
 
@@ -447,17 +431,17 @@ static void allow_lds() {
 void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, GemmProj gate,
                    GemmProj up, GemmProj sgate, GemmProj sup, const int32_t *blocks,
                    const int32_t *num_blocks, int max_blocks, const int32_t *row_token,
-                   uint16_t *h, hipStream_t s) {
+                   uint16_t *h, float *hsum, hipStream_t s) {
     GemmArgs a{};
     a.A = xp;
     a.Asum = xsum;
     a.K = sh.H;
     a.G = sh.H / 64;
+    a.N = sh.I;
     a.p0 = gate;
     a.p1 = up;
     a.s0 = sgate;
     a.s1 = sup;
-    a.N = sh.I;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks;
@@ -468,10 +452,10 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, G
     a.n_tiles = sh.I / 128;
     a.n_shared = shared_blocks(sh.T);
     a.h = h;
-    a.ldo = sh.I;
+    a.hsum = hsum;
     allow_lds<0>();
     const int nmb = max_blocks + a.n_shared;
-    hipLaunchKernelGGL(q4_gemm_kernel<0>, dim3(nmb * a.n_tiles), dim3(64 * NWAVE), L_TOTAL, s, a);
+    hipLaunchKernelGGL(q4_gemm_kernel<0>, dim3(nmb * a.n_tiles), dim3(NTHR), L_TOTAL, s, a);
 }
 
 // y[t] += sum_j stage[tok_row[t][j]] in pick order j = 0..k-1: a fixed order, so
@@ -505,9 +489,9 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, Gemm
     a.Asum = hsum;
     a.K = sh.I;
     a.G = sh.I / 64;
+    a.N = sh.H;
     a.p0 = down;
     a.s0 = sdown;
-    a.N = sh.H;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks;
@@ -520,11 +504,10 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, Gemm
     a.n_shared = shared_blocks(sh.T);
     a.y = y;
     a.stage = stage;
-    a.ldo = sh.H;
     allow_lds<1>();
     // shared-expert blocks write y, routed blocks their weighted staging rows ...
     const int nmb = max_blocks + a.n_shared;
-    hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(nmb * a.n_tiles), dim3(64 * NWAVE), L_TOTAL, s, a);
+    hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(nmb * a.n_tiles), dim3(NTHR), L_TOTAL, s, a);
     // ... then each token adds its eight routed rows
     const size_t n4 = (size_t)sh.T * sh.H / 4;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, stage,

@@ -188,10 +188,21 @@ __device__ __forceinline__ int wave_argmax4(const uint32_t (&key)[4], const bool
     return -1;
 }
 
+// 8 bf16 values k = 0..7 -> fp16 in the GEMM operand order (0,4,1,5,2,6,3,7).
+// Exact for |x| in the fp16 normal range (bf16 has 8 significant bits, fp16 11).
+__device__ __forceinline__ u32x4 permute_to_f16(u32x4 v) {
+    u32x4 o;
+    o.x = pack_f16x2(bf16_lo(v.x), bf16_lo(v.z));
+    o.y = pack_f16x2(bf16_hi(v.x), bf16_hi(v.z));
+    o.z = pack_f16x2(bf16_lo(v.y), bf16_lo(v.w));
+    o.w = pack_f16x2(bf16_hi(v.y), bf16_hi(v.w));
+    return o;
+}
+
 // Approximate logits (no bias), partial over K range s: part[s][t][e].  The
 // same pass also prepares x for the expert GEMM (workgroups of expert tile 0:
-// the 8-block permutation (0,4,1,5,2,6,3,7), and per group of 64 the sum and
-// the sum of squares), and the squared norms of the router rows per K range
+// fp16 with the 8-block permutation (0,4,1,5,2,6,3,7), and per group of 64 the
+// sum and the sum of squares), and the squared norms of the router rows per K range
 // (workgroups of token tile 0).
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int H, int E, int S,
@@ -248,12 +259,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                     s2 = __builtin_fmaf(bf16_lo(v[r]), bf16_lo(v[r]), s2);
                     s2 = __builtin_fmaf(bf16_hi(v[r]), bf16_hi(v[r]), s2);
                 }
-                u32x4 o;
-                o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-                o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-                o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-                o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-                *(u32x4 *)(q + 16 * j) = o;
+                *(u32x4 *)(q + 16 * j) = permute_to_f16(v);
             }
             s1 += __shfl_xor(s1, 32);
             s2 += __shfl_xor(s2, 32);
@@ -620,30 +626,8 @@ void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                        tok_row, row_w);
 }
 
-// ---------------------------------------------------------------------------
-// Group sums of a bf16 matrix: out[r][g] = sum of a[r][64g .. 64g+63] in fp32.
-// The GEMMs feed exact 4-bit codes (plus a constant 128) to the MFMA and use
-// these sums to remove that constant and to apply the per-group bias.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *__restrict__ a, int rows,
-                                                         int K, float *__restrict__ out) {
-    const int G = K / 64;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (size_t)rows * G) return;
-    const size_t r = i / G, g = i % G;
-    const u32x4 *p = (const u32x4 *)(a + r * K + g * 64);
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const u32x4 v = p[j];
-        s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
-             bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
-    }
-    out[i] = s;
-}
-
-// Activation preparation for the GEMM: the 8-block permutation (0,4,1,5,2,6,3,7)
-// of every row plus the group sums, one thread per (row, group of 64).
+// Activation preparation for the GEMM: fp16 copy with the 8-block permutation
+// (0,4,1,5,2,6,3,7) of every row plus the group sums, one thread per (row, group of 64).
 __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restrict__ x, int rows,
                                                        int K, uint16_t *__restrict__ xp,
                                                        float *__restrict__ out,
@@ -665,12 +649,7 @@ __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restric
             s2 = __builtin_fmaf(bf16_lo(v[q]), bf16_lo(v[q]), s2);
             s2 = __builtin_fmaf(bf16_hi(v[q]), bf16_hi(v[q]), s2);
         }
-        u32x4 o;
-        o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-        o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-        o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-        o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-        q[j] = o;
+        q[j] = permute_to_f16(v);
     }
     out[i] = s;
     if (sq) sq[i] = s2;
@@ -682,13 +661,6 @@ void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xs
     if (n == 0) return;
     hipLaunchKernelGGL(prep_act_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, rows,
                        K, xp, xsum, xsq);
-}
-
-void launch_group_sums(const uint16_t *a, int rows, int K, float *out, hipStream_t s) {
-    const size_t n = (size_t)rows * (K / 64);
-    if (n == 0) return;
-    hipLaunchKernelGGL(group_sums_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
-                       rows, K, out);
 }
 
 }  // namespace moe

@@ -113,20 +113,25 @@ moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weight
  * 4-bit codes directly (mechatronicstore.cl "Prefill: ...": weights rebuilt
  * tile by tile inside the grouped GEMM, FP32 accumulation), with the SwiGLU
  * epilogue h = silu(W_gate x) * (W_up x).
- * h: bf16 [T*top_k + T][I]; rows 0..T*top_k-1 follow routing order, row
- * T*top_k + t is the shared expert of token t.  Within each row, every block
- * of 8 consecutive columns is stored in the order 0,4,1,5,2,6,3,7 (the
- * order in which the down GEMM consumes it).  Needs moe_route's outputs and
- * workspace. */
+ * h: fp16 [T*top_k + T][I] (bits as uint16_t); rows 0..T*top_k-1 follow
+ * routing order, row T*top_k + t is the shared expert of token t.  Within each
+ * row, every block of 8 consecutive columns is stored in the order
+ * 0,4,1,5,2,6,3,7 (the order in which the down GEMM consumes it).  Needs
+ * moe_route's outputs and workspace; leaves the group sums of h in the
+ * workspace for moe_down_combine.
+ * Weights are rebuilt exactly as (q - 8) * scale in fp16 plus an fp32 term for
+ * bias + 8 * scale; the activations enter the matrix cores in fp16.  Exact for
+ * |scale| in [2^-13, 2^12] and |x| below 65504 (larger x overflows). */
 moe_status moe_expert_gemm_q4(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                               const moe_routing *r, uint16_t *h, void *ws, size_t ws_bytes,
                               void *stream);
 
 /* Down GEMM plus routing-weighted combine:
  * y[t] = sum_j topk_w[t][j] * W_down[ids[t][j]] h[tok_row[t][j]] + W_sh_down h[T*top_k + t].
- * y: fp32 [T][H] (overwritten).  Each routed row's weighted output goes to a
- * workspace staging row and every token then adds its eight rows in pick
- * order, so y is reproducible bit for bit. */
+ * y: fp32 [T][H] (overwritten).  h must be the output of moe_expert_gemm_q4
+ * with the same workspace (whose group sums of h it reads).  Each routed row's
+ * weighted output goes to a workspace staging row and every token then adds
+ * its eight rows in pick order, so y is reproducible bit for bit. */
 moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe_weights *w,
                             const moe_routing *r, float *y, void *ws, size_t ws_bytes,
                             void *stream);

@@ -77,10 +77,9 @@ class LayerRun:
                     blocks=r.blocks.cpu().numpy()[:nb], num_blocks=nb)
 
 
-def bf16_np(t: torch.Tensor) -> np.ndarray:
-    """int16/bf16 device tensor of bf16 bits -> float32 numpy."""
-    u = t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16
-    return u.view(np.float32)
+def f16_np(t: torch.Tensor) -> np.ndarray:
+    """int16 device tensor of fp16 bits -> float32 numpy."""
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.float16).astype(np.float32)
 
 
 def perm_pos(col):
