@@ -15,7 +15,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed fp32 arithmetic in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs: the router sums its partial products with VALU
+    # MFMA accumulators in VGPRs: the GEMM's register budget (two workgroups per
+    # CU) fits without spills only in this form
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]

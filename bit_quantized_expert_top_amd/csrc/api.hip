@@ -35,6 +35,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.stage = take((size_t)T * k * H * 4);
     L.blk_cnt = take(nTB * E * 4);
     L.lrank = take((size_t)T * k * 4);
+    L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
     L.dec = take(T == 1 ? decode_scratch_bytes(I, k) : 0);
     L.total = off;
     return L;
@@ -120,7 +121,7 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
     }
     launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, lrank, s->T, s->E, s->top_k, kBM,
                         r->counts, r->offsets, r->row_token, r->tok_row, r->row_w, r->blocks,
-                        r->num_blocks, st);
+                        r->num_blocks, (int32_t *)(ws + L.sched), st);
     return launched();
 }
 
@@ -129,8 +130,8 @@ moe_status enqueue_gateup(const moe_shape *s, const uint16_t *x, const moe_weigh
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
     (void)x;
     launch_gateup(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum), gp(w->gate), gp(w->up), gp(w->sh_gate),
-                  gp(w->sh_up), r->blocks, r->num_blocks, max_blocks_for(s->T, s->E, s->top_k),
-                  r->row_token, h, (float *)(ws + L.hsum), st);
+                  gp(w->sh_up), r->blocks, r->num_blocks, (const int32_t *)(ws + L.sched),
+                  max_blocks_for(s->T, s->E, s->top_k), r->row_token, h, (float *)(ws + L.hsum), st);
     return launched();
 }
 
@@ -140,7 +141,7 @@ moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights
     // group sums of h: left in the workspace by the gate/up pass
     const float *hsum = (const float *)(ws + L.hsum);
     launch_down(*s, h, hsum, gp(w->down), gp(w->sh_down), r->blocks, r->num_blocks,
-                max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
+                (const int32_t *)(ws + L.sched), max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
                 (float *)(ws + L.stage), y, st);
     return launched();
 }

@@ -74,6 +74,7 @@ struct WsLayout {
     size_t stage;       // fp32 [T*k][H]          routed down outputs times routing weight
     size_t blk_cnt;     // int32 [T/16][E]        per token-block expert counts / bases
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
+    size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (largest first)
     size_t dec;         // decode scratch
     size_t total;
 };
@@ -93,7 +94,7 @@ void launch_route_select(const float *part, const float *exact, const float *xsq
 void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
                          int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
-                         int32_t *blocks, int32_t *num_blocks, hipStream_t s);
+                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, hipStream_t s);
 void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
                      hipStream_t s);
 
@@ -105,10 +106,11 @@ struct GemmProj {
 
 void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum, GemmProj gate,
                    GemmProj up, GemmProj sgate, GemmProj sup, const int32_t *blocks,
-                   const int32_t *num_blocks, int max_blocks, const int32_t *row_token,
-                   uint16_t *h, float *hsum, hipStream_t s);
+                   const int32_t *num_blocks, const int32_t *sched, int max_blocks,
+                   const int32_t *row_token, uint16_t *h, float *hsum, hipStream_t s);
 void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
-                 GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks, int max_blocks,
+                 GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks,
+                 const int32_t *sched, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  float *stage, float *y, hipStream_t s);
 

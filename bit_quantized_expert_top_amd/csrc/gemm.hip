@@ -38,6 +38,8 @@
 // read is free of bank conflicts.  Two workgroups share a CU.
 #include "common.h"
 
+#include <algorithm>
+
 namespace moe {
 
 constexpr int NW = 4;                        // waves per workgroup
@@ -62,6 +64,7 @@ struct GemmArgs {
     GemmProj s0, s1;       // the shared expert's
     const int32_t *blocks;
     const int32_t *num_blocks;
+    const int32_t *sched;  // routed blocks in GEMM order
     int max_blocks;
     const int32_t *row_token;
     const float *row_w;
@@ -149,7 +152,9 @@ __device__ __forceinline__ void column_of(const GemmArgs &a, const Tile &t, int 
 template <int MODE, int MT>
 __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
-    const int tid = threadIdx.x, lane = tid & 63;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));              // recomputed per item: nothing lane-dependent is hoisted
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, gg = lane >> 5;
     const int K = a.K, G = a.G, nch = K / KC;
@@ -384,38 +389,61 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     }
 }
 
+// Persistent grid: workgroup g takes work items j = g, g + gridDim, ...  Item j
+// is (slot, n-tile) with slot = 8 (j / 8 / n_tiles) + j % 8 and n-tile
+// (j / 8) % n_tiles, so all n-tiles of one block (which share its activation
+// rows) land on workgroups with the same g mod 8, i.e. on the same XCD.  Slots
+// are the shared-expert blocks, then the routed blocks in the routing
+// schedule's order (largest first), so every round of the grid takes items of
+// similar cost and the tail is short.
 template <int MODE>
 __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    Tile t;
-    const int bid = (int)blockIdx.x / a.n_tiles;
-    t.ntile = (int)blockIdx.x % a.n_tiles;
-    // shared-expert blocks first (full tiles), then the routed block map
-    t.shared = bid < a.n_shared;
-    t.e = 0;
-    if (!t.shared) {
-        const int mb = bid - a.n_shared;
-        if (mb >= a.num_blocks[0] || mb >= a.max_blocks) return;
-        t.e = a.blocks[3 * mb];
-        t.r0 = a.blocks[3 * mb + 1];
-        t.nrows = a.blocks[3 * mb + 2];
-        // a malformed block map turns into a no-op, never an out-of-bounds access
-        if (t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
-            t.r0 + t.nrows > a.T * a.topk)
-            return;
-    } else {
-        t.r0 = a.T * a.topk + bid * kBM;
-        t.nrows = min(kBM, a.T - bid * kBM);
-    }
-    switch ((t.nrows + 31) >> 5) {
-        case 1: gemm_tile<MODE, 1>(a, t, smem); break;
-        case 2: gemm_tile<MODE, 2>(a, t, smem); break;
-        case 3: gemm_tile<MODE, 3>(a, t, smem); break;
-        default: gemm_tile<MODE, 4>(a, t, smem); break;
+    const int nb = min(a.num_blocks[0], a.max_blocks);
+    const int S = a.n_shared + max(nb, 0);
+    const int jend = ((S + 7) >> 3) * 8 * a.n_tiles;
+    for (int j = blockIdx.x; j < jend; j += gridDim.x) {
+        const int q = j >> 3;
+        const int slot = (q / a.n_tiles) * 8 + (j & 7);
+        if (slot >= S) continue;
+        Tile t;
+        t.ntile = q % a.n_tiles;
+        t.shared = slot < a.n_shared;
+        t.e = 0;
+        if (!t.shared) {
+            const int mb = a.sched[slot - a.n_shared];
+            if (mb < 0 || mb >= nb) continue;
+            t.e = a.blocks[3 * mb];
+            t.r0 = a.blocks[3 * mb + 1];
+            t.nrows = a.blocks[3 * mb + 2];
+            // a malformed block map turns into a no-op, never an out-of-bounds access
+            if (t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
+                t.r0 + t.nrows > a.T * a.topk)
+                continue;
+        } else {
+            t.r0 = a.T * a.topk + slot * kBM;
+            t.nrows = min(kBM, a.T - slot * kBM);
+        }
+        __syncthreads();                         // the previous item is done with the LDS
+        switch ((t.nrows + 31) >> 5) {
+            case 1: gemm_tile<MODE, 1>(a, t, smem); break;
+            case 2: gemm_tile<MODE, 2>(a, t, smem); break;
+            case 3: gemm_tile<MODE, 3>(a, t, smem); break;
+            default: gemm_tile<MODE, 4>(a, t, smem); break;
+        }
     }
 }
 
 static int shared_blocks(int T) { return (T + kBM - 1) / kBM; }
+
+// persistent grid: two workgroups per CU, never more than there are work items
+static unsigned grid_for(int n_shared, int max_blocks, int n_tiles) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const long items = (long)((n_shared + max_blocks + 7) / 8) * 8 * n_tiles;
+    return (unsigned)std::min<long>(items, 2L * cus);
+}
 
 // the GEMM needs more dynamic LDS than the default launch limit
 template <int MODE>
@@ -430,8 +458,8 @@ static void allow_lds() {
 
 void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, GemmProj gate,
                    GemmProj up, GemmProj sgate, GemmProj sup, const int32_t *blocks,
-                   const int32_t *num_blocks, int max_blocks, const int32_t *row_token,
-                   uint16_t *h, float *hsum, hipStream_t s) {
+                   const int32_t *num_blocks, const int32_t *sched, int max_blocks,
+                   const int32_t *row_token, uint16_t *h, float *hsum, hipStream_t s) {
     GemmArgs a{};
     a.A = xp;
     a.Asum = xsum;
@@ -444,6 +472,7 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, G
     a.s1 = sup;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
+    a.sched = sched;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.T = sh.T;
@@ -454,8 +483,8 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, G
     a.h = h;
     a.hsum = hsum;
     allow_lds<0>();
-    const int nmb = max_blocks + a.n_shared;
-    hipLaunchKernelGGL(q4_gemm_kernel<0>, dim3(nmb * a.n_tiles), dim3(NTHR), L_TOTAL, s, a);
+    hipLaunchKernelGGL(q4_gemm_kernel<0>, dim3(grid_for(a.n_shared, max_blocks, a.n_tiles)),
+                       dim3(NTHR), L_TOTAL, s, a);
 }
 
 // y[t] += sum_j stage[tok_row[t][j]] in pick order j = 0..k-1: a fixed order, so
@@ -481,7 +510,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
-                 GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks, int max_blocks,
+                 GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks,
+                 const int32_t *sched, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  float *stage, float *y, hipStream_t s) {
     GemmArgs a{};
@@ -494,6 +524,7 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, Gemm
     a.s0 = sdown;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
+    a.sched = sched;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.row_w = row_w;
@@ -506,8 +537,8 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, Gemm
     a.stage = stage;
     allow_lds<1>();
     // shared-expert blocks write y, routed blocks their weighted staging rows ...
-    const int nmb = max_blocks + a.n_shared;
-    hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(nmb * a.n_tiles), dim3(NTHR), L_TOTAL, s, a);
+    hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(grid_for(a.n_shared, max_blocks, a.n_tiles)),
+                       dim3(NTHR), L_TOTAL, s, a);
     // ... then each token adds its eight routed rows
     const size_t n4 = (size_t)sh.T * sh.H / 4;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, stage,

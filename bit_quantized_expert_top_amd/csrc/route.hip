@@ -563,9 +563,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t *__restrict__ blk_base, const int32_t *__restrict__ lrank,
     const int32_t *__restrict__ counts, int T, int E, int k, int BM,
     int32_t *__restrict__ offsets, int32_t *__restrict__ blocks, int32_t *__restrict__ num_blocks,
-    int32_t *__restrict__ row_token, int32_t *__restrict__ tok_row, float *__restrict__ row_w) {
+    int32_t *__restrict__ row_token, int32_t *__restrict__ tok_row, float *__restrict__ row_w,
+    int32_t *__restrict__ sched) {
     __shared__ int tmp[256];
     __shared__ int s_off[256];
+    __shared__ unsigned long long cls_scan[256];
     const int tid = threadIdx.x;
     const int cnt = counts[tid];
     tmp[tid] = cnt;
@@ -601,6 +603,30 @@ __global__ __launch_bounds__(256) void scatter_kernel(
             bp[1] = off + i * BM;
             bp[2] = min(BM, cnt - i * BM);
         }
+        // GEMM schedule: blocks by cost class (32-row M tiles: 4, 3, 2, 1), then by
+        // expert.  Four 16-bit class counters per expert are scanned as one word.
+        const int last_rows = nblk ? cnt - (nblk - 1) * BM : 0;
+        const int last_cls = nblk ? 4 - min(4, (last_rows + 31) >> 5) : 0;   // 0 = 4 tiles
+        unsigned long long mine = 0;
+        if (nblk) mine = (unsigned long long)(nblk - 1) + (1ull << (16 * last_cls));
+        cls_scan[tid] = mine;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const unsigned long long a = tid >= o ? cls_scan[tid - o] : 0ull;
+            __syncthreads();
+            cls_scan[tid] += a;
+            __syncthreads();
+        }
+        const unsigned long long tot = cls_scan[255], pre = cls_scan[tid] - mine;
+        int base[4];
+        base[0] = 0;
+        for (int c = 1; c < 4; ++c) base[c] = base[c - 1] + (int)((tot >> (16 * (c - 1))) & 0xFFFF);
+        int p0 = base[0] + (int)(pre & 0xFFFF);
+        for (int i = 0; i + 1 < nblk; ++i) sched[p0++] = bstart + i;
+        if (nblk) {
+            const int pl = last_cls == 0 ? p0 : base[last_cls] + (int)((pre >> (16 * last_cls)) & 0xFFFF);
+            sched[pl] = bstart + nblk - 1;
+        }
     }
     __syncthreads();
     const int idx = blockIdx.x * 256 + tid;
@@ -618,12 +644,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
                          int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
-                         int32_t *blocks, int32_t *num_blocks, hipStream_t s) {
+                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, hipStream_t s) {
     const int nTB = (T + TB - 1) / TB;
     hipLaunchKernelGGL(scan_experts_kernel, dim3(E), dim3(256), 0, s, blk_cnt, nTB, E, counts);
     hipLaunchKernelGGL(scatter_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w, blk_cnt,
                        lrank, counts, T, E, k, BM, offsets, blocks, num_blocks, row_token,
-                       tok_row, row_w);
+                       tok_row, row_w, sched);
 }
 
 // Activation preparation for the GEMM: fp16 copy with the 8-block permutation
