@@ -211,6 +211,9 @@ moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weigh
                       void *stream) {
     MOE_TRY(check_shape(shape));
     if (shape->T != 1) return MOE_ERR_INVALID_ARG;
+    // the decode kernels split a row over a power-of-two number of lanes
+    if ((shape->H & (shape->H - 1)) != 0 || (shape->I & (shape->I - 1)) != 0)
+        return MOE_ERR_UNSUPPORTED;
     if (!aligned(x) || !aligned(topk_ids) || !aligned(topk_w) || !aligned(y))
         return MOE_ERR_INVALID_ARG;
     MOE_TRY(check_weights(w, true, true, true));

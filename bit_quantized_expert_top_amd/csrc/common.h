@@ -54,6 +54,64 @@ __device__ __forceinline__ float f16_hi(uint32_t v) {
     return (float)__builtin_bit_cast(f16x2, v)[1];
 }
 
+// Monotone uint32 key of a float (larger float -> larger key; -0 ranks with +0)
+// and its inverse.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 ranks with +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t kh) {
+    return __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
+}
+
+
+// Wave-wide unsigned max, returned in every lane: DPP steps inside each row of
+// 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row
+// results read as scalars.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+    v = dpp_umax<0xB1>(v);
+    v = dpp_umax<0x4E>(v);
+    v = dpp_umax<0x141>(v);
+    v = dpp_umax<0x140>(v);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+
+// Largest key among 4 per lane (key[j] belongs to expert lane + 64 j; taken
+// entries excluded), ties to the lowest expert index.  Returns the expert.
+__device__ __forceinline__ int wave_argmax4(const uint32_t (&key)[4], const bool (&taken)[4],
+                                            uint32_t *kmax) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (!taken[j] && key[j] > m) m = key[j];
+    m = wave_umax(m);
+    *kmax = m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t b = __ballot(!taken[j] && key[j] == m);
+        if (b) return 64 * j + __builtin_ctzll(b);
+    }
+    return -1;
+}
+
+// Sum over aligned groups of n lanes (n = 1, 2, 4, 8 or 16) with DPP; every
+// lane of a group ends with the group's sum.
+__device__ __forceinline__ float group_sum_dpp(float v, int n) {
+    if (n >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    if (n >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    if (n >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if (n >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // Activations enter the GEMMs with every 8-column block stored in the order
 // (0,4,1,5,2,6,3,7), matching the pair order in which 4-bit codes unpack.
 // Position of column `col` in that storage.

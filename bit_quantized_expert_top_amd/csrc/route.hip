@@ -136,56 +136,10 @@ void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *
 constexpr int TB = 16;            // tokens per routing block (one wave each)
 constexpr int RS_SPLIT = 4;       // K splits of the approximate router
 
-__device__ __forceinline__ uint32_t ordered_key(float f) {
-    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 ranks with +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_to_float(uint32_t kh) {
-    return __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
-}
-
-
 __device__ __forceinline__ float wave_sum_f(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
     return v;
-}
-
-// Wave-wide unsigned max, returned in every lane: DPP steps inside each row of
-// 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row
-// results read as scalars.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-    return o > v ? o : v;
-}
-__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
-    v = dpp_umax<0xB1>(v);
-    v = dpp_umax<0x4E>(v);
-    v = dpp_umax<0x141>(v);
-    v = dpp_umax<0x140>(v);
-    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
-    return ab > cd ? ab : cd;
-}
-
-// Largest key among 4 per lane (key[j] belongs to expert lane + 64 j; taken
-// entries excluded), ties to the lowest expert index.  Returns the expert.
-__device__ __forceinline__ int wave_argmax4(const uint32_t (&key)[4], const bool (&taken)[4],
-                                            uint32_t *kmax) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (!taken[j] && key[j] > m) m = key[j];
-    m = wave_umax(m);
-    *kmax = m;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint64_t b = __ballot(!taken[j] && key[j] == m);
-        if (b) return 64 * j + __builtin_ctzll(b);
-    }
-    return -1;
 }
 
 // 8 bf16 values k = 0..7 -> fp16 in the GEMM operand order (0,4,1,5,2,6,3,7).

@@ -146,7 +146,9 @@ moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weight
  * only the selected experts' packed weights (mechatronicstore.cl "Decode:
  * mover menos bytes por token"; neuro-ai.ru "Спекулятивное ...": batch-1
  * decode is bound by weight bandwidth).  topk_ids [top_k], topk_w [top_k],
- * y fp32 [H] (overwritten). */
+ * y fp32 [H] (overwritten).  The ids equal those of the fixed-order logits;
+ * h is kept in fp16 between the two GEMVs.  MOE_ERR_UNSUPPORTED unless H and
+ * I are powers of two. */
 moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                       int32_t *topk_ids, float *topk_w, float *y, void *ws, size_t ws_bytes,
                       void *stream);

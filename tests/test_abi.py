@@ -132,6 +132,11 @@ def test_decode_needs_t1():
     _, need1, _, _ = query(s1)
     assert L.moe_decode(C.byref(s1), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE, need1 - 1,
                         None) == WS
+    # the decode kernels need power-of-two H and I
+    s3 = shape(T=1, H=768)
+    _, need3, _, _ = query(s3)
+    assert L.moe_decode(C.byref(s3), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE, need3,
+                        None) == UNSUP
 
 
 def test_misc_validation():
