@@ -24,7 +24,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
         off += align256(bytes);
         return o;
     };
-    const size_t nTB = (size_t)(T + 15) / 16;
+    const size_t nTB = (size_t)(T + kTB - 1) / kTB;
     L.logits = take((size_t)T * E * 4);
     L.xsum = take((size_t)T * (H / 64) * 4);
     L.xp = take((size_t)T * H * 2);

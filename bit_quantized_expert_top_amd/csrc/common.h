@@ -20,6 +20,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kGroup = 64;      // quantisation group along K
 constexpr int kBM = 128;        // rows per routing block (GEMM M tile)
+constexpr int kTB = 8;          // tokens per routing token block (one wave each)
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
@@ -130,7 +131,7 @@ struct WsLayout {
     size_t wn2;         // fp32 [4][E]            squared norms of the router rows, per K split
     size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h (fp16 values)
     size_t stage;       // fp32 [T*k][H]          routed down outputs times routing weight
-    size_t blk_cnt;     // int32 [T/16][E]        per token-block expert counts / bases
+    size_t blk_cnt;     // int32 [T/kTB][E]       per token-block expert counts / bases
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
     size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (largest first)
     size_t dec;         // decode scratch

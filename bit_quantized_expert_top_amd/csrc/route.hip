@@ -133,7 +133,7 @@ void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *
 //    (same order as router_logits) and the top-8 is taken from those.  Either
 //    way the ids equal those of the fixed-order logits, bit for bit.
 // ---------------------------------------------------------------------------
-constexpr int TB = 16;            // tokens per routing block (one wave each)
+constexpr int TB = kTB;           // tokens per routing block (one wave each)
 constexpr int RS_SPLIT = 4;       // K splits of the approximate router
 
 __device__ __forceinline__ float wave_sum_f(float v) {
@@ -178,20 +178,31 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     const floatx16 zero = {};
     const int nch = klen / 64;
     float wsq = 0.0f;
-    u32x4 av[4], bv[4], an[4], bn[4];
+    // 4-slot register ring, loads issued three chunks ahead (nch <= 8 since H <= 2048
+    // and S = 4); fully unrolled so that every slot index is static
+    constexpr int RING = 4, MAXCH = 8;
+    u32x4 ra[RING][4], rb[RING][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        av[j] = *(const u32x4 *)(pa + 16 * j);
-        bv[j] = *(const u32x4 *)(pb + 16 * j);
-    }
-    for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) {
+    for (int c = 0; c < RING - 1; ++c)
+        if (c < nch) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                an[j] = *(const u32x4 *)(pa + 64 * (c + 1) + 16 * j);
-                bn[j] = *(const u32x4 *)(pb + 64 * (c + 1) + 16 * j);
+                ra[c][j] = *(const u32x4 *)(pa + 64 * c + 16 * j);
+                rb[c][j] = *(const u32x4 *)(pb + 64 * c + 16 * j);
             }
         }
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c) {
+        if (c >= nch) break;
+        if (c + RING - 1 < nch) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ra[(c + RING - 1) % RING][j] = *(const u32x4 *)(pa + 64 * (c + RING - 1) + 16 * j);
+                rb[(c + RING - 1) % RING][j] = *(const u32x4 *)(pb + 64 * (c + RING - 1) + 16 * j);
+            }
+        }
+        const u32x4(&av)[4] = ra[c % RING];
+        const u32x4(&bv)[4] = rb[c % RING];
         floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, av[0]), __builtin_bit_cast(bf16x8, bv[0]), zero, 0, 0, 0);
 #pragma unroll
@@ -232,13 +243,6 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                     wsq = __builtin_fmaf(bf16_hi(bv[j][r]), bf16_hi(bv[j][r]), wsq);
                 }
         }
-        if (c + 1 < nch) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                av[j] = an[j];
-                bv[j] = bn[j];
-            }
-        }
     }
     if (do_norm) {
         wsq += __shfl_xor(wsq, 32);
@@ -254,19 +258,16 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 
 // Fixed-order logit of one expert row for the half-wave `half` (lanes
 // 32*half .. +31): lane c computes chunk c sequentially from its first product
-// (xv: the token's 64 inputs of chunk c, already in registers); the chunk
-// partials go through LDS (scratch: 64 floats for the wave) and the first lane
-// of each half adds them in chunk order, then the bias.  Called by the whole
-// wave; the result is valid in lanes 0 (half 0) and 32 (half 1).
-__device__ float canon_logit_half(const u32x4 (&xv)[8], const uint16_t *wrow, int H, float bias_e,
-                                  int lane, float *scratch) {
+// (xv: the token's 64 inputs of chunk c, wv: the expert's, both already in
+// registers); the chunk partials go through LDS (scratch: 64 floats for the
+// wave) and the first lane of each half adds them in chunk order, then the
+// bias.  Called by the whole wave; the result is valid in lanes 0 (half 0) and
+// 32 (half 1).
+__device__ float canon_logit_half(const u32x4 (&xv)[8], const u32x4 (&wv)[8], bool live, int H,
+                                  float bias_e, int lane, float *scratch) {
     const int c = lane & 31, nch = H / 64;
     float part = 0.0f;
-    if (c < nch && wrow) {
-        const u32x4 *pw = (const u32x4 *)(wrow + 64 * c);
-        u32x4 wv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) wv[q] = pw[q];      // all loads in flight before use
+    if (c < nch && live) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
 #pragma unroll
@@ -295,6 +296,41 @@ __device__ float canon_logit_half(const u32x4 (&xv)[8], const uint16_t *wrow, in
     }
     __builtin_amdgcn_wave_barrier();
     return total;
+}
+
+// Fixed-order logits of the nc experts cand_e[0..nc) of token row xr into
+// cand_l, two per step (one per half-wave); the next step's router rows are
+// loaded while the current step is summed.
+__device__ void recompute_candidates(const uint32_t *cand_e, float *cand_l, int nc,
+                                     const uint16_t *__restrict__ xr,
+                                     const uint16_t *__restrict__ wr, const float *__restrict__ bias,
+                                     int H, int lane, float *scratch) {
+    const int c = lane & 31;
+    const bool has_chunk = c < H / 64;
+    u32x4 xv[8], wv[8], wn[8];
+    if (has_chunk) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xv[q] = ((const u32x4 *)(xr + 64 * c))[q];
+    }
+    auto load = [&](int c0, u32x4 (&dst)[8]) {
+        const int ci = c0 + (lane >> 5);
+        const int e = ci < nc ? (int)cand_e[ci] : -1;
+        if (has_chunk && e >= 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) dst[q] = ((const u32x4 *)(wr + (size_t)e * H + 64 * c))[q];
+        }
+    };
+    load(0, wv);
+    for (int c0 = 0; c0 < nc; c0 += 2) {
+        if (c0 + 2 < nc) load(c0 + 2, wn);
+        const int ci = c0 + (lane >> 5);
+        const int e = ci < nc ? (int)cand_e[ci] : -1;
+        const float b = (e >= 0 && bias) ? bias[e] : 0.0f;
+        const float L = canon_logit_half(xv, wv, e >= 0, H, b, lane, scratch);
+        if (c == 0 && ci < nc) cand_l[ci] = L;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wv[q] = wn[q];
+    }
 }
 
 __global__ __launch_bounds__(64 * TB) void route_select_kernel(
@@ -336,75 +372,125 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 dl[j] = 0x1p-16f * (sqrtf(w2) * nx * 1.001f + fabsf(b)) + 0x1p-100f;
             }
         }
-        // ---- top-k by the (approximate) logits, ties to the lower index
-        uint32_t key[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) key[j] = ordered_key(lt[j]);
-        bool taken[4] = {false, false, false, false};
+        // ---- top-k by the (approximate) logits, ties to the lower index, then the
+        // certificate.  Up to two rounds: if the first fails, only the experts in
+        // ambiguous clusters (adjacent picks whose intervals overlap, plus the
+        // boundary between the k-th pick and the rest) get their fixed-order
+        // logit, with a zero radius, and the selection is certified again.
+        bool taken[4];
         int my_pick = -1;
         float my_l = 0.0f, my_lb = 0.0f, my_ub = 0.0f;
-        for (int p = 0; p < k; ++p) {
-            uint32_t km;
-            const int e = wave_argmax4(key, taken, &km);
-            float lb = 0.0f, ub = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (lane + 64 * j == e) {
-                    taken[j] = true;
-                    lb = lt[j] - dl[j];
-                    ub = lt[j] + dl[j];
-                }
-            const float lbe = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lb), e & 63));
-            const float ube = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ub), e & 63));
-            if (lane == p) {
-                my_pick = e;
-                my_l = key_to_float(km);
-                my_lb = lbe;
-                my_ub = ube;
-            }
-        }
-        // ---- certification: disjoint intervals in rank order, nothing else reaching the 8th
         float m8 = INFINITY;
-        for (int p = 0; p < k; ++p)
-            m8 = fminf(m8, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_lb), p)));
-        // lane p < k-1 compares its lower bound with the upper bound of pick p+1
-        float next_ub = 0.0f;
-        for (int p = 0; p + 1 < k; ++p) {
-            const float nu = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ub), p + 1));
-            if (lane == p) next_ub = nu;
-        }
-        const bool pair_ok = (lane >= k - 1) || (my_lb > next_ub);
-        bool extra = false;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (!taken[j] && lt[j] + dl[j] >= m8) extra = true;
-        const bool certified = __all(pair_ok) && !__any(extra);
-        float wl = my_l;   // logit used for the weights (lanes < k)
-        if (!certified) {
-            // candidates: every expert whose interval reaches m8 (includes the k picks)
-            const uint16_t *xr = x + (size_t)t * H;
-            u32x4 xv[8];
-            if ((lane & 31) < H / 64) {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) xv[q] = ((const u32x4 *)(xr + 64 * (lane & 31)))[q];
-            }
-            int nc = 0;
+        bool certified = false;
+        for (int round = 0; round < 2; ++round) {
+            uint32_t key[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bool c = taken[j] || (lt[j] + dl[j] >= m8);
+                key[j] = ordered_key(lt[j]);
+                taken[j] = false;
+            }
+            for (int p = 0; p < k; ++p) {
+                uint32_t km;
+                const int e = wave_argmax4(key, taken, &km);
+                float lb = 0.0f, ub = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (lane + 64 * j == e) {
+                        taken[j] = true;
+                        lb = lt[j] - dl[j];
+                        ub = lt[j] + dl[j];
+                    }
+                const float lbe = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lb), e & 63));
+                const float ube = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ub), e & 63));
+                if (lane == p) {
+                    my_pick = e;
+                    my_l = key_to_float(km);
+                    my_lb = lbe;
+                    my_ub = ube;
+                }
+            }
+            // certificate: disjoint intervals in rank order, nothing else reaching the k-th
+            m8 = INFINITY;
+            for (int p = 0; p < k; ++p)
+                m8 = fminf(m8, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_lb), p)));
+            // lane p < k-1 compares its lower bound with the upper bound of pick p+1
+            float next_ub = 0.0f, prev_lb = INFINITY;
+            for (int p = 0; p + 1 < k; ++p) {
+                const float nu = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ub), p + 1));
+                const float pl = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_lb), p));
+                if (lane == p) next_ub = nu;
+                if (lane == p + 1) prev_lb = pl;
+            }
+            const bool pair_ok = (lane >= k - 1) || (my_lb > next_ub);
+            bool extra = false;
+            float extra_ub = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!taken[j] && lt[j] + dl[j] >= m8) {
+                    extra = true;
+                    extra_ub = fmaxf(extra_ub, lt[j] + dl[j]);
+                }
+            certified = __all(pair_ok) && !__any(extra);
+            if (certified || round == 1) break;
+
+            // ---- cluster recompute: the ambiguous picks and the extras
+            const float max_xub = key_to_float(wave_umax(ordered_key(extra_ub)));
+            const bool amb_pick = lane < k && ((lane + 1 < k && my_lb <= next_ub) ||
+                                               (lane > 0 && prev_lb <= my_ub) || my_lb <= max_xub);
+            int nc = 0;
+            {
+                const uint64_t bal = __ballot(amb_pick);
+                const int pos = (int)__popcll(bal & ((1ull << lane) - 1ull));
+                if (amb_pick) cand_e[tl][pos] = my_pick;
+                nc = (int)__popcll(bal);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool c = !taken[j] && lt[j] + dl[j] >= m8;
                 const uint64_t bal = __ballot(c);
                 const int pos = nc + (int)__popcll(bal & ((1ull << lane) - 1ull));
                 if (c) cand_e[tl][pos] = lane + 64 * j;
                 nc += (int)__popcll(bal);
             }
             __builtin_amdgcn_wave_barrier();
-            for (int c0 = 0; c0 < nc; c0 += 2) {
-                const int ci = c0 + (lane >> 5);
-                const int e = ci < nc ? (int)cand_e[tl][ci] : -1;
-                const float b = (e >= 0 && bias) ? bias[e] : 0.0f;
-                const float L = canon_logit_half(xv, e >= 0 ? wr + (size_t)e * H : nullptr, H, b,
-                                                 lane, scr[tl]);
-                if ((lane & 31) == 0 && ci < nc) cand_l[tl][ci] = L;
+            recompute_candidates(cand_e[tl], cand_l[tl], nc, x + (size_t)t * H, wr, bias, H, lane,
+                                 scr[tl]);
+            __builtin_amdgcn_wave_barrier();
+            for (int ci = 0; ci < nc; ++ci) {
+                const int e = (int)cand_e[tl][ci];
+                const float L = cand_l[tl][ci];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (lane + 64 * j == e) {
+                        lt[j] = L;
+                        dl[j] = 0.0f;
+                    }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        float wl = my_l;   // logit used for the weights (lanes < k)
+        if (!certified) {
+            // candidates: every expert whose interval reaches m8 (includes the k picks);
+            // those not yet exact first (they are recomputed), then the exact ones
+            int nc = 0;
+            for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool c = (taken[j] || (lt[j] + dl[j] >= m8)) &&
+                                   ((dl[j] == 0.0f) == (pass == 1));
+                    const uint64_t bal = __ballot(c);
+                    const int pos = nc + (int)__popcll(bal & ((1ull << lane) - 1ull));
+                    if (c) {
+                        cand_e[tl][pos] = lane + 64 * j;
+                        if (pass == 1) cand_l[tl][pos] = lt[j];
+                    }
+                    nc += (int)__popcll(bal);
+                }
+                if (pass == 0) {
+                    __builtin_amdgcn_wave_barrier();
+                    recompute_candidates(cand_e[tl], cand_l[tl], nc, x + (size_t)t * H, wr, bias, H,
+                                         lane, scr[tl]);
+                }
             }
             __builtin_amdgcn_wave_barrier();
             // top-k among the candidates by the exact logits (ties to the lower index)
