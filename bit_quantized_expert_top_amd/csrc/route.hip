@@ -170,8 +170,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     const bool do_prep = blockIdx.y == 0 && (wave >> 1) == 0 && t0 + l32 < T;
     const bool do_norm = blockIdx.x == 0 && (wave & 1) == 0;
     const int G = H / 64;
-    const uint16_t *pa = x + (size_t)trow * H + kbeg + 8 * gg;
-    const uint16_t *pb = wr + (size_t)(e0 + l32) * H + kbeg + 8 * gg;
+    // k order inside a chunk: step j of half gg holds k = 32 gg + 8 j + 0..7, so
+    // each lane reads 64 contiguous bytes of its row (the same order for both
+    // operands; the approximate logits are certified afterwards)
+    const uint16_t *pa = x + (size_t)trow * H + kbeg + 32 * gg;
+    const uint16_t *pb = wr + (size_t)(e0 + l32) * H + kbeg + 32 * gg;
     floatx16 tot;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tot[i] = 0.0f;
@@ -187,8 +190,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         if (c < nch) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                ra[c][j] = *(const u32x4 *)(pa + 64 * c + 16 * j);
-                rb[c][j] = *(const u32x4 *)(pb + 64 * c + 16 * j);
+                ra[c][j] = *(const u32x4 *)(pa + 64 * c + 8 * j);
+                rb[c][j] = *(const u32x4 *)(pb + 64 * c + 8 * j);
             }
         }
 #pragma unroll
@@ -197,8 +200,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         if (c + RING - 1 < nch) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                ra[(c + RING - 1) % RING][j] = *(const u32x4 *)(pa + 64 * (c + RING - 1) + 16 * j);
-                rb[(c + RING - 1) % RING][j] = *(const u32x4 *)(pb + 64 * (c + RING - 1) + 16 * j);
+                ra[(c + RING - 1) % RING][j] = *(const u32x4 *)(pa + 64 * (c + RING - 1) + 8 * j);
+                rb[(c + RING - 1) % RING][j] = *(const u32x4 *)(pb + 64 * (c + RING - 1) + 8 * j);
             }
         }
         const u32x4(&av)[4] = ra[c % RING];
@@ -212,9 +215,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) tot[i] += p[i];
         if (do_prep) {
-            // this lane holds k = 16j + 8gg + 0..7 of the chunk's group
+            // this lane holds k = 32gg + 8j + 0..7 of the chunk's group
             float s1 = 0.0f, s2 = 0.0f;
-            uint16_t *q = xp + (size_t)(t0 + l32) * H + kbeg + 64 * c + 8 * gg;
+            uint16_t *q = xp + (size_t)(t0 + l32) * H + kbeg + 64 * c + 32 * gg;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4 v = av[j];
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                     s2 = __builtin_fmaf(bf16_lo(v[r]), bf16_lo(v[r]), s2);
                     s2 = __builtin_fmaf(bf16_hi(v[r]), bf16_hi(v[r]), s2);
                 }
-                *(u32x4 *)(q + 16 * j) = permute_to_f16(v);
+                *(u32x4 *)(q + 8 * j) = permute_to_f16(v);
             }
             s1 += __shfl_xor(s1, 32);
             s2 += __shfl_xor(s2, 32);
