@@ -32,6 +32,34 @@ SEED_PREFILL = 4000
 SEED_DECODE = 2000
 
 
+# HBM traffic of the gate/up GEMM launch on this workload, from two rocprofv3 --pmc
+# runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean of 19
+# dispatches), each scaled by what the same counter reports for a plain 256 MiB
+# device-to-device copy (bench.py --copy-calibration 256: FETCH_SIZE reads
+# 131085.5 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
+# source these counters were taken on; otherwise the JSON reports null.
+GATEUP_TRAFFIC = {
+    "gemm_src_sha256": "b3f07a2ec21d3a6f3bb74a68b0c9df16a5d2d7fec626e79ae464f291ddc1a7ed",
+    "fetch_kib": 244373.6, "fetch_scale": 2.0,
+    "write_kib": 23063.5, "write_scale": 1.0,
+    "profile": "profiles/q4_gemm_gateup_prefill2048_zipf_hbm_traffic.md",
+}
+
+
+def gateup_traffic_bytes():
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                       "bit_quantized_expert_top_amd", "csrc", "gemm.hip")
+    try:
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    t = GATEUP_TRAFFIC
+    if h != t["gemm_src_sha256"]:
+        return None
+    return round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
+
+
 def expert_bytes(H, I):
     """Packed bytes of one expert: codes (0.5 B/weight) + bf16 scale and bias per 64 weights."""
     return 3 * H * I // 2 + 3 * H * (I // 64) * 4
@@ -235,7 +263,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "q4_gemm_kernel<0> (gate/up + SwiGLU)",
                      "achieved": round(gateup_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gateup_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_launch_us": round(gateup_ms * 1e3, 2),
+                     "traffic": gateup_traffic_bytes(), "avg_launch_us": round(gateup_ms * 1e3, 2),
                      "flops_per_launch": flops_gateup},
         "layer_mfma_frac": round(layer_mfma_frac, 4),
         "phase_us": {"route": round(route_ms * 1e3, 2), "gateup": round(gateup_ms * 1e3, 2),

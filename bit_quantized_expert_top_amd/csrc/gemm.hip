@@ -48,9 +48,12 @@ constexpr int KC = 64;                       // K per stage: one quantisation gr
 constexpr int NSTAGE = 3;
 constexpr int A_BYTES = kBM * KC * 2;        // [128 rows][8 x 16 B], 16 B slots XOR-swizzled
 constexpr int B_BYTES = 256 * 32;            // [256 columns][2 x 16 B halves], halves swizzled
-constexpr int S_BYTES = 256 * 4;             // one dword per column (bf16 in the low half)
-constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;   // + the group's bias per column
-constexpr int L_TOTAL = NSTAGE * STAGE;      // 79872: two workgroups per CU
+constexpr int STAGE = A_BYTES + B_BYTES;
+// scales and biases travel in pairs of groups (one dword per column, copied on
+// even chunks) through a 2-slot ring: [slot][s | b][256 columns] dwords
+constexpr int PAIR_BYTES = 2 * 256 * 4;
+constexpr int L_PAIR = NSTAGE * STAGE;
+constexpr int L_TOTAL = L_PAIR + 2 * PAIR_BYTES;   // 77824: two workgroups per CU
 constexpr int HS_LD = 272;                   // epilogue h tile row stride (bytes)
 constexpr int YS_LD = 1056;                  // epilogue y tile row stride (bytes)
 static_assert(kBM * HS_LD <= L_TOTAL && 32 * YS_LD <= L_TOTAL, "epilogue tiles fit the ring");
@@ -103,16 +106,15 @@ __device__ __forceinline__ floatx16 mfma16(f16x8 a, f16x8 b, floatx16 c) {
 }
 
 // Asynchronous global->LDS copies.  Lane i of the wave writes LDS bytes
-// [lds + 16 i, +16) (ushort form: the value zero-extended to the dword at
-// lds + 4 i).  Issued through inline assembly so that the compiler does not
+// [lds + 16 i, +16) (dword form: [lds + 4 i, +4)).  Issued through inline assembly so that the compiler does not
 // wait for them before every LDS read; completion is awaited explicitly
 // (s_waitcnt vmcnt) before the barrier that publishes a stage.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void dma2(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(lds)
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
 
@@ -198,10 +200,14 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             dma16(qsrc[i] + c * 8, base + (uint32_t)(A_BYTES + (i * 256 + wave * 64) * 16));
-        dma2(ssrc + c, base + (uint32_t)(A_BYTES + B_BYTES + wave * 64 * 4));
-        dma2(bsrc + c, base + (uint32_t)(A_BYTES + B_BYTES + S_BYTES + wave * 64 * 4));
+        if ((c & 1) == 0) {                      // groups c, c+1 (G is even)
+            const uint32_t pb = lds0 + (uint32_t)(L_PAIR + ((c >> 1) & 1) * PAIR_BYTES + wave * 256);
+            dma4(ssrc + c, pb);
+            dma4(bsrc + c, pb + 1024);
+        }
     };
-    // 8 copies per thread per stage: "all but the newest 8" = all of the older stage
+    // copies per thread: 8 for an even stage, 6 for an odd one.  Waiting for
+    // "all but the newest n" with n = the count of the stage issued after it.
 
     issue(0);
     if (nch > 1) issue(1);
@@ -220,10 +226,12 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     bool nz = false;                             // any group with b != -8 s in my columns
 
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch)
+        if (c + 1 >= nch)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (((c + 1) & 1) == 0)
             asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
         __syncthreads();                         // stage c visible; stage c-1 no longer read
         if (c + 2 < nch) issue(c + 2);
 
@@ -234,10 +242,10 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
         for (int nt = 0; nt < 2; ++nt) {
             const int bc = 64 * wave + 32 * nt + l32;
             wq[nt] = *(const u32x4 *)(sb + A_BYTES + bc * 32 + 16 * (gg ^ swb));
-            const uint32_t sv = *(const uint32_t *)(sb + A_BYTES + B_BYTES + bc * 4);
-            const uint32_t bv = *(const uint32_t *)(sb + A_BYTES + B_BYTES + S_BYTES + bc * 4);
-            const float sf = bf16_lo(sv);
-            nz |= bf16_lo(bv) != -8.0f * sf;
+            const uint8_t *pr = smem + L_PAIR + ((c >> 1) & 1) * PAIR_BYTES + bc * 4;
+            const uint32_t sv = *(const uint32_t *)pr, bv = *(const uint32_t *)(pr + 1024);
+            const float sf = (c & 1) ? bf16_hi(sv) : bf16_lo(sv);
+            nz |= ((c & 1) ? bf16_hi(bv) : bf16_lo(bv)) != -8.0f * sf;
             const _Float16 sh = (_Float16)sf;
             ss[nt] = f16x2{sh, sh};
         }
