@@ -32,7 +32,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.part = take((size_t)4 * T * E * 4);
     L.wn2 = take((size_t)4 * E * 4);
     L.hsum = take((size_t)(T * k + T) * (I / 64) * 4);
-    L.stage = take((size_t)T * k * H * 4);
+    L.stage = take((size_t)T * k * H * 2);
     L.blk_cnt = take(nTB * E * 4);
     L.lrank = take((size_t)T * k * 4);
     L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
@@ -142,7 +142,7 @@ moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights
     const float *hsum = (const float *)(ws + L.hsum);
     launch_down(*s, h, hsum, gp(w->down), gp(w->sh_down), r->blocks, r->num_blocks,
                 (const int32_t *)(ws + L.sched), max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
-                (float *)(ws + L.stage), y, st);
+                (uint16_t *)(ws + L.stage), y, st);
     return launched();
 }
 

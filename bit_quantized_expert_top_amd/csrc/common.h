@@ -130,7 +130,7 @@ struct WsLayout {
     size_t part;        // fp32 [4][T][E]         K-split approximate router logits
     size_t wn2;         // fp32 [4][E]            squared norms of the router rows, per K split
     size_t hsum;        // fp32 [T*k + T][I/64]   group sums of h (fp16 values)
-    size_t stage;       // fp32 [T*k][H]          routed down outputs times routing weight
+    size_t stage;       // bf16 [T*k][H]          routed down outputs times routing weight
     size_t blk_cnt;     // int32 [T/kTB][E]       per token-block expert counts / bases
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
     size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (largest first)
@@ -171,7 +171,7 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, Gemm
                  GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks,
                  const int32_t *sched, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
-                 float *stage, float *y, hipStream_t s);
+                 uint16_t *stage, float *y, hipStream_t s);
 
 void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w, int32_t *ids,
                    float *tw, float *y, void *scratch, hipStream_t s);

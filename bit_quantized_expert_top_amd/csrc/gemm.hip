@@ -77,7 +77,7 @@ struct GemmArgs {
     uint16_t *h;           // gate/up output, fp16 [T*topk + T][I]
     float *hsum;           // gate/up output, group sums of h [T*topk + T][I/64]
     float *y;
-    float *stage;          // routed down outputs times their routing weight [T*topk][H]
+    uint16_t *stage;       // routed down outputs times their routing weight, bf16 [T*topk][H]
 };
 
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
@@ -377,20 +377,27 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
             const int row = 32 * mt + rr;
             if (row < t.nrows) {
                 const uint8_t *src = smem + rr * YS_LD + seg * 128;
-                float *dst;
-                float wr = 1.0f;
+                const int col = t.ntile * 256 + seg * 32;
                 if (t.shared) {
-                    dst = a.y + (size_t)(t.r0 - Trk + row) * a.N;
-                } else {
-                    dst = a.stage + (size_t)(t.r0 + row) * a.N;
-                    wr = a.row_w[t.r0 + row];
-                }
-                dst += t.ntile * 256 + seg * 32;
+                    float *dst = a.y + (size_t)(t.r0 - Trk + row) * a.N + col;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    floatx4 v = *(const floatx4 *)(src + 16 * q);
-                    v *= wr;
-                    *(floatx4 *)(dst + 4 * q) = v;
+                    for (int q = 0; q < 8; ++q)
+                        *(floatx4 *)(dst + 4 * q) = *(const floatx4 *)(src + 16 * q);
+                } else {
+                    // routed row: weighted output staged in bf16 (fp32 range; the combine adds in fp32)
+                    uint16_t *dst = a.stage + (size_t)(t.r0 + row) * a.N + col;
+                    const float wr = a.row_w[t.r0 + row];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const floatx4 v0 = *(const floatx4 *)(src + 32 * q);
+                        const floatx4 v1 = *(const floatx4 *)(src + 32 * q + 16);
+                        u32x4 o;
+                        o.x = pack_bf16x2(wr * v0[0], wr * v0[1]);
+                        o.y = pack_bf16x2(wr * v0[2], wr * v0[3]);
+                        o.z = pack_bf16x2(wr * v1[0], wr * v1[1]);
+                        o.w = pack_bf16x2(wr * v1[2], wr * v1[3]);
+                        *(u32x4 *)(dst + 8 * q) = o;
+                    }
                 }
             }
         }
@@ -495,33 +502,46 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, G
                        dim3(NTHR), L_TOTAL, s, a);
 }
 
-// y[t] += sum_j stage[tok_row[t][j]] in pick order j = 0..k-1: a fixed order, so
-// the combined output is reproducible bit for bit.  One thread per 4 outputs.
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ stage,
+// y[t] += sum_j stage[tok_row[t][j]] in pick order j = 0..k-1, in fp32: a fixed
+// order, so the combined output is reproducible bit for bit.  One thread per 8
+// outputs (16 bytes of each bf16 staging row).
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ stage,
                                                       const int32_t *__restrict__ tok_row, int T,
                                                       int H, int k, float *__restrict__ y) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t per = (size_t)H / 4;
+    const size_t per = (size_t)H / 8;
     if (i >= (size_t)T * per) return;
-    const size_t t = i / per, n = (i % per) * 4;
-    float4 acc = *(const float4 *)(y + t * H + n);
-    for (int j = 0; j < k; ++j) {
-        const int r = tok_row[t * k + j];
-        if (r < 0 || r >= T * k) continue;
-        const float4 v = *(const float4 *)(stage + (size_t)r * H + n);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    const size_t t = i / per, n = (i % per) * 8;
+    float4 a0 = *(const float4 *)(y + t * H + n);
+    float4 a1 = *(const float4 *)(y + t * H + n + 4);
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = j < k ? tok_row[t * k + j] : -1;
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (rows[j] >= 0 && rows[j] < T * k) v[j] = *(const u32x4 *)(stage + (size_t)rows[j] * H + n);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (rows[j] < 0 || rows[j] >= T * k) continue;
+        a0.x += bf16_lo(v[j].x);
+        a0.y += bf16_hi(v[j].x);
+        a0.z += bf16_lo(v[j].y);
+        a0.w += bf16_hi(v[j].y);
+        a1.x += bf16_lo(v[j].z);
+        a1.y += bf16_hi(v[j].z);
+        a1.z += bf16_lo(v[j].w);
+        a1.w += bf16_hi(v[j].w);
     }
-    *(float4 *)(y + t * H + n) = acc;
+    *(float4 *)(y + t * H + n) = a0;
+    *(float4 *)(y + t * H + n + 4) = a1;
 }
 
 void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
                  GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks,
                  const int32_t *sched, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
-                 float *stage, float *y, hipStream_t s) {
+                 uint16_t *stage, float *y, hipStream_t s) {
     GemmArgs a{};
     a.A = h;
     a.Asum = hsum;
@@ -548,8 +568,8 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, Gemm
     hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(grid_for(a.n_shared, max_blocks, a.n_tiles)),
                        dim3(NTHR), L_TOTAL, s, a);
     // ... then each token adds its eight routed rows
-    const size_t n4 = (size_t)sh.T * sh.H / 4;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, stage,
+    const size_t n8 = (size_t)sh.T * sh.H / 8;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, stage,
                        tok_row, sh.T, sh.H, sh.top_k, y);
 }
 

@@ -130,8 +130,9 @@ moe_status moe_expert_gemm_q4(const moe_shape *shape, const uint16_t *x, const m
  * y[t] = sum_j topk_w[t][j] * W_down[ids[t][j]] h[tok_row[t][j]] + W_sh_down h[T*top_k + t].
  * y: fp32 [T][H] (overwritten).  h must be the output of moe_expert_gemm_q4
  * with the same workspace (whose group sums of h it reads).  Each routed row's
- * weighted output goes to a workspace staging row and every token then adds
- * its eight rows in pick order, so y is reproducible bit for bit. */
+ * weighted output is rounded to bf16 into a workspace staging row (fp32 range,
+ * relative error at most 2^-9 per routed term) and every token then adds its
+ * eight rows in pick order in fp32, so y is reproducible bit for bit. */
 moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe_weights *w,
                             const moe_routing *r, float *y, void *ws, size_t ws_bytes,
                             void *stream);
