@@ -105,7 +105,8 @@ def main():
 
     def device_layer(d):
         proj = {n: d[n] for n in moe.DeviceLayer.NAMES}
-        return moe.DeviceLayer(proj, d["router_wt"], d["router_bias"], device=dev)
+        # packed into the tile layout once, like a weight load; row copies dropped
+        return moe.DeviceLayer(proj, d["router_wt"], d["router_bias"], device=dev, keep_rows=False)
 
     # ---------------- prefill: T=2048, Zipf-skewed routing ----------------
     print(f"[bench] generating {args.sets} prefill weight sets", file=sys.stderr, flush=True)

@@ -3,7 +3,8 @@
 Thin Python binding over the C ABI of ``libmoeq4.so`` (``include/moe_q4.h``).
 The functions carry the C names (``moe_route``, ``moe_expert_gemm_q4``,
 ``moe_down_combine``, ``moe_layer``, ``moe_decode``, ``moe_rmsnorm_residual``,
-``moe_dequant_q4``, ``moe_query``); they only check tensors and marshal
+``moe_dequant_q4``, ``moe_query``, ``moe_packed_bytes``; ``moe_pack_weights``
+runs inside ``DeviceLayer``); they only check tensors and marshal
 pointers: every step of the layer runs in the library's HIP kernels.  PyTorch
 provides device memory and the stream.  Loading fails loudly when the library
 has not been built (``python -m bit_quantized_expert_top_amd.build`` or
@@ -20,6 +21,7 @@ from .binding import (  # noqa: F401
     moe_down_combine,
     moe_expert_gemm_q4,
     moe_layer,
+    moe_packed_bytes,
     moe_query,
     moe_rmsnorm_residual,
     moe_route,

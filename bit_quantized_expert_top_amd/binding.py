@@ -26,7 +26,7 @@ class _Q4(C.Structure):
 
 class _Weights(C.Structure):
     _fields_ = [("gate", _Q4), ("up", _Q4), ("down", _Q4), ("sh_gate", _Q4), ("sh_up", _Q4),
-                ("sh_down", _Q4), ("router_wt", P), ("router_bias", P)]
+                ("sh_down", _Q4), ("router_wt", P), ("router_bias", P), ("packed", P)]
 
 
 class _Routing(C.Structure):
@@ -40,6 +40,8 @@ _lib = None
 # every entry point of include/moe_q4.h with its ctypes signature
 _SIGS = {
     "moe_query": ([C.POINTER(_Shape), C.POINTER(C.c_size_t), C.POINTER(i32), C.POINTER(i32)], i32),
+    "moe_packed_bytes": ([C.POINTER(_Shape), C.POINTER(C.c_size_t)], i32),
+    "moe_pack_weights": ([C.POINTER(_Shape), C.POINTER(_Weights), P, C.c_size_t, P], i32),
     "moe_route": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, C.c_size_t,
                    P], i32),
     "moe_expert_gemm_q4": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P,
@@ -171,16 +173,25 @@ def _to_dev(a, device, dtype):
     return t.contiguous().view(dtype).to(device)
 
 
+def moe_packed_bytes(shape: Shape) -> int:
+    n = C.c_size_t()
+    _check(lib().moe_packed_bytes(C.byref(shape.c()), C.byref(n)), "moe_packed_bytes")
+    return n.value
+
+
 class DeviceLayer:
     """The layer's weights on the device (moe_weights).
 
     Each projection is given as (codes uint32, scale bf16-bits, bias bf16-bits)
-    arrays, numpy or torch; routed ones stacked [E][N][...].
+    arrays, numpy or torch; routed ones stacked [E][N][...].  The constructor
+    regroups them into the tile layout with moe_pack_weights (on the current
+    stream); keep_rows=False then drops the row-layout copies.
     """
 
     NAMES = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
-    def __init__(self, projections: dict, router_wt, router_bias=None, device="cuda"):
+    def __init__(self, projections: dict, router_wt, router_bias=None, device="cuda",
+                 keep_rows: bool = True):
         self.t = {}
         for n in self.NAMES:
             q, s, b = projections[n]
@@ -188,12 +199,29 @@ class DeviceLayer:
                          _to_dev(b, device, torch.int16))
         self.router_wt = _to_dev(router_wt, device, torch.int16)
         self.router_bias = None if router_bias is None else _to_dev(router_bias, device, torch.float32)
+        E, I, W = self.t["gate"][0].shape
+        self.shape = Shape(T=1, H=8 * W, I=I, E=E)
+        nbytes = moe_packed_bytes(self.shape)
+        self.packed = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.packed.data_ptr()) % 256               # 256-byte aligned start
+        self.packed = self.packed[off:off + nbytes]
+        _check(lib().moe_pack_weights(C.byref(self.shape.c()), C.byref(self.c()),
+                                      self.packed.data_ptr(), nbytes, _stream(None)),
+               "moe_pack_weights")
+        if not keep_rows:
+            torch.cuda.current_stream().synchronize()
+            self.t = None
 
     def c(self) -> _Weights:
-        q4 = {n: _Q4(*(_ptr(x, None, n) for x in self.t[n])) for n in self.NAMES}
+        if self.t is None:
+            q4 = {n: _Q4(None, None, None) for n in self.NAMES}
+        else:
+            q4 = {n: _Q4(*(_ptr(x, None, n) for x in self.t[n])) for n in self.NAMES}
+        packed = getattr(self, "packed", None)
         return _Weights(q4["gate"], q4["up"], q4["down"], q4["sh_gate"], q4["sh_up"], q4["sh_down"],
                         _ptr(self.router_wt, _B16, "router_wt"),
-                        _ptr(self.router_bias, _F32, "router_bias"))
+                        _ptr(self.router_bias, _F32, "router_bias"),
+                        None if packed is None else packed.data_ptr())
 
 
 def moe_route(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, ws: torch.Tensor,

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoeq4.so")
-SOURCES = ["api.hip", "route.hip", "gemm.hip", "decode.hip", "misc.hip"]
+SOURCES = ["api.hip", "route.hip", "gemm.hip", "decode.hip", "misc.hip", "pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -36,6 +36,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.blk_cnt = take(nTB * E * 4);
     L.lrank = take((size_t)T * k * 4);
     L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
+    L.qctl = take((size_t)QCTL_WORDS * 4);
     L.dec = take(T == 1 ? decode_scratch_bytes(I, k) : 0);
     L.total = off;
     return L;
@@ -68,9 +69,9 @@ moe_status check_weights(const moe_weights *w, bool need_router, bool need_gu, b
         if (!aligned(w->router_wt)) return MOE_ERR_INVALID_ARG;
         if (w->router_bias && !aligned(w->router_bias)) return MOE_ERR_INVALID_ARG;
     }
-    if (need_gu && !(q4_ok(w->gate) && q4_ok(w->up) && q4_ok(w->sh_gate) && q4_ok(w->sh_up)))
+    // the expert GEMMs and decode read the tile-layout buffer only
+    if ((need_gu || need_down) && (!w->packed || (((uintptr_t)w->packed) & 255u) != 0))
         return MOE_ERR_INVALID_ARG;
-    if (need_down && !(q4_ok(w->down) && q4_ok(w->sh_down))) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -121,7 +122,7 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
     }
     launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, lrank, s->T, s->E, s->top_k, kBM,
                         r->counts, r->offsets, r->row_token, r->tok_row, r->row_w, r->blocks,
-                        r->num_blocks, (int32_t *)(ws + L.sched), st);
+                        r->num_blocks, (int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl), st);
     return launched();
 }
 
@@ -129,8 +130,10 @@ moe_status enqueue_gateup(const moe_shape *s, const uint16_t *x, const moe_weigh
                           const moe_routing *r, uint16_t *h, char *ws, hipStream_t st) {
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
     (void)x;
-    launch_gateup(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum), gp(w->gate), gp(w->up), gp(w->sh_gate),
-                  gp(w->sh_up), r->blocks, r->num_blocks, (const int32_t *)(ws + L.sched),
+    const PackLayout P = pack_layout(s->H, s->I, s->E);
+    const uint8_t *pk = (const uint8_t *)w->packed;
+    launch_gateup(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum), pk + P.gu,
+                  pk + P.sh_gu, r->blocks, r->num_blocks, (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
                   max_blocks_for(s->T, s->E, s->top_k), r->row_token, h, (float *)(ws + L.hsum), st);
     return launched();
 }
@@ -140,8 +143,10 @@ moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
     // group sums of h: left in the workspace by the gate/up pass
     const float *hsum = (const float *)(ws + L.hsum);
-    launch_down(*s, h, hsum, gp(w->down), gp(w->sh_down), r->blocks, r->num_blocks,
-                (const int32_t *)(ws + L.sched), max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
+    const PackLayout P = pack_layout(s->H, s->I, s->E);
+    const uint8_t *pk = (const uint8_t *)w->packed;
+    launch_down(*s, h, hsum, pk + P.down, pk + P.sh_down, r->blocks, r->num_blocks,
+                (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl), max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
                 (uint16_t *)(ws + L.stage), y, st);
     return launched();
 }
@@ -158,6 +163,26 @@ moe_status moe_query(const moe_shape *shape, size_t *workspace_bytes, int32_t *m
     if (max_blocks) *max_blocks = max_blocks_for(shape->T, shape->E, shape->top_k);
     if (block_rows) *block_rows = kBM;
     return MOE_OK;
+}
+
+moe_status moe_packed_bytes(const moe_shape *shape, size_t *packed_bytes) {
+    MOE_TRY(check_shape(shape));
+    if (!packed_bytes) return MOE_ERR_INVALID_ARG;
+    *packed_bytes = pack_layout(shape->H, shape->I, shape->E).total;
+    return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_shape *shape, const moe_weights *w, void *packed,
+                            size_t packed_bytes, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!w || !(q4_ok(w->gate) && q4_ok(w->up) && q4_ok(w->down) && q4_ok(w->sh_gate) &&
+                q4_ok(w->sh_up) && q4_ok(w->sh_down)))
+        return MOE_ERR_INVALID_ARG;
+    if (!packed || (((uintptr_t)packed) & 255u) != 0 ||
+        packed_bytes < pack_layout(shape->H, shape->I, shape->E).total)
+        return MOE_ERR_INVALID_ARG;
+    launch_pack(*shape, *w, (uint8_t *)packed, (hipStream_t)stream);
+    return launched();
 }
 
 moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weights *w,

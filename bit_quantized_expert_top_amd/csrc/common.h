@@ -121,6 +121,30 @@ __host__ __device__ __forceinline__ int perm_pos(int col) {
     return (col & ~7) | ((p & 3) << 1) | (p >> 2);
 }
 
+// GEMM work queues (int32 words of the workspace's qctl area).  The routing
+// scatter writes the routed block counts per cost class and zeroes the
+// counters; each GEMM launch drains its eight per-XCD queues and its last
+// workgroup zeroes them again.  Every counter has a 128-byte line of its own
+// (atomics on one shared line serialise).
+constexpr int QCTL_LINE = 32;                       // words per counter
+constexpr int QCTL_GATEUP = 0;                      // 8 queue heads + finished count
+constexpr int QCTL_DOWN = 9 * QCTL_LINE;            // same for the down GEMM
+constexpr int QCTL_CLASS = 18 * QCTL_LINE;          // routed blocks with 4, 3, 2, 1 M tiles
+constexpr int QCTL_WORDS = 19 * QCTL_LINE;
+
+// Tile layout of the expert weights: one block per (tile of 256 columns, group
+// of 64 inputs), codes then scales then biases (the block format is documented
+// with moe_pack_weights).
+constexpr int PK_BLOCK = 9216;
+constexpr int PK_CODES = 8192;      // byte offset of the scales; biases at +512
+struct PackLayout {
+    size_t gu, sh_gu, down, sh_down, total;   // byte offsets of the four sections
+};
+PackLayout pack_layout(int H, int I, int E);
+// column c of a gate/up block of tile j: projection (c >> 5) & 1 (0 gate,
+// 1 up), row 128 j + 32 (c >> 6) + (c & 31); of a down block: row 256 j + c
+void launch_pack(const moe_shape &sh, const moe_weights &w, uint8_t *dst, hipStream_t s);
+
 // Workspace layout (byte offsets), shared by route/gemm/decode.  All host-known.
 struct WsLayout {
     size_t logits;      // fp32 [T][E]            (used when routing.logits == NULL)
@@ -133,7 +157,8 @@ struct WsLayout {
     size_t stage;       // bf16 [T*k][H]          routed down outputs times routing weight
     size_t blk_cnt;     // int32 [T/kTB][E]       per token-block expert counts / bases
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
-    size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (largest first)
+    size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (by cost class)
+    size_t qctl;        // int32 [64]             GEMM work-queue counters and class counts
     size_t dec;         // decode scratch
     size_t total;
 };
@@ -153,7 +178,8 @@ void launch_route_select(const float *part, const float *exact, const float *xsq
 void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
                          int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
-                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, hipStream_t s);
+                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, int32_t *qctl,
+                         hipStream_t s);
 void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
                      hipStream_t s);
 
@@ -163,13 +189,13 @@ struct GemmProj {
     const uint16_t *b;
 };
 
-void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum, GemmProj gate,
-                   GemmProj up, GemmProj sgate, GemmProj sup, const int32_t *blocks,
-                   const int32_t *num_blocks, const int32_t *sched, int max_blocks,
+void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum,
+                   const uint8_t *pk, const uint8_t *pk_sh, const int32_t *blocks,
+                   const int32_t *num_blocks, const int32_t *sched, int32_t *qctl, int max_blocks,
                    const int32_t *row_token, uint16_t *h, float *hsum, hipStream_t s);
-void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
-                 GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks,
-                 const int32_t *sched, int max_blocks,
+void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const uint8_t *pk,
+                 const uint8_t *pk_sh, const int32_t *blocks, const int32_t *num_blocks,
+                 const int32_t *sched, int32_t *qctl, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  uint16_t *stage, float *y, hipStream_t s);
 

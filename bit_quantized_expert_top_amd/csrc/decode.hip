@@ -124,7 +124,7 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
 // any arithmetic.
 __global__ __launch_bounds__(256) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
-    GemmProj gate, GemmProj up, GemmProj sgate, GemmProj sup, int32_t *__restrict__ ids_out,
+    const uint8_t *__restrict__ pk, const uint8_t *__restrict__ pk_sh, int32_t *__restrict__ ids_out,
     float *__restrict__ tw_out, uint16_t *__restrict__ hbuf) {
     __shared__ int s_ids[8];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
     const int LPR = H / 32, RPI = 64 / LPR;
     const int sub = lane / LPR, lj = lane % LPR;
     const int kpos = 32 * lj, g = kpos / 64;
-    const int W = H / 8, G = H / 64;
+    const int G = H / 64;
     // x slice in pair order (0,4),(1,5),(2,6),(3,7) of each 8-block, and its sum
     uint32_t xp[16];
     float sx = 0.0f;
@@ -185,14 +185,17 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
         const bool sh = slot == k;
         int ex = sh ? 0 : s_ids[slot];
         ex = (ex < 0 || ex >= E) ? 0 : ex;
-        const size_t rr = sh ? (size_t)i : (size_t)ex * I + i;
-        const GemmProj pg = sh ? sgate : gate, pu = sh ? sup : up;
-        wg[it] = *(const u32x4 *)(pg.q + rr * W + 4 * lj);
-        wu[it] = *(const u32x4 *)(pu.q + rr * W + 4 * lj);
-        sgr[it] = pg.s[rr * G + g];
-        bgr[it] = pg.b[rr * G + g];
-        sur[it] = pu.s[rr * G + g];
-        bur[it] = pu.b[rr * G + g];
+        // tile-layout block (tile i/128, group g); gate column cg, up column cg + 32
+        const int j = i >> 7, cg = 64 * ((i & 127) >> 5) + (i & 31);
+        const uint8_t *blk = sh ? pk_sh + ((size_t)j * G + g) * PK_BLOCK
+                                : pk + (((size_t)ex * (I / 128) + j) * G + g) * PK_BLOCK;
+        const int hh = lj & 1;                    // half of the group this lane covers
+        wg[it] = *(const u32x4 *)(blk + 32 * cg + 16 * (hh ^ ((cg >> 3) & 1)));
+        wu[it] = *(const u32x4 *)(blk + 32 * (cg + 32) + 16 * (hh ^ (((cg + 32) >> 3) & 1)));
+        sgr[it] = *(const uint16_t *)(blk + PK_CODES + 2 * cg);
+        bgr[it] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * cg);
+        sur[it] = *(const uint16_t *)(blk + PK_CODES + 2 * (cg + 32));
+        bur[it] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * (cg + 32));
     }
 #pragma unroll
     for (int it = 0; it < DEC_ROWS_PER_WAVE; ++it) {
@@ -228,7 +231,8 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
 constexpr int DOWN_STEPS = 5;
 __global__ __launch_bounds__(256) void decode_down_kernel(
     const uint16_t *__restrict__ hbuf, int H, int I, const int32_t *__restrict__ ids,
-    const float *__restrict__ tw, int k, int E, GemmProj down, GemmProj sdown,
+    const float *__restrict__ tw, int k, int E, const uint8_t *__restrict__ pk,
+    const uint8_t *__restrict__ pk_sh,
     float *__restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     uint16_t *hs = (uint16_t *)dsm;                           // [(k+1)][I] fp16, permuted
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const int LPR = I / 32, RPI = 64 / LPR;
     const int sub = lane / LPR, lj = lane % LPR;
-    const int W = I / 8, G = I / 64, g = lj / 2;
+    const int G = I / 64, g = lj / 2, hh = lj & 1;
     uint32_t cM = 0x000F000Fu, cC = 0x64006400u;
     asm volatile("" : "+v"(cM), "+v"(cC));
     const int nrow = 2 * (k + 1);                             // (output, slot) pairs of this wave
@@ -261,11 +265,13 @@ __global__ __launch_bounds__(256) void decode_down_kernel(
             for (int r = 0; r < 8; ++r)
                 if (r == slot) ex = sid[r];
             ex = (sh || ex < 0 || ex >= E) ? 0 : ex;
-            const size_t row = sh ? (size_t)n : (size_t)ex * H + n;
-            const GemmProj p = sh ? sdown : down;
-            wq[st] = *(const u32x4 *)(p.q + row * W + 4 * lj);
-            sr[st] = p.s[row * G + g];
-            br[st] = p.b[row * G + g];
+            // tile-layout block (tile n/256, group g), column n % 256
+            const int j = n >> 8, c = n & 255;
+            const uint8_t *blk = sh ? pk_sh + ((size_t)j * G + g) * PK_BLOCK
+                                    : pk + (((size_t)ex * (H / 256) + j) * G + g) * PK_BLOCK;
+            wq[st] = *(const u32x4 *)(blk + 32 * c + 16 * (hh ^ ((c >> 3) & 1)));
+            sr[st] = *(const uint16_t *)(blk + PK_CODES + 2 * c);
+            br[st] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * c);
         }
         if (!staged) {
             for (int u = tid; u < nh; u += 256) ((u32x4 *)hs)[u] = ((const u32x4 *)hbuf)[u];
@@ -317,20 +323,17 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     float *logits = (float *)p;         // [E]
     p += 4096;
     uint16_t *hbuf = (uint16_t *)p;     // fp16 [k+1][I]
-    const GemmProj gate{w.gate.q, w.gate.scale, w.gate.bias}, up{w.up.q, w.up.scale, w.up.bias};
-    const GemmProj sgate{w.sh_gate.q, w.sh_gate.scale, w.sh_gate.bias};
-    const GemmProj sup{w.sh_up.q, w.sh_up.scale, w.sh_up.bias};
-    const GemmProj down{w.down.q, w.down.scale, w.down.bias};
-    const GemmProj sdown{w.sh_down.q, w.sh_down.scale, w.sh_down.bias};
+    const PackLayout P = pack_layout(H, I, E);
+    const uint8_t *pk = (const uint8_t *)w.packed;
     hipLaunchKernelGGL(decode_router_kernel, dim3((E + 3) / 4), dim3(256), 0, s, x, w.router_wt,
                        w.router_bias, H, E, logits);
     const int rows = (k + 1) * I, rpi = 64 / (H / 32);
     const int per_wg = 4 * DEC_ROWS_PER_WAVE * rpi;
     hipLaunchKernelGGL(decode_gateup_kernel, dim3((rows + per_wg - 1) / per_wg), dim3(256), 0, s,
-                       x, logits, H, I, k, E, gate, up, sgate, sup, ids, tw, hbuf);
+                       x, logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf);
     const size_t lds = (size_t)(k + 1) * I * 2 + 4 * 2 * (k + 1) * 4;
     hipLaunchKernelGGL(decode_down_kernel, dim3((H + 7) / 8), dim3(256), lds, s, hbuf, H, I, ids,
-                       tw, k, E, down, sdown, y);
+                       tw, k, E, pk + P.down, pk + P.sh_down, y);
 }
 
 size_t decode_scratch_bytes(int I, int k) { return 4096 + (size_t)(k + 1) * I * 2; }

@@ -45,15 +45,25 @@ namespace moe {
 constexpr int NW = 4;                        // waves per workgroup
 constexpr int NTHR = 64 * NW;
 constexpr int KC = 64;                       // K per stage: one quantisation group
-constexpr int NSTAGE = 3;
-constexpr int A_BYTES = kBM * KC * 2;        // [128 rows][8 x 16 B], 16 B slots XOR-swizzled
-constexpr int B_BYTES = 256 * 32;            // [256 columns][2 x 16 B halves], halves swizzled
-constexpr int STAGE = A_BYTES + B_BYTES;
-// scales and biases travel in pairs of groups (one dword per column, copied on
-// even chunks) through a 2-slot ring: [slot][s | b][256 columns] dwords
-constexpr int PAIR_BYTES = 2 * 256 * 4;
-constexpr int L_PAIR = NSTAGE * STAGE;
-constexpr int L_TOTAL = L_PAIR + 2 * PAIR_BYTES;   // 77824: two workgroups per CU
+// One ring stage holds, for one 64-wide K step:
+//   A  [32 MT rows][8 x 16 B]      activations, 16 B slots XOR-swizzled
+//   B  [256 columns][2 x 16 B]     code words, halves swizzled      } one tile-layout
+//   S  [256] bf16 scales, [256] bf16 biases                          } block, as stored
+// A block of fewer rows has a smaller stage and so more stages in flight.
+constexpr int B_BYTES = PK_CODES;
+constexpr int S_BYTES = PK_BLOCK - PK_CODES;
+template <int MT> struct Ring {
+    static constexpr int A_BYTES = MT * 32 * KC * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int NST = MT == 1 ? 5 : MT == 2 ? 4 : 3;   // stages
+    static constexpr int AHEAD = NST - 1;                         // stages issued ahead
+    static constexpr int PER = MT + 3;                            // copies per thread and stage
+};
+constexpr int L_TOTAL = 3 * Ring<4>::STAGE;  // 76800: two workgroups per CU
+static_assert(Ring<1>::NST * Ring<1>::STAGE <= L_TOTAL && Ring<2>::NST * Ring<2>::STAGE <= L_TOTAL &&
+                  Ring<3>::NST * Ring<3>::STAGE <= L_TOTAL, "rings fit");
+static_assert((Ring<1>::AHEAD - 1) * Ring<1>::PER < 64 && (Ring<2>::AHEAD - 1) * Ring<2>::PER < 64,
+              "vmcnt range");
 constexpr int HS_LD = 272;                   // epilogue h tile row stride (bytes)
 constexpr int YS_LD = 1056;                  // epilogue y tile row stride (bytes)
 static_assert(kBM * HS_LD <= L_TOTAL && 32 * YS_LD <= L_TOTAL, "epilogue tiles fit the ring");
@@ -63,11 +73,13 @@ struct GemmArgs {
     const float *Asum;     // group sums of A rows: by token [T][G] or by row [rows][G]
     int K, G;
     int N;                 // rows of one projection: I (gate/up) or H (down)
-    GemmProj p0, p1;       // routed projections: gate, up  |  down, -
-    GemmProj s0, s1;       // the shared expert's
+    const uint8_t *pk;     // routed experts' tile-layout blocks [E][n_tiles][G]
+    const uint8_t *pk_sh;  // the shared expert's [n_tiles][G]
     const int32_t *blocks;
     const int32_t *num_blocks;
-    const int32_t *sched;  // routed blocks in GEMM order
+    const int32_t *sched;  // routed blocks by cost class (4, 3, 2, 1 M tiles), then expert
+    int32_t *qctl;         // this GEMM's eight queue heads and finished-workgroup count
+    const int32_t *ccount; // routed blocks per cost class
     int max_blocks;
     const int32_t *row_token;
     const float *row_w;
@@ -118,6 +130,12 @@ __device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// s_waitcnt vmcnt(n) for a compile-time n
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // One tile: a routing block (or a shared-expert block) times 256 weight columns.
 struct Tile {
     bool shared;
@@ -135,22 +153,6 @@ __device__ __forceinline__ int src_row(const GemmArgs &a, const Tile &t, int m) 
     return t.r0 + mm;
 }
 
-// projection and row of weight column bc (0..255) of the tile
-template <int MODE>
-__device__ __forceinline__ void column_of(const GemmArgs &a, const Tile &t, int bc, GemmProj &p,
-                                          size_t &row) {
-    const int w = bc >> 6, nt = (bc >> 5) & 1, l = bc & 31;
-    int n;
-    if (MODE == 0) {
-        p = t.shared ? (nt ? a.s1 : a.s0) : (nt ? a.p1 : a.p0);
-        n = t.ntile * 128 + 32 * w + l;
-    } else {
-        p = t.shared ? a.s0 : a.p0;
-        n = t.ntile * 256 + 64 * w + 32 * nt + l;
-    }
-    row = (t.shared ? 0 : (size_t)t.e * a.N) + n;
-}
-
 template <int MODE, int MT>
 __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
@@ -161,56 +163,50 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     const int l32 = lane & 31, gg = lane >> 5;
     const int K = a.K, G = a.G, nch = K / KC;
 
+    using RG = Ring<MT>;
     // ---- DMA sources of this thread
-    // A: rows 32i + tid/8 (i = 0..3); 16 B slot tid&7 of a row holds its
+    // A: rows 32i + tid/8 (i < MT); 16 B slot tid&7 of a row holds its
     // segment slot ^ ((row >> 1) & 7)
-    uint32_t aoff[4];
+    uint32_t aoff[MT];
     {
         const int seg = (tid & 7) ^ ((tid >> 4) & 7);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MT; ++i) {
             const int m = 32 * i + (tid >> 3);
             aoff[i] = (uint32_t)src_row<MODE>(a, t, m) * (uint32_t)K + (uint32_t)(8 * seg);
         }
     }
-    // B: columns 128i + tid/2 (i = 0, 1); LDS half tid&1 holds code words
-    // 4 * ((tid&1) ^ ((col >> 3) & 1)) .. +3 of the group
-    const uint32_t *qsrc[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        GemmProj p;
-        size_t row;
-        column_of<MODE>(a, t, 128 * i + (tid >> 1), p, row);
-        qsrc[i] = p.q + row * (size_t)(K / 8) + 4 * ((tid & 1) ^ ((tid >> 4) & 1));
-    }
-    // scale and bias of column tid
-    const uint16_t *ssrc, *bsrc;
-    {
-        GemmProj p;
-        size_t row;
-        column_of<MODE>(a, t, tid, p, row);
-        ssrc = p.s + row * (size_t)G;
-        bsrc = p.b + row * (size_t)G;
-    }
+    // B and S: the tile's block of K step c is one contiguous tile-layout
+    // block, copied as stored: 16 B pieces tid and 256 + tid of the codes,
+    // and dword lane of the wave's quarter of the scale/bias bytes
+    const uint8_t *tb = t.shared ? a.pk_sh + (size_t)t.ntile * G * PK_BLOCK
+                                 : a.pk + ((size_t)t.e * a.n_tiles + t.ntile) * G * PK_BLOCK;
+    const uint8_t *bsrc = tb + 16 * tid;
+    const uint8_t *ssrc = tb + PK_CODES + 256 * wave + 4 * lane;
     auto issue = [&](int c) {
-        const uint32_t base = lds0 + (uint32_t)((c % NSTAGE) * STAGE);
+        const uint32_t base = lds0 + (uint32_t)((c % RG::NST) * RG::STAGE);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MT; ++i)
             dma16(a.A + (size_t)aoff[i] + c * KC, base + (uint32_t)((i * 256 + wave * 64) * 16));
+        const uint8_t *blk = bsrc + (size_t)c * PK_BLOCK;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            dma16(qsrc[i] + c * 8, base + (uint32_t)(A_BYTES + (i * 256 + wave * 64) * 16));
-        if ((c & 1) == 0) {                      // groups c, c+1 (G is even)
-            const uint32_t pb = lds0 + (uint32_t)(L_PAIR + ((c >> 1) & 1) * PAIR_BYTES + wave * 256);
-            dma4(ssrc + c, pb);
-            dma4(bsrc + c, pb + 1024);
-        }
+            dma16(blk + 4096 * i, base + (uint32_t)(RG::A_BYTES + (i * 256 + wave * 64) * 16));
+        dma4(ssrc + (size_t)c * PK_BLOCK, base + (uint32_t)(RG::A_BYTES + B_BYTES + wave * 256));
     };
-    // copies per thread: 8 for an even stage, 6 for an odd one.  Waiting for
-    // "all but the newest n" with n = the count of the stage issued after it.
-
-    issue(0);
-    if (nch > 1) issue(1);
+    // RG::PER copies per thread and stage, completing in order: stage c is in
+    // once at most (stages issued after it) * PER copies are outstanding.
+#pragma unroll
+    for (int p = 0; p < RG::AHEAD; ++p)
+        if (p < nch) issue(p);
+    // routing weights of the rows this thread writes in the down epilogue,
+    // loaded now: a load there would also wait for the epilogue's own stores
+    float wrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int row = 32 * mt + (tid >> 3);
+        wrow[mt] = (MODE == 1 && !t.shared && row < t.nrows) ? a.row_w[t.r0 + row] : 0.0f;
+    }
 
     floatx16 acc[MT][2];
 #pragma unroll
@@ -226,26 +222,29 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     bool nz = false;                             // any group with b != -8 s in my columns
 
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 >= nch)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if (((c + 1) & 1) == 0)
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        // stages issued after c: min(AHEAD - 1, nch - 1 - c)
+        const int after = min(RG::AHEAD - 1, nch - 1 - c);
+        if (after <= 0)
+            wait_vm<0>();
+        else if (after == 1)
+            wait_vm<RG::PER>();
+        else if (after == 2)
+            wait_vm<(RG::AHEAD > 2 ? 2 : 0) * RG::PER>();
         else
-            asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+            wait_vm<(RG::AHEAD > 3 ? 3 : 0) * RG::PER>();
         __syncthreads();                         // stage c visible; stage c-1 no longer read
-        if (c + 2 < nch) issue(c + 2);
+        if (c + RG::AHEAD < nch) issue(c + RG::AHEAD);   // into the slot of stage c-1
 
-        const uint8_t *sb = smem + (c % NSTAGE) * STAGE;
+        const uint8_t *sb = smem + (c % RG::NST) * RG::STAGE;
         u32x4 wq[2];
         f16x2 ss[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int bc = 64 * wave + 32 * nt + l32;
-            wq[nt] = *(const u32x4 *)(sb + A_BYTES + bc * 32 + 16 * (gg ^ swb));
-            const uint8_t *pr = smem + L_PAIR + ((c >> 1) & 1) * PAIR_BYTES + bc * 4;
-            const uint32_t sv = *(const uint32_t *)pr, bv = *(const uint32_t *)(pr + 1024);
-            const float sf = (c & 1) ? bf16_hi(sv) : bf16_lo(sv);
-            nz |= ((c & 1) ? bf16_hi(bv) : bf16_lo(bv)) != -8.0f * sf;
+            wq[nt] = *(const u32x4 *)(sb + RG::A_BYTES + bc * 32 + 16 * (gg ^ swb));
+            const uint8_t *pr = sb + RG::A_BYTES + B_BYTES + bc * 2;
+            const float sf = bf16_to_f32(*(const uint16_t *)pr);
+            nz |= bf16_to_f32(*(const uint16_t *)(pr + 512)) != -8.0f * sf;
             const _Float16 sh = (_Float16)sf;
             ss[nt] = f16x2{sh, sh};
         }
@@ -270,15 +269,10 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
         int srcr[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) srcr[mt] = src_row<MODE>(a, t, 32 * mt + l32);
-        const uint16_t *cs[2], *cb[2];
+        // scale and bias of my columns, group g: tile block g, bytes PK_CODES + 2 c
+        const uint8_t *cs[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            GemmProj p;
-            size_t row;
-            column_of<MODE>(a, t, 64 * wave + 32 * nt + l32, p, row);
-            cs[nt] = p.s + row * (size_t)G;
-            cb[nt] = p.b + row * (size_t)G;
-        }
+        for (int nt = 0; nt < 2; ++nt) cs[nt] = tb + PK_CODES + 2 * (64 * wave + 32 * nt + l32);
         for (int j3 = 0; j3 < (K3 + 15) / 16; ++j3) {
             uint32_t bw[2][4], aw[MT][4];
 #pragma unroll
@@ -293,7 +287,9 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
                     for (int nt = 0; nt < 2; ++nt) {
                         float v = 0.0f;
                         if (tau < 3) {
-                            const float cf = bf16_to_f32(cb[nt][g]) + 8.0f * bf16_to_f32(cs[nt][g]);
+                            const uint8_t *sp = cs[nt] + (size_t)g * PK_BLOCK;
+                            const float cf = bf16_to_f32(*(const uint16_t *)(sp + 512)) +
+                                             8.0f * bf16_to_f32(*(const uint16_t *)sp);
                             const float hi = (float)(_Float16)cf;
                             v = tau < 2 ? hi : (float)(_Float16)(cf - hi);
                         }
@@ -386,7 +382,7 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
                 } else {
                     // routed row: weighted output staged in bf16 (fp32 range; the combine adds in fp32)
                     uint16_t *dst = a.stage + (size_t)(t.r0 + row) * a.N + col;
-                    const float wr = a.row_w[t.r0 + row];
+                    const float wr = wrow[mt];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const floatx4 v0 = *(const floatx4 *)(src + 32 * q);
@@ -404,29 +400,100 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     }
 }
 
-// Persistent grid: workgroup g takes work items j = g, g + gridDim, ...  Item j
-// is (slot, n-tile) with slot = 8 (j / 8 / n_tiles) + j % 8 and n-tile
-// (j / 8) % n_tiles, so all n-tiles of one block (which share its activation
-// rows) land on workgroups with the same g mod 8, i.e. on the same XCD.  Slots
-// are the shared-expert blocks, then the routed blocks in the routing
-// schedule's order (largest first), so every round of the grid takes items of
-// similar cost and the tail is short.
+// XCD (accelerator complex die) that runs this workgroup; each has its own L2.
+__device__ __forceinline__ int xcd_id() {
+    int v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+    return v & 7;
+}
+
+// Work queues.  The slots (shared-expert blocks, then the routed blocks of
+// cost class 4, 3, 2, 1 M tiles, each class ordered by expert) are dealt to
+// eight queues, one per XCD: queue x holds the x-th eighth of every segment,
+// so the queues carry equal work and an expert's blocks mostly share one
+// queue, hence one L2 for its weights.  A queue entry is (slot, n-tile), n-tile
+// fastest, so the n-tiles of a block (which read the same activation rows) run
+// side by side.  A workgroup drains the queue of its own XCD with an atomic
+// head, then helps the others in turn, so every entry is taken exactly once
+// whatever the placement of workgroups on XCDs.
+struct Queues {
+    int seg[5];        // segment sizes: shared, class 4, 3, 2, 1
+    int base[5];       // first slot of each segment (sched index for classes)
+};
+
+__device__ __forceinline__ int seg_lo(int n, int x) { return (n * x) >> 3; }
+
+// slots of queue x
+__device__ __forceinline__ int queue_slots(const Queues &Q, int x) {
+    int n = 0;
+#pragma unroll
+    for (int g = 0; g < 5; ++g) n += seg_lo(Q.seg[g], x + 1) - seg_lo(Q.seg[g], x);
+    return n;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    __shared__ int s_pick[2];
     const int nb = min(a.num_blocks[0], a.max_blocks);
-    const int S = a.n_shared + max(nb, 0);
-    const int jend = ((S + 7) >> 3) * 8 * a.n_tiles;
-    for (int j = blockIdx.x; j < jend; j += gridDim.x) {
-        const int q = j >> 3;
-        const int slot = (q / a.n_tiles) * 8 + (j & 7);
-        if (slot >= S) continue;
+    Queues Q;
+    Q.seg[0] = a.n_shared;
+    Q.base[0] = 0;
+    int left = max(nb, 0);
+#pragma unroll
+    for (int g = 1; g < 5; ++g) {
+        Q.seg[g] = min(max(a.ccount[g - 1], 0), left);    // never past the block map
+        left -= Q.seg[g];
+        Q.base[g] = g == 1 ? 0 : Q.base[g - 1] + Q.seg[g - 1];
+    }
+    // thread 0's queue state; `pend` is the head already taken from queue q
+    // for the next item (fetched while the current one runs), -1 if none
+    int q = xcd_id(), hops = 0, pend = -1;
+    for (;;) {
+        __syncthreads();                         // the previous item is done with the LDS
+        if (threadIdx.x == 0) {
+            int k = -1;
+            while (hops < 8) {
+                const int len = queue_slots(Q, q) * a.n_tiles;
+                if (len > 0) {
+                    k = pend >= 0 ? pend : atomicAdd(&a.qctl[q * QCTL_LINE], 1);
+                    pend = -1;
+                    if (k < len) break;
+                }
+                pend = -1;
+                k = -1;
+                q = (q + 1) & 7;
+                ++hops;
+            }
+            s_pick[0] = k;
+            s_pick[1] = q;
+            if (k >= 0) pend = atomicAdd(&a.qctl[q * QCTL_LINE], 1);
+        }
+        __syncthreads();
+        const int k = s_pick[0], x = s_pick[1];
+        if (k < 0) break;
+        // entry k of queue x -> segment, slot
+        int i = k / a.n_tiles, g = 0, slot = -1;
+#pragma unroll
+        for (int gg = 0; gg < 5; ++gg) {
+            const int lo = seg_lo(Q.seg[gg], x), n = seg_lo(Q.seg[gg], x + 1) - lo;
+            if (slot < 0) {
+                if (i < n) {
+                    slot = Q.base[gg] + lo + i;
+                    g = gg;
+                } else {
+                    i -= n;
+                }
+            }
+        }
+        if (slot < 0) continue;
         Tile t;
-        t.ntile = q % a.n_tiles;
-        t.shared = slot < a.n_shared;
+        t.ntile = k % a.n_tiles;
+        t.shared = g == 0;
         t.e = 0;
         if (!t.shared) {
-            const int mb = a.sched[slot - a.n_shared];
+            if (slot >= a.max_blocks) continue;
+            const int mb = a.sched[slot];
             if (mb < 0 || mb >= nb) continue;
             t.e = a.blocks[3 * mb];
             t.r0 = a.blocks[3 * mb + 1];
@@ -439,13 +506,16 @@ __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
             t.r0 = a.T * a.topk + slot * kBM;
             t.nrows = min(kBM, a.T - slot * kBM);
         }
-        __syncthreads();                         // the previous item is done with the LDS
         switch ((t.nrows + 31) >> 5) {
             case 1: gemm_tile<MODE, 1>(a, t, smem); break;
             case 2: gemm_tile<MODE, 2>(a, t, smem); break;
             case 3: gemm_tile<MODE, 3>(a, t, smem); break;
             default: gemm_tile<MODE, 4>(a, t, smem); break;
         }
+    }
+    // the last workgroup out re-arms the queues for the next launch
+    if (threadIdx.x == 0 && atomicAdd(&a.qctl[8 * QCTL_LINE], 1) == (int)gridDim.x - 1) {
+        for (int j = 0; j < 9; ++j) atomicExch(&a.qctl[j * QCTL_LINE], 0);
     }
 }
 
@@ -456,8 +526,8 @@ static unsigned grid_for(int n_shared, int max_blocks, int n_tiles) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const long items = (long)((n_shared + max_blocks + 7) / 8) * 8 * n_tiles;
-    return (unsigned)std::min<long>(items, 2L * cus);
+    const long items = (long)(n_shared + max_blocks) * n_tiles;
+    return (unsigned)std::max<long>(1, std::min<long>(items, 2L * cus));
 }
 
 // the GEMM needs more dynamic LDS than the default launch limit
@@ -471,9 +541,9 @@ static void allow_lds() {
     }
 }
 
-void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, GemmProj gate,
-                   GemmProj up, GemmProj sgate, GemmProj sup, const int32_t *blocks,
-                   const int32_t *num_blocks, const int32_t *sched, int max_blocks,
+void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum,
+                   const uint8_t *pk, const uint8_t *pk_sh, const int32_t *blocks,
+                   const int32_t *num_blocks, const int32_t *sched, int32_t *qctl, int max_blocks,
                    const int32_t *row_token, uint16_t *h, float *hsum, hipStream_t s) {
     GemmArgs a{};
     a.A = xp;
@@ -481,13 +551,13 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, G
     a.K = sh.H;
     a.G = sh.H / 64;
     a.N = sh.I;
-    a.p0 = gate;
-    a.p1 = up;
-    a.s0 = sgate;
-    a.s1 = sup;
+    a.pk = pk;
+    a.pk_sh = pk_sh;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.sched = sched;
+    a.qctl = qctl + QCTL_GATEUP;
+    a.ccount = qctl + QCTL_CLASS;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.T = sh.T;
@@ -537,9 +607,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     *(float4 *)(y + t * H + n + 4) = a1;
 }
 
-void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, GemmProj down,
-                 GemmProj sdown, const int32_t *blocks, const int32_t *num_blocks,
-                 const int32_t *sched, int max_blocks,
+void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const uint8_t *pk,
+                 const uint8_t *pk_sh, const int32_t *blocks, const int32_t *num_blocks,
+                 const int32_t *sched, int32_t *qctl, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  uint16_t *stage, float *y, hipStream_t s) {
     GemmArgs a{};
@@ -548,11 +618,13 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, Gemm
     a.K = sh.I;
     a.G = sh.I / 64;
     a.N = sh.H;
-    a.p0 = down;
-    a.s0 = sdown;
+    a.pk = pk;
+    a.pk_sh = pk_sh;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.sched = sched;
+    a.qctl = qctl + QCTL_DOWN;
+    a.ccount = qctl + QCTL_CLASS;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.row_w = row_w;

@@ -607,7 +607,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t *__restrict__ counts, int T, int E, int k, int BM,
     int32_t *__restrict__ offsets, int32_t *__restrict__ blocks, int32_t *__restrict__ num_blocks,
     int32_t *__restrict__ row_token, int32_t *__restrict__ tok_row, float *__restrict__ row_w,
-    int32_t *__restrict__ sched) {
+    int32_t *__restrict__ sched, int32_t *__restrict__ qctl) {
     __shared__ int tmp[256];
     __shared__ int s_off[256];
     __shared__ unsigned long long cls_scan[256];
@@ -661,6 +661,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(
             __syncthreads();
         }
         const unsigned long long tot = cls_scan[255], pre = cls_scan[tid] - mine;
+        // class sizes for the GEMMs' per-XCD queues, and their counters at zero
+        if (tid < 18) qctl[tid * QCTL_LINE] = 0;
+        if (tid < 4) qctl[QCTL_CLASS + tid] = (int)((tot >> (16 * tid)) & 0xFFFF);
         int base[4];
         base[0] = 0;
         for (int c = 1; c < 4; ++c) base[c] = base[c - 1] + (int)((tot >> (16 * (c - 1))) & 0xFFFF);
@@ -687,12 +690,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
                          int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
-                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, hipStream_t s) {
+                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, int32_t *qctl,
+                         hipStream_t s) {
     const int nTB = (T + TB - 1) / TB;
     hipLaunchKernelGGL(scan_experts_kernel, dim3(E), dim3(256), 0, s, blk_cnt, nTB, E, counts);
     hipLaunchKernelGGL(scatter_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w, blk_cnt,
                        lrank, counts, T, E, k, BM, offsets, blocks, num_blocks, row_token,
-                       tok_row, row_w, sched);
+                       tok_row, row_w, sched, qctl);
 }
 
 // Activation preparation for the GEMM: fp16 copy with the 8-block permutation

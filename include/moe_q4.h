@@ -22,6 +22,27 @@
  *     first); scale and bias are bf16 [N][K/64]; w[n][k] = q*scale + bias
  *     with group k/64.  Routed experts stack E projections: [E][N][...].
  *     gate and up have N = I, K = H; down has N = H, K = I.
+ *     This row layout is the checkpoint format; moe_pack_weights turns it
+ *     into the tile layout below, which is what the layer calls read.
+ *   - Tile layout (the `packed` buffer, written by moe_pack_weights): the
+ *     same bytes regrouped so that one 64-wide K step of one 256-column GEMM
+ *     tile is one contiguous 9216-byte block, read by a few whole-line copies
+ *     (the pages rebuild weights tile by tile inside the grouped GEMM and get
+ *     their decode bandwidth from coalesced reads: mechatronicstore.cl,
+ *     "Prefill: ..." and "Decode: ...").  A block is
+ *       bytes [0, 8192):     codes of 256 columns, 32 bytes each: 16-byte
+ *                            half hh of column c holds code words
+ *                            4 * (hh ^ ((c >> 3) & 1)) .. +3 of the group;
+ *       bytes [8192, 8704):  bf16 scales of the 256 columns;
+ *       bytes [8704, 9216):  bf16 biases of the 256 columns.
+ *     Sections, in this order, each starting 256-byte aligned:
+ *       routed gate/up  [E][I/128][H/64] blocks: block (e, j, g) column c is
+ *                       row 128 j + 32 (c / 64) + c % 32 of gate (c % 64 < 32)
+ *                       or of up (c % 64 >= 32), group g;
+ *       shared gate/up  [I/128][H/64] blocks, the same columns;
+ *       routed down     [E][H/256][I/64] blocks: column c is row 256 j + c;
+ *       shared down     [H/256][I/64] blocks.
+ *     moe_packed_bytes gives the size.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
  *     only ENQUEUES work on `stream`; none synchronises or copies
  *     device->host.  The caller owns every buffer; the library never
@@ -74,6 +95,10 @@ typedef struct {
     moe_q4 sh_gate, sh_up, sh_down; /* the shared expert                     */
     const uint16_t *router_wt;      /* bf16 [E][H]: router weight, row/expert */
     const float *router_bias;       /* fp32 [E] additive logit bias, or NULL  */
+    const void *packed;             /* the six projections in the tile layout
+                                       (moe_pack_weights), 256-byte aligned;
+                                       the expert GEMMs and decode read only
+                                       this and the router fields            */
 } moe_weights;
 
 /* Routing outputs (host struct holding device pointers).  Row r of the
@@ -99,6 +124,17 @@ typedef struct {
 moe_status moe_query(const moe_shape *shape, size_t *workspace_bytes, int32_t *max_blocks,
                      int32_t *block_rows);
 
+/* Host only.  Bytes of the tile-layout buffer for `shape`. */
+moe_status moe_packed_bytes(const moe_shape *shape, size_t *packed_bytes);
+
+/* Regroup the six row-layout projections of w into the tile layout (a pure
+ * permutation of bytes, done once when the weights are loaded).  packed:
+ * device buffer of at least moe_packed_bytes bytes, 256-byte aligned, not
+ * overlapping the sources; w->packed is not read.  MOE_ERR_INVALID_ARG for a
+ * NULL or misaligned pointer or a short buffer. */
+moe_status moe_pack_weights(const moe_shape *shape, const moe_weights *w, void *packed,
+                            size_t packed_bytes, void *stream);
+
 /* Router and routing (the pages' "histogram, prefix scan, scatter and block
  * map in one GPU command buffer", mechatronicstore.cl "Prefill: ...").
  * x: bf16 [T][H].  Logits are float32 in a fixed order (within each chunk
@@ -119,6 +155,7 @@ moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weight
  * 0,4,1,5,2,6,3,7 (the order in which the down GEMM consumes it).  Needs
  * moe_route's outputs and workspace; leaves the group sums of h in the
  * workspace for moe_down_combine.
+ * Reads the expert weights from w->packed (tile layout).
  * Weights are rebuilt exactly as (q - 8) * scale in fp16 plus an fp32 term for
  * bias + 8 * scale; the activations enter the matrix cores in fp16.  Exact for
  * |scale| in [2^-13, 2^12] and |x| below 65504 (larger x overflows). */
@@ -128,7 +165,8 @@ moe_status moe_expert_gemm_q4(const moe_shape *shape, const uint16_t *x, const m
 
 /* Down GEMM plus routing-weighted combine:
  * y[t] = sum_j topk_w[t][j] * W_down[ids[t][j]] h[tok_row[t][j]] + W_sh_down h[T*top_k + t].
- * y: fp32 [T][H] (overwritten).  h must be the output of moe_expert_gemm_q4
+ * y: fp32 [T][H] (overwritten).  Reads the expert weights from w->packed.
+ * h must be the output of moe_expert_gemm_q4
  * with the same workspace (whose group sums of h it reads).  Each routed row's
  * weighted output is rounded to bf16 into a workspace staging row (fp32 range,
  * relative error at most 2^-9 per routed term) and every token then adds its
@@ -147,7 +185,8 @@ moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weight
  * only the selected experts' packed weights (mechatronicstore.cl "Decode:
  * mover menos bytes por token"; neuro-ai.ru "Спекулятивное ...": batch-1
  * decode is bound by weight bandwidth).  topk_ids [top_k], topk_w [top_k],
- * y fp32 [H] (overwritten).  The ids equal those of the fixed-order logits;
+ * y fp32 [H] (overwritten).  Reads the expert weights from w->packed and
+ * the router from w->router_wt.  The ids equal those of the fixed-order logits;
  * h is kept in fp16 between the two GEMVs.  MOE_ERR_UNSUPPORTED unless H and
  * I are powers of two. */
 moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weights *w,

@@ -72,10 +72,14 @@ FAKE = 0x10000   # aligned, never dereferenced: validation fails before any laun
 
 def _weights(bad=None):
     q = B._Q4(FAKE, FAKE, FAKE)
-    w = B._Weights(q, q, q, q, q, q, FAKE, None)
+    w = B._Weights(q, q, q, q, q, q, FAKE, None, FAKE)
     if bad == "null_router":
         w.router_wt = None
     if bad == "misaligned":
+        w.packed = FAKE + 16          # the tile-layout buffer must be 256-byte aligned
+    if bad == "null_packed":
+        w.packed = None
+    if bad == "misaligned_rows":
         w.gate = B._Q4(FAKE + 4, FAKE, FAKE)
     return w
 
@@ -113,6 +117,8 @@ def test_gemm_and_down_validation_before_launch():
     r = _routing()
     assert L.moe_expert_gemm_q4(C.byref(s), FAKE, C.byref(_weights("misaligned")), C.byref(r), FAKE,
                                 FAKE, need, None) == INVALID
+    assert L.moe_expert_gemm_q4(C.byref(s), FAKE, C.byref(_weights("null_packed")), C.byref(r),
+                                FAKE, FAKE, need, None) == INVALID
     assert L.moe_expert_gemm_q4(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), None, FAKE, need,
                                 None) == INVALID
     assert L.moe_down_combine(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), FAKE + 8, FAKE,
@@ -160,3 +166,28 @@ def test_python_binding_checks_tensors():
                            torch.zeros(2, dtype=torch.int16), 1, 128,
                            torch.zeros(128, dtype=torch.int16))
     assert moe.moe_query(s)[2] == 128
+
+
+def test_packed_bytes_and_pack_validation():
+    """The tile layout holds exactly the row layout's bytes (four sections, each
+    rounded up to 256 bytes); moe_pack_weights validates before any launch."""
+    L = B.lib()
+    for H, I in [(2048, 512), (512, 128), (1024, 256)]:
+        s = shape(T=1, H=H, I=I)
+        n = C.c_size_t()
+        assert L.moe_packed_bytes(C.byref(s), C.byref(n)) == OK
+        per_expert = 3 * H * I // 2 + 3 * 2 * 2 * H * I // 64     # codes + scales + biases
+        assert n.value >= 257 * per_expert and n.value < 257 * per_expert + 4 * 256
+        assert n.value % 256 == 0
+    s = shape(T=1)
+    n = C.c_size_t()
+    assert L.moe_packed_bytes(C.byref(s), C.byref(n)) == OK
+    w = _weights()
+    assert L.moe_pack_weights(C.byref(s), C.byref(w), FAKE + 16, n.value, None) == INVALID
+    assert L.moe_pack_weights(C.byref(s), C.byref(w), FAKE, n.value - 1, None) == INVALID
+    assert L.moe_pack_weights(C.byref(s), C.byref(w), None, n.value, None) == INVALID
+    assert L.moe_pack_weights(C.byref(s), C.byref(_weights("misaligned_rows")), FAKE, n.value,
+                              None) == INVALID
+    assert L.moe_pack_weights(C.byref(shape(T=1, bits=8)), C.byref(w), FAKE, n.value,
+                              None) == UNSUP
+    assert L.moe_packed_bytes(C.byref(s), None) == INVALID
