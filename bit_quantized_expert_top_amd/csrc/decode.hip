@@ -5,43 +5,33 @@
 // por token"; neuro-ai.ru, "Спекулятивное декодирование не взлетело").  Only
 // the picked experts' rows are read; the expert ids never leave the device.
 //
-// Three short kernels:
+// Three short kernels over the tile layout (one 9216-byte block per 256
+// columns x 64 inputs); no kernel combines results across workgroups:
 //  1. router: one wave per expert computes its logit exactly in the fixed
 //     order (sequential within each 64-chunk, then over chunks, then + bias),
 //     so the ids need no certification step at batch 1;
-//  2. gate/up: one wave per workgroup first takes the top-8 (logit
-//     descending, index ascending) and the softmax weights restricted to them;
-//     rows streamed with 16-byte loads, a wave keeps its slice of x
-//     in registers for all its rows; codes become 128+q in bf16 with one
-//     and-or per pair and meet x in packed bf16 dot products:
+//  2. gate/up: a workgroup takes one slot and 32 gate + the 32 matching up
+//     columns (2 KB of each block, contiguous) over all of K.  Every wave
+//     takes the top-8 itself (logit descending, index ascending; softmax
+//     weights restricted to them) and then issues all of its loads at once.
+//     Codes become 128+q in bf16 with one and-or per pair and meet x in packed
+//     bf16 dot products:
 //        sum_k x_k (q_k s + b) = s (sum x (128 + q) - 128 sum x) + b sum x;
-//     h = silu(gate) * up is written in fp16, 8-blocks permuted like the codes;
-//  3. down: each workgroup stages h in LDS; codes become 1024+q in fp16 and
-//     meet h in packed fp16 dot products; the nine slot results of an output
-//     are summed in slot order with their routing weights.
+//     the two halves of a column meet by DPP, the waves' groups through LDS
+//     in order, and h = silu(gate) * up is written in fp16;
+//  3. down: a workgroup takes 32 outputs (1 KB of each block) for all nine
+//     slots and all groups, with h of every slot staged in LDS; codes become
+//     1024+q in fp16.  Each lane adds its slots in pick order with their
+//     routing weights, then the shared expert, group by group.
 #include "common.h"
 
 namespace moe {
 
-constexpr int DEC_ROWS_PER_WAVE = 4;   // gate/up rows (per lane group) handled by one wave
 
 __device__ __forceinline__ uint32_t dec_and_or(uint32_t a, uint32_t m, uint32_t c) {
     uint32_t r;
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
     return r;
-}
-
-// Sum of a row spread over LPR lanes (a power of two up to 64, groups aligned);
-// the result is valid in every lane of the group.
-__device__ __forceinline__ float row_total(float v, int LPR, int sub) {
-    v = group_sum_dpp(v, LPR < 16 ? LPR : 16);
-    if (LPR <= 16) return v;
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    if (LPR == 32) return sub == 0 ? r0 + r1 : r2 + r3;
-    return (r0 + r1) + (r2 + r3);
 }
 
 // 1. logits[e] = sum over chunks c (in order) of sum_{k in chunk c} x_k w_ek (in order), + bias
@@ -116,23 +106,45 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
     for (int r = 0; r < 8; ++r) pick_w[r] = pick_w[r] / sum;
 }
 
-// 2. gate/up rows.  Wave 0 of every workgroup selects the experts (workgroup 0
-// also writes them out); meanwhile all waves load their slice of x.  A lane
-// group of LPR = H/32 lanes covers one row (each lane 32 consecutive inputs:
-// four code words, half a quantisation group); a wave covers RPI = 64/LPR rows
-// per step and DEC_ROWS_PER_WAVE steps, all of whose loads are issued before
-// any arithmetic.
-__global__ __launch_bounds__(256) void decode_gateup_kernel(
+constexpr int DW = 8;                  // waves per decode workgroup
+constexpr int NSLOT = 9;               // top-8 routed experts + the shared one (top_k is 8)
+
+// code pair p of word w as two 16-bit values q_p, q_{p+4} in a magic-number
+// format (and-or with C = 128.0 bf16 pairs or 1024.0 fp16 pairs)
+// x (or h) pairs in the same order: (v_p, v_{p+4}) of each 8-block
+__device__ __forceinline__ void pair_order(const u32x4 v, uint32_t *o) {
+    o[0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+}
+
+// sum of lanes l and l ^ 1
+__device__ __forceinline__ float pair_sum(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// 2. gate/up.  Workgroup (slot, tile j, slice q of 32 gate + 32 up columns);
+// wave w takes groups w, w + DW, ...
+__global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
     const uint8_t *__restrict__ pk, const uint8_t *__restrict__ pk_sh, int32_t *__restrict__ ids_out,
     float *__restrict__ tw_out, uint16_t *__restrict__ hbuf) {
-    __shared__ int s_ids[8];
+    __shared__ float red[DW][2][32];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (wave == 0) {
+    const int G = H / 64, JT = I / 128;
+    const int b = blockIdx.x;
+    const int slot = b / (JT * 4), j = (b >> 2) % JT, q = b & 3;
+    int ex = 0;
+    if (slot < k) {
         int pe[8];
         float pw[8];
         select_topk(logits, E, k, pe, pw);
-        if (lane < k) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (r == slot) ex = pe[r];
+        ex = (ex < 0 || ex >= E) ? 0 : ex;
+        if (b == 0 && wave == 0 && lane < k) {
             int e = 0;
             float wv = 0.0f;
 #pragma unroll
@@ -141,178 +153,169 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
                     e = pe[r];
                     wv = pw[r];
                 }
-            s_ids[lane] = e;
-            if (blockIdx.x == 0) {
-                ids_out[lane] = e;
-                tw_out[lane] = wv;
-            }
+            ids_out[lane] = e;
+            tw_out[lane] = wv;
         }
     }
-    const int LPR = H / 32, RPI = 64 / LPR;
-    const int sub = lane / LPR, lj = lane % LPR;
-    const int kpos = 32 * lj, g = kpos / 64;
-    const int G = H / 64;
-    // x slice in pair order (0,4),(1,5),(2,6),(3,7) of each 8-block, and its sum
-    uint32_t xp[16];
-    float sx = 0.0f;
-    {
-        const u32x4 *px = (const u32x4 *)(x + kpos);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const u32x4 v = px[b];
-            xp[4 * b + 0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-            xp[4 * b + 1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-            xp[4 * b + 2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-            xp[4 * b + 3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sx += bf16_lo(v[r]) + bf16_hi(v[r]);
-        }
-    }
-    __syncthreads();
+    const uint8_t *tile = slot == k ? pk_sh + (size_t)j * G * PK_BLOCK
+                                    : pk + ((size_t)ex * JT + j) * G * PK_BLOCK;
+    const int hh = (lane & 1) ^ ((lane >> 4) & 1);      // logical half of my pieces
+    const int cg = 64 * q + (lane >> 1);                 // my gate column; up is cg + 32
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     uint32_t cM = 0x000F000Fu, cC = 0x43004300u;
     asm volatile("" : "+v"(cM), "+v"(cC));
-    const int R = (k + 1) * I;
-    const int base = ((blockIdx.x * 4 + wave) * DEC_ROWS_PER_WAVE) * RPI;
-    u32x4 wg[DEC_ROWS_PER_WAVE], wu[DEC_ROWS_PER_WAVE];
-    uint16_t sgr[DEC_ROWS_PER_WAVE], bgr[DEC_ROWS_PER_WAVE], sur[DEC_ROWS_PER_WAVE],
-        bur[DEC_ROWS_PER_WAVE];
+    float ag = 0.0f, au = 0.0f;
+    constexpr int GPW = 4;                               // groups per pass of a wave
+    for (int g0 = wave; g0 < G; g0 += DW * GPW) {
+        u32x4 cw[GPW][2];
+        uint16_t sv[GPW][2], bv[GPW][2];
 #pragma unroll
-    for (int it = 0; it < DEC_ROWS_PER_WAVE; ++it) {
-        int row = base + it * RPI + sub;
-        row = row < R ? row : R - 1;              // past the end: repeat the last row
-        const int slot = row / I, i = row - slot * I;
-        const bool sh = slot == k;
-        int ex = sh ? 0 : s_ids[slot];
-        ex = (ex < 0 || ex >= E) ? 0 : ex;
-        // tile-layout block (tile i/128, group g); gate column cg, up column cg + 32
-        const int j = i >> 7, cg = 64 * ((i & 127) >> 5) + (i & 31);
-        const uint8_t *blk = sh ? pk_sh + ((size_t)j * G + g) * PK_BLOCK
-                                : pk + (((size_t)ex * (I / 128) + j) * G + g) * PK_BLOCK;
-        const int hh = lj & 1;                    // half of the group this lane covers
-        wg[it] = *(const u32x4 *)(blk + 32 * cg + 16 * (hh ^ ((cg >> 3) & 1)));
-        wu[it] = *(const u32x4 *)(blk + 32 * (cg + 32) + 16 * (hh ^ (((cg + 32) >> 3) & 1)));
-        sgr[it] = *(const uint16_t *)(blk + PK_CODES + 2 * cg);
-        bgr[it] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * cg);
-        sur[it] = *(const uint16_t *)(blk + PK_CODES + 2 * (cg + 32));
-        bur[it] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * (cg + 32));
-    }
+        for (int t = 0; t < GPW; ++t) {
+            const int g = min(g0 + DW * t, G - 1);
+            const uint8_t *blk = tile + (size_t)g * PK_BLOCK;
 #pragma unroll
-    for (int it = 0; it < DEC_ROWS_PER_WAVE; ++it) {
-        const int row = base + it * RPI + sub;
-        float dg = 0.0f, du = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const bf16x2 xv = __builtin_bit_cast(bf16x2, xp[4 * j + p]);
-                const uint32_t cg = dec_and_or(wg[it][j] >> (4 * p), cM, cC);
-                const uint32_t cu = dec_and_or(wu[it][j] >> (4 * p), cM, cC);
-                dg = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cg), xv, dg, false);
-                du = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cu), xv, du, false);
+            for (int r = 0; r < 2; ++r) {
+                cw[t][r] = *(const u32x4 *)(blk + 16 * (128 * q + 64 * r + lane));
+                sv[t][r] = *(const uint16_t *)(blk + PK_CODES + 2 * (cg + 32 * r));
+                bv[t][r] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * (cg + 32 * r));
             }
         }
-        float vg = bf16_to_f32(sgr[it]) * (dg - 128.0f * sx) + bf16_to_f32(bgr[it]) * sx;
-        float vu = bf16_to_f32(sur[it]) * (du - 128.0f * sx) + bf16_to_f32(bur[it]) * sx;
-        vg = row_total(vg, LPR, sub);
-        vu = row_total(vu, LPR, sub);
-        if (row < R && lj == 0) {
-            const int slot = row / I, i = row - slot * I;
-            const float hv = vg / (1.0f + expf(-vg)) * vu;
-            hbuf[(size_t)slot * I + perm_pos(i)] = f32_to_f16(hv);
+#pragma unroll
+        for (int t = 0; t < GPW; ++t) {
+            const int g = g0 + DW * t;
+            if (g >= G) break;
+            const u32x4 *px = (const u32x4 *)(x + 64 * g + 32 * hh);
+            uint32_t xp[16];
+            float sx = 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const u32x4 v = px[qq];
+                pair_order(v, xp + 4 * qq);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sx += bf16_lo(v[r]) + bf16_hi(v[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                float d = 0.0f;
+                const uint32_t ww[4] = {cw[t][r].x, cw[t][r].y, cw[t][r].z, cw[t][r].w};
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const uint32_t c = dec_and_or(ww[qq] >> (4 * p), cM, cC);
+                        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c),
+                                                            __builtin_bit_cast(bf16x2, xp[4 * qq + p]), d, false);
+                    }
+                const float v = bf16_to_f32(sv[t][r]) * (d - 128.0f * sx) + bf16_to_f32(bv[t][r]) * sx;
+                if (r == 0) ag += v; else au += v;
+            }
         }
+    }
+    ag = pair_sum(ag);
+    au = pair_sum(au);
+    if ((lane & 1) == 0) {
+        red[wave][0][lane >> 1] = ag;
+        red[wave][1][lane >> 1] = au;
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+        const int m = threadIdx.x;
+        float gs = red[0][0][m], us = red[0][1][m];
+#pragma unroll
+        for (int w = 1; w < DW; ++w) {
+            gs += red[w][0][m];
+            us += red[w][1][m];
+        }
+        const int i = 128 * j + 32 * q + m;
+        hbuf[(size_t)slot * I + i] = f32_to_f16(gs / (1.0f + expf(-gs)) * us);
     }
 }
 
-// 3. down.  Workgroup: 8 outputs; wave: 2 outputs x (k+1) slots = 2(k+1) rows,
-// in batches of DOWN_STEPS steps of RPI rows (a lane group of LPR = I/32 lanes
-// covers one row); the weight loads of a batch are issued before the h tile
-// is needed.
-constexpr int DOWN_STEPS = 5;
-__global__ __launch_bounds__(256) void decode_down_kernel(
+// 3. down.  Workgroup (tile j, slice q of 32 outputs); wave w takes groups
+// w, w + DW, .. of every slot.
+__global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     const uint16_t *__restrict__ hbuf, int H, int I, const int32_t *__restrict__ ids,
     const float *__restrict__ tw, int k, int E, const uint8_t *__restrict__ pk,
-    const uint8_t *__restrict__ pk_sh,
-    float *__restrict__ y) {
+    const uint8_t *__restrict__ pk_sh, float *__restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-    uint16_t *hs = (uint16_t *)dsm;                           // [(k+1)][I] fp16, permuted
-    float *res = (float *)(dsm + (size_t)(k + 1) * I * 2);    // [4 waves][2 (k+1)]
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    uint16_t *hs = (uint16_t *)dsm;                                  // fp16 [k+1][I]
+    float *red = (float *)(dsm + (size_t)(k + 1) * I * 2);           // [DW][32]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int G = I / 64, JD = H / 256;
+    const int j = blockIdx.x >> 3, q = blockIdx.x & 7;
+    const int hh = (lane & 1) ^ ((lane >> 4) & 1);
+    const int col = 32 * q + (lane >> 1);
+    int sid[8];
+    float sw[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int e = r < k ? ids[r] : 0;
+        sid[r] = (e < 0 || e >= E) ? 0 : e;
+        sw[r] = r < k ? tw[r] : 0.0f;
+    }
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const int LPR = I / 32, RPI = 64 / LPR;
-    const int sub = lane / LPR, lj = lane % LPR;
-    const int G = I / 64, g = lj / 2, hh = lj & 1;
     uint32_t cM = 0x000F000Fu, cC = 0x64006400u;
     asm volatile("" : "+v"(cM), "+v"(cC));
-    const int nrow = 2 * (k + 1);                             // (output, slot) pairs of this wave
-    const int n0 = blockIdx.x * 8 + 2 * wave;
-    int sid[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) sid[r] = r < k ? ids[r] : 0;
-    const int nh = (k + 1) * I / 8;                           // 16-byte units of h
+    float acc = 0.0f;
     bool staged = false;
-    for (int r0 = 0; r0 < nrow; r0 += DOWN_STEPS * RPI) {
-        u32x4 wq[DOWN_STEPS];
-        uint16_t sr[DOWN_STEPS], br[DOWN_STEPS];
+    for (int g = wave; g < G || !staged; g += DW) {
+        const int gg = min(g, G - 1);
+        // this group's 1 KB slice of every slot's block
+        u32x4 cw[NSLOT];
+        uint16_t sv[NSLOT], bv[NSLOT];
 #pragma unroll
-        for (int st = 0; st < DOWN_STEPS; ++st) {
-            int rr = r0 + st * RPI + sub;
-            rr = rr < nrow ? rr : nrow - 1;
-            const int n = min(n0 + rr / (k + 1), H - 1), slot = rr % (k + 1);
-            const bool sh = slot == k;
-            int ex = 0;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (r == slot) ex = sid[r];
-            ex = (sh || ex < 0 || ex >= E) ? 0 : ex;
-            // tile-layout block (tile n/256, group g), column n % 256
-            const int j = n >> 8, c = n & 255;
-            const uint8_t *blk = sh ? pk_sh + ((size_t)j * G + g) * PK_BLOCK
-                                    : pk + (((size_t)ex * (H / 256) + j) * G + g) * PK_BLOCK;
-            wq[st] = *(const u32x4 *)(blk + 32 * c + 16 * (hh ^ ((c >> 3) & 1)));
-            sr[st] = *(const uint16_t *)(blk + PK_CODES + 2 * c);
-            br[st] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * c);
+        for (int s = 0; s < NSLOT; ++s) {
+            const uint8_t *blk = (s == k ? pk_sh + (size_t)j * G * PK_BLOCK
+                                         : pk + ((size_t)sid[s] * JD + j) * G * PK_BLOCK) +
+                                 (size_t)gg * PK_BLOCK;
+            cw[s] = *(const u32x4 *)(blk + 16 * (64 * q + lane));
+            sv[s] = *(const uint16_t *)(blk + PK_CODES + 2 * col);
+            bv[s] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * col);
         }
-        if (!staged) {
-            for (int u = tid; u < nh; u += 256) ((u32x4 *)hs)[u] = ((const u32x4 *)hbuf)[u];
+        if (!staged) {                                  // h of every slot into LDS
+            const int nh = (k + 1) * I / 8;
+            for (int u = tid; u < nh; u += 64 * DW) ((u32x4 *)hs)[u] = ((const u32x4 *)hbuf)[u];
             __syncthreads();
             staged = true;
         }
+        if (g >= G) break;
 #pragma unroll
-        for (int st = 0; st < DOWN_STEPS; ++st) {
-            const int rr = r0 + st * RPI + sub;
-            const int slot = (rr < nrow ? rr : nrow - 1) % (k + 1);
-            const u32x4 *hp = (const u32x4 *)(hs + (size_t)slot * I + 32 * lj);
-            float d = 0.0f, sh_sum = 0.0f;
+        for (int s = 0; s < NSLOT; ++s) {
+            uint32_t hp[16];
+            float shs = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32x4 hv = hp[j];
-                // the four h words as plain scalars (an element of the vector
-                // bit-cast straight into the dot builtin selects the wrong word)
-                const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+            for (int qq = 0; qq < 4; ++qq) {
+                const u32x4 v = *(const u32x4 *)(hs + (size_t)s * I + 64 * g + 32 * hh + 8 * qq);
+                pair_order(v, hp + 4 * qq);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t c = dec_and_or(wq[st][j] >> (4 * q), cM, cC);
-                    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, c), __builtin_bit_cast(h2, hw[q]),
-                                               d, false);
-                    sh_sum += f16_lo(hw[q]) + f16_hi(hw[q]);
-                }
+                for (int r = 0; r < 4; ++r) shs += f16_lo(v[r]) + f16_hi(v[r]);
             }
-            float v = bf16_to_f32(sr[st]) * (d - 1024.0f * sh_sum) + bf16_to_f32(br[st]) * sh_sum;
-            v = row_total(v, LPR, sub);
-            if (rr < nrow && n0 + rr / (k + 1) < H && lj == 0) res[wave * nrow + rr] = v;
+            float d = 0.0f;
+            const uint32_t ww[4] = {cw[s].x, cw[s].y, cw[s].z, cw[s].w};
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t c = dec_and_or(ww[qq] >> (4 * p), cM, cC);
+                    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, c), __builtin_bit_cast(h2, hp[4 * qq + p]),
+                                               d, false);
+                }
+            const float v = bf16_to_f32(sv[s]) * (d - 1024.0f * shs) + bf16_to_f32(bv[s]) * shs;
+            float wgt = 1.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (r == s) wgt = sw[r];
+            acc = s < k ? __builtin_fmaf(wgt, v, acc) : acc + v;
         }
     }
+    acc = pair_sum(acc);
+    if ((lane & 1) == 0) red[wave * 32 + (lane >> 1)] = acc;
     __syncthreads();
-    if (lane < 2) {
-        const int n = n0 + lane;
-        if (n < H) {
-            float total = 0.0f;
-            for (int slot = 0; slot < k; ++slot)
-                total = __builtin_fmaf(tw[slot], res[wave * nrow + lane * (k + 1) + slot], total);
-            total += res[wave * nrow + lane * (k + 1) + k];
-            y[n] = total;
-        }
+    if (tid < 32) {
+        float sum = red[tid];
+#pragma unroll
+        for (int w = 1; w < DW; ++w) sum += red[w * 32 + tid];
+        y[256 * j + 32 * q + tid] = sum;
     }
 }
 
@@ -320,22 +323,23 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
                    float *tw, float *y, void *scratch, hipStream_t s) {
     const int H = sh.H, I = sh.I, E = sh.E, k = sh.top_k;
     char *p = (char *)scratch;
-    float *logits = (float *)p;         // [E]
-    p += 4096;
-    uint16_t *hbuf = (uint16_t *)p;     // fp16 [k+1][I]
+    float *logits = (float *)p;                 // [E]
+    uint16_t *hbuf = (uint16_t *)(p + 4096);    // fp16 [k+1][I]
+    if (k + 1 != NSLOT) return;                 // the API admits top_k = 8 only
     const PackLayout P = pack_layout(H, I, E);
     const uint8_t *pk = (const uint8_t *)w.packed;
     hipLaunchKernelGGL(decode_router_kernel, dim3((E + 3) / 4), dim3(256), 0, s, x, w.router_wt,
                        w.router_bias, H, E, logits);
-    const int rows = (k + 1) * I, rpi = 64 / (H / 32);
-    const int per_wg = 4 * DEC_ROWS_PER_WAVE * rpi;
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3((rows + per_wg - 1) / per_wg), dim3(256), 0, s,
-                       x, logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf);
-    const size_t lds = (size_t)(k + 1) * I * 2 + 4 * 2 * (k + 1) * 4;
-    hipLaunchKernelGGL(decode_down_kernel, dim3((H + 7) / 8), dim3(256), lds, s, hbuf, H, I, ids,
-                       tw, k, E, pk + P.down, pk + P.sh_down, y);
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / 128) * 4), dim3(64 * DW), 0, s, x,
+                       logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf);
+    const size_t lds = (size_t)(k + 1) * I * 2 + DW * 32 * 4;
+    hipLaunchKernelGGL(decode_down_kernel, dim3((H / 256) * 8), dim3(64 * DW), lds, s, hbuf, H, I,
+                       ids, tw, k, E, pk + P.down, pk + P.sh_down, y);
 }
 
-size_t decode_scratch_bytes(int I, int k) { return 4096 + (size_t)(k + 1) * I * 2; }
+size_t decode_scratch_bytes(int H, int I, int k) {
+    (void)H;
+    return 4096 + (size_t)(k + 1) * I * 2;
+}
 
 }  // namespace moe

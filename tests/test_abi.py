@@ -138,11 +138,13 @@ def test_decode_needs_t1():
     _, need1, _, _ = query(s1)
     assert L.moe_decode(C.byref(s1), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE, need1 - 1,
                         None) == WS
-    # the decode kernels need power-of-two H and I
-    s3 = shape(T=1, H=768)
+    # any supported H and I (multiples of 256 and 128): validation reaches the workspace check
+    s3 = shape(T=1, H=768, I=384)
     _, need3, _, _ = query(s3)
-    assert L.moe_decode(C.byref(s3), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE, need3,
-                        None) == UNSUP
+    assert L.moe_decode(C.byref(s3), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE, need3 - 1,
+                        None) == WS
+    assert L.moe_decode(C.byref(s3), FAKE, C.byref(_weights("null_packed")), FAKE, FAKE, FAKE, FAKE,
+                        need3, None) == INVALID
 
 
 def test_misc_validation():

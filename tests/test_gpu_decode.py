@@ -37,7 +37,9 @@ def test_decode_matches_oracle(seed):
 
 
 def test_decode_tiny_and_zipf():
-    for kw, seed in ((dict(T=1, H=512, I=128), 1030), (dict(T=1, H=2048, I=512, zipf_s=1.1), 4010)):
+    for kw, seed in ((dict(T=1, H=512, I=128), 1030), (dict(T=1, H=2048, I=512, zipf_s=1.1), 4010),
+                     (dict(T=1, H=768, I=384), 1031), (dict(T=1, H=256, I=1024), 1032)):
+        print(f"[decode] {kw} seed={seed}", flush=True)
         inp = make_layer(seed, **kw)
         ids, tw, y = run_decode(inp)
         y_ref, ids_ref, _ = oracle.Layer(inp).tokens([0])
