@@ -121,16 +121,14 @@ __host__ __device__ __forceinline__ int perm_pos(int col) {
     return (col & ~7) | ((p & 3) << 1) | (p >> 2);
 }
 
-// GEMM work queues (int32 words of the workspace's qctl area).  The routing
-// scatter writes the routed block counts per cost class and zeroes the
-// counters; each GEMM launch drains its eight per-XCD queues and its last
-// workgroup zeroes them again.  Every counter has a 128-byte line of its own
-// (atomics on one shared line serialise).
+// GEMM work queues (int32 words of the workspace's qctl area): per GEMM a
+// queue head and a finished-workgroup count.  The routing scatter zeroes
+// them; each GEMM launch's last workgroup zeroes its own again.  Every counter
+// has a 128-byte line of its own (atomics on one shared line serialise).
 constexpr int QCTL_LINE = 32;                       // words per counter
-constexpr int QCTL_GATEUP = 0;                      // 8 queue heads + finished count
-constexpr int QCTL_DOWN = 9 * QCTL_LINE;            // same for the down GEMM
-constexpr int QCTL_CLASS = 18 * QCTL_LINE;          // routed blocks with 4, 3, 2, 1 M tiles
-constexpr int QCTL_WORDS = 19 * QCTL_LINE;
+constexpr int QCTL_GATEUP = 0;                      // head, then finished count
+constexpr int QCTL_DOWN = 2 * QCTL_LINE;            // same for the down GEMM
+constexpr int QCTL_WORDS = 4 * QCTL_LINE;
 
 // Tile layout of the expert weights: one block per (tile of 256 columns, group
 // of 64 inputs), codes then scales then biases (the block format is documented

@@ -78,8 +78,7 @@ struct GemmArgs {
     const int32_t *blocks;
     const int32_t *num_blocks;
     const int32_t *sched;  // routed blocks by cost class (4, 3, 2, 1 M tiles), then expert
-    int32_t *qctl;         // this GEMM's eight queue heads and finished-workgroup count
-    const int32_t *ccount; // routed blocks per cost class
+    int32_t *qctl;         // this GEMM's queue head [0] and finished-workgroup count [QCTL_LINE]
     int max_blocks;
     const int32_t *row_token;
     const float *row_w;
@@ -400,100 +399,38 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
     }
 }
 
-// XCD (accelerator complex die) that runs this workgroup; each has its own L2.
-__device__ __forceinline__ int xcd_id() {
-    int v;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
-    return v & 7;
-}
-
-// Work queues.  The slots (shared-expert blocks, then the routed blocks of
-// cost class 4, 3, 2, 1 M tiles, each class ordered by expert) are dealt to
-// eight queues, one per XCD: queue x holds the x-th eighth of every segment,
-// so the queues carry equal work and an expert's blocks mostly share one
-// queue, hence one L2 for its weights.  A queue entry is (slot, n-tile), n-tile
-// fastest, so the n-tiles of a block (which read the same activation rows) run
-// side by side.  A workgroup drains the queue of its own XCD with an atomic
-// head, then helps the others in turn, so every entry is taken exactly once
-// whatever the placement of workgroups on XCDs.
-struct Queues {
-    int seg[5];        // segment sizes: shared, class 4, 3, 2, 1
-    int base[5];       // first slot of each segment (sched index for classes)
-};
-
-__device__ __forceinline__ int seg_lo(int n, int x) { return (n * x) >> 3; }
-
-// slots of queue x
-__device__ __forceinline__ int queue_slots(const Queues &Q, int x) {
-    int n = 0;
-#pragma unroll
-    for (int g = 0; g < 5; ++g) n += seg_lo(Q.seg[g], x + 1) - seg_lo(Q.seg[g], x);
-    return n;
-}
-
+// Work items: (slot, n-tile) with the n-tile fastest, so the n-tiles of a
+// block (which read the same activation rows) run side by side; slots are the
+// shared-expert blocks, then the routed blocks in the routing schedule's order
+// (cost class 4, 3, 2, 1 M tiles, each class by expert), i.e. longest first.
+// Workgroup g takes item g, then items from one atomic head in that order, so
+// the long items all start in the first round and the short ones fill in
+// behind them wherever a workgroup comes free.
 template <int MODE>
 __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    __shared__ int s_pick[2];
-    const int nb = min(a.num_blocks[0], a.max_blocks);
-    Queues Q;
-    Q.seg[0] = a.n_shared;
-    Q.base[0] = 0;
-    int left = max(nb, 0);
-#pragma unroll
-    for (int g = 1; g < 5; ++g) {
-        Q.seg[g] = min(max(a.ccount[g - 1], 0), left);    // never past the block map
-        left -= Q.seg[g];
-        Q.base[g] = g == 1 ? 0 : Q.base[g - 1] + Q.seg[g - 1];
-    }
-    // thread 0's queue state; `pend` is the head already taken from queue q
-    // for the next item (fetched while the current one runs), -1 if none
-    int q = xcd_id(), hops = 0, pend = -1;
+    __shared__ int s_pick;
+    const int nb = min(max(a.num_blocks[0], 0), a.max_blocks);
+    const int n_items = (a.n_shared + nb) * a.n_tiles;
+    int next = blockIdx.x;                       // thread 0: the item after the current one
+    int pend = -1;
     for (;;) {
         __syncthreads();                         // the previous item is done with the LDS
         if (threadIdx.x == 0) {
-            int k = -1;
-            while (hops < 8) {
-                const int len = queue_slots(Q, q) * a.n_tiles;
-                if (len > 0) {
-                    k = pend >= 0 ? pend : atomicAdd(&a.qctl[q * QCTL_LINE], 1);
-                    pend = -1;
-                    if (k < len) break;
-                }
-                pend = -1;
-                k = -1;
-                q = (q + 1) & 7;
-                ++hops;
-            }
-            s_pick[0] = k;
-            s_pick[1] = q;
-            if (k >= 0) pend = atomicAdd(&a.qctl[q * QCTL_LINE], 1);
+            const int k = pend >= 0 ? (int)gridDim.x + pend : next;
+            s_pick = k < n_items ? k : -1;
+            pend = k < n_items ? atomicAdd(&a.qctl[0], 1) : -1;   // the one after, fetched now
         }
         __syncthreads();
-        const int k = s_pick[0], x = s_pick[1];
+        const int k = s_pick;
         if (k < 0) break;
-        // entry k of queue x -> segment, slot
-        int i = k / a.n_tiles, g = 0, slot = -1;
-#pragma unroll
-        for (int gg = 0; gg < 5; ++gg) {
-            const int lo = seg_lo(Q.seg[gg], x), n = seg_lo(Q.seg[gg], x + 1) - lo;
-            if (slot < 0) {
-                if (i < n) {
-                    slot = Q.base[gg] + lo + i;
-                    g = gg;
-                } else {
-                    i -= n;
-                }
-            }
-        }
-        if (slot < 0) continue;
+        const int slot = k / a.n_tiles;
         Tile t;
-        t.ntile = k % a.n_tiles;
-        t.shared = g == 0;
+        t.ntile = k - slot * a.n_tiles;
+        t.shared = slot < a.n_shared;
         t.e = 0;
         if (!t.shared) {
-            if (slot >= a.max_blocks) continue;
-            const int mb = a.sched[slot];
+            const int mb = a.sched[slot - a.n_shared];
             if (mb < 0 || mb >= nb) continue;
             t.e = a.blocks[3 * mb];
             t.r0 = a.blocks[3 * mb + 1];
@@ -513,9 +450,10 @@ __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
             default: gemm_tile<MODE, 4>(a, t, smem); break;
         }
     }
-    // the last workgroup out re-arms the queues for the next launch
-    if (threadIdx.x == 0 && atomicAdd(&a.qctl[8 * QCTL_LINE], 1) == (int)gridDim.x - 1) {
-        for (int j = 0; j < 9; ++j) atomicExch(&a.qctl[j * QCTL_LINE], 0);
+    // the last workgroup out re-arms the head for the next launch
+    if (threadIdx.x == 0 && atomicAdd(&a.qctl[QCTL_LINE], 1) == (int)gridDim.x - 1) {
+        atomicExch(&a.qctl[0], 0);
+        atomicExch(&a.qctl[QCTL_LINE], 0);
     }
 }
 
@@ -557,7 +495,6 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum,
     a.num_blocks = num_blocks;
     a.sched = sched;
     a.qctl = qctl + QCTL_GATEUP;
-    a.ccount = qctl + QCTL_CLASS;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.T = sh.T;
@@ -624,7 +561,6 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
     a.num_blocks = num_blocks;
     a.sched = sched;
     a.qctl = qctl + QCTL_DOWN;
-    a.ccount = qctl + QCTL_CLASS;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.row_w = row_w;

@@ -661,9 +661,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
             __syncthreads();
         }
         const unsigned long long tot = cls_scan[255], pre = cls_scan[tid] - mine;
-        // class sizes for the GEMMs' per-XCD queues, and their counters at zero
-        if (tid < 18) qctl[tid * QCTL_LINE] = 0;
-        if (tid < 4) qctl[QCTL_CLASS + tid] = (int)((tot >> (16 * tid)) & 0xFFFF);
+        // the GEMMs' queue counters start at zero
+        if (tid < 4) qctl[tid * QCTL_LINE] = 0;
         int base[4];
         base[0] = 0;
         for (int c = 1; c < 4; ++c) base[c] = base[c - 1] + (int)((tot >> (16 * (c - 1))) & 0xFFFF);
