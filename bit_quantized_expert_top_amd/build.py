@@ -18,6 +18,9 @@ FLAGS = [
     # MFMA accumulators in VGPRs: the GEMM's register budget (two workgroups per
     # CU) fits without spills only in this form
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # atomics stay plain: the aggregating rewrite consumes the result at once,
+    # which would stall the GEMM's work-queue fetch that is meant to overlap
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -97,13 +97,18 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
     return r;
 }
 
-// 8 codes of one word -> 8 fp16 weights (q - 8) * s, element order (0,4,1,5,2,6,3,7)
-__device__ __forceinline__ f16x8 rebuild8(uint32_t w, uint32_t M, uint32_t C, f16x2 m1032,
-                                          f16x2 ss) {
-    const f16x2 p0 = (__builtin_bit_cast(f16x2, and_or(w, M, C)) + m1032) * ss;
-    const f16x2 p1 = (__builtin_bit_cast(f16x2, and_or(w >> 4, M, C)) + m1032) * ss;
-    const f16x2 p2 = (__builtin_bit_cast(f16x2, and_or(w >> 8, M, C)) + m1032) * ss;
-    const f16x2 p3 = (__builtin_bit_cast(f16x2, and_or(w >> 12, M, C)) + m1032) * ss;
+// 8 codes of one word -> 8 fp16 weights (q - 8) * s, element order (0,4,1,5,2,6,3,7).
+// Even nibbles (mask M1 = 0x000F000F) land as 1024 + q, odd ones (M2 =
+// 0x00F000F0) as 1024 + 16 q; subtracting 1032 resp. 1152 leaves q - 8 resp.
+// 16 (q - 8), and the scale s resp. s / 16 (exact in fp16 for |s| >= 2^-13,
+// as a subnormal at worst) gives (q - 8) s exactly: 13 operations per word.
+__device__ __forceinline__ f16x8 rebuild8(uint32_t w, uint32_t M1, uint32_t M2, uint32_t C,
+                                          f16x2 a1, f16x2 a2, f16x2 s1, f16x2 s16) {
+    const uint32_t w8 = w >> 8;
+    const f16x2 p0 = (__builtin_bit_cast(f16x2, and_or(w, M1, C)) + a1) * s1;
+    const f16x2 p1 = (__builtin_bit_cast(f16x2, and_or(w, M2, C)) + a2) * s16;
+    const f16x2 p2 = (__builtin_bit_cast(f16x2, and_or(w8, M1, C)) + a1) * s1;
+    const f16x2 p3 = (__builtin_bit_cast(f16x2, and_or(w8, M2, C)) + a2) * s16;
     u32x4 v;
     v.x = __builtin_bit_cast(uint32_t, p0);
     v.y = __builtin_bit_cast(uint32_t, p1);
@@ -152,8 +157,10 @@ __device__ __forceinline__ int src_row(const GemmArgs &a, const Tile &t, int m) 
     return t.r0 + mm;
 }
 
+// One tile.  Thread 0 also takes the workgroup's next work item from the queue
+// head during the main loop and leaves it in *s_next.
 template <int MODE, int MT>
-__device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
+__device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *s_next) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));              // recomputed per item: nothing lane-dependent is hoisted
@@ -213,12 +220,14 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mt][0][i] = acc[mt][1][i] = 0.0f;
 
-    uint32_t cM = 0x000F000Fu, cC = 0x64006400u;
-    asm volatile("" : "+v"(cM), "+v"(cC));       // keep the unpack constants in VGPRs
+    uint32_t cM = 0x000F000Fu, cM2 = 0x00F000F0u, cC = 0x64006400u;
+    asm volatile("" : "+v"(cM), "+v"(cM2), "+v"(cC));   // keep the unpack constants in VGPRs
     const f16x2 m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const f16x2 m1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     const int sw = (l32 >> 1) & 7;
     const int swb = (l32 >> 3) & 1;
     bool nz = false;                             // any group with b != -8 s in my columns
+    int next = 0;
 
     for (int c = 0; c < nch; ++c) {
         // stages issued after c: min(AHEAD - 1, nch - 1 - c)
@@ -233,10 +242,11 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
             wait_vm<(RG::AHEAD > 3 ? 3 : 0) * RG::PER>();
         __syncthreads();                         // stage c visible; stage c-1 no longer read
         if (c + RG::AHEAD < nch) issue(c + RG::AHEAD);   // into the slot of stage c-1
+        if (c == 1 && tid == 0) next = atomicAdd(&a.qctl[0], 1);   // overlaps the tile
 
         const uint8_t *sb = smem + (c % RG::NST) * RG::STAGE;
         u32x4 wq[2];
-        f16x2 ss[2];
+        f16x2 ss[2], ss16[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int bc = 64 * wave + 32 * nt + l32;
@@ -244,14 +254,15 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
             const uint8_t *pr = sb + RG::A_BYTES + B_BYTES + bc * 2;
             const float sf = bf16_to_f32(*(const uint16_t *)pr);
             nz |= bf16_to_f32(*(const uint16_t *)(pr + 512)) != -8.0f * sf;
-            const _Float16 sh = (_Float16)sf;
+            const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
             ss[nt] = f16x2{sh, sh};
+            ss16[nt] = f16x2{sh16, sh16};
         }
         const uint8_t *arow = sb + l32 * (KC * 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f16x8 b0 = rebuild8(wq[0][j], cM, cC, m1032, ss[0]);
-            const f16x8 b1 = rebuild8(wq[1][j], cM, cC, m1032, ss[1]);
+            const f16x8 b0 = rebuild8(wq[0][j], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
+            const f16x8 b1 = rebuild8(wq[1][j], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const f16x8 af =
@@ -262,6 +273,7 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
         }
     }
 
+    if (tid == 0) *s_next = next;                // read after the caller's next barrier
     // ---- rank-G term for groups whose bias is not -8 s (none for symmetric codes)
     if (__any(nz)) {
         const int K3 = 3 * G;
@@ -409,46 +421,47 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem) {
 template <int MODE>
 __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    __shared__ int s_pick;
+    __shared__ int s_next;
     const int nb = min(max(a.num_blocks[0], 0), a.max_blocks);
     const int n_items = (a.n_shared + nb) * a.n_tiles;
-    int next = blockIdx.x;                       // thread 0: the item after the current one
-    int pend = -1;
-    for (;;) {
-        __syncthreads();                         // the previous item is done with the LDS
-        if (threadIdx.x == 0) {
-            const int k = pend >= 0 ? (int)gridDim.x + pend : next;
-            s_pick = k < n_items ? k : -1;
-            pend = k < n_items ? atomicAdd(&a.qctl[0], 1) : -1;   // the one after, fetched now
-        }
-        __syncthreads();
-        const int k = s_pick;
-        if (k < 0) break;
+    // an item that turns out empty still takes the next one from the head
+    auto skip = [&]() {
+        if (threadIdx.x == 0) s_next = atomicAdd(&a.qctl[0], 1);
+    };
+    for (int k = blockIdx.x; k < n_items; k = (int)gridDim.x + s_next) {
+        __syncthreads();                         // s_next has been read by every thread
         const int slot = k / a.n_tiles;
         Tile t;
         t.ntile = k - slot * a.n_tiles;
         t.shared = slot < a.n_shared;
         t.e = 0;
+        bool ok = true;
         if (!t.shared) {
             const int mb = a.sched[slot - a.n_shared];
-            if (mb < 0 || mb >= nb) continue;
-            t.e = a.blocks[3 * mb];
-            t.r0 = a.blocks[3 * mb + 1];
-            t.nrows = a.blocks[3 * mb + 2];
-            // a malformed block map turns into a no-op, never an out-of-bounds access
-            if (t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
-                t.r0 + t.nrows > a.T * a.topk)
-                continue;
+            ok = mb >= 0 && mb < nb;
+            if (ok) {
+                t.e = a.blocks[3 * mb];
+                t.r0 = a.blocks[3 * mb + 1];
+                t.nrows = a.blocks[3 * mb + 2];
+                // a malformed block map turns into a no-op, never an out-of-bounds access
+                ok = !(t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
+                       t.r0 + t.nrows > a.T * a.topk);
+            }
         } else {
             t.r0 = a.T * a.topk + slot * kBM;
             t.nrows = min(kBM, a.T - slot * kBM);
         }
-        switch ((t.nrows + 31) >> 5) {
-            case 1: gemm_tile<MODE, 1>(a, t, smem); break;
-            case 2: gemm_tile<MODE, 2>(a, t, smem); break;
-            case 3: gemm_tile<MODE, 3>(a, t, smem); break;
-            default: gemm_tile<MODE, 4>(a, t, smem); break;
+        if (!ok) {
+            skip();
+        } else {
+            switch ((t.nrows + 31) >> 5) {
+                case 1: gemm_tile<MODE, 1>(a, t, smem, &s_next); break;
+                case 2: gemm_tile<MODE, 2>(a, t, smem, &s_next); break;
+                case 3: gemm_tile<MODE, 3>(a, t, smem, &s_next); break;
+                default: gemm_tile<MODE, 4>(a, t, smem, &s_next); break;
+            }
         }
+        __syncthreads();                         // s_next written; the tile is done with the LDS
     }
     // the last workgroup out re-arms the head for the next launch
     if (threadIdx.x == 0 && atomicAdd(&a.qctl[QCTL_LINE], 1) == (int)gridDim.x - 1) {

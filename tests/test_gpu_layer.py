@@ -143,3 +143,40 @@ def test_layer_asymmetric_bias(name, kw, seed):
             r = int(got["tok_row"][t, j])
             bound = 2.0 ** -10 * np.abs(a) + 1e-4 * np.sqrt(np.mean(a ** 2))
             assert np.all(np.abs(h[r] - a) <= bound), (t, j, e, np.max(np.abs(h[r] - a) - bound))
+
+
+@pytest.mark.parametrize("lo,hi", [(-13, -9), (8, 12)], ids=["small", "large"])
+def test_hidden_rows_scale_extremes(lo, hi):
+    """Scales at both ends of the range where the rebuilt fp16 weights are exact
+    ([2^-13, 2^12]; at the low end s / 16 is an fp16 subnormal): h still matches
+    the oracle to the fp16 storage bound."""
+    from synth.inputs import f32_to_bf16_bits
+    print(f"[scale-extremes] 2^{lo} .. 2^{hi}", flush=True)
+    inp = make_layer(4100 + lo, T=64, H=512, I=128)
+    rng = np.random.default_rng(lo + 50)
+    for p in (inp.gate, inp.up, inp.sh_gate, inp.sh_up):
+        e = rng.integers(lo, hi + 1, size=p.scale.shape)
+        m = 1.0 + rng.integers(0, 128, size=p.scale.shape) / 128.0
+        s = (m * 2.0 ** e).astype(np.float32)
+        p.scale[...] = f32_to_bf16_bits(s)
+        p.bias[...] = f32_to_bf16_bits(-8.0 * s)
+    # |x| in [2^-14, 2^-13) (large scales) or [1, 2) (small ones): fp16 normal
+    # values, and h stays well inside the fp16 range
+    mag = rng.uniform(1.0, 2.0, size=inp.x.shape) * (2.0 ** -14 if hi > 0 else 1.0)
+    sign = np.where(rng.random(size=inp.x.shape) < 0.5, -1.0, 1.0)
+    inp.x[...] = f32_to_bf16_bits((sign * mag).astype(np.float32))
+    run = LayerRun(inp).route().gemm().sync()
+    got = run.routing_np()
+    h = unpermute_cols(f16_np(run.h))
+    L = oracle.Layer(inp)
+    T, k = inp.T, inp.top_k
+    for t in range(0, T, 7):
+        for j in (0, 3, 7):
+            e = int(got["ids"][t, j])
+            a = L.expert_act(e, t)
+            r = int(got["tok_row"][t, j])
+            bound = 2.0 ** -10 * np.abs(a) + 1e-4 * np.sqrt(np.mean(a ** 2))
+            assert np.all(np.abs(h[r] - a) <= bound), (t, j, e, np.max(np.abs(h[r] - a) - bound))
+        a = L.expert_act(inp.E, t)
+        bound = 2.0 ** -10 * np.abs(a) + 1e-4 * np.sqrt(np.mean(a ** 2))
+        assert np.all(np.abs(h[T * k + t] - a) <= bound), t
