@@ -66,7 +66,7 @@ static_assert((Ring<1>::AHEAD - 1) * Ring<1>::PER < 64 && (Ring<2>::AHEAD - 1) *
               "vmcnt range");
 constexpr int HS_LD = 272;                   // epilogue h tile row stride (bytes)
 constexpr int YS_LD = 1056;                  // epilogue y tile row stride (bytes)
-static_assert(kBM * HS_LD <= L_TOTAL && 32 * YS_LD <= L_TOTAL, "epilogue tiles fit the ring");
+static_assert(kBM * HS_LD <= L_TOTAL && 64 * YS_LD <= L_TOTAL, "epilogue tiles fit the ring");
 
 struct GemmArgs {
     const uint16_t *A;     // fp16 permuted activations: x [T][H] (gate/up) or h [rows][I] (down)
@@ -160,7 +160,8 @@ __device__ __forceinline__ int src_row(const GemmArgs &a, const Tile &t, int m) 
 // One tile.  Thread 0 also takes the workgroup's next work item from the queue
 // head during the main loop and leaves it in *s_next.
 template <int MODE, int MT>
-__device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *s_next) {
+__device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *s_next,
+                          float *s_roww) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));              // recomputed per item: nothing lane-dependent is hoisted
@@ -202,17 +203,18 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     };
     // RG::PER copies per thread and stage, completing in order: stage c is in
     // once at most (stages issued after it) * PER copies are outstanding.
+    // routing weights of the tile's rows (down, routed): copied into LDS by DMA
+    // before the stage copies (so older than all of them) and complete with the
+    // main loop's last wait.  A plain load would be waited for in the epilogue
+    // behind the epilogue's own stores.
+    if (MODE == 1 && !t.shared && wave < 2) {
+        const uint32_t lw = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)s_roww;
+        const int m = min(64 * wave + lane, t.nrows - 1);
+        dma4(a.row_w + t.r0 + m, lw + (uint32_t)(256 * wave));
+    }
 #pragma unroll
     for (int p = 0; p < RG::AHEAD; ++p)
         if (p < nch) issue(p);
-    // routing weights of the rows this thread writes in the down epilogue,
-    // loaded now: a load there would also wait for the epilogue's own stores
-    float wrow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int row = 32 * mt + (tid >> 3);
-        wrow[mt] = (MODE == 1 && !t.shared && row < t.nrows) ? a.row_w[t.r0 + row] : 0.0f;
-    }
 
     floatx16 acc[MT][2];
 #pragma unroll
@@ -368,42 +370,53 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
         }
     } else {
         const int Trk = a.T * a.topk;
+        // two m-tiles (64 rows) per pass through the LDS y tile
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if (mt > 0) __syncthreads();
+        for (int p = 0; p < (MT + 1) / 2; ++p) {
+            if (p > 0) __syncthreads();
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int mt = 2 * p + h2;
+                if (mt < MT) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int rr = 8 * (i >> 2) + 4 * gg + (i & 3);
-                    *(float *)(smem + rr * YS_LD + 4 * (64 * wave + 32 * nt + l32)) = acc[mt][nt][i];
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int rr = 32 * h2 + 8 * (i >> 2) + 4 * gg + (i & 3);
+                            *(float *)(smem + rr * YS_LD + 4 * (64 * wave + 32 * nt + l32)) = acc[mt][nt][i];
+                        }
                 }
+            }
             __syncthreads();
-            // thread: row tid/8 of the 32-row tile, 32 columns from (tid&7)*32
-            const int rr = tid >> 3, seg = tid & 7;
-            const int row = 32 * mt + rr;
-            if (row < t.nrows) {
-                const uint8_t *src = smem + rr * YS_LD + seg * 128;
-                const int col = t.ntile * 256 + seg * 32;
-                if (t.shared) {
-                    float *dst = a.y + (size_t)(t.r0 - Trk + row) * a.N + col;
+            // thread: row tid/8 of each 32-row half, 32 columns from (tid&7)*32
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        *(floatx4 *)(dst + 4 * q) = *(const floatx4 *)(src + 16 * q);
-                } else {
-                    // routed row: weighted output staged in bf16 (fp32 range; the combine adds in fp32)
-                    uint16_t *dst = a.stage + (size_t)(t.r0 + row) * a.N + col;
-                    const float wr = wrow[mt];
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int mt = 2 * p + h2;
+                const int rr = 32 * h2 + (tid >> 3), seg = tid & 7;
+                const int row = 32 * mt + (tid >> 3);
+                if (mt < MT && row < t.nrows) {
+                    const uint8_t *src = smem + rr * YS_LD + seg * 128;
+                    const int col = t.ntile * 256 + seg * 32;
+                    if (t.shared) {
+                        float *dst = a.y + (size_t)(t.r0 - Trk + row) * a.N + col;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const floatx4 v0 = *(const floatx4 *)(src + 32 * q);
-                        const floatx4 v1 = *(const floatx4 *)(src + 32 * q + 16);
-                        u32x4 o;
-                        o.x = pack_bf16x2(wr * v0[0], wr * v0[1]);
-                        o.y = pack_bf16x2(wr * v0[2], wr * v0[3]);
-                        o.z = pack_bf16x2(wr * v1[0], wr * v1[1]);
-                        o.w = pack_bf16x2(wr * v1[2], wr * v1[3]);
-                        *(u32x4 *)(dst + 8 * q) = o;
+                        for (int q = 0; q < 8; ++q)
+                            *(floatx4 *)(dst + 4 * q) = *(const floatx4 *)(src + 16 * q);
+                    } else {
+                        // routed row: weighted output staged in bf16 (fp32 range; the combine adds in fp32)
+                        uint16_t *dst = a.stage + (size_t)(t.r0 + row) * a.N + col;
+                        const float wr = s_roww[row];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const floatx4 v0 = *(const floatx4 *)(src + 32 * q);
+                            const floatx4 v1 = *(const floatx4 *)(src + 32 * q + 16);
+                            u32x4 o;
+                            o.x = pack_bf16x2(wr * v0[0], wr * v0[1]);
+                            o.y = pack_bf16x2(wr * v0[2], wr * v0[3]);
+                            o.z = pack_bf16x2(wr * v1[0], wr * v1[1]);
+                            o.w = pack_bf16x2(wr * v1[2], wr * v1[3]);
+                            *(u32x4 *)(dst + 8 * q) = o;
+                        }
                     }
                 }
             }
@@ -422,6 +435,7 @@ template <int MODE>
 __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     __shared__ int s_next;
+    __shared__ float s_roww[kBM];
     const int nb = min(max(a.num_blocks[0], 0), a.max_blocks);
     const int n_items = (a.n_shared + nb) * a.n_tiles;
     // an item that turns out empty still takes the next one from the head
@@ -455,10 +469,10 @@ __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
             skip();
         } else {
             switch ((t.nrows + 31) >> 5) {
-                case 1: gemm_tile<MODE, 1>(a, t, smem, &s_next); break;
-                case 2: gemm_tile<MODE, 2>(a, t, smem, &s_next); break;
-                case 3: gemm_tile<MODE, 3>(a, t, smem, &s_next); break;
-                default: gemm_tile<MODE, 4>(a, t, smem, &s_next); break;
+                case 1: gemm_tile<MODE, 1>(a, t, smem, &s_next, s_roww); break;
+                case 2: gemm_tile<MODE, 2>(a, t, smem, &s_next, s_roww); break;
+                case 3: gemm_tile<MODE, 3>(a, t, smem, &s_next, s_roww); break;
+                default: gemm_tile<MODE, 4>(a, t, smem, &s_next, s_roww); break;
             }
         }
         __syncthreads();                         // s_next written; the tile is done with the LDS

@@ -153,110 +153,143 @@ __device__ __forceinline__ u32x4 permute_to_f16(u32x4 v) {
     return o;
 }
 
-// Approximate logits (no bias), partial over K range s: part[s][t][e].  The
-// same pass also prepares x for the expert GEMM (workgroups of expert tile 0:
-// fp16 with the 8-block permutation (0,4,1,5,2,6,3,7), and per group of 64 the
-// sum and the sum of squares), and the squared norms of the router rows per K range
-// (workgroups of token tile 0).
+// Approximate logits (no bias), partial over K range s: part[s][t][e].  A
+// workgroup takes 32 tokens x all 256 experts x one K range: per 64-wide
+// chunk the x rows (4 KB) and the router rows (32 KB) are copied into an LDS
+// ring by whole-line DMA (16-byte slots XOR-swizzled by row so that the MFMA
+// operand reads are free of bank conflicts), and wave w computes experts
+// 64 w .. 64 w + 63.  The same pass prepares x for the expert GEMM from the
+// staged chunk (fp16 with the 8-block permutation (0,4,1,5,2,6,3,7), and per
+// group of 64 the sum and the sum of squares), and the workgroups of token
+// tile 0 the squared norms of the router rows per K range.
+constexpr int RT_TOK = 32;
+constexpr int RX_BYTES = RT_TOK * 128;            // x chunk [32 rows][8 x 16 B]
+constexpr int RW_BYTES = 256 * 128;               // router chunk [256 rows][8 x 16 B]
+constexpr int R_STAGE = RX_BYTES + RW_BYTES;
+constexpr int R_NST = 3;
+
+__device__ __forceinline__ void rdma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int H, int E, int S,
     float *__restrict__ part, uint16_t *__restrict__ xp, float *__restrict__ xsum,
     float *__restrict__ xsq, float *__restrict__ wn2part) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t rsm[];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)rsm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, gg = lane >> 5;
-    const int t0 = blockIdx.x * 64 + 32 * (wave & 1), e0 = blockIdx.y * 64 + 32 * (wave >> 1);
-    const int sp = blockIdx.z, klen = H / S, kbeg = sp * klen;
-    const int trow = min(t0 + l32, T - 1);
-    const bool do_prep = blockIdx.y == 0 && (wave >> 1) == 0 && t0 + l32 < T;
-    const bool do_norm = blockIdx.x == 0 && (wave & 1) == 0;
-    const int G = H / 64;
-    // k order inside a chunk: step j of half gg holds k = 32 gg + 8 j + 0..7, so
-    // each lane reads 64 contiguous bytes of its row (the same order for both
-    // operands; the approximate logits are certified afterwards)
-    const uint16_t *pa = x + (size_t)trow * H + kbeg + 32 * gg;
-    const uint16_t *pb = wr + (size_t)(e0 + l32) * H + kbeg + 32 * gg;
-    floatx16 tot;
+    const int t0 = blockIdx.x * RT_TOK, sp = blockIdx.y;
+    const int klen = H / S, kbeg = sp * klen, nch = klen / 64, G = H / 64;
+    // DMA: thread tid copies slot tid&7 of row tid/8 (x) and of rows 32 i + tid/8
+    // (router); the slot holds segment slot ^ (row & 7) of the row's 128 bytes
+    const int seg = (tid & 7) ^ ((tid >> 3) & 7);
+    const uint16_t *xsrc = x + (size_t)min(t0 + (tid >> 3), T - 1) * H + kbeg + 8 * seg;
+    const uint16_t *wsrc = wr + (size_t)(tid >> 3) * H + kbeg + 8 * seg;
+    auto issue = [&](int c) {
+        const uint32_t base = lds0 + (uint32_t)((c % R_NST) * R_STAGE);
+        rdma16(xsrc + 64 * c, base + (uint32_t)(wave * 1024));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tot[i] = 0.0f;
+        for (int i = 0; i < 8; ++i)
+            rdma16(wsrc + (size_t)32 * i * H + 64 * c, base + (uint32_t)(RX_BYTES + 4096 * i + wave * 1024));
+    };
+    issue(0);
+    if (nch > 1) issue(1);
+    floatx16 tot[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot[0][i] = tot[1][i] = 0.0f;
     const floatx16 zero = {};
-    const int nch = klen / 64;
     float wsq = 0.0f;
-    // 4-slot register ring, loads issued three chunks ahead (nch <= 8 since H <= 2048
-    // and S = 4); fully unrolled so that every slot index is static
-    constexpr int RING = 4, MAXCH = 8;
-    u32x4 ra[RING][4], rb[RING][4];
-#pragma unroll
-    for (int c = 0; c < RING - 1; ++c)
-        if (c < nch) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ra[c][j] = *(const u32x4 *)(pa + 64 * c + 8 * j);
-                rb[c][j] = *(const u32x4 *)(pb + 64 * c + 8 * j);
-            }
-        }
+    const bool do_norm = blockIdx.x == 0;
+    // x preparation results, stored after the loop: a store issued inside it
+    // would count against the DMA waits (one vmcnt for loads and stores)
+    constexpr int MAXCH = 8;                       // H <= 2048, four K ranges
+    u32x4 xpv[MAXCH];
+    float s1v[MAXCH], s2v[MAXCH];
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c) {
         if (c >= nch) break;
-        if (c + RING - 1 < nch) {
+        if (c + 1 < nch)
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                           // chunk c in; chunk c-1 no longer read
+        if (c + 2 < nch) issue(c + 2);
+        const uint8_t *sx = rsm + (c % R_NST) * R_STAGE;
+        const uint8_t *sw = sx + RX_BYTES;
+        // 32 x 64 experts: per 16-wide k step j, segment 2 j + gg of the rows
+        floatx16 p[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ra[(c + RING - 1) % RING][j] = *(const u32x4 *)(pa + 64 * (c + RING - 1) + 8 * j);
-                rb[(c + RING - 1) % RING][j] = *(const u32x4 *)(pb + 64 * (c + RING - 1) + 8 * j);
+        for (int j = 0; j < 4; ++j) {
+            const int sg = 2 * j + gg;
+            const bf16x8 av = *(const bf16x8 *)(sx + l32 * 128 + 16 * (sg ^ (l32 & 7)));
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int e = 64 * wave + 32 * nt + l32;
+                const bf16x8 bv = *(const bf16x8 *)(sw + e * 128 + 16 * (sg ^ (e & 7)));
+                p[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, j == 0 ? zero : p[nt], 0, 0, 0);
             }
         }
-        const u32x4(&av)[4] = ra[c % RING];
-        const u32x4(&bv)[4] = rb[c % RING];
-        floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, av[0]), __builtin_bit_cast(bf16x8, bv[0]), zero, 0, 0, 0);
 #pragma unroll
-        for (int j = 1; j < 4; ++j)
-            p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]),
-                                                        __builtin_bit_cast(bf16x8, bv[j]), p, 0, 0, 0);
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tot[i] += p[i];
-        if (do_prep) {
-            // this lane holds k = 32gg + 8j + 0..7 of the chunk's group
+            for (int i = 0; i < 16; ++i) tot[nt][i] += p[nt][i];
+        // x preparation: thread -> row tid/8, 16-byte segment tid&7 of the chunk
+        {
+            const int row = tid >> 3, sg = tid & 7;
+            const u32x4 v = *(const u32x4 *)(sx + row * 128 + 16 * (sg ^ (row & 7)));
             float s1 = 0.0f, s2 = 0.0f;
-            uint16_t *q = xp + (size_t)(t0 + l32) * H + kbeg + 64 * c + 32 * gg;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32x4 v = av[j];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    s1 += bf16_lo(v[r]) + bf16_hi(v[r]);
-                    s2 = __builtin_fmaf(bf16_lo(v[r]), bf16_lo(v[r]), s2);
-                    s2 = __builtin_fmaf(bf16_hi(v[r]), bf16_hi(v[r]), s2);
-                }
-                *(u32x4 *)(q + 8 * j) = permute_to_f16(v);
+            for (int q = 0; q < 4; ++q) {
+                s1 += bf16_lo(v[q]) + bf16_hi(v[q]);
+                s2 = __builtin_fmaf(bf16_lo(v[q]), bf16_lo(v[q]), s2);
+                s2 = __builtin_fmaf(bf16_hi(v[q]), bf16_hi(v[q]), s2);
             }
-            s1 += __shfl_xor(s1, 32);
-            s2 += __shfl_xor(s2, 32);
-            if (gg == 0) {
-                const size_t gi = (size_t)(t0 + l32) * G + kbeg / 64 + c;
-                xsum[gi] = s1;
-                xsq[gi] = s2;
-            }
+            s1v[c] = group_sum_dpp(s1, 8);
+            s2v[c] = group_sum_dpp(s2, 8);
+            xpv[c] = permute_to_f16(v);
         }
-        if (do_norm) {
+        if (do_norm) {                             // thread tid = router row tid
+            const uint8_t *rw = sw + tid * 128;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int sg = 0; sg < 8; ++sg) {
+                // slots in a row-dependent order: eight lanes read eight banks
+                const u32x4 v = *(const u32x4 *)(rw + 16 * (sg ^ (tid & 7)));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    wsq = __builtin_fmaf(bf16_lo(bv[j][r]), bf16_lo(bv[j][r]), wsq);
-                    wsq = __builtin_fmaf(bf16_hi(bv[j][r]), bf16_hi(bv[j][r]), wsq);
+                for (int q = 0; q < 4; ++q) {
+                    wsq = __builtin_fmaf(bf16_lo(v[q]), bf16_lo(v[q]), wsq);
+                    wsq = __builtin_fmaf(bf16_hi(v[q]), bf16_hi(v[q]), wsq);
                 }
+            }
         }
     }
-    if (do_norm) {
-        wsq += __shfl_xor(wsq, 32);
-        if (gg == 0) wn2part[(size_t)sp * E + e0 + l32] = wsq;
+    if (do_norm) wn2part[(size_t)sp * E + tid] = wsq;
+    {
+        const int row = tid >> 3, sg = tid & 7;
+        if (t0 + row < T) {
+#pragma unroll
+            for (int c = 0; c < MAXCH; ++c) {
+                if (c >= nch) break;
+                *(u32x4 *)(xp + (size_t)(t0 + row) * H + kbeg + 64 * c + 8 * sg) = xpv[c];
+                if (sg == 0) {
+                    const size_t gi = (size_t)(t0 + row) * G + kbeg / 64 + c;
+                    xsum[gi] = s1v[c];
+                    xsq[gi] = s2v[c];
+                }
+            }
+        }
     }
     float *out = part + (size_t)sp * T * E;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = t0 + 8 * (i >> 2) + 4 * gg + (i & 3);
-        if (t < T) out[(size_t)t * E + e0 + l32] = tot[i];
-    }
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = t0 + 8 * (i >> 2) + 4 * gg + (i & 3);
+            if (t < T) out[(size_t)t * E + 64 * wave + 32 * nt + l32] = tot[nt][i];
+        }
 }
 
 // Fixed-order logit of one expert row for the half-wave `half` (lanes
@@ -367,11 +400,20 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 lt[j] = exact[(size_t)t * E + e];
                 dl[j] = 0.0f;
             } else {
-                float v = part[(size_t)t * E + e];
-                for (int sp = 1; sp < S; ++sp) v += part[((size_t)sp * T + t) * E + e];
+                // all RS_SPLIT partials and norms are loaded at once (S == RS_SPLIT)
+                float pv[RS_SPLIT], wv[RS_SPLIT];
+#pragma unroll
+                for (int sp = 0; sp < RS_SPLIT; ++sp) {
+                    pv[sp] = part[((size_t)sp * T + t) * E + e];
+                    wv[sp] = wn2[(size_t)sp * E + e];
+                }
+                float v = pv[0], w2 = wv[0];
+#pragma unroll
+                for (int sp = 1; sp < RS_SPLIT; ++sp) {
+                    v += pv[sp];
+                    w2 += wv[sp];
+                }
                 lt[j] = v + b;
-                float w2 = wn2[e];
-                for (int sp = 1; sp < S; ++sp) w2 += wn2[(size_t)sp * E + e];
                 dl[j] = 0x1p-16f * (sqrtf(w2) * nx * 1.001f + fabsf(b)) + 0x1p-100f;
             }
         }
@@ -554,16 +596,22 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
 
 void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
                         float *wn2part, uint16_t *xp, float *xsum, float *xsq, hipStream_t s) {
-    const int S = min(RS_SPLIT, H / 64);
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 63) / 64, E / 64, S), dim3(256), 0, s, x, wr,
-                       T, H, E, S, part, xp, xsum, xsq, wn2part);
+    const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
+    static bool lds_set = false;
+    if (!lds_set) {
+        (void)hipFuncSetAttribute((const void *)router_mfma_kernel,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, R_NST * R_STAGE);
+        lds_set = true;
+    }
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + RT_TOK - 1) / RT_TOK, S), dim3(256),
+                       R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq, wn2part);
 }
 
 void launch_route_select(const float *part, const float *exact, const float *xsq,
                          const float *wn2, const float *bias, const uint16_t *x,
                          const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,
                          int32_t *blk_cnt, int32_t *lrank, hipStream_t s) {
-    const int S = min(RS_SPLIT, H / 64);
+    const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
     hipLaunchKernelGGL(route_select_kernel, dim3((T + TB - 1) / TB), dim3(64 * TB), 0, s, part, S,
                        exact, xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank);
 }
