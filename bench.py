@@ -39,9 +39,9 @@ SEED_DECODE = 2000
 # 131085.5 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
 # source these counters were taken on; otherwise the JSON reports null.
 GATEUP_TRAFFIC = {
-    "gemm_src_sha256": "b3f07a2ec21d3a6f3bb74a68b0c9df16a5d2d7fec626e79ae464f291ddc1a7ed",
-    "fetch_kib": 244373.6, "fetch_scale": 2.0,
-    "write_kib": 23063.5, "write_scale": 1.0,
+    "gemm_src_sha256": "250116bba8ddeb9ce4b8d205701ee57f02c99f67433ec50967abf949b60309f2",
+    "fetch_kib": 147704.8, "fetch_scale": 2.0,
+    "write_kib": 20801.7, "write_scale": 1.0,
     "profile": "profiles/q4_gemm_gateup_prefill2048_zipf_hbm_traffic.md",
 }
 
