@@ -261,17 +261,27 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
             ss16[nt] = f16x2{sh16, sh16};
         }
         const uint8_t *arow = sb + l32 * (KC * 2);
+        // steps (j, mt) in order; the A fragment of step s is read two steps
+        // ahead into a 3-slot ring, so LDS latency overlaps two MFMA pairs
+        constexpr int NSTEP = 4 * MT;
+        auto a_frag = [&](int s) {
+            const int j = s / MT, mt = s % MT;
+            return *(const f16x8 *)(arow + mt * 32 * (KC * 2) + 16 * ((4 * gg + j) ^ sw));
+        };
+        f16x8 af[3];
+        af[0] = a_frag(0);
+        if (NSTEP > 1) af[1] = a_frag(1);
+        f16x8 b0, b1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const f16x8 b0 = rebuild8(wq[0][j], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
-            const f16x8 b1 = rebuild8(wq[1][j], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const f16x8 af =
-                    *(const f16x8 *)(arow + mt * 32 * (KC * 2) + 16 * ((4 * gg + j) ^ sw));
-                acc[mt][0] = mfma16(af, b0, acc[mt][0]);
-                acc[mt][1] = mfma16(af, b1, acc[mt][1]);
+        for (int s = 0; s < NSTEP; ++s) {
+            const int j = s / MT, mt = s % MT;
+            if (mt == 0) {
+                b0 = rebuild8(wq[0][j], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
+                b1 = rebuild8(wq[1][j], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
             }
+            if (s + 2 < NSTEP) af[(s + 2) % 3] = a_frag(s + 2);
+            acc[mt][0] = mfma16(af[s % 3], b0, acc[mt][0]);
+            acc[mt][1] = mfma16(af[s % 3], b1, acc[mt][1]);
         }
     }
 

@@ -369,6 +369,77 @@ __device__ void recompute_candidates(const uint32_t *cand_e, float *cand_l, int 
     }
 }
 
+// The k <= 8 largest of the wave's 256 keys (key[j] belongs to expert lane + 64 j),
+// ties to the lower expert index.  A bitwise search from the top bit finds the
+// k-th largest key value T (stopping early once exactly k keys reach the
+// candidate); the picks are the keys above T and the lowest-index keys equal to
+// T.  They are then ranked by (key desc, index asc) through wave-local LDS (wl:
+// 32 words).  Lane p < k ends with pick p; taken[j] marks the picks.
+__device__ void wave_topk_radix(const uint32_t (&key)[4], int k, bool (&taken)[4], int &pick_e,
+                                uint32_t &pick_key, uint32_t *wl) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t lo = 0;                     // #(key >= lo) >= k throughout
+    bool exact = false;                  // #(key >= lo) == k
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = lo | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt += (int)__popcll(__ballot(key[j] >= cand));
+        if (cnt >= k) {
+            lo = cand;
+            if (cnt == k) {
+                exact = true;
+                break;
+            }
+        }
+    }
+    if (exact) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) taken[j] = key[j] >= lo;
+    } else {
+        // lo is the k-th largest value: every key above it, then keys equal to it
+        // in ascending expert index (j, then lane) until k are taken
+        int need = k;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) need -= (int)__popcll(__ballot(key[j] > lo));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t eq = __ballot(key[j] == lo);
+            const bool mine = key[j] == lo && (int)__popcll(eq & below) < need;
+            taken[j] = key[j] > lo || mine;
+            need -= min((int)__popcll(eq), max(need, 0));
+        }
+    }
+    // compact the picks (any order), then rank them
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t bal = __ballot(taken[j]);
+        if (taken[j]) {
+            const int pos = base + (int)__popcll(bal & below);
+            wl[pos] = (uint32_t)(lane + 64 * j);
+            wl[8 + pos] = key[j];
+        }
+        base += (int)__popcll(bal);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) {
+        const uint32_t ep = wl[lane], kp = wl[8 + lane];
+        int rk = 0;
+        for (int q = 0; q < k; ++q) {
+            const uint32_t eq = wl[q], kq = wl[8 + q];
+            rk += (kq > kp || (kq == kp && eq < ep)) ? 1 : 0;
+        }
+        wl[16 + rk] = ep;
+        wl[24 + rk] = kp;
+    }
+    __builtin_amdgcn_wave_barrier();
+    pick_e = lane < k ? (int)wl[16 + lane] : -1;
+    pick_key = lane < k ? wl[24 + lane] : 0u;
+    __builtin_amdgcn_wave_barrier();
+}
+
 __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     const float *__restrict__ part, int S, const float *__restrict__ exact,
     const float *__restrict__ xsq, int G, const float *__restrict__ wn2,
@@ -387,34 +458,37 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     if (t < T) {
         // ---- logits (approximate or exact) and their error radius
         float lt[4], dl[4];
-        float nx = 0.0f;
-        if (!exact) {
-            float ss = (lane < G) ? xsq[(size_t)t * G + lane] : 0.0f;
-            nx = sqrtf(wave_sum_f(ss));
-        }
+        // every load of this phase goes out before the first wait: the token's
+        // sums of squares, all RS_SPLIT partials and norms, and the biases
+        float ss = 0.0f, bv[4], pv[4][RS_SPLIT], wv[4][RS_SPLIT];
+        if (!exact && lane < G) ss = xsq[(size_t)t * G + lane];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane + 64 * j;
-            const float b = bias ? bias[e] : 0.0f;
+            bv[j] = bias ? bias[e] : 0.0f;
             if (exact) {
                 lt[j] = exact[(size_t)t * E + e];
                 dl[j] = 0.0f;
             } else {
-                // all RS_SPLIT partials and norms are loaded at once (S == RS_SPLIT)
-                float pv[RS_SPLIT], wv[RS_SPLIT];
 #pragma unroll
                 for (int sp = 0; sp < RS_SPLIT; ++sp) {
-                    pv[sp] = part[((size_t)sp * T + t) * E + e];
-                    wv[sp] = wn2[(size_t)sp * E + e];
+                    pv[j][sp] = part[((size_t)sp * T + t) * E + e];
+                    wv[j][sp] = wn2[(size_t)sp * E + e];
                 }
-                float v = pv[0], w2 = wv[0];
+            }
+        }
+        if (!exact) {
+            const float nx = sqrtf(wave_sum_f(ss));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = pv[j][0], w2 = wv[j][0];
 #pragma unroll
                 for (int sp = 1; sp < RS_SPLIT; ++sp) {
-                    v += pv[sp];
-                    w2 += wv[sp];
+                    v += pv[j][sp];
+                    w2 += wv[j][sp];
                 }
-                lt[j] = v + b;
-                dl[j] = 0x1p-16f * (sqrtf(w2) * nx * 1.001f + fabsf(b)) + 0x1p-100f;
+                lt[j] = v + bv[j];
+                dl[j] = 0x1p-16f * (sqrtf(w2) * nx * 1.001f + fabsf(bv[j])) + 0x1p-100f;
             }
         }
         // ---- top-k by the (approximate) logits, ties to the lower index, then the
@@ -434,25 +508,25 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 key[j] = ordered_key(lt[j]);
                 taken[j] = false;
             }
-            for (int p = 0; p < k; ++p) {
-                uint32_t km;
-                const int e = wave_argmax4(key, taken, &km);
-                float lb = 0.0f, ub = 0.0f;
+            // the picks, then each pick's logit and radius from wave-local LDS
+            // (cand_l / cand_e are free between recompute rounds)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (lane + 64 * j == e) {
-                        taken[j] = true;
-                        lb = lt[j] - dl[j];
-                        ub = lt[j] + dl[j];
-                    }
-                const float lbe = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lb), e & 63));
-                const float ube = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ub), e & 63));
-                if (lane == p) {
-                    my_pick = e;
-                    my_l = key_to_float(km);
-                    my_lb = lbe;
-                    my_ub = ube;
+            for (int j = 0; j < 4; ++j) {
+                cand_l[tl][lane + 64 * j] = lt[j];
+                cand_e[tl][lane + 64 * j] = __float_as_uint(dl[j]);
+            }
+            {
+                int pe;
+                uint32_t pkey;
+                wave_topk_radix(key, k, taken, pe, pkey, (uint32_t *)scr[tl]);
+                if (lane < k) {
+                    const float l = cand_l[tl][pe], d = __uint_as_float(cand_e[tl][pe]);
+                    my_pick = pe;
+                    my_l = key_to_float(pkey);
+                    my_lb = l - d;
+                    my_ub = l + d;
                 }
+                __builtin_amdgcn_wave_barrier();
             }
             // certificate: disjoint intervals in rank order, nothing else reaching the k-th
             m8 = INFINITY;
