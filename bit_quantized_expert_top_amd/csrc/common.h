@@ -103,6 +103,77 @@ __device__ __forceinline__ int wave_argmax4(const uint32_t (&key)[4], const bool
     return -1;
 }
 
+// The k <= 8 largest of the wave's 256 keys (key[j] belongs to expert lane + 64 j),
+// ties to the lower expert index.  A bitwise search from the top bit finds the
+// k-th largest key value T (stopping early once exactly k keys reach the
+// candidate); the picks are the keys above T and the lowest-index keys equal to
+// T.  They are then ranked by (key desc, index asc) through wave-local LDS (wl:
+// 32 words).  Lane p < k ends with pick p; taken[j] marks the picks.
+__device__ inline void wave_topk_radix(const uint32_t (&key)[4], int k, bool (&taken)[4], int &pick_e,
+                                uint32_t &pick_key, uint32_t *wl) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t lo = 0;                     // #(key >= lo) >= k throughout
+    bool exact = false;                  // #(key >= lo) == k
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = lo | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt += (int)__popcll(__ballot(key[j] >= cand));
+        if (cnt >= k) {
+            lo = cand;
+            if (cnt == k) {
+                exact = true;
+                break;
+            }
+        }
+    }
+    if (exact) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) taken[j] = key[j] >= lo;
+    } else {
+        // lo is the k-th largest value: every key above it, then keys equal to it
+        // in ascending expert index (j, then lane) until k are taken
+        int need = k;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) need -= (int)__popcll(__ballot(key[j] > lo));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t eq = __ballot(key[j] == lo);
+            const bool mine = key[j] == lo && (int)__popcll(eq & below) < need;
+            taken[j] = key[j] > lo || mine;
+            need -= min((int)__popcll(eq), max(need, 0));
+        }
+    }
+    // compact the picks (any order), then rank them
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t bal = __ballot(taken[j]);
+        if (taken[j]) {
+            const int pos = base + (int)__popcll(bal & below);
+            wl[pos] = (uint32_t)(lane + 64 * j);
+            wl[8 + pos] = key[j];
+        }
+        base += (int)__popcll(bal);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) {
+        const uint32_t ep = wl[lane], kp = wl[8 + lane];
+        int rk = 0;
+        for (int q = 0; q < k; ++q) {
+            const uint32_t eq = wl[q], kq = wl[8 + q];
+            rk += (kq > kp || (kq == kp && eq < ep)) ? 1 : 0;
+        }
+        wl[16 + rk] = ep;
+        wl[24 + rk] = kp;
+    }
+    __builtin_amdgcn_wave_barrier();
+    pick_e = lane < k ? (int)wl[16 + lane] : -1;
+    pick_key = lane < k ? wl[24 + lane] : 0u;
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Sum over aligned groups of n lanes (n = 1, 2, 4, 8 or 16) with DPP; every
 // lane of a group ends with the group's sum.
 __device__ __forceinline__ float group_sum_dpp(float v, int n) {

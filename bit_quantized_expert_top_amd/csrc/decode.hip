@@ -70,10 +70,11 @@ __global__ __launch_bounds__(256) void decode_router_kernel(const uint16_t *__re
     if (lane == 0) logits[e] = l;
 }
 
-// Top-k (k <= 8) of E <= 256 logits by (logit desc, index asc) and the weights
+// Top-k (k <= 8) of E = 256 logits by (logit desc, index asc) and the weights
 // exp(l - l_1) / sum, computed by one wave (all lanes end with the same picks).
+// wl: 32 words of wave-local LDS.
 __device__ void select_topk(const float *__restrict__ logits, int E, int k, int *pick_e,
-                            float *pick_w) {
+                            float *pick_w, uint32_t *wl) {
     const int lane = threadIdx.x & 63;
     uint32_t key[4];
     bool taken[4];
@@ -81,19 +82,15 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
     for (int j = 0; j < 4; ++j) {
         const int e = lane + 64 * j;
         key[j] = e < E ? ordered_key(logits[e]) : 0u;
-        taken[j] = e >= E;
     }
+    int pe;
+    uint32_t pkey;
+    wave_topk_radix(key, k, taken, pe, pkey, wl);
     float pick_l[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        if (r >= k) break;
-        uint32_t km;
-        const int e = wave_argmax4(key, taken, &km);
-        pick_e[r] = e;
-        pick_l[r] = key_to_float(km);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (lane + 64 * j == e) taken[j] = true;
+        pick_e[r] = r < k ? __builtin_amdgcn_readlane(pe, r) : 0;
+        pick_l[r] = r < k ? key_to_float((uint32_t)__builtin_amdgcn_readlane((int)pkey, r)) : 0.0f;
     }
     const float m = pick_l[0];
     float sum = 0.0f;
@@ -131,6 +128,7 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     const uint8_t *__restrict__ pk, const uint8_t *__restrict__ pk_sh, int32_t *__restrict__ ids_out,
     float *__restrict__ tw_out, uint16_t *__restrict__ hbuf) {
     __shared__ float red[DW][2][32];
+    __shared__ uint32_t selw[DW][32];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = H / 64, JT = I / 128;
     const int b = blockIdx.x;
@@ -139,7 +137,7 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     if (slot < k) {
         int pe[8];
         float pw[8];
-        select_topk(logits, E, k, pe, pw);
+        select_topk(logits, E, k, pe, pw, selw[wave]);
 #pragma unroll
         for (int r = 0; r < 8; ++r)
             if (r == slot) ex = pe[r];

@@ -25,6 +25,10 @@ CASES = [
     ("T1_prefill_path", dict(T=1, H=2048, I=512), 2001, 1),
     ("prefill512", dict(T=512, H=2048, I=512), 3000, 40),
     ("prefill2048_zipf", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4000, 40),
+    # narrow H (one router chunk per K quarter, one down tile), wide I, ragged T
+    ("narrowH_wideI", dict(T=77, H=256, I=1024), 4200, 40),
+    # H not a power of two, I = 3 x 128
+    ("H768_I384", dict(T=200, H=768, I=384, zipf_s=1.1), 4201, 40),
 ]
 
 
