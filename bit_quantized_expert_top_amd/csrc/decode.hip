@@ -34,14 +34,15 @@ __device__ __forceinline__ uint32_t dec_and_or(uint32_t a, uint32_t m, uint32_t 
     return r;
 }
 
-// 1. logits[e] = sum over chunks c (in order) of sum_{k in chunk c} x_k w_ek (in order), + bias
-__global__ __launch_bounds__(256) void decode_router_kernel(const uint16_t *__restrict__ x,
-                                                            const uint16_t *__restrict__ wr,
-                                                            const float *__restrict__ bias, int H,
-                                                            int E, float *__restrict__ logits) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave;
-    if (e >= E) return;
+// 1. logits[e] = sum over chunks c (in order) of sum_{k in chunk c} x_k w_ek (in order), + bias.
+// One wave (one workgroup) per expert, so the 1 MB of router weights is read
+// by E workgroups at once.
+__global__ __launch_bounds__(64) void decode_router_kernel(const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ wr,
+                                                           const float *__restrict__ bias, int H,
+                                                           float *__restrict__ logits) {
+    const int lane = threadIdx.x;
+    const int e = blockIdx.x;
     const int G = H / 64;          // <= 32 chunks: lane c < G sums chunk c
     float P = 0.0f;
     if (lane < G) {
@@ -78,11 +79,11 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
     const int lane = threadIdx.x & 63;
     uint32_t key[4];
     bool taken[4];
+    float lv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        key[j] = e < E ? ordered_key(logits[e]) : 0u;
-    }
+    for (int j = 0; j < 4; ++j) lv[j] = logits[min(lane + 64 * j, E - 1)];   // one round trip
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[j] = lane + 64 * j < E ? ordered_key(lv[j]) : 0u;
     int pe;
     uint32_t pkey;
     wave_topk_radix(key, k, taken, pe, pkey, wl);
@@ -105,6 +106,9 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
 
 constexpr int DW = 8;                  // waves per decode workgroup
 constexpr int NSLOT = 9;               // top-8 routed experts + the shared one (top_k is 8)
+constexpr int DOUT = 8;                // outputs per decode workgroup (gate/up and down)
+constexpr int DN_BATCH = 3;            // down: (slot, group) pairs per lane loaded at once
+constexpr int DN_MAXP = NSLOT * 32;    // down: (slot, group) pairs for I <= 2048
 
 // code pair p of word w as two 16-bit values q_p, q_{p+4} in a magic-number
 // format (and-or with C = 128.0 bf16 pairs or 1024.0 fp16 pairs)
@@ -121,18 +125,37 @@ __device__ __forceinline__ float pair_sum(float v) {
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
-// 2. gate/up.  Workgroup (slot, tile j, slice q of 32 gate + 32 up columns);
-// wave w takes groups w, w + DW, ...
+// 2. gate/up.  Workgroup (slot, 8 outputs i = 8 o .. 8 o + 7 of I): their
+// gate and up columns are two 256-byte runs of every block of the slot's tile.
+// Lane (gi, cc, ph) of wave w holds physical half ph of gate and up column cc
+// of group 4 w + gi (+ 32 per further pass), so one load instruction of a wave
+// covers four groups.  x is loaded before the selection, the weights right
+// after it, all at once.
 __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
     const uint8_t *__restrict__ pk, const uint8_t *__restrict__ pk_sh, int32_t *__restrict__ ids_out,
     float *__restrict__ tw_out, uint16_t *__restrict__ hbuf) {
-    __shared__ float red[DW][2][32];
+    __shared__ float red[DW][4][DOUT][2];
     __shared__ uint32_t selw[DW][32];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int G = H / 64, JT = I / 128;
-    const int b = blockIdx.x;
-    const int slot = b / (JT * 4), j = (b >> 2) % JT, q = b & 3;
+    const int G = H / 64, JT = I / 128, OPS = I / DOUT;
+    const int slot = blockIdx.x / OPS, o = blockIdx.x % OPS;
+    const int j = o >> 4, u = (o >> 2) & 3, v = o & 3;            // 8 o = 128 j + 32 u + 8 v
+    const int gi = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
+    const int lh = ph ^ (v & 1);                                  // logical half of my pieces
+    const int tcg = 64 * u + 8 * v + cc;                          // my gate column; up is tcg + 32
+    // x of my groups: 32 values from 64 g + 32 lh
+    constexpr int NP = 2;                                         // passes: G <= 32 needs one
+    u32x4 xv[NP][4];
+    bool act[NP];
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+        const int g = 4 * (wave + DW * it) + gi;
+        act[it] = g < G;
+        const u32x4 *px = (const u32x4 *)(x + 64 * min(g, G - 1) + 32 * lh);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) xv[it][qq] = px[qq];       // clamped: loads stay unconditional
+    }
     int ex = 0;
     if (slot < k) {
         int pe[8];
@@ -142,7 +165,7 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
         for (int r = 0; r < 8; ++r)
             if (r == slot) ex = pe[r];
         ex = (ex < 0 || ex >= E) ? 0 : ex;
-        if (b == 0 && wave == 0 && lane < k) {
+        if (blockIdx.x == 0 && wave == 0 && lane < k) {
             int e = 0;
             float wv = 0.0f;
 #pragma unroll
@@ -157,139 +180,139 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     }
     const uint8_t *tile = slot == k ? pk_sh + (size_t)j * G * PK_BLOCK
                                     : pk + ((size_t)ex * JT + j) * G * PK_BLOCK;
-    const int hh = (lane & 1) ^ ((lane >> 4) & 1);      // logical half of my pieces
-    const int cg = 64 * q + (lane >> 1);                 // my gate column; up is cg + 32
+    u32x4 cw[NP][2];
+    uint16_t sv[NP][2], bv[NP][2];
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+        const int g = min(4 * (wave + DW * it) + gi, G - 1);
+        const uint8_t *blk = tile + (size_t)g * PK_BLOCK;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int tc = tcg + 32 * r;
+            cw[it][r] = *(const u32x4 *)(blk + 32 * tc + 16 * ph);
+            sv[it][r] = *(const uint16_t *)(blk + PK_CODES + 2 * tc);
+            bv[it][r] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * tc);
+        }
+    }
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     uint32_t cM = 0x000F000Fu, cC = 0x43004300u;
     asm volatile("" : "+v"(cM), "+v"(cC));
     float ag = 0.0f, au = 0.0f;
-    constexpr int GPW = 4;                               // groups per pass of a wave
-    for (int g0 = wave; g0 < G; g0 += DW * GPW) {
-        u32x4 cw[GPW][2];
-        uint16_t sv[GPW][2], bv[GPW][2];
 #pragma unroll
-        for (int t = 0; t < GPW; ++t) {
-            const int g = min(g0 + DW * t, G - 1);
-            const uint8_t *blk = tile + (size_t)g * PK_BLOCK;
+    for (int it = 0; it < NP; ++it) {
+        if (!act[it]) continue;
+        uint32_t xp[16];
+        float sx = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                cw[t][r] = *(const u32x4 *)(blk + 16 * (128 * q + 64 * r + lane));
-                sv[t][r] = *(const uint16_t *)(blk + PK_CODES + 2 * (cg + 32 * r));
-                bv[t][r] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * (cg + 32 * r));
-            }
+        for (int qq = 0; qq < 4; ++qq) {
+            pair_order(xv[it][qq], xp + 4 * qq);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sx += bf16_lo(xv[it][qq][r]) + bf16_hi(xv[it][qq][r]);
         }
 #pragma unroll
-        for (int t = 0; t < GPW; ++t) {
-            const int g = g0 + DW * t;
-            if (g >= G) break;
-            const u32x4 *px = (const u32x4 *)(x + 64 * g + 32 * hh);
-            uint32_t xp[16];
-            float sx = 0.0f;
+        for (int r = 0; r < 2; ++r) {
+            float d = 0.0f;
+            const uint32_t ww[4] = {cw[it][r].x, cw[it][r].y, cw[it][r].z, cw[it][r].w};
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const u32x4 v = px[qq];
-                pair_order(v, xp + 4 * qq);
+            for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sx += bf16_lo(v[r]) + bf16_hi(v[r]);
-            }
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                float d = 0.0f;
-                const uint32_t ww[4] = {cw[t][r].x, cw[t][r].y, cw[t][r].z, cw[t][r].w};
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const uint32_t c = dec_and_or(ww[qq] >> (4 * p), cM, cC);
-                        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c),
-                                                            __builtin_bit_cast(bf16x2, xp[4 * qq + p]), d, false);
-                    }
-                const float v = bf16_to_f32(sv[t][r]) * (d - 128.0f * sx) + bf16_to_f32(bv[t][r]) * sx;
-                if (r == 0) ag += v; else au += v;
-            }
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t c = dec_and_or(ww[qq] >> (4 * p), cM, cC);
+                    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c),
+                                                        __builtin_bit_cast(bf16x2, xp[4 * qq + p]), d, false);
+                }
+            // sum_k x_k (q_k s + b) = s (sum x (128 + q) - 128 sum x) + b sum x
+            const float val = bf16_to_f32(sv[it][r]) * (d - 128.0f * sx) + bf16_to_f32(bv[it][r]) * sx;
+            if (r == 0) ag += val; else au += val;
         }
     }
     ag = pair_sum(ag);
     au = pair_sum(au);
-    if ((lane & 1) == 0) {
-        red[wave][0][lane >> 1] = ag;
-        red[wave][1][lane >> 1] = au;
+    if (ph == 0) {
+        red[wave][gi][cc][0] = ag;
+        red[wave][gi][cc][1] = au;
     }
     __syncthreads();
-    if (threadIdx.x < 32) {
+    if (threadIdx.x < DOUT) {
         const int m = threadIdx.x;
-        float gs = red[0][0][m], us = red[0][1][m];
+        float gs = 0.0f, us = 0.0f;
 #pragma unroll
-        for (int w = 1; w < DW; ++w) {
-            gs += red[w][0][m];
-            us += red[w][1][m];
-        }
-        const int i = 128 * j + 32 * q + m;
-        hbuf[(size_t)slot * I + i] = f32_to_f16(gs / (1.0f + expf(-gs)) * us);
+        for (int w = 0; w < DW; ++w)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gs += red[w][q][m][0];
+                us += red[w][q][m][1];
+            }
+        hbuf[(size_t)slot * I + DOUT * o + m] = f32_to_f16(gs / (1.0f + expf(-gs)) * us);
     }
 }
 
-// 3. down.  Workgroup (tile j, slice q of 32 outputs); wave w takes groups
-// w, w + DW, .. of every slot.
+// 3. down.  Workgroup: 8 outputs n = 8 v' .. 8 v' + 7 of H (a 256-byte run of
+// every block of their tile) for all nine slots and all groups of I.  Lane
+// (sub, cc, ph) of wave w takes pair 4 (w + 8 it) + sub of the (slot, group)
+// pairs, physical half ph of column cc; the pairs' partial sums meet in LDS and
+// are added per output in a fixed order: groups, then slots in pick order with
+// their routing weights, then the shared expert.
 __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     const uint16_t *__restrict__ hbuf, int H, int I, const int32_t *__restrict__ ids,
     const float *__restrict__ tw, int k, int E, const uint8_t *__restrict__ pk,
     const uint8_t *__restrict__ pk_sh, float *__restrict__ y) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-    uint16_t *hs = (uint16_t *)dsm;                                  // fp16 [k+1][I]
-    float *red = (float *)(dsm + (size_t)(k + 1) * I * 2);           // [DW][32]
+    __shared__ float part[DN_MAXP][DOUT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
-    const int G = I / 64, JD = H / 256;
-    const int j = blockIdx.x >> 3, q = blockIdx.x & 7;
-    const int hh = (lane & 1) ^ ((lane >> 4) & 1);
-    const int col = 32 * q + (lane >> 1);
-    int sid[8];
-    float sw[8];
+    const int G = I / 64, JD = H / 256, NPAIR = (k + 1) * G;
+    const int j = blockIdx.x >> 5, v = blockIdx.x & 31;          // outputs 256 j + 8 v + (0..7)
+    const int sub = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
+    const int tc = 8 * v + cc;
+    const int lh = ph ^ (v & 1);
+    int sid[NSLOT];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int e = r < k ? ids[r] : 0;
-        sid[r] = (e < 0 || e >= E) ? 0 : e;
-        sw[r] = r < k ? tw[r] : 0.0f;
+    for (int s = 0; s < NSLOT; ++s) {
+        const int e = s < k ? ids[s] : 0;
+        sid[s] = (e < 0 || e >= E) ? 0 : e;
     }
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     uint32_t cM = 0x000F000Fu, cC = 0x64006400u;
     asm volatile("" : "+v"(cM), "+v"(cC));
-    float acc = 0.0f;
-    bool staged = false;
-    for (int g = wave; g < G || !staged; g += DW) {
-        const int gg = min(g, G - 1);
-        // this group's 1 KB slice of every slot's block
-        u32x4 cw[NSLOT];
-        uint16_t sv[NSLOT], bv[NSLOT];
+    const int npass = (NPAIR + 4 * DW - 1) / (4 * DW);
+    for (int it0 = 0; it0 < npass; it0 += DN_BATCH) {
+        u32x4 cw[DN_BATCH], hv[DN_BATCH][4];
+        uint16_t sv[DN_BATCH], bv[DN_BATCH];
+        int pp[DN_BATCH];
 #pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
+        for (int b = 0; b < DN_BATCH; ++b) {
+            const int p = 4 * (wave + DW * (it0 + b)) + sub;
+            pp[b] = p;
+            const int pc = min(p, NPAIR - 1);
+            const int s = pc / G, g = pc - s * G;
+            int e = 0;
+#pragma unroll
+            for (int r = 0; r < NSLOT; ++r)
+                if (r == s) e = sid[r];
             const uint8_t *blk = (s == k ? pk_sh + (size_t)j * G * PK_BLOCK
-                                         : pk + ((size_t)sid[s] * JD + j) * G * PK_BLOCK) +
-                                 (size_t)gg * PK_BLOCK;
-            cw[s] = *(const u32x4 *)(blk + 16 * (64 * q + lane));
-            sv[s] = *(const uint16_t *)(blk + PK_CODES + 2 * col);
-            bv[s] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * col);
-        }
-        if (!staged) {                                  // h of every slot into LDS
-            const int nh = (k + 1) * I / 8;
-            for (int u = tid; u < nh; u += 64 * DW) ((u32x4 *)hs)[u] = ((const u32x4 *)hbuf)[u];
-            __syncthreads();
-            staged = true;
-        }
-        if (g >= G) break;
+                                         : pk + ((size_t)e * JD + j) * G * PK_BLOCK) +
+                                 (size_t)g * PK_BLOCK;
+            // pairs past the end load the last pair again (unconditional loads are
+            // issued together) and are skipped below
+            cw[b] = *(const u32x4 *)(blk + 32 * tc + 16 * ph);
+            sv[b] = *(const uint16_t *)(blk + PK_CODES + 2 * tc);
+            bv[b] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * tc);
+            const u32x4 *ph4 = (const u32x4 *)(hbuf + (size_t)s * I + 64 * g + 32 * lh);
 #pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
+            for (int qq = 0; qq < 4; ++qq) hv[b][qq] = ph4[qq];
+        }
+#pragma unroll
+        for (int b = 0; b < DN_BATCH; ++b) {
+            if (pp[b] >= NPAIR) continue;
             uint32_t hp[16];
             float shs = 0.0f;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                const u32x4 v = *(const u32x4 *)(hs + (size_t)s * I + 64 * g + 32 * hh + 8 * qq);
-                pair_order(v, hp + 4 * qq);
+                pair_order(hv[b][qq], hp + 4 * qq);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) shs += f16_lo(v[r]) + f16_hi(v[r]);
+                for (int r = 0; r < 4; ++r) shs += f16_lo(hv[b][qq][r]) + f16_hi(hv[b][qq][r]);
             }
             float d = 0.0f;
-            const uint32_t ww[4] = {cw[s].x, cw[s].y, cw[s].z, cw[s].w};
+            const uint32_t ww[4] = {cw[b].x, cw[b].y, cw[b].z, cw[b].w};
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
@@ -298,22 +321,20 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
                     d = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, c), __builtin_bit_cast(h2, hp[4 * qq + p]),
                                                d, false);
                 }
-            const float v = bf16_to_f32(sv[s]) * (d - 1024.0f * shs) + bf16_to_f32(bv[s]) * shs;
-            float wgt = 1.0f;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (r == s) wgt = sw[r];
-            acc = s < k ? __builtin_fmaf(wgt, v, acc) : acc + v;
+            // sum_i h_i (q_i s + b) = s (sum h (1024 + q) - 1024 sum h) + b sum h
+            const float val = pair_sum(bf16_to_f32(sv[b]) * (d - 1024.0f * shs) + bf16_to_f32(bv[b]) * shs);
+            if (ph == 0) part[pp[b]][cc] = val;
         }
     }
-    acc = pair_sum(acc);
-    if ((lane & 1) == 0) red[wave * 32 + (lane >> 1)] = acc;
     __syncthreads();
-    if (tid < 32) {
-        float sum = red[tid];
-#pragma unroll
-        for (int w = 1; w < DW; ++w) sum += red[w * 32 + tid];
-        y[256 * j + 32 * q + tid] = sum;
+    if (tid < DOUT) {
+        float sum = 0.0f;
+        for (int s = 0; s <= k; ++s) {
+            float a = 0.0f;
+            for (int g = 0; g < G; ++g) a += part[s * G + g][tid];
+            sum = s < k ? __builtin_fmaf(tw[s], a, sum) : sum + a;
+        }
+        y[256 * j + DOUT * v + tid] = sum;
     }
 }
 
@@ -323,16 +344,16 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     char *p = (char *)scratch;
     float *logits = (float *)p;                 // [E]
     uint16_t *hbuf = (uint16_t *)(p + 4096);    // fp16 [k+1][I]
-    if (k + 1 != NSLOT) return;                 // the API admits top_k = 8 only
+    // the API admits top_k = 8, E <= 256, H <= 2048 (G <= 32), I <= 2048
+    if (k + 1 != NSLOT || E > 256 || H > 2048 || I > 2048) return;
     const PackLayout P = pack_layout(H, I, E);
     const uint8_t *pk = (const uint8_t *)w.packed;
-    hipLaunchKernelGGL(decode_router_kernel, dim3((E + 3) / 4), dim3(256), 0, s, x, w.router_wt,
-                       w.router_bias, H, E, logits);
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / 128) * 4), dim3(64 * DW), 0, s, x,
-                       logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf);
-    const size_t lds = (size_t)(k + 1) * I * 2 + DW * 32 * 4;
-    hipLaunchKernelGGL(decode_down_kernel, dim3((H / 256) * 8), dim3(64 * DW), lds, s, hbuf, H, I,
-                       ids, tw, k, E, pk + P.down, pk + P.sh_down, y);
+    hipLaunchKernelGGL(decode_router_kernel, dim3(E), dim3(64), 0, s, x, w.router_wt, w.router_bias, H,
+                       logits);
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT)), dim3(64 * DW), 0, s, x, logits,
+                       H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf);
+    hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT), dim3(64 * DW), 0, s, hbuf, H, I, ids, tw, k,
+                       E, pk + P.down, pk + P.sh_down, y);
 }
 
 size_t decode_scratch_bytes(int H, int I, int k) {
