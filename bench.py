@@ -10,7 +10,10 @@ layers) so that no step finds its weights in the 256 MB last-level cache.
 
 Also reported: the gate/up GEMM kernel's MFMA roofline fraction (HIP events
 around its launch inside the timed loop), the batch-1 decode path's HBM
-bandwidth, and the CPU oracle's throughput on a bounded token sample.
+bandwidth, the T=512 layer with uniform-ish routing (every expert active: HBM
+bandwidth over the weights read), a stack of 40 layers at T=4096 with the
+residual add and RMSNorm between layers (tokens/s, no host synchronisation in
+the pass), and the CPU oracle's throughput on a bounded token sample.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -30,6 +33,8 @@ T, H, I, E, K_TOP = 2048, 2048, 512, 256, 8
 ZIPF_S = 1.1
 SEED_PREFILL = 4000
 SEED_DECODE = 2000
+SEED_UNIFORM = 3000
+SEED_STACK = 5000
 
 
 # HBM traffic of the gate/up GEMM launch on this workload, from two rocprofv3 --pmc
@@ -73,6 +78,10 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="weight sets rotated in the prefill loop")
     ap.add_argument("--decode-sets", type=int, default=32)
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--uniform-sets", type=int, default=4,
+                    help="weight sets of the T=512 uniform-routing leg (0: skip it)")
+    ap.add_argument("--stack-layers", type=int, default=40,
+                    help="layers of the T=4096 stack leg (0: skip it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -219,6 +228,114 @@ def main():
     del dsets
     torch.cuda.empty_cache()
 
+    # ---------------- prefill T=512, uniform-ish routing: every expert is active ----------------
+    uni = None
+    if args.uniform_sets:
+        Tu = 512
+        print(f"[bench] T={Tu} uniform routing, {args.uniform_sets} weight sets", file=sys.stderr,
+              flush=True)
+        ushape = moe.Shape(T=Tu, H=H, I=I, E=E, top_k=K_TOP)
+        raw = make_layer_device(SEED_UNIFORM, Tu, H, I, E, zipf_s=None, device=dev)
+        xu = raw["x"]
+        usets = [device_layer(raw)]
+        del raw
+        for s in range(1, args.uniform_sets):
+            usets.append(device_layer(make_layer_device(SEED_UNIFORM + 100 * s, Tu, H, I, E,
+                                                        zipf_s=None, device=dev, with_x=False)))
+        ur = moe.Routing(ushape, dev, with_logits=False)
+        uws = moe.workspace(ushape, dev)
+        uh = torch.empty((Tu * K_TOP + Tu, I), dtype=torch.int16, device=dev)
+        uy = torch.empty((Tu, H), dtype=torch.float32, device=dev)
+
+        def ustep(w):
+            moe.moe_route(ushape, xu, w, ur, uws)
+            moe.moe_expert_gemm_q4(ushape, xu, w, ur, uh, uws)
+            moe.moe_down_combine(ushape, uh, w, ur, uy, uws)
+
+        for w in usets:
+            ustep(w)
+        torch.cuda.synchronize()
+        active = int((ur.counts > 0).sum().item())
+        ug = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ug):
+            for w in usets:
+                ustep(w)
+        ug.replay()
+        torch.cuda.synchronize()
+        ureps = max(1, 24 // len(usets))
+        u0 = torch.cuda.Event(enable_timing=True)
+        u1 = torch.cuda.Event(enable_timing=True)
+        u0.record()
+        for _ in range(ureps):
+            ug.replay()
+        u1.record()
+        torch.cuda.synchronize()
+        u_us = u0.elapsed_time(u1) / (ureps * len(usets)) * 1e3
+        # algorithmic bytes: the active experts' and the shared expert's packed weights,
+        # the router weights, x (bf16) and y (fp32)
+        u_bytes = (active + 1) * expert_bytes(H, I) + E * H * 2 + Tu * H * 2 + Tu * H * 4
+        u_gbs = u_bytes / (u_us * 1e-6) / 1e9
+        uni = {"workload": f"prefill{Tu}_uniform: one MoE layer, T={Tu}, random router, "
+                           f"{active} of {E} experts active",
+               "us_per_step": round(u_us, 2), "tokens_per_s": round(Tu / (u_us * 1e-6), 1),
+               "bytes_per_step": u_bytes, "hbm_gbs": round(u_gbs, 1),
+               "hbm_frac": round(u_gbs / PEAK_HBM_GBS, 4), "weight_sets": len(usets)}
+        del ug, usets, ur, uws, uh, uy, xu
+        torch.cuda.empty_cache()
+
+    # ---------------- 40-layer stack at T=4096: residual + RMSNorm between layers ----------------
+    stack = None
+    if args.stack_layers:
+        Ts, L = 4096, args.stack_layers
+        print(f"[bench] stack of {L} layers at T={Ts}", file=sys.stderr, flush=True)
+        sshape = moe.Shape(T=Ts, H=H, I=I, E=E, top_k=K_TOP)
+        x0 = make_layer_device(SEED_STACK, Ts, H, I, E, device=dev)["x"]
+        layers = [device_layer(make_layer_device(SEED_STACK + l, Ts, H, I, E, device=dev,
+                                                 with_x=False)) for l in range(L)]
+        sr = moe.Routing(sshape, dev, with_logits=False)
+        sws = moe.workspace(sshape, dev)
+        sh_ = torch.empty((Ts * K_TOP + Ts, I), dtype=torch.int16, device=dev)
+        sy = torch.empty((Ts, H), dtype=torch.float32, device=dev)
+        res = torch.empty((Ts, H), dtype=torch.float32, device=dev)
+        u = torch.empty_like(x0)
+
+        def stack_pass():
+            # r_0 = x, u_0 = x; every layer: y = MoE(u); r += y; u = bf16(RMSNorm(r))
+            res.copy_(x0.view(torch.bfloat16))
+            u.copy_(x0)
+            for w in layers:
+                moe.moe_route(sshape, u, w, sr, sws)
+                moe.moe_expert_gemm_q4(sshape, u, w, sr, sh_, sws)
+                moe.moe_down_combine(sshape, sh_, w, sr, sy, sws)
+                moe.moe_rmsnorm_residual(Ts, H, 1e-6, res, sy, u)
+
+        stack_pass()
+        torch.cuda.synchronize()
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg):
+            stack_pass()
+        sg.replay()
+        torch.cuda.synchronize()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        sreps = 3
+        s0.record()
+        for _ in range(sreps):
+            sg.replay()
+        s1.record()
+        torch.cuda.synchronize()
+        s_ms = s0.elapsed_time(s1) / sreps
+        srows = Ts * K_TOP + Ts
+        s_flops = L * 2.0 * srows * 3 * I * H
+        stack = {"workload": f"stack{L}_T{Ts}: {L} MoE layers with residual add + RMSNorm between "
+                             f"them, T={Ts}, random routers, independent weights per layer",
+                 "ms_per_pass": round(s_ms, 3), "us_per_layer": round(s_ms * 1e3 / L, 2),
+                 "tokens_per_s": round(Ts / (s_ms * 1e-3), 1),
+                 "layer_mfma_frac": round(s_flops / (s_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                 "host_syncs_per_pass": 0}
+        del sg, layers, sr, sws, sh_, sy, res, u, x0
+        torch.cuda.empty_cache()
+
     # ---------------- CPU oracle baseline (rank 0, N=1) ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -273,6 +390,8 @@ def main():
         "decode": {"metric": "T=1 decode HBM GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
                    "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(dec_us, 2),
                    "bytes_per_call": dec_bytes, "weight_sets": args.decode_sets},
+        "prefill512_uniform": uni,
+        "stack": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -25,6 +25,8 @@ CASES = [
     ("T1_prefill_path", dict(T=1, H=2048, I=512), 2001, 1),
     ("prefill512", dict(T=512, H=2048, I=512), 3000, 40),
     ("prefill2048_zipf", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4000, 40),
+    # one layer of the 40-layer stack workload (T=4096, random router)
+    ("stack_layer_T4096", dict(T=4096, H=2048, I=512), 5000, 40),
     # narrow H (one router chunk per K quarter, one down tile), wide I, ragged T
     ("narrowH_wideI", dict(T=77, H=256, I=1024), 4200, 40),
     # H not a power of two, I = 3 x 128

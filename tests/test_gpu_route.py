@@ -17,6 +17,8 @@ CASES = [
     ("prefill512", dict(T=512, H=2048, I=512), 3000),
     ("prefill2048_zipf", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4000),
     ("prefill2048_zipf_s1", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4001),
+    # one layer of the 40-layer stack workload (T=4096, random router)
+    ("stack_layer_T4096", dict(T=4096, H=2048, I=512), 5000),
 ]
 
 
