@@ -39,6 +39,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <utility>
 
 namespace moe {
 
@@ -125,13 +126,30 @@ __device__ __forceinline__ floatx16 mfma16(f16x8 a, f16x8 b, floatx16 c) {
 // [lds + 16 i, +16) (dword form: [lds + 4 i, +4)).  Issued through inline assembly so that the compiler does not
 // wait for them before every LDS read; completion is awaited explicitly
 // (s_waitcnt vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-                 : "memory", "m0");
-}
 __device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
+}
+
+// The same copies with a wave-uniform base address in SGPRs and a per-lane
+// 32-bit byte offset: the per-lane offsets stay fixed over the K loop and each
+// K step only moves the scalar base.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // s_waitcnt vmcnt(n) for a compile-time n
@@ -174,13 +192,14 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     // ---- DMA sources of this thread
     // A: rows 32i + tid/8 (i < MT); 16 B slot tid&7 of a row holds its
     // segment slot ^ ((row >> 1) & 7)
+    // (byte offsets from the wave-uniform bases, fixed over the K loop)
     uint32_t aoff[MT];
     {
         const int seg = (tid & 7) ^ ((tid >> 4) & 7);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int m = 32 * i + (tid >> 3);
-            aoff[i] = (uint32_t)src_row<MODE>(a, t, m) * (uint32_t)K + (uint32_t)(8 * seg);
+            aoff[i] = ((uint32_t)src_row<MODE>(a, t, m) * (uint32_t)K + (uint32_t)(8 * seg)) * 2u;
         }
     }
     // B and S: the tile's block of K step c is one contiguous tile-layout
@@ -188,18 +207,18 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     // and dword lane of the wave's quarter of the scale/bias bytes
     const uint8_t *tb = t.shared ? a.pk_sh + (size_t)t.ntile * G * PK_BLOCK
                                  : a.pk + ((size_t)t.e * a.n_tiles + t.ntile) * G * PK_BLOCK;
-    const uint8_t *bsrc = tb + 16 * tid;
-    const uint8_t *ssrc = tb + PK_CODES + 256 * wave + 4 * lane;
-    auto issue = [&](int c) {
-        const uint32_t base = lds0 + (uint32_t)((c % RG::NST) * RG::STAGE);
+    const uint32_t boff = 16u * (uint32_t)tid;
+    const uint32_t soff = (uint32_t)(PK_CODES + 256 * wave + 4 * lane);
+    // stage c into ring slot SLOT (c % NST, known at compile time)
+    auto issue = [&](int c, auto SLOT) {
+        constexpr uint32_t base = (uint32_t)(decltype(SLOT)::value * RG::STAGE);
+        const uint8_t *ag = (const uint8_t *)a.A + (size_t)c * (KC * 2);
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-            dma16(a.A + (size_t)aoff[i] + c * KC, base + (uint32_t)((i * 256 + wave * 64) * 16));
-        const uint8_t *blk = bsrc + (size_t)c * PK_BLOCK;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            dma16(blk + 4096 * i, base + (uint32_t)(RG::A_BYTES + (i * 256 + wave * 64) * 16));
-        dma4(ssrc + (size_t)c * PK_BLOCK, base + (uint32_t)(RG::A_BYTES + B_BYTES + wave * 256));
+        for (int i = 0; i < MT; ++i) dma16s(ag, aoff[i], lds0 + base + (uint32_t)((i * 256 + wave * 64) * 16));
+        const uint8_t *blk = tb + (size_t)c * PK_BLOCK;
+        dma16s(blk, boff, lds0 + base + (uint32_t)(RG::A_BYTES + wave * 64 * 16));
+        dma16s(blk + 4096, boff, lds0 + base + (uint32_t)(RG::A_BYTES + (256 + wave * 64) * 16));
+        dma4s(blk, soff, lds0 + base + (uint32_t)(RG::A_BYTES + B_BYTES + wave * 256));
     };
     // RG::PER copies per thread and stage, completing in order: stage c is in
     // once at most (stages issued after it) * PER copies are outstanding.
@@ -212,9 +231,9 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
         const int m = min(64 * wave + lane, t.nrows - 1);
         dma4(a.row_w + t.r0 + m, lw + (uint32_t)(256 * wave));
     }
-#pragma unroll
-    for (int p = 0; p < RG::AHEAD; ++p)
-        if (p < nch) issue(p);
+    static_for<RG::AHEAD>([&](auto P) {
+        if (decltype(P)::value < nch) issue(decltype(P)::value, P);
+    });
 
     floatx16 acc[MT][2];
 #pragma unroll
@@ -231,58 +250,66 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     bool nz = false;                             // any group with b != -8 s in my columns
     int next = 0;
 
-    for (int c = 0; c < nch; ++c) {
-        // stages issued after c: min(AHEAD - 1, nch - 1 - c)
-        const int after = min(RG::AHEAD - 1, nch - 1 - c);
-        if (after <= 0)
-            wait_vm<0>();
-        else if (after == 1)
-            wait_vm<RG::PER>();
-        else if (after == 2)
-            wait_vm<(RG::AHEAD > 2 ? 2 : 0) * RG::PER>();
-        else
-            wait_vm<(RG::AHEAD > 3 ? 3 : 0) * RG::PER>();
-        __syncthreads();                         // stage c visible; stage c-1 no longer read
-        if (c + RG::AHEAD < nch) issue(c + RG::AHEAD);   // into the slot of stage c-1
-        if (c == 1 && tid == 0) next = atomicAdd(&a.qctl[0], 1);   // overlaps the tile
+    // K loop unrolled by the ring depth, so that stage c's ring slot (c % NST)
+    // and with it every LDS address of the step is a compile-time constant
+    for (int c0 = 0; c0 < nch; c0 += RG::NST) {
+        static_for<RG::NST>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            const int c = c0 + u;
+            if (c >= nch) return;
+            // stages issued after c: min(AHEAD - 1, nch - 1 - c)
+            const int after = min(RG::AHEAD - 1, nch - 1 - c);
+            if (after <= 0)
+                wait_vm<0>();
+            else if (after == 1)
+                wait_vm<RG::PER>();
+            else if (after == 2)
+                wait_vm<(RG::AHEAD > 2 ? 2 : 0) * RG::PER>();
+            else
+                wait_vm<(RG::AHEAD > 3 ? 3 : 0) * RG::PER>();
+            __syncthreads();                     // stage c visible; stage c-1 no longer read
+            if (c + RG::AHEAD < nch)             // into the slot of stage c-1
+                issue(c + RG::AHEAD, std::integral_constant<int, (u + RG::AHEAD) % RG::NST>{});
+            if (c == 1 && tid == 0) next = atomicAdd(&a.qctl[0], 1);   // overlaps the tile
 
-        const uint8_t *sb = smem + (c % RG::NST) * RG::STAGE;
-        u32x4 wq[2];
-        f16x2 ss[2], ss16[2];
+            const uint8_t *sb = smem + u * RG::STAGE;
+            u32x4 wq[2];
+            f16x2 ss[2], ss16[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int bc = 64 * wave + 32 * nt + l32;
-            wq[nt] = *(const u32x4 *)(sb + RG::A_BYTES + bc * 32 + 16 * (gg ^ swb));
-            const uint8_t *pr = sb + RG::A_BYTES + B_BYTES + bc * 2;
-            const float sf = bf16_to_f32(*(const uint16_t *)pr);
-            nz |= bf16_to_f32(*(const uint16_t *)(pr + 512)) != -8.0f * sf;
-            const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
-            ss[nt] = f16x2{sh, sh};
-            ss16[nt] = f16x2{sh16, sh16};
-        }
-        const uint8_t *arow = sb + l32 * (KC * 2);
-        // steps (j, mt) in order; the A fragment of step s is read two steps
-        // ahead into a 3-slot ring, so LDS latency overlaps two MFMA pairs
-        constexpr int NSTEP = 4 * MT;
-        auto a_frag = [&](int s) {
-            const int j = s / MT, mt = s % MT;
-            return *(const f16x8 *)(arow + mt * 32 * (KC * 2) + 16 * ((4 * gg + j) ^ sw));
-        };
-        f16x8 af[3];
-        af[0] = a_frag(0);
-        if (NSTEP > 1) af[1] = a_frag(1);
-        f16x8 b0, b1;
-#pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-            const int j = s / MT, mt = s % MT;
-            if (mt == 0) {
-                b0 = rebuild8(wq[0][j], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
-                b1 = rebuild8(wq[1][j], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
+            for (int nt = 0; nt < 2; ++nt) {
+                const int bc = 64 * wave + 32 * nt + l32;
+                wq[nt] = *(const u32x4 *)(sb + RG::A_BYTES + bc * 32 + 16 * (gg ^ swb));
+                const uint8_t *pr = sb + RG::A_BYTES + B_BYTES + bc * 2;
+                const float sf = bf16_to_f32(*(const uint16_t *)pr);
+                nz |= bf16_to_f32(*(const uint16_t *)(pr + 512)) != -8.0f * sf;
+                const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
+                ss[nt] = f16x2{sh, sh};
+                ss16[nt] = f16x2{sh16, sh16};
             }
-            if (s + 2 < NSTEP) af[(s + 2) % 3] = a_frag(s + 2);
-            acc[mt][0] = mfma16(af[s % 3], b0, acc[mt][0]);
-            acc[mt][1] = mfma16(af[s % 3], b1, acc[mt][1]);
-        }
+            const uint8_t *arow = sb + l32 * (KC * 2);
+            // steps (j, mt) in order; the A fragment of step s is read two steps
+            // ahead into a 3-slot ring, so LDS latency overlaps two MFMA pairs
+            constexpr int NSTEP = 4 * MT;
+            auto a_frag = [&](int s) {
+                const int j = s / MT, mt = s % MT;
+                return *(const f16x8 *)(arow + mt * 32 * (KC * 2) + 16 * ((4 * gg + j) ^ sw));
+            };
+            f16x8 af[3];
+            af[0] = a_frag(0);
+            if (NSTEP > 1) af[1] = a_frag(1);
+            f16x8 b0, b1;
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s) {
+                const int j = s / MT, mt = s % MT;
+                if (mt == 0) {
+                    b0 = rebuild8(wq[0][j], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
+                    b1 = rebuild8(wq[1][j], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
+                }
+                if (s + 2 < NSTEP) af[(s + 2) % 3] = a_frag(s + 2);
+                acc[mt][0] = mfma16(af[s % 3], b0, acc[mt][0]);
+                acc[mt][1] = mfma16(af[s % 3], b1, acc[mt][1]);
+            }
+        });
     }
 
     if (tid == 0) *s_next = next;                // read after the caller's next barrier
