@@ -44,9 +44,9 @@ SEED_STACK = 5000
 # 131085.5 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
 # source these counters were taken on; otherwise the JSON reports null.
 GATEUP_TRAFFIC = {
-    "gemm_src_sha256": "250116bba8ddeb9ce4b8d205701ee57f02c99f67433ec50967abf949b60309f2",
-    "fetch_kib": 147704.8, "fetch_scale": 2.0,
-    "write_kib": 20801.7, "write_scale": 1.0,
+    "gemm_src_sha256": "0350e8ab35e6782fa2d4de12cea969238ec23b4fc72efb3d8a7f252f3bc67669",
+    "fetch_kib": 153978.9, "fetch_scale": 2.0,
+    "write_kib": 20752.4, "write_scale": 1.0,
     "profile": "profiles/q4_gemm_gateup_prefill2048_zipf_hbm_traffic.md",
 }
 
