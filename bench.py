@@ -10,7 +10,9 @@ layers) so that no step finds its weights in the 256 MB last-level cache.
 
 Also reported: the gate/up GEMM kernel's MFMA roofline fraction (HIP events
 around its launch inside the timed loop), the batch-1 decode path's HBM
-bandwidth, the T=512 layer with uniform-ish routing (every expert active: HBM
+bandwidth (40 independently weighted layers, one call each) and the per-layer
+latency of the same 40 layers chained through the residual add and RMSNorm (one
+HIP graph, no host synchronisation), the T=512 layer with uniform-ish routing (every expert active: HBM
 bandwidth over the weights read), a stack of 40 layers at T=4096 with the
 residual add and RMSNorm between layers (tokens/s, no host synchronisation in
 the pass), and the CPU oracle's throughput on a bounded token sample.
@@ -76,8 +78,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=6, help="weight sets rotated in the prefill loop")
-    ap.add_argument("--decode-sets", type=int, default=32)
-    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-sets", type=int, default=40,
+                    help="T=1 layers (independent weights): decode calls and the chained stack")
+    ap.add_argument("--decode-steps", type=int, default=400)
     ap.add_argument("--uniform-sets", type=int, default=4,
                     help="weight sets of the T=512 uniform-routing leg (0: skip it)")
     ap.add_argument("--stack-layers", type=int, default=40,
@@ -189,6 +192,10 @@ def main():
     layer_mfma_frac = (flops_gateup + flops_down) / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
     # ---------------- decode: T=1 ----------------
+    # One weight set per layer of a 40-layer decode stack.  (i) decode-path bandwidth: one
+    # moe_decode per layer on that layer's own token, independent calls in one HIP graph;
+    # (ii) the chained stack: every layer decodes the previous layer's output after the
+    # residual add and RMSNorm, 40 layers in one HIP graph with no host synchronisation.
     print(f"[bench] prefill {ms_step * 1e3:.1f} us/step; decode with {args.decode_sets} weight sets",
           file=sys.stderr, flush=True)
     del sets
@@ -206,26 +213,53 @@ def main():
         xd, wd = dsets[i % len(dsets)]
         moe.moe_decode(dshape, xd, wd, ids, tw, yd, dws)
     torch.cuda.synchronize()
-    # one HIP graph holding one decode per weight set, replayed
-    dgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(dgraph):
+
+    def graph_us_per_layer(fn, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / (reps * len(dsets)) * 1e3
+
+    def independent():
         for xd, wd in dsets:
             moe.moe_decode(dshape, xd, wd, ids, tw, yd, dws)
-    dgraph.replay()
-    torch.cuda.synchronize()
+
     dreps = max(1, args.decode_steps // len(dsets))
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record()
-    for _ in range(dreps):
-        dgraph.replay()
-    d1.record()
-    torch.cuda.synchronize()
-    dec_us = d0.elapsed_time(d1) / (dreps * len(dsets)) * 1e3
-    del dgraph
+    dec_us = graph_us_per_layer(independent, dreps)
     dec_bytes = 9 * expert_bytes(H, I) + E * H * 2 + H * 2 + H * 4 + K_TOP * 8
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
-    del dsets
+
+    dres = torch.empty(H, dtype=torch.float32, device=dev)
+    du = torch.empty(H, dtype=torch.int16, device=dev)
+    dx0 = dsets[0][0].view(H)
+
+    def chained():
+        # r_0 = x, u_0 = x; every layer: y = MoE(u); r += y; u = bf16(RMSNorm(r))
+        dres.copy_(dx0.view(torch.bfloat16))
+        du.copy_(dx0)
+        for _, wd in dsets:
+            moe.moe_decode(dshape, du, wd, ids, tw, yd, dws)
+            moe.moe_rmsnorm_residual(1, H, 1e-6, dres, yd, du)
+
+    dstack_us = graph_us_per_layer(chained, dreps)
+    dstack = {"workload": f"decode_stack{len(dsets)}: {len(dsets)} MoE layers at T=1 chained "
+                          f"through the residual add + RMSNorm, independent weights per layer",
+              "us_per_layer": round(dstack_us, 2),
+              "hbm_gbs": round(dec_bytes / (dstack_us * 1e-6) / 1e9, 1),
+              "hbm_frac": round(dec_bytes / (dstack_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+              "tokens_per_s": round(1.0 / (dstack_us * 1e-6 * len(dsets)), 1),
+              "host_syncs_per_pass": 0}
+    del dsets, dres, du
     torch.cuda.empty_cache()
 
     # ---------------- prefill T=512, uniform-ish routing: every expert is active ----------------
@@ -390,6 +424,7 @@ def main():
         "decode": {"metric": "T=1 decode HBM GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
                    "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(dec_us, 2),
                    "bytes_per_call": dec_bytes, "weight_sets": args.decode_sets},
+        "decode_stack": dstack,
         "prefill512_uniform": uni,
         "stack": stack,
         "cpu_baseline": cpu,
