@@ -259,6 +259,37 @@ def main():
               "hbm_frac": round(dec_bytes / (dstack_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
               "tokens_per_s": round(1.0 / (dstack_us * 1e-6 * len(dsets)), 1),
               "host_syncs_per_pass": 0}
+
+    # small decode batches (T = 2, 4, 8 tokens per call, e.g. a verify step): one call per
+    # layer, independent calls in one HIP graph.  Bandwidth is counted over the union of the
+    # experts the call's tokens picked (each read once), the shared expert, the router rows,
+    # x and y.
+    dbatch = {}
+    gx = torch.Generator(device=dev)
+    gx.manual_seed(SEED_DECODE + 999)
+    xb = torch.randn((8, H), generator=gx, device=dev).to(torch.bfloat16).view(torch.int16)
+    for Tb in (2, 4, 8):
+        bshape = moe.Shape(T=Tb, H=H, I=I, E=E, top_k=K_TOP)
+        bws = moe.workspace(bshape, dev)
+        bids = torch.empty((len(dsets), Tb, K_TOP), dtype=torch.int32, device=dev)
+        btw = torch.empty((Tb, K_TOP), dtype=torch.float32, device=dev)
+        by = torch.empty((Tb, H), dtype=torch.float32, device=dev)
+        xT = xb[:Tb].contiguous()
+
+        def batched():
+            for li, (_, wd) in enumerate(dsets):
+                moe.moe_decode(bshape, xT, wd, bids[li], btw, by, bws)
+
+        b_us = graph_us_per_layer(batched, dreps)
+        uniq = [len(set(bids[li].flatten().tolist())) for li in range(len(dsets))]
+        b_bytes = ((sum(uniq) / len(uniq) + 1) * expert_bytes(H, I) + E * H * 2 + Tb * H * 2
+                   + Tb * H * 4 + Tb * K_TOP * 8)
+        dbatch[f"T{Tb}"] = {"us_per_call": round(b_us, 2), "tokens_per_s": round(Tb / (b_us * 1e-6), 1),
+                            "distinct_experts_mean": round(sum(uniq) / len(uniq), 2),
+                            "bytes_per_call": round(b_bytes),
+                            "hbm_gbs": round(b_bytes / (b_us * 1e-6) / 1e9, 1),
+                            "hbm_frac": round(b_bytes / (b_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del bws, bids, btw, by
     del dsets, dres, du
     torch.cuda.empty_cache()
 
@@ -425,6 +456,7 @@ def main():
                    "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(dec_us, 2),
                    "bytes_per_call": dec_bytes, "weight_sets": args.decode_sets},
         "decode_stack": dstack,
+        "decode_batch": dbatch,
         "prefill512_uniform": uni,
         "stack": stack,
         "cpu_baseline": cpu,

@@ -100,6 +100,13 @@ def _ptr(t: Optional[torch.Tensor], dtypes=None, name="tensor") -> Optional[int]
     return t.data_ptr()
 
 
+def _need(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
+    """The kernels address n elements of t: refuse a smaller tensor before launching."""
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call addresses {n}")
+    return t
+
+
 _B16 = (torch.bfloat16, torch.int16, torch.uint16)
 _H16 = (torch.float16, torch.int16, torch.uint16)      # h: fp16 bits
 _U32 = (torch.int32, torch.uint32)
@@ -253,6 +260,13 @@ def moe_layer(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torc
 
 def moe_decode(shape: Shape, x: torch.Tensor, w: DeviceLayer, ids: torch.Tensor, tw: torch.Tensor,
                y: torch.Tensor, ws: torch.Tensor, stream=None):
+    """Decode of shape.T <= 8 tokens: x [T][H] bf16, ids [T][top_k] int32, tw [T][top_k] fp32,
+    y [T][H] fp32."""
+    T, H, k = shape.T, shape.H, shape.top_k
+    _need(x, T * H, "x")
+    _need(ids, T * k, "ids")
+    _need(tw, T * k, "topk_w")
+    _need(y, T * H, "y")
     _check(lib().moe_decode(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
                             _ptr(ids, _I32, "ids"), _ptr(tw, _F32, "topk_w"), _ptr(y, _F32, "y"),
                             _ptr(ws, None, "ws"), ws.numel(), _stream(stream)), "moe_decode")

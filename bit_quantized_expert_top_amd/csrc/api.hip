@@ -14,7 +14,7 @@ int max_blocks_for(int T, int E, int k) {
     return (rows + kBM - 1) / kBM + (rows < E ? rows : E);
 }
 
-size_t decode_scratch_bytes(int H, int I, int k);
+size_t decode_scratch_bytes(int T, int H, int I, int k);
 
 WsLayout ws_layout(int T, int H, int I, int E, int k) {
     WsLayout L{};
@@ -37,7 +37,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.lrank = take((size_t)T * k * 4);
     L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
     L.qctl = take((size_t)QCTL_WORDS * 4);
-    L.dec = take(T == 1 ? decode_scratch_bytes(H, I, k) : 0);
+    L.dec = take(T <= kDecodeMaxT ? decode_scratch_bytes(T, H, I, k) : 0);
     L.total = off;
     return L;
 }
@@ -235,12 +235,12 @@ moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weigh
                       int32_t *topk_ids, float *topk_w, float *y, void *ws, size_t ws_bytes,
                       void *stream) {
     MOE_TRY(check_shape(shape));
-    if (shape->T != 1) return MOE_ERR_INVALID_ARG;
+    if (shape->T > kDecodeMaxT) return MOE_ERR_INVALID_ARG;
     if (!aligned(x) || !aligned(topk_ids) || !aligned(topk_w) || !aligned(y))
         return MOE_ERR_INVALID_ARG;
     MOE_TRY(check_weights(w, true, true, true));
     MOE_TRY(check_ws(shape, ws, ws_bytes));
-    const WsLayout L = ws_layout(1, shape->H, shape->I, shape->E, shape->top_k);
+    const WsLayout L = ws_layout(shape->T, shape->H, shape->I, shape->E, shape->top_k);
     launch_decode(*shape, x, *w, topk_ids, topk_w, y, (char *)ws + L.dec, (hipStream_t)stream);
     return launched();
 }

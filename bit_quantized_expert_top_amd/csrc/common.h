@@ -21,6 +21,7 @@ constexpr int kWave = 64;
 constexpr int kGroup = 64;      // quantisation group along K
 constexpr int kBM = 128;        // rows per routing block (GEMM M tile)
 constexpr int kTB = 8;          // tokens per routing token block (one wave each)
+constexpr int kDecodeMaxT = 8;  // moe_decode: tokens per call (each an independent GEMV problem)
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }

@@ -1,4 +1,5 @@
-// Batch-1 decode: one token through the router, top-8 and the nine selected
+// Decode: each token (up to 8 per call, independent problems in the same
+// launches, token = blockIdx.y) through the router, top-8 and the nine selected
 // experts (eight routed + the shared one).  At batch 1 there is no weight
 // reuse, so the path is bound by how fast the selected experts' packed
 // weights stream from HBM (mechatronicstore.cl, "Decode: mover menos bytes
@@ -10,19 +11,23 @@
 //  1. router: one wave per expert computes its logit exactly in the fixed
 //     order (sequential within each 64-chunk, then over chunks, then + bias),
 //     so the ids need no certification step at batch 1;
-//  2. gate/up: a workgroup takes one slot and 32 gate + the 32 matching up
-//     columns (2 KB of each block, contiguous) over all of K.  Every wave
-//     takes the top-8 itself (logit descending, index ascending; softmax
-//     weights restricted to them) and then issues all of its loads at once.
+//  2. gate/up: a workgroup takes one slot and 8 gate + the 8 matching up
+//     columns over all of K.  At one token every wave takes the top-8 itself
+//     (logit descending, index ascending; softmax weights restricted to them),
+//     which keeps a launch off the latency chain; with more tokens a small
+//     kernel takes each token's top-8 once and the workgroups read the ids.
+//     Then every wave issues all of its loads at once.
 //     Codes become 128+q in bf16 with one and-or per pair and meet x in packed
 //     bf16 dot products:
 //        sum_k x_k (q_k s + b) = s (sum x (128 + q) - 128 sum x) + b sum x;
 //     the two halves of a column meet by DPP, the waves' groups through LDS
 //     in order, and h = silu(gate) * up is written in fp16;
-//  3. down: a workgroup takes 32 outputs (1 KB of each block) for all nine
-//     slots and all groups, with h of every slot staged in LDS; codes become
-//     1024+q in fp16.  Each lane adds its slots in pick order with their
-//     routing weights, then the shared expert, group by group.
+//  3. down: a workgroup takes 8 outputs (a 256-byte run of every block of
+//     their tile) for all nine slots and all groups; each lane loads the codes
+//     and the h values of its (slot, group) pairs directly, and codes become
+//     1024+q in fp16.  The partial sums meet in LDS and are added per output
+//     in a fixed order: groups, then slots in pick order with their routing
+//     weights, then the shared expert.
 #include "common.h"
 
 namespace moe {
@@ -43,6 +48,9 @@ __global__ __launch_bounds__(64) void decode_router_kernel(const uint16_t *__res
                                                            float *__restrict__ logits) {
     const int lane = threadIdx.x;
     const int e = blockIdx.x;
+    const int E = gridDim.x;
+    x += (size_t)blockIdx.y * H;   // token blockIdx.y
+    logits += (size_t)blockIdx.y * E;
     const int G = H / 64;          // <= 32 chunks: lane c < G sums chunk c
     float P = 0.0f;
     if (lane < G) {
@@ -104,6 +112,33 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
     for (int r = 0; r < 8; ++r) pick_w[r] = pick_w[r] / sum;
 }
 
+// scratch: the logits of every token, 256-byte aligned
+static size_t logits_bytes(int T, int E) { return ((size_t)T * E * 4 + 255) & ~(size_t)255; }
+
+// 1b. (decode of two or more tokens) the top-k and weights of token blockIdx.x,
+// once per token, for the gate/up and down workgroups to read.
+__global__ __launch_bounds__(64) void decode_select_kernel(const float *__restrict__ logits, int E,
+                                                           int k, int32_t *__restrict__ ids,
+                                                           float *__restrict__ tw) {
+    __shared__ uint32_t wl[32];
+    const int t = blockIdx.x, lane = threadIdx.x;
+    int pe[8];
+    float pw[8];
+    select_topk(logits + (size_t)t * E, E, k, pe, pw, wl);
+    int e = 0;
+    float wv = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        if (r == lane) {
+            e = pe[r];
+            wv = pw[r];
+        }
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = e;
+        tw[(size_t)t * k + lane] = wv;
+    }
+}
+
 constexpr int DW = 8;                  // waves per decode workgroup
 constexpr int NSLOT = 9;               // top-8 routed experts + the shared one (top_k is 8)
 constexpr int DOUT = 8;                // outputs per decode workgroup (gate/up and down)
@@ -134,12 +169,20 @@ __device__ __forceinline__ float pair_sum(float v) {
 __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
     const uint8_t *__restrict__ pk, const uint8_t *__restrict__ pk_sh, int32_t *__restrict__ ids_out,
-    float *__restrict__ tw_out, uint16_t *__restrict__ hbuf) {
+    float *__restrict__ tw_out, uint16_t *__restrict__ hbuf, bool picks_given) {
     __shared__ float red[DW][4][DOUT][2];
     __shared__ uint32_t selw[DW][32];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = H / 64, JT = I / 128, OPS = I / DOUT;
     const int slot = blockIdx.x / OPS, o = blockIdx.x % OPS;
+    {   // token blockIdx.y: its input row, logits, picks and h block
+        const size_t t = blockIdx.y;
+        x += t * H;
+        logits += t * E;
+        ids_out += t * k;
+        tw_out += t * k;
+        hbuf += t * NSLOT * I;
+    }
     const int j = o >> 4, u = (o >> 2) & 3, v = o & 3;            // 8 o = 128 j + 32 u + 8 v
     const int gi = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
     const int lh = ph ^ (v & 1);                                  // logical half of my pieces
@@ -157,7 +200,10 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
         for (int qq = 0; qq < 4; ++qq) xv[it][qq] = px[qq];       // clamped: loads stay unconditional
     }
     int ex = 0;
-    if (slot < k) {
+    if (slot < k && picks_given) {
+        ex = ids_out[slot];                                       // written by decode_select_kernel
+        ex = (ex < 0 || ex >= E) ? 0 : ex;
+    } else if (slot < k) {
         int pe[8];
         float pw[8];
         select_topk(logits, E, k, pe, pw, selw[wave]);
@@ -260,6 +306,13 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     __shared__ float part[DN_MAXP][DOUT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
     const int G = I / 64, JD = H / 256, NPAIR = (k + 1) * G;
+    {   // token blockIdx.y: its h block, picks and output row
+        const size_t t = blockIdx.y;
+        hbuf += t * NSLOT * I;
+        ids += t * k;
+        tw += t * k;
+        y += t * H;
+    }
     const int j = blockIdx.x >> 5, v = blockIdx.x & 31;          // outputs 256 j + 8 v + (0..7)
     const int sub = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
     const int tc = 8 * v + cc;
@@ -340,25 +393,31 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
 
 void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w, int32_t *ids,
                    float *tw, float *y, void *scratch, hipStream_t s) {
-    const int H = sh.H, I = sh.I, E = sh.E, k = sh.top_k;
+    const int T = sh.T, H = sh.H, I = sh.I, E = sh.E, k = sh.top_k;
     char *p = (char *)scratch;
-    float *logits = (float *)p;                 // [E]
-    uint16_t *hbuf = (uint16_t *)(p + 4096);    // fp16 [k+1][I]
-    // the API admits top_k = 8, E <= 256, H <= 2048 (G <= 32), I <= 2048
-    if (k + 1 != NSLOT || E > 256 || H > 2048 || I > 2048) return;
+    float *logits = (float *)p;                                   // [T][E]
+    uint16_t *hbuf = (uint16_t *)(p + logits_bytes(T, E));        // fp16 [T][k+1][I]
+    // the API admits top_k = 8, E <= 256, H <= 2048 (G <= 32), I <= 2048, T <= kDecodeMaxT
+    if (k + 1 != NSLOT || E > 256 || H > 2048 || I > 2048 || T < 1 || T > kDecodeMaxT) return;
     const PackLayout P = pack_layout(H, I, E);
     const uint8_t *pk = (const uint8_t *)w.packed;
-    hipLaunchKernelGGL(decode_router_kernel, dim3(E), dim3(64), 0, s, x, w.router_wt, w.router_bias, H,
-                       logits);
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT)), dim3(64 * DW), 0, s, x, logits,
-                       H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf);
-    hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT), dim3(64 * DW), 0, s, hbuf, H, I, ids, tw, k,
-                       E, pk + P.down, pk + P.sh_down, y);
+    // every kernel takes token t = blockIdx.y; the tokens are independent problems
+    hipLaunchKernelGGL(decode_router_kernel, dim3(E, T), dim3(64), 0, s, x, w.router_wt, w.router_bias,
+                       H, logits);
+    // one token: every gate/up wave takes the top-k itself (no extra launch on the
+    // latency chain); more tokens: the picks are taken once per token
+    const bool picks_given = T > 1;
+    if (picks_given)
+        hipLaunchKernelGGL(decode_select_kernel, dim3(T), dim3(64), 0, s, logits, E, k, ids, tw);
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT), T), dim3(64 * DW), 0, s, x,
+                       logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf, picks_given);
+    hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT, T), dim3(64 * DW), 0, s, hbuf, H, I, ids, tw,
+                       k, E, pk + P.down, pk + P.sh_down, y);
 }
 
-size_t decode_scratch_bytes(int H, int I, int k) {
+size_t decode_scratch_bytes(int T, int H, int I, int k) {
     (void)H;
-    return 4096 + (size_t)(k + 1) * I * 2;
+    return logits_bytes(T, 256) + (size_t)T * (k + 1) * I * 2;
 }
 
 }  // namespace moe

@@ -180,15 +180,19 @@ moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weight
                      const moe_routing *r, uint16_t *h, float *y, void *ws, size_t ws_bytes,
                      void *stream);
 
-/* Batch-1 decode (T must be 1): router, top-8 and weights, then the eight
- * routed experts and the shared expert as weight-streaming GEMVs that read
- * only the selected experts' packed weights (mechatronicstore.cl "Decode:
- * mover menos bytes por token"; neuro-ai.ru "Спекулятивное ...": batch-1
- * decode is bound by weight bandwidth).  topk_ids [top_k], topk_w [top_k],
- * y fp32 [H] (overwritten).  Reads the expert weights from w->packed and
- * the router from w->router_wt.  The ids equal those of the fixed-order logits;
- * h is kept in fp16 between the two GEMVs.  MOE_ERR_UNSUPPORTED unless H and
- * I are powers of two. */
+/* Decode of 1 <= T <= 8 tokens (MOE_ERR_INVALID_ARG above 8): per token the
+ * router, top-8 and weights, then the eight routed experts and the shared
+ * expert as weight-streaming GEMVs that read only the selected experts' packed
+ * weights (mechatronicstore.cl "Decode: mover menos bytes por token";
+ * neuro-ai.ru "Спекулятивное декодирование не взлетело": decode at batch 1 and
+ * small verify batches is bound by weight bandwidth).  The tokens are
+ * independent problems in the same launches; an expert picked by several
+ * tokens is streamed once per token (the repeats come from the caches).
+ * x: bf16 [T][H]; topk_ids int32 [T][top_k], topk_w fp32 [T][top_k] (picks in
+ * rank order), y fp32 [T][H] (overwritten).  Reads the expert weights from
+ * w->packed and the router from w->router_wt (+ router_bias).  The ids equal
+ * those of the fixed-order logits; h is kept in fp16 between the two GEMVs.
+ * The workspace comes from moe_query for the same shape. */
 moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                       int32_t *topk_ids, float *topk_w, float *y, void *ws, size_t ws_bytes,
                       void *stream);

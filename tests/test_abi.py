@@ -128,12 +128,19 @@ def test_gemm_and_down_validation_before_launch():
     assert L.moe_layer(C.byref(s), FAKE, None, C.byref(r), FAKE, FAKE, FAKE, need, None) == INVALID
 
 
-def test_decode_needs_t1():
+def test_decode_token_limit():
     L = B.lib()
-    s = shape(T=2)
+    # at most 8 tokens per decode call
+    s = shape(T=9)
     _, need, _, _ = query(s)
     assert L.moe_decode(C.byref(s), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE, need,
                         None) == INVALID
+    # 2..8 tokens: validation reaches the workspace check, sized per token count
+    for T in (2, 8):
+        sT = shape(T=T)
+        _, needT, _, _ = query(sT)
+        assert L.moe_decode(C.byref(sT), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE,
+                            needT - 1, None) == WS
     s1 = shape(T=1)
     _, need1, _, _ = query(s1)
     assert L.moe_decode(C.byref(s1), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE, FAKE, need1 - 1,

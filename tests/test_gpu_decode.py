@@ -12,16 +12,19 @@ pytestmark = pytest.mark.gpu
 
 
 def run_decode(inp, w=None):
+    """moe_decode of all inp.T tokens; at T=1 the arrays are [top_k] and [H]."""
     dev = device()
     w = w or upload(inp, dev)
     sh = shape_of(inp)
-    ids = torch.empty(inp.top_k, dtype=torch.int32, device=dev)
-    tw = torch.empty(inp.top_k, dtype=torch.float32, device=dev)
-    y = torch.empty(inp.H, dtype=torch.float32, device=dev)
+    T = inp.T
+    ids = torch.empty((T, inp.top_k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, inp.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, inp.H), dtype=torch.float32, device=dev)
     ws = moe.workspace(sh, dev)
     moe.moe_decode(sh, x_dev(inp, dev), w, ids, tw, y, ws)
     torch.cuda.synchronize()
-    return ids.cpu().numpy(), tw.cpu().numpy(), y.cpu().numpy()
+    out = ids.cpu().numpy(), tw.cpu().numpy(), y.cpu().numpy()
+    return tuple(a[0] for a in out) if T == 1 else out
 
 
 @pytest.mark.parametrize("seed", [2000, 2001, 2002, 2003])
@@ -111,3 +114,33 @@ def test_decode_stack_teacher_forced_and_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(r, r_eager) and torch.equal(u, u_eager), rep
+
+
+@pytest.mark.parametrize("T,seed,zipf", [(2, 2200, None), (3, 2201, None), (5, 2202, None),
+                                         (8, 2203, None), (8, 4020, 1.1)])
+def test_small_batch_decode_matches_oracle(T, seed, zipf):
+    """Decode of T = 2..8 tokens in one call: every token's picks bit-exact, its weights and
+    output within the layer tolerance.  With the Zipf router bias the tokens share experts."""
+    print(f"[decode-batch] T={T} seed={seed} zipf={zipf}", flush=True)
+    inp = make_layer(seed, T=T, H=2048, I=512, zipf_s=zipf)
+    ids, tw, y = run_decode(inp)
+    y_ref, ids_ref, w_ref = oracle.Layer(inp).tokens(range(T))
+    np.testing.assert_array_equal(ids, ids_ref)
+    np.testing.assert_allclose(tw, w_ref, rtol=2e-5, atol=2e-7)
+    ratio = check_y(y, y_ref)
+    print(f"  max err / rms = {ratio:.4g}, distinct experts = {len(set(ids.ravel().tolist()))}",
+          flush=True)
+
+
+def test_small_batch_equals_single_tokens():
+    """Each token of a batched decode gets exactly what a batch-1 call on it alone returns."""
+    inp = make_layer(2210, T=8, H=768, I=384)
+    w = upload(inp)
+    ids, tw, y = run_decode(inp, w)
+    for t in range(inp.T):
+        one = make_layer(2210, T=1, H=768, I=384, with_x=False)
+        one.x = inp.x[t:t + 1].copy()
+        i1, w1, y1 = run_decode(one, w)
+        np.testing.assert_array_equal(i1, ids[t])
+        np.testing.assert_array_equal(w1, tw[t])
+        np.testing.assert_array_equal(y1, y[t])
