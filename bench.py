@@ -12,7 +12,9 @@ Also reported: the gate/up GEMM kernel's MFMA roofline fraction (HIP events
 around its launch inside the timed loop), the batch-1 decode path's HBM
 bandwidth (40 independently weighted layers, one call each) and the per-layer
 latency of the same 40 layers chained through the residual add and RMSNorm (one
-HIP graph, no host synchronisation), the T=512 layer with uniform-ish routing (every expert active: HBM
+HIP graph, no host synchronisation), decode calls of 2, 4 and 8 tokens, a
+16384-token prompt through one layer in chunks of 2048 tokens (workspace bounded
+by the chunk) next to the single call, the T=512 layer with uniform-ish routing (every expert active: HBM
 bandwidth over the weights read), a stack of 40 layers at T=4096 with the
 residual add and RMSNorm between layers (tokens/s, no host synchronisation in
 the pass), and the CPU oracle's throughput on a bounded token sample.
@@ -85,6 +87,8 @@ def main():
                     help="weight sets of the T=512 uniform-routing leg (0: skip it)")
     ap.add_argument("--stack-layers", type=int, default=40,
                     help="layers of the T=4096 stack leg (0: skip it)")
+    ap.add_argument("--chunked-tokens", type=int, default=16384,
+                    help="prompt length of the chunked-prefill leg (0 skips it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -348,6 +352,49 @@ def main():
         del ug, usets, ur, uws, uh, uy, xu
         torch.cuda.empty_cache()
 
+    # ---------------- long prompt: chunked prefill vs one call ----------------
+    chunked = None
+    if args.chunked_tokens:
+        Tl, Cl = args.chunked_tokens, 2048
+        print(f"[bench] T={Tl} prompt in chunks of {Cl}", file=sys.stderr, flush=True)
+        lshape = moe.Shape(T=Tl, H=H, I=I, E=E, top_k=K_TOP)
+        raw = make_layer_device(SEED_UNIFORM + 7, Tl, H, I, E, zipf_s=None, device=dev)
+        xl = raw["x"]
+        wl = device_layer(raw)
+        del raw
+        yl = torch.empty((Tl, H), dtype=torch.float32, device=dev)
+        cws = moe.workspace_chunked(lshape, Cl, dev)
+
+        def timed(fn, reps=4):
+            fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        c_ms = timed(lambda: moe.moe_layer_chunked(lshape, xl, wl, yl, Cl, cws))
+        lr = moe.Routing(lshape, dev, with_logits=False)
+        lws = moe.workspace(lshape, dev)
+        lh = torch.empty((Tl * K_TOP + Tl, I), dtype=torch.int16, device=dev)
+        f_ms = timed(lambda: moe.moe_layer(lshape, xl, wl, lr, lh, yl, lws))
+        whole_bytes = lws.numel() + sum(t.numel() * t.element_size() for t in
+                                        (lh, lr.topk_ids, lr.topk_w, lr.counts, lr.offsets,
+                                         lr.row_token, lr.tok_row, lr.row_w, lr.blocks))
+        chunked = {"workload": f"prefill{Tl}: one MoE layer over a {Tl}-token prompt, random "
+                               f"router, in chunks of {Cl} tokens",
+                   "chunk": Cl, "ms": round(c_ms, 3), "tokens_per_s": round(Tl / (c_ms * 1e-3), 1),
+                   "workspace_bytes": cws.numel(),
+                   "single_call_ms": round(f_ms, 3),
+                   "single_call_tokens_per_s": round(Tl / (f_ms * 1e-3), 1),
+                   "single_call_scratch_bytes": whole_bytes}
+        del wl, xl, yl, cws, lr, lws, lh
+        torch.cuda.empty_cache()
+
     # ---------------- 40-layer stack at T=4096: residual + RMSNorm between layers ----------------
     stack = None
     if args.stack_layers:
@@ -459,6 +506,7 @@ def main():
         "decode_batch": dbatch,
         "prefill512_uniform": uni,
         "stack": stack,
+        "prefill_chunked": chunked,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

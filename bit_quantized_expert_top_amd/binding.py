@@ -50,6 +50,9 @@ _SIGS = {
                           C.c_size_t, P], i32),
     "moe_layer": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P, P,
                    C.c_size_t, P], i32),
+    "moe_query_chunked": ([C.POINTER(_Shape), i32, C.POINTER(C.c_size_t)], i32),
+    "moe_layer_chunked": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, i32, P, C.c_size_t, P],
+                          i32),
     "moe_decode": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, P, P, P, C.c_size_t, P], i32),
     "moe_rmsnorm_residual": ([i32, i32, C.c_float, P, P, P, P], i32),
     "moe_dequant_q4": ([C.POINTER(_Q4), i32, i32, P, P], i32),
@@ -256,6 +259,27 @@ def moe_layer(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torc
     _check(lib().moe_layer(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()), C.byref(r.c()),
                            _ptr(h, _H16, "h"), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
                            ws.numel(), _stream(stream)), "moe_layer")
+
+
+def moe_query_chunked(shape: Shape, chunk: int) -> int:
+    """Workspace bytes of moe_layer_chunked for `shape` in chunks of `chunk` tokens."""
+    n = C.c_size_t(0)
+    _check(lib().moe_query_chunked(C.byref(shape.c()), int(chunk), C.byref(n)), "moe_query_chunked")
+    return n.value
+
+
+def workspace_chunked(shape: Shape, chunk: int, device) -> torch.Tensor:
+    return torch.empty(moe_query_chunked(shape, chunk), dtype=torch.uint8, device=device)
+
+
+def moe_layer_chunked(shape: Shape, x: torch.Tensor, w: DeviceLayer, y: torch.Tensor, chunk: int,
+                      ws: torch.Tensor, stream=None):
+    """The layer over chunks of `chunk` tokens: x bf16 [T][H] -> y fp32 [T][H]."""
+    _need(x, shape.T * shape.H, "x")
+    _need(y, shape.T * shape.H, "y")
+    _check(lib().moe_layer_chunked(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
+                                   _ptr(y, _F32, "y"), int(chunk), _ptr(ws, None, "ws"), ws.numel(),
+                                   _stream(stream)), "moe_layer_chunked")
 
 
 def moe_decode(shape: Shape, x: torch.Tensor, w: DeviceLayer, ids: torch.Tensor, tw: torch.Tensor,

@@ -3,6 +3,8 @@
 // means nothing was enqueued.
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -38,6 +40,36 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
     L.qctl = take((size_t)QCTL_WORDS * 4);
     L.dec = take(T <= kDecodeMaxT ? decode_scratch_bytes(T, H, I, k) : 0);
+    L.total = off;
+    return L;
+}
+
+// Workspace of moe_layer_chunked for chunks of C tokens: the layer workspace of the
+// largest chunk, then the chunk's routing arrays and h.
+struct ChunkLayout {
+    size_t ids, tw, counts, offsets, row_token, tok_row, row_w, blocks, num_blocks, h, total;
+};
+
+static ChunkLayout chunk_layout(int T, int C, int H, int I, int E, int k) {
+    ChunkLayout L{};
+    const int last = T % C;
+    size_t off = ws_layout(C, H, I, E, k).total;
+    if (last) off = std::max(off, ws_layout(last, H, I, E, k).total);
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    L.ids = take((size_t)C * k * 4);
+    L.tw = take((size_t)C * k * 4);
+    L.counts = take((size_t)E * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.row_token = take((size_t)C * k * 4);
+    L.tok_row = take((size_t)C * k * 4);
+    L.row_w = take((size_t)C * k * 4);
+    L.blocks = take((size_t)max_blocks_for(C, E, k) * 3 * 4);
+    L.num_blocks = take(4);
+    L.h = take((size_t)(C * k + C) * I * 2);
     L.total = off;
     return L;
 }
@@ -89,6 +121,17 @@ moe_status check_ws(const moe_shape *s, void *ws, size_t ws_bytes) {
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
     if (!ws || (((uintptr_t)ws) & 255u) != 0 || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     return MOE_OK;
+}
+
+// moe_layer_chunked: any number of tokens up to kChunkedMaxT, chunks that a single layer
+// call admits
+constexpr long kChunkedMaxT = 1L << 24;
+moe_status check_chunked(const moe_shape *s, int32_t chunk) {
+    if (!s || chunk < 1 || s->T < 1) return MOE_ERR_INVALID_ARG;
+    if (s->T > kChunkedMaxT) return MOE_ERR_UNSUPPORTED;
+    moe_shape sc = *s;
+    sc.T = std::min<int32_t>(chunk, s->T);
+    return check_shape(&sc);
 }
 
 moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -229,6 +272,49 @@ moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weight
     MOE_TRY(enqueue_route(shape, x, w, r, (char *)ws, st));
     MOE_TRY(enqueue_gateup(shape, x, w, r, h, (char *)ws, st));
     return enqueue_down(shape, h, w, r, y, (char *)ws, st);
+}
+
+moe_status moe_query_chunked(const moe_shape *shape, int32_t chunk, size_t *workspace_bytes) {
+    MOE_TRY(check_chunked(shape, chunk));
+    const int C = std::min<int>(chunk, shape->T);
+    if (workspace_bytes)
+        *workspace_bytes = chunk_layout(shape->T, C, shape->H, shape->I, shape->E, shape->top_k).total;
+    return MOE_OK;
+}
+
+moe_status moe_layer_chunked(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                             float *y, int32_t chunk, void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_chunked(shape, chunk));
+    if (!aligned(x) || !aligned(y)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, true, true, true));
+    const int T = shape->T, H = shape->H, C = std::min<int>(chunk, T);
+    const ChunkLayout CL = chunk_layout(T, C, H, shape->I, shape->E, shape->top_k);
+    if (!ws || (((uintptr_t)ws) & 255u) != 0 || ws_bytes < CL.total) return MOE_ERR_WORKSPACE;
+    char *base = (char *)ws;
+    moe_routing r{};
+    r.logits = nullptr;
+    r.topk_ids = (int32_t *)(base + CL.ids);
+    r.topk_w = (float *)(base + CL.tw);
+    r.counts = (int32_t *)(base + CL.counts);
+    r.offsets = (int32_t *)(base + CL.offsets);
+    r.row_token = (int32_t *)(base + CL.row_token);
+    r.tok_row = (int32_t *)(base + CL.tok_row);
+    r.row_w = (float *)(base + CL.row_w);
+    r.blocks = (int32_t *)(base + CL.blocks);
+    r.num_blocks = (int32_t *)(base + CL.num_blocks);
+    uint16_t *h = (uint16_t *)(base + CL.h);
+    hipStream_t st = (hipStream_t)stream;
+    // each chunk is a whole layer call on its tokens; nothing leaves the device between them
+    for (long c0 = 0; c0 < T; c0 += C) {
+        moe_shape sc = *shape;
+        sc.T = (int32_t)std::min<long>(C, T - c0);
+        const uint16_t *xc = x + (size_t)c0 * H;
+        float *yc = y + (size_t)c0 * H;
+        MOE_TRY(enqueue_route(&sc, xc, w, &r, base, st));
+        MOE_TRY(enqueue_gateup(&sc, xc, w, &r, h, base, st));
+        MOE_TRY(enqueue_down(&sc, h, w, &r, yc, base, st));
+    }
+    return MOE_OK;
 }
 
 moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weights *w,

@@ -180,6 +180,25 @@ moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weight
                      const moe_routing *r, uint16_t *h, float *y, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* Chunked prefill for long prompts (greatopti.com, "Les gains viennent surtout
+ * des mouvements de données": long prompts are processed in fragments so that
+ * the temporary activations stay bounded).  The layer runs on consecutive
+ * chunks of at most `chunk` tokens, each a complete moe_layer over its tokens
+ * (every token's routing and output depend on that token alone, so the result
+ * equals the unchunked layer's).  The routing arrays and h of one chunk live in
+ * the workspace, which is sized by moe_query_chunked for (shape, chunk) and so
+ * bounded by the chunk, not by T.  All chunks are enqueued on `stream` with no
+ * host synchronisation between them.
+ * x: bf16 [T][H]; y: fp32 [T][H] (overwritten).  1 <= T <= 2^24
+ * (MOE_ERR_UNSUPPORTED above); chunk >= 1 (MOE_ERR_INVALID_ARG otherwise) and
+ * min(chunk, T) must be a token count that moe_query admits.  Weights as for
+ * moe_layer (router + tile-layout buffer).  MOE_ERR_WORKSPACE if ws is not
+ * 256-byte aligned or smaller than moe_query_chunked's size.  Validation
+ * happens before anything is enqueued. */
+moe_status moe_query_chunked(const moe_shape *shape, int32_t chunk, size_t *workspace_bytes);
+moe_status moe_layer_chunked(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                             float *y, int32_t chunk, void *ws, size_t ws_bytes, void *stream);
+
 /* Decode of 1 <= T <= 8 tokens (MOE_ERR_INVALID_ARG above 8): per token the
  * router, top-8 and weights, then the eight routed experts and the shared
  * expert as weight-streaming GEMVs that read only the selected experts' packed

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("moe_query", "moe_route", "moe_expert_gemm_q4", "moe_down_combine", "moe_layer",
-              "moe_decode", "moe_rmsnorm_residual", "moe_dequant_q4", "moe_status_str"):
+              "moe_query_chunked", "moe_layer_chunked", "moe_decode", "moe_rmsnorm_residual",
+              "moe_dequant_q4", "moe_status_str"):
         assert n in names
 
 
@@ -200,3 +201,41 @@ def test_packed_bytes_and_pack_validation():
     assert L.moe_pack_weights(C.byref(shape(T=1, bits=8)), C.byref(w), FAKE, n.value,
                               None) == UNSUP
     assert L.moe_packed_bytes(C.byref(s), None) == INVALID
+
+
+def query_chunked(s, chunk):
+    ws = C.c_size_t()
+    st = B.lib().moe_query_chunked(C.byref(s), chunk, C.byref(ws))
+    return st, ws.value
+
+
+def test_chunked_query_is_bounded_by_the_chunk():
+    # the workspace follows the chunk, not the token count
+    st1, a = query_chunked(shape(T=1 << 20), 2048)
+    st2, b = query_chunked(shape(T=8192), 2048)
+    assert st1 == OK and st2 == OK and a == b
+    # one chunk holding every token needs at least the single-call workspace
+    st3, c = query_chunked(shape(T=2048), 4096)
+    assert st3 == OK and c > query(shape(T=2048))[1]
+    # a ragged last chunk of at most 8 tokens is covered as well
+    st4, d = query_chunked(shape(T=2048 + 5), 2048)
+    assert st4 == OK and d >= b
+
+
+@pytest.mark.parametrize("T,chunk,code", [(4096, 0, INVALID), (4096, -1, INVALID), (0, 64, INVALID),
+                                          ((1 << 24) + 1, 4096, UNSUP), (1 << 20, 70000, UNSUP)])
+def test_chunked_rejects(T, chunk, code):
+    assert query_chunked(shape(T=T), chunk)[0] == code
+
+
+def test_chunked_validation_before_launch():
+    L = B.lib()
+    s = shape(T=5000)
+    _, need = query_chunked(s, 2048)
+    w = _weights()
+    assert L.moe_layer_chunked(C.byref(s), FAKE, C.byref(w), FAKE, 2048, FAKE, need - 1, None) == WS
+    assert L.moe_layer_chunked(C.byref(s), FAKE + 2, C.byref(w), FAKE, 2048, FAKE, need,
+                               None) == INVALID
+    assert L.moe_layer_chunked(C.byref(s), FAKE, C.byref(_weights("null_packed")), FAKE, 2048, FAKE,
+                               need, None) == INVALID
+    assert L.moe_layer_chunked(C.byref(s), FAKE, C.byref(w), FAKE, 0, FAKE, need, None) == INVALID
