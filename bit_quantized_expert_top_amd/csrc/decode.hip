@@ -16,7 +16,8 @@
 //     (logit descending, index ascending; softmax weights restricted to them),
 //     which keeps a launch off the latency chain; with more tokens a small
 //     kernel takes each token's top-8 once and the workgroups read the ids.
-//     Then every wave issues all of its loads at once.
+//     Then every wave issues all of its weight loads at once; the token's x is
+//     loaded once per workgroup and read by the column lanes from LDS.
 //     Codes become 128+q in bf16 with one and-or per pair and meet x in packed
 //     bf16 dot products:
 //        sum_k x_k (q_k s + b) = s (sum x (128 + q) - 128 sum x) + b sum x;
@@ -24,8 +25,8 @@
 //     in order, and h = silu(gate) * up is written in fp16;
 //  3. down: a workgroup takes 8 outputs (a 256-byte run of every block of
 //     their tile) for all nine slots and all groups; each lane loads the codes
-//     and the h values of its (slot, group) pairs directly, and codes become
-//     1024+q in fp16.  The partial sums meet in LDS and are added per output
+//     of its (slot, group) pairs, the token's h block is loaded once per
+//     workgroup and read from LDS, and codes become 1024+q in fp16.  The partial sums meet in LDS and are added per output
 //     in a fixed order: groups, then slots in pick order with their routing
 //     weights, then the shared expert.
 #include "common.h"
@@ -172,6 +173,7 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     float *__restrict__ tw_out, uint16_t *__restrict__ hbuf, bool picks_given) {
     __shared__ float red[DW][4][DOUT][2];
     __shared__ uint32_t selw[DW][32];
+    __shared__ u32x4 xs[256];                                     // the token's x, H <= 2048
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = H / 64, JT = I / 128, OPS = I / DOUT;
     const int slot = blockIdx.x / OPS, o = blockIdx.x % OPS;
@@ -187,18 +189,15 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     const int gi = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
     const int lh = ph ^ (v & 1);                                  // logical half of my pieces
     const int tcg = 64 * u + 8 * v + cc;                          // my gate column; up is tcg + 32
-    // x of my groups: 32 values from 64 g + 32 lh
-    constexpr int NP = 2;                                         // passes: G <= 32 needs one
-    u32x4 xv[NP][4];
-    bool act[NP];
-#pragma unroll
-    for (int it = 0; it < NP; ++it) {
-        const int g = 4 * (wave + DW * it) + gi;
-        act[it] = g < G;
-        const u32x4 *px = (const u32x4 *)(x + 64 * min(g, G - 1) + 32 * lh);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) xv[it][qq] = px[qq];       // clamped: loads stay unconditional
-    }
+    // my group g = 4 wave + gi (G <= 32: one pass of the 8 waves covers every group).  The
+    // token's x (at most 4 KB) is loaded once per workgroup, 16 bytes per thread, and staged
+    // in LDS after the weight loads are out; the eight column lanes of a group then read
+    // their 64 bytes from there instead of each loading them from L2.
+    const int g = 4 * wave + gi;
+    const bool act = g < G;
+    const int gc = min(g, G - 1);
+    u32x4 xl = {0u, 0u, 0u, 0u};
+    if ((int)threadIdx.x < H / 8) xl = *(const u32x4 *)(x + 8 * threadIdx.x);
     int ex = 0;
     if (slot < k && picks_given) {
         ex = ids_out[slot];                                       // written by decode_select_kernel
@@ -226,39 +225,40 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     }
     const uint8_t *tile = slot == k ? pk_sh + (size_t)j * G * PK_BLOCK
                                     : pk + ((size_t)ex * JT + j) * G * PK_BLOCK;
-    u32x4 cw[NP][2];
-    uint16_t sv[NP][2], bv[NP][2];
-#pragma unroll
-    for (int it = 0; it < NP; ++it) {
-        const int g = min(4 * (wave + DW * it) + gi, G - 1);
-        const uint8_t *blk = tile + (size_t)g * PK_BLOCK;
+    u32x4 cw[2];
+    uint16_t sv[2], bv[2];
+    {
+        const uint8_t *blk = tile + (size_t)gc * PK_BLOCK;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int tc = tcg + 32 * r;
-            cw[it][r] = *(const u32x4 *)(blk + 32 * tc + 16 * ph);
-            sv[it][r] = *(const uint16_t *)(blk + PK_CODES + 2 * tc);
-            bv[it][r] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * tc);
+            cw[r] = *(const u32x4 *)(blk + 32 * tc + 16 * ph);
+            sv[r] = *(const uint16_t *)(blk + PK_CODES + 2 * tc);
+            bv[r] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * tc);
         }
     }
+    if ((int)threadIdx.x < H / 8) xs[threadIdx.x] = xl;
+    __syncthreads();
+    u32x4 xv[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) xv[qq] = xs[8 * gc + 4 * lh + qq];
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     uint32_t cM = 0x000F000Fu, cC = 0x43004300u;
     asm volatile("" : "+v"(cM), "+v"(cC));
     float ag = 0.0f, au = 0.0f;
-#pragma unroll
-    for (int it = 0; it < NP; ++it) {
-        if (!act[it]) continue;
+    if (act) {
         uint32_t xp[16];
         float sx = 0.0f;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-            pair_order(xv[it][qq], xp + 4 * qq);
+            pair_order(xv[qq], xp + 4 * qq);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sx += bf16_lo(xv[it][qq][r]) + bf16_hi(xv[it][qq][r]);
+            for (int r = 0; r < 4; ++r) sx += bf16_lo(xv[qq][r]) + bf16_hi(xv[qq][r]);
         }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             float d = 0.0f;
-            const uint32_t ww[4] = {cw[it][r].x, cw[it][r].y, cw[it][r].z, cw[it][r].w};
+            const uint32_t ww[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
                                                         __builtin_bit_cast(bf16x2, xp[4 * qq + p]), d, false);
                 }
             // sum_k x_k (q_k s + b) = s (sum x (128 + q) - 128 sum x) + b sum x
-            const float val = bf16_to_f32(sv[it][r]) * (d - 128.0f * sx) + bf16_to_f32(bv[it][r]) * sx;
+            const float val = bf16_to_f32(sv[r]) * (d - 128.0f * sx) + bf16_to_f32(bv[r]) * sx;
             if (r == 0) ag += val; else au += val;
         }
     }
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     const float *__restrict__ tw, int k, int E, const uint8_t *__restrict__ pk,
     const uint8_t *__restrict__ pk_sh, float *__restrict__ y) {
     __shared__ float part[DN_MAXP][DOUT];
+    extern __shared__ u32x4 hsh[];                                // the token's h block, (k+1) I fp16
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
     const int G = I / 64, JD = H / 256, NPAIR = (k + 1) * G;
     {   // token blockIdx.y: its h block, picks and output row
@@ -317,6 +318,15 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     const int sub = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
     const int tc = 8 * v + cc;
     const int lh = ph ^ (v & 1);
+    // the h block (9 KB at I = 512) is loaded once per workgroup, 16 bytes per thread and
+    // pass, before the ids (it does not depend on them), and staged in LDS once the first
+    // weight loads are out; every lane then reads its pairs' h values from LDS
+    const int nh = (k + 1) * I / 8;
+    constexpr int HCH = (NSLOT * 2048 / 8 + 64 * DW - 1) / (64 * DW);   // chunks per thread, I <= 2048
+    u32x4 hl[HCH];
+#pragma unroll
+    for (int q = 0; q < HCH; ++q)
+        if (tid + 64 * DW * q < nh) hl[q] = ((const u32x4 *)hbuf)[tid + 64 * DW * q];
     int sid[NSLOT];
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     for (int it0 = 0; it0 < npass; it0 += DN_BATCH) {
         u32x4 cw[DN_BATCH], hv[DN_BATCH][4];
         uint16_t sv[DN_BATCH], bv[DN_BATCH];
-        int pp[DN_BATCH];
+        int pp[DN_BATCH], hcs[DN_BATCH];
 #pragma unroll
         for (int b = 0; b < DN_BATCH; ++b) {
             const int p = 4 * (wave + DW * (it0 + b)) + sub;
@@ -349,10 +359,18 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
             cw[b] = *(const u32x4 *)(blk + 32 * tc + 16 * ph);
             sv[b] = *(const uint16_t *)(blk + PK_CODES + 2 * tc);
             bv[b] = *(const uint16_t *)(blk + PK_CODES + 512 + 2 * tc);
-            const u32x4 *ph4 = (const u32x4 *)(hbuf + (size_t)s * I + 64 * g + 32 * lh);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) hv[b][qq] = ph4[qq];
+            hcs[b] = s * I / 8 + 8 * g + 4 * lh;                       // its h values in LDS
         }
+        if (it0 == 0) {
+#pragma unroll
+            for (int q = 0; q < HCH; ++q)
+                if (tid + 64 * DW * q < nh) hsh[tid + 64 * DW * q] = hl[q];
+            __syncthreads();
+        }
+#pragma unroll
+        for (int b = 0; b < DN_BATCH; ++b)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) hv[b][qq] = hsh[hcs[b] + qq];
 #pragma unroll
         for (int b = 0; b < DN_BATCH; ++b) {
             if (pp[b] >= NPAIR) continue;
@@ -411,8 +429,8 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
         hipLaunchKernelGGL(decode_select_kernel, dim3(T), dim3(64), 0, s, logits, E, k, ids, tw);
     hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT), T), dim3(64 * DW), 0, s, x,
                        logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf, picks_given);
-    hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT, T), dim3(64 * DW), 0, s, hbuf, H, I, ids, tw,
-                       k, E, pk + P.down, pk + P.sh_down, y);
+    hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT, T), dim3(64 * DW), (size_t)(k + 1) * I * 2, s,
+                       hbuf, H, I, ids, tw, k, E, pk + P.down, pk + P.sh_down, y);
 }
 
 size_t decode_scratch_bytes(int T, int H, int I, int k) {
