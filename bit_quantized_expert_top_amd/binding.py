@@ -54,6 +54,8 @@ _SIGS = {
     "moe_layer_chunked": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, i32, P, C.c_size_t, P],
                           i32),
     "moe_decode": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, P, P, P, C.c_size_t, P], i32),
+    "moe_decode_residual": ([C.POINTER(_Shape), P, P, C.c_float, P, C.POINTER(_Weights), P, P, P, P,
+                             C.c_size_t, P], i32),
     "moe_rmsnorm_residual": ([i32, i32, C.c_float, P, P, P, P], i32),
     "moe_dequant_q4": ([C.POINTER(_Q4), i32, i32, P, P], i32),
     "moe_status_str": ([i32], C.c_char_p),
@@ -294,6 +296,22 @@ def moe_decode(shape: Shape, x: torch.Tensor, w: DeviceLayer, ids: torch.Tensor,
     _check(lib().moe_decode(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
                             _ptr(ids, _I32, "ids"), _ptr(tw, _F32, "topk_w"), _ptr(y, _F32, "y"),
                             _ptr(ws, None, "ws"), ws.numel(), _stream(stream)), "moe_decode")
+
+
+def moe_decode_residual(shape: Shape, r: torch.Tensor, y_prev: torch.Tensor, eps: float,
+                        u: torch.Tensor, w: DeviceLayer, ids: torch.Tensor, tw: torch.Tensor,
+                        y: torch.Tensor, ws: torch.Tensor, stream=None):
+    """Decode-stack layer: r += y_prev; u = bf16(RMSNorm(r)); y = layer(u) (T <= 8 tokens)."""
+    T, H, k = shape.T, shape.H, shape.top_k
+    for t, n, name in ((r, T * H, "r"), (y_prev, T * H, "y_prev"), (u, T * H, "u"),
+                       (ids, T * k, "ids"), (tw, T * k, "topk_w"), (y, T * H, "y")):
+        _need(t, n, name)
+    _check(lib().moe_decode_residual(C.byref(shape.c()), _ptr(r, _F32, "r"),
+                                     _ptr(y_prev, _F32, "y_prev"), C.c_float(eps),
+                                     _ptr(u, _B16, "u"), C.byref(w.c()), _ptr(ids, _I32, "ids"),
+                                     _ptr(tw, _F32, "topk_w"), _ptr(y, _F32, "y"),
+                                     _ptr(ws, None, "ws"), ws.numel(), _stream(stream)),
+           "moe_decode_residual")
 
 
 def moe_rmsnorm_residual(T: int, H: int, eps: float, r: torch.Tensor, y: torch.Tensor,

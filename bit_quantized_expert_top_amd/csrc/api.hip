@@ -331,6 +331,24 @@ moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weigh
     return launched();
 }
 
+moe_status moe_decode_residual(const moe_shape *shape, float *r, const float *y_prev, float eps,
+                               uint16_t *u, const moe_weights *w, int32_t *topk_ids, float *topk_w,
+                               float *y, void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (shape->T > kDecodeMaxT || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(r) || !aligned(y_prev) || !aligned(u) || !aligned(topk_ids) || !aligned(topk_w) ||
+        !aligned(y))
+        return MOE_ERR_INVALID_ARG;
+    if ((const void *)r == (const void *)y_prev || (const void *)u == (const void *)r)
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, true, true, true));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(shape->T, shape->H, shape->I, shape->E, shape->top_k);
+    launch_decode(*shape, nullptr, *w, topk_ids, topk_w, y, (char *)ws + L.dec, (hipStream_t)stream,
+                  r, y_prev, eps, u);
+    return launched();
+}
+
 moe_status moe_rmsnorm_residual(int32_t T, int32_t H, float eps, float *r, const float *y,
                                 uint16_t *u, void *stream) {
     if (T < 1 || H < 4 || H % 4 != 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;

@@ -269,8 +269,11 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  uint16_t *stage, float *y, hipStream_t s);
 
+// res == NULL: decode x.  Otherwise x is ignored and the input is bf16(RMSNorm(res + yprev)),
+// written to u_out; res <- res + yprev (a decode stack's residual step).
 void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w, int32_t *ids,
-                   float *tw, float *y, void *scratch, hipStream_t s);
+                   float *tw, float *y, void *scratch, hipStream_t s, float *res = nullptr,
+                   const float *yprev = nullptr, float eps = 0.0f, uint16_t *u_out = nullptr);
 
 void launch_rmsnorm_residual(int T, int H, float eps, float *r, const float *y, uint16_t *u,
                              hipStream_t s);

@@ -42,27 +42,66 @@ __device__ __forceinline__ uint32_t dec_and_or(uint32_t a, uint32_t m, uint32_t 
 
 // 1. logits[e] = sum over chunks c (in order) of sum_{k in chunk c} x_k w_ek (in order), + bias.
 // One wave (one workgroup) per expert, so the 1 MB of router weights is read
-// by E workgroups at once.
+// by E workgroups at once.  With a residual (res != NULL, a decode stack's layer
+// after the first) the layer input is made here: x = bf16((res + yprev) /
+// sqrt(mean((res + yprev)^2) + eps)); every wave computes it from the whole row
+// (lane c holds elements 64 c .. 64 c + 63) and the expert-0 wave also writes it
+// to u_out for the gate/up and down kernels.  res itself is updated by the
+// gate/up kernel, after every wave here has read it.
 __global__ __launch_bounds__(64) void decode_router_kernel(const uint16_t *__restrict__ x,
                                                            const uint16_t *__restrict__ wr,
                                                            const float *__restrict__ bias, int H,
-                                                           float *__restrict__ logits) {
+                                                           float *__restrict__ logits,
+                                                           const float *__restrict__ res,
+                                                           const float *__restrict__ yprev, float eps,
+                                                           uint16_t *__restrict__ u_out) {
     const int lane = threadIdx.x;
     const int e = blockIdx.x;
     const int E = gridDim.x;
-    x += (size_t)blockIdx.y * H;   // token blockIdx.y
-    logits += (size_t)blockIdx.y * E;
+    const size_t t = blockIdx.y;   // token
+    logits += t * E;
     const int G = H / 64;          // <= 32 chunks: lane c < G sums chunk c
-    float P = 0.0f;
-    if (lane < G) {
-        const u32x4 *px = (const u32x4 *)(x + 64 * lane);
-        const u32x4 *pw = (const u32x4 *)(wr + (size_t)e * H + 64 * lane);
-        u32x4 xv[8], wv[8];
+    const int c = min(lane, G - 1);
+    u32x4 xv[8], wv[8];
+    {
+        const u32x4 *pw = (const u32x4 *)(wr + (size_t)e * H + 64 * c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[j] = pw[j];
+    }
+    if (res == nullptr) {
+        const u32x4 *px = (const u32x4 *)(x + t * H + 64 * c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = px[j];
+    } else {
+        const floatx4 *pr = (const floatx4 *)(res + t * H + 64 * c);
+        const floatx4 *py = (const floatx4 *)(yprev + t * H + 64 * c);
+        floatx4 a[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[j] = pr[j] + py[j];
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ss = __builtin_fmaf(a[j][q], a[j][q], ss);
+        ss = lane < G ? ss : 0.0f;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        const float inv = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            xv[j] = px[j];
-            wv[j] = pw[j];
+            xv[j].x = pack_bf16x2(a[2 * j][0] * inv, a[2 * j][1] * inv);
+            xv[j].y = pack_bf16x2(a[2 * j][2] * inv, a[2 * j][3] * inv);
+            xv[j].z = pack_bf16x2(a[2 * j + 1][0] * inv, a[2 * j + 1][1] * inv);
+            xv[j].w = pack_bf16x2(a[2 * j + 1][2] * inv, a[2 * j + 1][3] * inv);
         }
+        if (e == 0 && lane < G) {
+            u32x4 *pu = (u32x4 *)(u_out + t * H + 64 * lane);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pu[j] = xv[j];
+        }
+    }
+    float P = 0.0f;
+    if (lane < G) {
         // bf16 x bf16 products are exact in fp32, so each fma adds one product
         // with a single rounding, exactly as the sequential sum does
 #pragma unroll
@@ -170,7 +209,8 @@ __device__ __forceinline__ float pair_sum(float v) {
 __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
     const uint8_t *__restrict__ pk, const uint8_t *__restrict__ pk_sh, int32_t *__restrict__ ids_out,
-    float *__restrict__ tw_out, uint16_t *__restrict__ hbuf, bool picks_given) {
+    float *__restrict__ tw_out, uint16_t *__restrict__ hbuf, bool picks_given,
+    float *__restrict__ res, const float *__restrict__ yprev) {
     __shared__ float red[DW][4][DOUT][2];
     __shared__ uint32_t selw[DW][32];
     __shared__ u32x4 xs[256];                                     // the token's x, H <= 2048
@@ -184,6 +224,13 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
         ids_out += t * k;
         tw_out += t * k;
         hbuf += t * NSLOT * I;
+        // decode stack: the residual add the router kernel folded into this layer's input
+        // is committed here, once every router wave has read res and yprev
+        if (res != nullptr && blockIdx.x == 0)
+            for (int i = 4 * threadIdx.x; i < H; i += 4 * 64 * DW) {
+                floatx4 *pr = (floatx4 *)(res + t * H + i);
+                *pr = *pr + *(const floatx4 *)(yprev + t * H + i);
+            }
     }
     const int j = o >> 4, u = (o >> 2) & 3, v = o & 3;            // 8 o = 128 j + 32 u + 8 v
     const int gi = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
@@ -410,7 +457,8 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
 }
 
 void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w, int32_t *ids,
-                   float *tw, float *y, void *scratch, hipStream_t s) {
+                   float *tw, float *y, void *scratch, hipStream_t s, float *res, const float *yprev,
+                   float eps, uint16_t *u_out) {
     const int T = sh.T, H = sh.H, I = sh.I, E = sh.E, k = sh.top_k;
     char *p = (char *)scratch;
     float *logits = (float *)p;                                   // [T][E]
@@ -419,16 +467,19 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     if (k + 1 != NSLOT || E > 256 || H > 2048 || I > 2048 || T < 1 || T > kDecodeMaxT) return;
     const PackLayout P = pack_layout(H, I, E);
     const uint8_t *pk = (const uint8_t *)w.packed;
+    // with a residual the router kernel makes the layer input and writes it to u_out
+    const uint16_t *xin = res ? u_out : x;
     // every kernel takes token t = blockIdx.y; the tokens are independent problems
     hipLaunchKernelGGL(decode_router_kernel, dim3(E, T), dim3(64), 0, s, x, w.router_wt, w.router_bias,
-                       H, logits);
+                       H, logits, res, yprev, eps, u_out);
     // one token: every gate/up wave takes the top-k itself (no extra launch on the
     // latency chain); more tokens: the picks are taken once per token
     const bool picks_given = T > 1;
     if (picks_given)
         hipLaunchKernelGGL(decode_select_kernel, dim3(T), dim3(64), 0, s, logits, E, k, ids, tw);
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT), T), dim3(64 * DW), 0, s, x,
-                       logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf, picks_given);
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT), T), dim3(64 * DW), 0, s, xin,
+                       logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf, picks_given, res,
+                       yprev);
     hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT, T), dim3(64 * DW), (size_t)(k + 1) * I * 2, s,
                        hbuf, H, I, ids, tw, k, E, pk + P.down, pk + P.sh_down, y);
 }

@@ -216,6 +216,21 @@ moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weigh
                       int32_t *topk_ids, float *topk_w, float *y, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* One layer of a decode stack after the first (the stacked-layer workload: a
+ * residual add and RMSNorm with unit weight between MoE layers), with the add
+ * and the norm folded into the layer's router pass instead of a kernel of
+ * their own:
+ *   r <- r + y_prev (fp32);  u = bf16(r / sqrt(mean(r^2) + eps));
+ *   then exactly moe_decode on u (ids, weights, y).
+ * r, y_prev: fp32 [T][H]; u: bf16 [T][H] (written: the layer input, for the
+ * caller's use); y: fp32 [T][H] (overwritten).  y_prev may be the same buffer
+ * as y (the previous layer's output); r, y_prev and u must not overlap each
+ * other otherwise (MOE_ERR_INVALID_ARG if r == y_prev or u == r).  T <= 8,
+ * eps >= 0.  The first layer of a stack is plain moe_decode on x with r = x. */
+moe_status moe_decode_residual(const moe_shape *shape, float *r, const float *y_prev, float eps,
+                               uint16_t *u, const moe_weights *w, int32_t *topk_ids, float *topk_w,
+                               float *y, void *ws, size_t ws_bytes, void *stream);
+
 /* Between stacked layers: r <- r + y (fp32), u = bf16(r / sqrt(mean(r^2) + eps))
  * (unit RMSNorm weight).  r, y: fp32 [T][H]; u: bf16 [T][H]. */
 moe_status moe_rmsnorm_residual(int32_t T, int32_t H, float eps, float *r, const float *y,

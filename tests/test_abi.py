@@ -239,3 +239,26 @@ def test_chunked_validation_before_launch():
     assert L.moe_layer_chunked(C.byref(s), FAKE, C.byref(_weights("null_packed")), FAKE, 2048, FAKE,
                                need, None) == INVALID
     assert L.moe_layer_chunked(C.byref(s), FAKE, C.byref(w), FAKE, 0, FAKE, need, None) == INVALID
+
+
+def test_decode_residual_validation_before_launch():
+    L = B.lib()
+    s = shape(T=1)
+    _, need, _, _ = query(s)
+    w = _weights()
+    F2 = FAKE + 0x10000
+    F3 = FAKE + 0x20000
+    eps = C.c_float(1e-6)
+    # r == y_prev and u == r are refused; T above 8 and a negative eps too
+    assert L.moe_decode_residual(C.byref(s), FAKE, FAKE, eps, F2, C.byref(w), FAKE, FAKE, FAKE, FAKE,
+                                 need, None) == INVALID
+    assert L.moe_decode_residual(C.byref(s), FAKE, F2, eps, FAKE, C.byref(w), FAKE, FAKE, FAKE, FAKE,
+                                 need, None) == INVALID
+    assert L.moe_decode_residual(C.byref(s), FAKE, F2, C.c_float(-1.0), F3, C.byref(w), FAKE, FAKE,
+                                 FAKE, FAKE, need, None) == INVALID
+    s9 = shape(T=9)
+    assert L.moe_decode_residual(C.byref(s9), FAKE, F2, eps, F3, C.byref(w), FAKE, FAKE, FAKE, FAKE,
+                                 need, None) == INVALID
+    # well-formed arguments reach the workspace check
+    assert L.moe_decode_residual(C.byref(s), FAKE, F2, eps, F3, C.byref(w), FAKE, FAKE, FAKE, FAKE,
+                                 need - 1, None) == WS

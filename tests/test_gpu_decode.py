@@ -7,6 +7,7 @@ import bit_quantized_expert_top_amd as moe
 import oracle
 from synth import make_layer
 from moe_case import LayerRun, check_y, device, shape_of, upload, x_dev
+from synth.inputs import bf16_bits_to_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +145,62 @@ def test_small_batch_equals_single_tokens():
         np.testing.assert_array_equal(i1, ids[t])
         np.testing.assert_array_equal(w1, tw[t])
         np.testing.assert_array_equal(y1, y[t])
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_stack_fused_residual(T):
+    """Layers after the first through moe_decode_residual, which folds the residual add and
+    RMSNorm into the router pass: r must be the exact fp32 sum, u within one bf16 ulp of the
+    oracle's RMSNorm of it, and each layer is checked against the oracle on the u it wrote
+    (teacher forcing).  The y of the previous layer is overwritten in place.  The whole chain
+    captured in a HIP graph replays bit for bit."""
+    H, I, L = 2048, 512, 4
+    print(f"[decode-stack-fused] T={T} layers={L}", flush=True)
+    dev = device()
+    layers = [make_layer(2300 + 10 * T + l, T=T, H=H, I=I, with_x=(l == 0)) for l in range(L)]
+    ws_ = [upload(inp, dev) for inp in layers]
+    sh = shape_of(layers[0])
+    ws = moe.workspace(sh, dev)
+    x0 = torch.from_numpy(layers[0].x.copy()).view(torch.int16).to(dev)
+    ids = torch.empty((T, 8), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, 8), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    r = torch.empty((T, H), dtype=torch.float32, device=dev)
+    u = torch.empty((T, H), dtype=torch.int16, device=dev)
+
+    def chain(check):
+        r.copy_(x0.view(torch.bfloat16).float())
+        moe.moe_decode(sh, x0, ws_[0], ids, tw, y, ws)
+        for l in range(1, L):
+            if check:
+                torch.cuda.synchronize()
+                r_prev, y_prev = r.cpu().numpy().copy(), y.cpu().numpy().copy()
+            moe.moe_decode_residual(sh, r, y, 1e-6, u, ws_[l], ids, tw, y, ws)
+            if check:
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(r.cpu().numpy(), r_prev + y_prev)
+                _, u_ref = oracle.rmsnorm_residual(r_prev.astype(np.float64),
+                                                   y_prev.astype(np.float64), 1e-6)
+                ug = bf16_bits_to_f32(u.cpu().numpy().view(np.uint16)).astype(np.float64)
+                ur = bf16_bits_to_f32(u_ref).astype(np.float64)
+                assert np.all(np.abs(ug - ur) <= 2.0 ** -7 * np.abs(ur) + 1e-30), l
+                inp = layers[l]
+                inp.x = u.cpu().numpy().view(np.uint16).copy()
+                y_ref, ids_ref, _ = oracle.Layer(inp).tokens(range(T))
+                np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+                ratio = check_y(y.cpu().numpy(), y_ref)
+                print(f"  layer {l}: max err / rms = {ratio:.4g}", flush=True)
+
+    chain(check=True)
+    torch.cuda.synchronize()
+    r_eager, y_eager = r.clone(), y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain(check=False)
+    for rep in range(3):
+        r.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r, r_eager) and torch.equal(y, y_eager), rep
