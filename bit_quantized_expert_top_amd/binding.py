@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import ctypes as C
+import functools
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -236,14 +237,47 @@ class DeviceLayer:
                         None if packed is None else packed.data_ptr())
 
 
+@functools.lru_cache(maxsize=64)
+def _max_blocks(T, H, I, E, k) -> int:
+    return moe_query(Shape(T=T, H=H, I=I, E=E, top_k=k))[1]
+
+
+def _args(shape: Shape, w: DeviceLayer, r: Routing = None, x=None, h=None, y=None):
+    """Refuse tensors the kernels would address past their end: weights packed for another
+    (H, I, E), routing buffers allocated for fewer tokens, short x / h / y."""
+    ws_ = w.shape
+    if (ws_.H, ws_.I, ws_.E) != (shape.H, shape.I, shape.E):
+        raise ValueError(f"weights are packed for H={ws_.H} I={ws_.I} E={ws_.E}, the call has "
+                         f"H={shape.H} I={shape.I} E={shape.E}")
+    T, H, I, k = shape.T, shape.H, shape.I, shape.top_k
+    if r is not None:
+        max_blocks = _max_blocks(shape.T, shape.H, shape.I, shape.E, shape.top_k)
+        for t, n, name in ((r.topk_ids, T * k, "topk_ids"), (r.topk_w, T * k, "topk_w"),
+                           (r.counts, shape.E, "counts"), (r.offsets, shape.E + 1, "offsets"),
+                           (r.row_token, T * k, "row_token"), (r.tok_row, T * k, "tok_row"),
+                           (r.row_w, T * k, "row_w"), (r.blocks, 3 * max_blocks, "blocks"),
+                           (r.num_blocks, 1, "num_blocks")):
+            _need(t, n, name)
+        if r.logits is not None:
+            _need(r.logits, T * shape.E, "logits")
+    if x is not None:
+        _need(x, T * H, "x")
+    if h is not None:
+        _need(h, (T * k + T) * I, "h")
+    if y is not None:
+        _need(y, T * H, "y")
+
+
 def moe_route(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, ws: torch.Tensor,
               stream=None):
+    _args(shape, w, r, x=x)
     _check(lib().moe_route(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()), C.byref(r.c()),
                            _ptr(ws, None, "ws"), ws.numel(), _stream(stream)), "moe_route")
 
 
 def moe_expert_gemm_q4(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,
                        ws: torch.Tensor, stream=None):
+    _args(shape, w, r, x=x, h=h)
     _check(lib().moe_expert_gemm_q4(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
                                     C.byref(r.c()), _ptr(h, _H16, "h"), _ptr(ws, None, "ws"),
                                     ws.numel(), _stream(stream)), "moe_expert_gemm_q4")
@@ -251,6 +285,7 @@ def moe_expert_gemm_q4(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing
 
 def moe_down_combine(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing, y: torch.Tensor,
                      ws: torch.Tensor, stream=None):
+    _args(shape, w, r, h=h, y=y)
     _check(lib().moe_down_combine(C.byref(shape.c()), _ptr(h, _H16, "h"), C.byref(w.c()),
                                   C.byref(r.c()), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
                                   ws.numel(), _stream(stream)), "moe_down_combine")
@@ -258,6 +293,7 @@ def moe_down_combine(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing, 
 
 def moe_layer(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,
               y: torch.Tensor, ws: torch.Tensor, stream=None):
+    _args(shape, w, r, x=x, h=h, y=y)
     _check(lib().moe_layer(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()), C.byref(r.c()),
                            _ptr(h, _H16, "h"), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
                            ws.numel(), _stream(stream)), "moe_layer")
@@ -277,6 +313,7 @@ def workspace_chunked(shape: Shape, chunk: int, device) -> torch.Tensor:
 def moe_layer_chunked(shape: Shape, x: torch.Tensor, w: DeviceLayer, y: torch.Tensor, chunk: int,
                       ws: torch.Tensor, stream=None):
     """The layer over chunks of `chunk` tokens: x bf16 [T][H] -> y fp32 [T][H]."""
+    _args(shape, w)
     _need(x, shape.T * shape.H, "x")
     _need(y, shape.T * shape.H, "y")
     _check(lib().moe_layer_chunked(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
@@ -289,6 +326,7 @@ def moe_decode(shape: Shape, x: torch.Tensor, w: DeviceLayer, ids: torch.Tensor,
     """Decode of shape.T <= 8 tokens: x [T][H] bf16, ids [T][top_k] int32, tw [T][top_k] fp32,
     y [T][H] fp32."""
     T, H, k = shape.T, shape.H, shape.top_k
+    _args(shape, w)
     _need(x, T * H, "x")
     _need(ids, T * k, "ids")
     _need(tw, T * k, "topk_w")
@@ -303,6 +341,7 @@ def moe_decode_residual(shape: Shape, r: torch.Tensor, y_prev: torch.Tensor, eps
                         y: torch.Tensor, ws: torch.Tensor, stream=None):
     """Decode-stack layer: r += y_prev; u = bf16(RMSNorm(r)); y = layer(u) (T <= 8 tokens)."""
     T, H, k = shape.T, shape.H, shape.top_k
+    _args(shape, w)
     for t, n, name in ((r, T * H, "r"), (y_prev, T * H, "y_prev"), (u, T * H, "u"),
                        (ids, T * k, "ids"), (tw, T * k, "topk_w"), (y, T * H, "y")):
         _need(t, n, name)

@@ -262,3 +262,39 @@ def test_decode_residual_validation_before_launch():
     # well-formed arguments reach the workspace check
     assert L.moe_decode_residual(C.byref(s), FAKE, F2, eps, F3, C.byref(w), FAKE, FAKE, FAKE, FAKE,
                                  need - 1, None) == WS
+
+
+def test_binding_refuses_short_or_mismatched_tensors():
+    """The binding checks sizes before any launch: weights packed for another shape, routing
+    buffers for fewer tokens and short activations are refused (CPU tensors suffice: the check
+    runs before any pointer is taken)."""
+    import torch
+
+    class W:
+        shape = moe.Shape(T=1, H=512, I=128)
+
+    sh = moe.Shape(T=32, H=512, I=128)
+    x = torch.empty(32 * 512, dtype=torch.int16)
+    y = torch.empty(32 * 512, dtype=torch.float32)
+    B._args(sh, W(), x=x, y=y)                                   # well-formed: no error
+    with pytest.raises(ValueError, match="packed for"):
+        B._args(moe.Shape(T=32, H=1024, I=128), W(), x=x)
+    with pytest.raises(ValueError, match="y holds"):
+        B._args(sh, W(), y=y[:-1])
+    with pytest.raises(ValueError, match="h holds"):
+        B._args(sh, W(), h=torch.empty(32 * 9 * 128 - 1, dtype=torch.int16))
+
+    class R:                                                    # routing for 16 tokens only
+        logits = None
+        topk_ids = torch.empty(16 * 8, dtype=torch.int32)
+        topk_w = torch.empty(16 * 8)
+        counts = torch.empty(256, dtype=torch.int32)
+        offsets = torch.empty(257, dtype=torch.int32)
+        row_token = torch.empty(16 * 8, dtype=torch.int32)
+        tok_row = torch.empty(16 * 8, dtype=torch.int32)
+        row_w = torch.empty(16 * 8)
+        blocks = torch.empty(3 * 1000, dtype=torch.int32)
+        num_blocks = torch.empty(1, dtype=torch.int32)
+
+    with pytest.raises(ValueError, match="topk_ids holds"):
+        B._args(sh, W(), R(), x=x)
