@@ -45,12 +45,12 @@ SEED_STACK = 5000
 # runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean of 19
 # dispatches), each scaled by what the same counter reports for a plain 256 MiB
 # device-to-device copy (bench.py --copy-calibration 256: FETCH_SIZE reads
-# 131085.5 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
+# 131085.4 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
 # source these counters were taken on; otherwise the JSON reports null.
 GATEUP_TRAFFIC = {
-    "gemm_src_sha256": "0350e8ab35e6782fa2d4de12cea969238ec23b4fc72efb3d8a7f252f3bc67669",
-    "fetch_kib": 153978.9, "fetch_scale": 2.0,
-    "write_kib": 20752.4, "write_scale": 1.0,
+    "gemm_src_sha256": "172ea8df7e208c2b8649635765940d580a2ea501a7d92c7024179f9df6cc98d4",
+    "fetch_kib": 160964.9, "fetch_scale": 2.0,
+    "write_kib": 20704.8, "write_scale": 1.0,
     "profile": "profiles/q4_gemm_gateup_prefill2048_zipf_hbm_traffic.md",
 }
 

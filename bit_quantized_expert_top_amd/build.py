@@ -1,9 +1,15 @@
-"""Build libmoeq4.so (all HIP sources, gfx950) next to this file."""
+"""Build libmoeq4.so (all HIP sources, gfx950) next to this file.
+
+Each source compiles to its own object (in parallel, with its own scheduling flags) and the
+objects link into one shared library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -12,7 +18,7 @@ SOURCES = ["api.hip", "route.hip", "gemm.hip", "decode.hip", "misc.hip", "pack.h
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 arithmetic in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in VGPRs: the GEMM's register budget (two workgroups per
@@ -24,14 +30,31 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
+# iterative ILP scheduling keeps the GEMM's operand reads for a k slice grouped ahead of the
+# MFMAs that use them (the default scheduler sinks each read next to its use and waits for it
+# there): measured 4 us faster on the down GEMM and 1 us on routing, gate/up level
+ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+PER_SOURCE = {"gemm.hip": ILP, "route.hip": ILP}
+
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    with tempfile.TemporaryDirectory(prefix="moeq4_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            cmd = [HIPCC, *FLAGS, *PER_SOURCE.get(src, []), "-c", "-o", obj,
+                   os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.check_call(cmd)
+            return obj
+
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as pool:
+            objs = list(pool.map(compile_one, SOURCES))
+        tmp = LIB + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB
 

@@ -287,27 +287,32 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 ss16[nt] = f16x2{sh16, sh16};
             }
             const uint8_t *arow = sb + l32 * (KC * 2);
-            // steps (j, mt) in order; the A fragment of step s is read two steps
-            // ahead into a 3-slot ring, so LDS latency overlaps two MFMA pairs
-            constexpr int NSTEP = 4 * MT;
-            auto a_frag = [&](int s) {
-                const int j = s / MT, mt = s % MT;
+            // per 16-wide k slice j: the MT A fragments of slice j+1 are read together and
+            // its two B fragments rebuilt while slice j runs its 2 MT MFMAs (both
+            // double-buffered); the build's iterative-ILP scheduler keeps this order, so the
+            // LDS latency hides behind the matrix core instead of stalling each MFMA pair
+            auto a_frag = [&](int j, int mt) {
                 return *(const f16x8 *)(arow + mt * 32 * (KC * 2) + 16 * ((4 * gg + j) ^ sw));
             };
-            f16x8 af[3];
-            af[0] = a_frag(0);
-            if (NSTEP > 1) af[1] = a_frag(1);
-            f16x8 b0, b1;
+            f16x8 af[2][MT], bf[2][2];
 #pragma unroll
-            for (int s = 0; s < NSTEP; ++s) {
-                const int j = s / MT, mt = s % MT;
-                if (mt == 0) {
-                    b0 = rebuild8(wq[0][j], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
-                    b1 = rebuild8(wq[1][j], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
+            for (int mt = 0; mt < MT; ++mt) af[0][mt] = a_frag(0, mt);
+            bf[0][0] = rebuild8(wq[0][0], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
+            bf[0][1] = rebuild8(wq[1][0], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cur = j & 1, nxt = cur ^ 1;
+                if (j < 3) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) af[nxt][mt] = a_frag(j + 1, mt);
+                    bf[nxt][0] = rebuild8(wq[0][j + 1], cM, cM2, cC, m1032, m1152, ss[0], ss16[0]);
+                    bf[nxt][1] = rebuild8(wq[1][j + 1], cM, cM2, cC, m1032, m1152, ss[1], ss16[1]);
                 }
-                if (s + 2 < NSTEP) af[(s + 2) % 3] = a_frag(s + 2);
-                acc[mt][0] = mfma16(af[s % 3], b0, acc[mt][0]);
-                acc[mt][1] = mfma16(af[s % 3], b1, acc[mt][1]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[mt][0] = mfma16(af[cur][mt], bf[cur][0], acc[mt][0]);
+                    acc[mt][1] = mfma16(af[cur][mt], bf[cur][1], acc[mt][1]);
+                }
             }
         });
     }
