@@ -9,9 +9,12 @@
  *   expert that every token uses; GPU-resident routing (expert histogram,
  *   prefix scan, token scatter, block map) with no host synchronisation;
  *   a grouped SwiGLU expert GEMM that reads the 4-bit weights directly and
- *   accumulates in FP32; a routing-weighted combine.  Batch-1 decode is a
- *   separate weight-streaming path (mechatronicstore.cl, "Decode: mover menos
- *   bytes por token"; neuro-ai.ru, "Спекулятивное декодирование не взлетело").
+ *   accumulates in FP32; a routing-weighted combine.  Decode (1 to 8 tokens
+ *   per call) is a separate weight-streaming path (mechatronicstore.cl,
+ *   "Decode: mover menos bytes por token"; neuro-ai.ru, "Спекулятивное
+ *   декодирование не взлетело"); long prompts can run in chunks with a
+ *   bounded workspace (greatopti.com, "Les gains viennent surtout des
+ *   mouvements de données").
  *
  * Conventions common to every entry point
  *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory)
@@ -53,8 +56,8 @@
  *     MOE_ERR_INVALID_ARG: NULL or misaligned pointer, T < 1, bad sizes.
  *     MOE_ERR_UNSUPPORTED: bits != 4, group != 64, E != 256, top_k != 8,
  *       H not a multiple of 256 or above 2048, I not a multiple of 128 or
- *       above 2048, T > 65536 (the checkpoint-format validation that
- *       refuses every other format).
+ *       above 2048, T > 65536 (moe_layer_chunked: T > 2^24), the
+ *       checkpoint-format validation that refuses every other format.
  *     MOE_ERR_WORKSPACE: workspace NULL, not 256-byte aligned, or smaller
  *       than moe_query reports.
  *     MOE_ERR_HIP: a launch failed (hipGetLastError after the launch).
