@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
     (300, 512, 128, 128, None, 1300),      # three chunks, ragged last (44 tokens)
     (300, 512, 128, 1000, None, 1301),     # one chunk larger than T
     (2053, 2048, 512, 1024, 1.1, 4030),    # skewed routing, last chunk of 5 tokens
+    (20, 768, 384, 7, None, 1302),         # chunks of 7, 7 and 6 tokens
 ])
 def test_chunked_equals_single_call_and_oracle(T, H, I, chunk, zipf, seed):
     print(f"[chunked] T={T} H={H} I={I} chunk={chunk} zipf={zipf}", flush=True)

@@ -147,15 +147,15 @@ def test_small_batch_equals_single_tokens():
         np.testing.assert_array_equal(y1, y[t])
 
 
-@pytest.mark.parametrize("T", [1, 3])
-def test_decode_stack_fused_residual(T):
+@pytest.mark.parametrize("T,H,I", [(1, 2048, 512), (3, 2048, 512), (2, 768, 384)])
+def test_decode_stack_fused_residual(T, H, I):
     """Layers after the first through moe_decode_residual, which folds the residual add and
     RMSNorm into the router pass: r must be the exact fp32 sum, u within one bf16 ulp of the
     oracle's RMSNorm of it, and each layer is checked against the oracle on the u it wrote
     (teacher forcing).  The y of the previous layer is overwritten in place.  The whole chain
     captured in a HIP graph replays bit for bit."""
-    H, I, L = 2048, 512, 4
-    print(f"[decode-stack-fused] T={T} layers={L}", flush=True)
+    L = 4
+    print(f"[decode-stack-fused] T={T} H={H} I={I} layers={L}", flush=True)
     dev = device()
     layers = [make_layer(2300 + 10 * T + l, T=T, H=H, I=I, with_x=(l == 0)) for l in range(L)]
     ws_ = [upload(inp, dev) for inp in layers]
