@@ -216,7 +216,11 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     __shared__ u32x4 xs[256];                                     // the token's x, H <= 2048
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = H / 64, JT = I / 128, OPS = I / DOUT;
-    const int slot = blockIdx.x / OPS, o = blockIdx.x % OPS;
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, and the ones on one
+    // XCD take consecutive output groups, so the scale/bias lines they share (64 columns)
+    // are fetched into one L2 rather than into all eight (OPS is a multiple of 16)
+    const int slot = blockIdx.x / OPS, bl = blockIdx.x % OPS;
+    const int o = (bl & 7) * (OPS >> 3) + (bl >> 3);
     {   // token blockIdx.y: its input row, logits, picks and h block
         const size_t t = blockIdx.y;
         x += t * H;
@@ -361,7 +365,9 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
         tw += t * k;
         y += t * H;
     }
-    const int j = blockIdx.x >> 5, v = blockIdx.x & 31;          // outputs 256 j + 8 v + (0..7)
+    // outputs 256 j + 8 v + (0..7); XCD-aware order: with the workgroups dealt to the 8 XCDs
+    // round robin, the ones on one XCD share tile j and with it its scale/bias lines
+    const int j = blockIdx.x % JD, v = blockIdx.x / JD;
     const int sub = lane >> 4, cc = (lane >> 1) & 7, ph = lane & 1;
     const int tc = 8 * v + cc;
     const int lh = ph ^ (v & 1);
