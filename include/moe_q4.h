@@ -50,7 +50,9 @@
  *     only ENQUEUES work on `stream`; none synchronises or copies
  *     device->host.  The caller owns every buffer; the library never
  *     allocates, frees or caches device memory and keeps no global state,
- *     so calls on different streams are independent.
+ *     so calls on different streams are independent as long as they use
+ *     different workspaces (a workspace holds a call's scratch rows and the
+ *     GEMMs' work-queue counters: two calls in flight on one workspace race).
  *   - Errors: arguments are validated on the host before anything is
  *     enqueued; a call that returns an error has enqueued nothing.
  *     MOE_ERR_INVALID_ARG: NULL or misaligned pointer, T < 1, bad sizes.
