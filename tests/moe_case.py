@@ -100,3 +100,15 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float = TOL):
     assert np.all(np.isfinite(y_gpu)), "non-finite output"
     assert err <= tol * rms, f"max err {err:.4g} > {tol} * rms {rms:.4g} (ratio {err / rms:.4g})"
     return err / rms
+
+
+def asymmetric_bias(inp, seed):
+    """Biases b = bf16(-8 s + d) with d ~ U(-2s, 2s) in a random half of the groups
+    (the rest keep b = -8 s), so the GEMMs' rank-G bias term is exercised."""
+    from synth.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    for p in (inp.gate, inp.up, inp.down, inp.sh_gate, inp.sh_up, inp.sh_down):
+        s = bf16_bits_to_f32(p.scale)
+        d = rng.uniform(-2.0, 2.0, size=s.shape).astype(np.float32) * s
+        d[rng.random(size=s.shape) < 0.5] = 0.0
+        p.bias[...] = f32_to_bf16_bits(-8.0 * s + d)

@@ -8,7 +8,7 @@ import torch
 
 import bit_quantized_expert_top_amd as moe
 import oracle
-from moe_case import LayerRun, check_y, device, shape_of
+from moe_case import LayerRun, asymmetric_bias, check_y, device, shape_of
 from synth import make_layer
 
 pytestmark = pytest.mark.gpu
@@ -53,3 +53,24 @@ def test_chunked_workspace_reuse_across_calls():
         moe.moe_layer_chunked(sh, run.x, run.w, y, chunk, ws)
         torch.cuda.synchronize()
         assert torch.equal(y, run.y), (T, chunk)
+
+
+def test_chunked_asymmetric_bias():
+    """Chunks over weights with b != -8 s in half of the groups: equal to the single call
+    bit for bit, and to the oracle within the layer tolerance."""
+    T, H, I, chunk, seed = 500, 1024, 256, 192, 1310
+    print(f"[chunked-bias] T={T} H={H} I={I} chunk={chunk}", flush=True)
+    dev = device()
+    inp = make_layer(seed, T=T, H=H, I=I)
+    asymmetric_bias(inp, seed)
+    run = LayerRun(inp).layer().sync()
+    sh = shape_of(inp)
+    ws = moe.workspace_chunked(sh, chunk, dev)
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+    moe.moe_layer_chunked(sh, run.x, run.w, y, chunk, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, run.y), "chunked layer differs from the single call"
+    toks = [0, 1, 191, 192, 383, 384, 499]
+    y_ref, _, _ = oracle.Layer(inp).tokens(toks)
+    ratio = check_y(y.cpu().numpy()[toks], y_ref)
+    print(f"  max err / rms = {ratio:.4g}", flush=True)

@@ -6,7 +6,7 @@ import torch
 import bit_quantized_expert_top_amd as moe
 import oracle
 from synth import make_layer
-from moe_case import LayerRun, check_y, device, shape_of, upload, x_dev
+from moe_case import LayerRun, asymmetric_bias, check_y, device, shape_of, upload, x_dev
 from synth.inputs import bf16_bits_to_f32
 
 pytestmark = pytest.mark.gpu
@@ -131,6 +131,23 @@ def test_small_batch_decode_matches_oracle(T, seed, zipf):
     ratio = check_y(y, y_ref)
     print(f"  max err / rms = {ratio:.4g}, distinct experts = {len(set(ids.ravel().tolist()))}",
           flush=True)
+
+
+@pytest.mark.parametrize("T,seed", [(1, 2300), (4, 2301)])
+def test_decode_asymmetric_bias(T, seed):
+    """Decode with biases b != -8 s in half of the groups (the affine format's general
+    case): picks bit-exact, output within the layer tolerance."""
+    print(f"[decode-bias] T={T} seed={seed}", flush=True)
+    inp = make_layer(seed, T=T, H=2048, I=512)
+    asymmetric_bias(inp, seed)
+    ids, tw, y = run_decode(inp)
+    y_ref, ids_ref, w_ref = oracle.Layer(inp).tokens(range(T))
+    if T == 1:
+        ids, tw, y = ids[None], tw[None], y[None]
+    np.testing.assert_array_equal(ids, ids_ref)
+    np.testing.assert_allclose(tw, w_ref, rtol=2e-5, atol=2e-7)
+    ratio = check_y(y, y_ref)
+    print(f"  max err / rms = {ratio:.4g}", flush=True)
 
 
 def test_small_batch_equals_single_tokens():

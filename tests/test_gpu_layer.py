@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from synth import make_layer
-from moe_case import LayerRun, check_y, f16_np, unpermute_cols
+from moe_case import LayerRun, asymmetric_bias, check_y, f16_np, unpermute_cols
 
 pytestmark = pytest.mark.gpu
 
@@ -113,18 +113,6 @@ def test_layer_repeat_bit_identical():
     assert torch.equal(run.y, y1)
 
 
-def _asymmetric_bias(inp, seed):
-    """Biases b = bf16(-8 s + d) with d ~ U(-2s, 2s) in a random half of the groups
-    (the rest keep b = -8 s), so the GEMMs' rank-G bias term is exercised."""
-    from synth.inputs import bf16_bits_to_f32, f32_to_bf16_bits
-    rng = np.random.default_rng(seed)
-    for p in (inp.gate, inp.up, inp.down, inp.sh_gate, inp.sh_up, inp.sh_down):
-        s = bf16_bits_to_f32(p.scale)
-        d = rng.uniform(-2.0, 2.0, size=s.shape).astype(np.float32) * s
-        d[rng.random(size=s.shape) < 0.5] = 0.0
-        p.bias[...] = f32_to_bf16_bits(-8.0 * s + d)
-
-
 @pytest.mark.parametrize("name,kw,seed", [
     ("tiny", dict(T=32, H=512, I=128), 1100),
     ("medium_zipf", dict(T=256, H=2048, I=512, zipf_s=1.1), 1101),
@@ -132,7 +120,7 @@ def _asymmetric_bias(inp, seed):
 def test_layer_asymmetric_bias(name, kw, seed):
     print(f"[layer-bias] {name} seed={seed} {kw}", flush=True)
     inp = make_layer(seed, **kw)
-    _asymmetric_bias(inp, seed)
+    asymmetric_bias(inp, seed)
     run = LayerRun(inp).route().gemm().down().sync()
     toks = sample_tokens(inp.T, 32, seed)
     y_ref, ids_ref, _ = oracle.Layer(inp).tokens(toks)
