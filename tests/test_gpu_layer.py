@@ -3,9 +3,10 @@ import numpy as np
 import pytest
 import torch
 
+import bit_quantized_expert_top_amd as moe
 import oracle
 from synth import make_layer
-from moe_case import LayerRun, asymmetric_bias, check_y, f16_np, unpermute_cols
+from moe_case import LayerRun, asymmetric_bias, check_y, device, f16_np, unpermute_cols, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +47,36 @@ def test_layer_matches_oracle(name, kw, seed, nsamp):
     np.testing.assert_array_equal(got["ids"][toks], ids_ref)
     ratio = check_y(y[toks], y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)
+
+
+def test_largest_shape_prefill_and_decode():
+    """The largest supported shape, H = I = 2048 (gate/up over 16 n-tiles, down with K = 2048),
+    through the prefill layer (sampled tokens) and the T=1 decode path on the same weights."""
+    T, H, I, seed = 96, 2048, 2048, 4202
+    print(f"[layer-max] T={T} H={H} I={I}", flush=True)
+    inp = make_layer(seed, T=T, H=H, I=I)
+    dev = device()
+    w = upload(inp, dev)
+    run = LayerRun(inp, w=w).layer().sync()
+    toks = sample_tokens(T, 10, seed)
+    L = oracle.Layer(inp)
+    y_ref, ids_ref, w_ref = L.tokens(toks)
+    got = run.routing_np()
+    np.testing.assert_array_equal(got["ids"][toks], ids_ref)
+    ratio = check_y(run.y.cpu().numpy()[toks], y_ref)
+    print(f"  prefill max err / rms = {ratio:.4g}", flush=True)
+    # token 0 alone through moe_decode
+    sh1 = moe.Shape(T=1, H=H, I=I, E=inp.E, top_k=inp.top_k)
+    ids = torch.empty((1, inp.top_k), dtype=torch.int32, device=dev)
+    tw = torch.empty((1, inp.top_k), dtype=torch.float32, device=dev)
+    y1 = torch.empty((1, H), dtype=torch.float32, device=dev)
+    moe.moe_decode(sh1, run.x[:1].contiguous(), w, ids, tw, y1, moe.workspace(sh1, dev))
+    torch.cuda.synchronize()
+    i0 = toks.index(0)
+    np.testing.assert_array_equal(ids.cpu().numpy()[0], ids_ref[i0])
+    np.testing.assert_allclose(tw.cpu().numpy()[0], w_ref[i0], rtol=2e-5, atol=2e-7)
+    ratio = check_y(y1.cpu().numpy(), y_ref[i0:i0 + 1])
+    print(f"  decode max err / rms = {ratio:.4g}", flush=True)
 
 
 def test_hidden_rows_match_oracle():
