@@ -175,6 +175,22 @@ __device__ inline void wave_topk_radix(const uint32_t (&key)[4], int k, bool (&t
     __builtin_amdgcn_wave_barrier();
 }
 
+// Routing weight of pick p, held by lane p < k (k <= 8) with its fixed-order logit l:
+// the softmax over all experts renormalised over the picks, i.e.
+//   w_p = exp(l_p - l_0) / sum_{j<k} exp(l_j - l_0),
+// evaluated in fp64 (the differences of two fp32 logits are exact there) and rounded
+// once to fp32.  Lanes >= k return 0.  Every lane of the wave must call it.
+__device__ inline float topk_weight(float l, int k) {
+    const int lane = threadIdx.x & 63;
+    const float l0 = __shfl(l, 0);
+    const double p = lane < k ? exp((double)l - (double)l0) : 0.0;
+    double s = p;
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);      // lanes 0..7: the sum over the (at most 8) picks
+    return lane < k ? (float)(p / s) : 0.0f;
+}
+
 // Sum over aligned groups of n lanes (n = 1, 2, 4, 8 or 16) with DPP; every
 // lane of a group ends with the group's sum.
 __device__ __forceinline__ float group_sum_dpp(float v, int n) {

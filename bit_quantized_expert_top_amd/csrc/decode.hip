@@ -119,11 +119,11 @@ __global__ __launch_bounds__(64) void decode_router_kernel(const uint16_t *__res
     if (lane == 0) logits[e] = l;
 }
 
-// Top-k (k <= 8) of E = 256 logits by (logit desc, index asc) and the weights
-// exp(l - l_1) / sum, computed by one wave (all lanes end with the same picks).
-// wl: 32 words of wave-local LDS.
-__device__ void select_topk(const float *__restrict__ logits, int E, int k, int *pick_e,
-                            float *pick_w, uint32_t *wl) {
+// Top-k (k <= 8) of E = 256 logits by (logit desc, index asc), computed by one
+// wave: lane p < k ends with pick p's expert and logit.  wl: 32 words of
+// wave-local LDS.
+__device__ void select_topk(const float *__restrict__ logits, int E, int k, int &pick_e,
+                            float &pick_l, uint32_t *wl) {
     const int lane = threadIdx.x & 63;
     uint32_t key[4];
     bool taken[4];
@@ -132,24 +132,9 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
     for (int j = 0; j < 4; ++j) lv[j] = logits[min(lane + 64 * j, E - 1)];   // one round trip
 #pragma unroll
     for (int j = 0; j < 4; ++j) key[j] = lane + 64 * j < E ? ordered_key(lv[j]) : 0u;
-    int pe;
     uint32_t pkey;
-    wave_topk_radix(key, k, taken, pe, pkey, wl);
-    float pick_l[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        pick_e[r] = r < k ? __builtin_amdgcn_readlane(pe, r) : 0;
-        pick_l[r] = r < k ? key_to_float((uint32_t)__builtin_amdgcn_readlane((int)pkey, r)) : 0.0f;
-    }
-    const float m = pick_l[0];
-    float sum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        pick_w[r] = r < k ? expf(pick_l[r] - m) : 0.0f;
-        sum += pick_w[r];
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) pick_w[r] = pick_w[r] / sum;
+    wave_topk_radix(key, k, taken, pick_e, pkey, wl);
+    pick_l = lane < k ? key_to_float(pkey) : 0.0f;
 }
 
 // scratch: the logits of every token, 256-byte aligned
@@ -162,19 +147,12 @@ __global__ __launch_bounds__(64) void decode_select_kernel(const float *__restri
                                                            float *__restrict__ tw) {
     __shared__ uint32_t wl[32];
     const int t = blockIdx.x, lane = threadIdx.x;
-    int pe[8];
-    float pw[8];
-    select_topk(logits + (size_t)t * E, E, k, pe, pw, wl);
-    int e = 0;
-    float wv = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        if (r == lane) {
-            e = pe[r];
-            wv = pw[r];
-        }
+    int pe;
+    float pl;
+    select_topk(logits + (size_t)t * E, E, k, pe, pl, wl);
+    const float wv = topk_weight(pl, k);
     if (lane < k) {
-        ids[(size_t)t * k + lane] = e;
+        ids[(size_t)t * k + lane] = pe;
         tw[(size_t)t * k + lane] = wv;
     }
 }
@@ -254,24 +232,17 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
         ex = ids_out[slot];                                       // written by decode_select_kernel
         ex = (ex < 0 || ex >= E) ? 0 : ex;
     } else if (slot < k) {
-        int pe[8];
-        float pw[8];
-        select_topk(logits, E, k, pe, pw, selw[wave]);
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-            if (r == slot) ex = pe[r];
+        int pe;
+        float pl;
+        select_topk(logits, E, k, pe, pl, selw[wave]);
+        ex = __builtin_amdgcn_readlane(pe, slot);
         ex = (ex < 0 || ex >= E) ? 0 : ex;
-        if (blockIdx.x == 0 && wave == 0 && lane < k) {
-            int e = 0;
-            float wv = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (r == lane) {
-                    e = pe[r];
-                    wv = pw[r];
-                }
-            ids_out[lane] = e;
-            tw_out[lane] = wv;
+        if (blockIdx.x == 0 && wave == 0) {
+            const float wv = topk_weight(pl, k);
+            if (lane < k) {
+                ids_out[lane] = pe;
+                tw_out[lane] = wv;
+            }
         }
     }
     const uint8_t *tile = slot == k ? pk_sh + (size_t)j * G * PK_BLOCK

@@ -369,6 +369,57 @@ __device__ void recompute_candidates(const uint32_t *cand_e, float *cand_l, int 
     }
 }
 
+// Fixed-order logits of up to 8 experts elist[0..n) of token row xr, with every
+// router row load of the four passes issued at once (a single round trip): half
+// h of the wave takes experts h, 2 + h, 4 + h, 6 + h, lane c of a half chunk c.
+// The chunk partials meet in wave-local LDS (part: 256 floats) and lane i < n
+// adds expert i's in chunk order, then its bias; lane i returns that logit.
+__device__ float exact_logits8(const uint32_t *elist, int n, const uint16_t *__restrict__ xr,
+                               const uint16_t *__restrict__ wr, const float *__restrict__ bias,
+                               int H, int lane, float *part) {
+    const int c = lane & 31, hh = lane >> 5, nch = H / 64;
+    const bool has_chunk = c < nch;
+    u32x4 xv[8], wv[4][8];
+    if (has_chunk) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xv[q] = ((const u32x4 *)(xr + 64 * c))[q];
+    }
+    int ev[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int ci = 2 * p + hh;
+        ev[p] = ci < n ? (int)elist[ci] : -1;
+        if (has_chunk && ev[p] >= 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) wv[p][q] = ((const u32x4 *)(wr + (size_t)ev[p] * H + 64 * c))[q];
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        if (!has_chunk || ev[p] < 0) continue;
+        // sequential within the chunk, from its first product (each fma adds one exact product)
+        float s = bf16_lo(xv[0][0]) * bf16_lo(wv[p][0][0]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (q > 0 || r > 0) s = __builtin_fmaf(bf16_lo(xv[q][r]), bf16_lo(wv[p][q][r]), s);
+                s = __builtin_fmaf(bf16_hi(xv[q][r]), bf16_hi(wv[p][q][r]), s);
+            }
+        part[32 * (2 * p + hh) + c] = s;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float L = 0.0f;
+    if (lane < n) {
+        const float *pp = part + 32 * lane;
+        L = pp[0];
+        for (int q = 1; q < nch; ++q) L = L + pp[q];
+        if (bias) L = L + bias[elist[lane]];
+    }
+    __builtin_amdgcn_wave_barrier();
+    return L;
+}
+
 __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     const float *__restrict__ part, int S, const float *__restrict__ exact,
     const float *__restrict__ xsq, int G, const float *__restrict__ wn2,
@@ -427,7 +478,7 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
         // logit, with a zero radius, and the selection is certified again.
         bool taken[4];
         int my_pick = -1;
-        float my_l = 0.0f, my_lb = 0.0f, my_ub = 0.0f;
+        float my_l = 0.0f, my_lb = 0.0f, my_ub = 0.0f, my_d = 0.0f;
         float m8 = INFINITY;
         bool certified = false;
         for (int round = 0; round < 2; ++round) {
@@ -452,6 +503,7 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                     const float l = cand_l[tl][pe], d = __uint_as_float(cand_e[tl][pe]);
                     my_pick = pe;
                     my_l = key_to_float(pkey);
+                    my_d = d;
                     my_lb = l - d;
                     my_ub = l + d;
                 }
@@ -517,6 +569,22 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
             __builtin_amdgcn_wave_barrier();
         }
         float wl = my_l;   // logit used for the weights (lanes < k)
+        if (certified) {
+            // the weights come from the picks' fixed-order logits: those that still carry
+            // an approximate logit (nonzero radius) are recomputed, 8 rows at most
+            const bool need = lane < k && my_d != 0.0f;
+            const uint64_t bal = __ballot(need);
+            const int pos = (int)__popcll(bal & ((1ull << lane) - 1ull));
+            if (need) cand_e[tl][pos] = (uint32_t)my_pick;
+            const int nc = (int)__popcll(bal);
+            __builtin_amdgcn_wave_barrier();
+            if (nc > 0) {
+                const float L = exact_logits8(cand_e[tl], nc, x + (size_t)t * H, wr, bias, H, lane,
+                                              cand_l[tl]);
+                const float Lp = __shfl(L, pos);
+                if (need) wl = Lp;
+            }
+        }
         if (!certified) {
             // candidates: every expert whose interval reaches m8 (includes the k picks);
             // those not yet exact first (they are recomputed), then the exact ones
@@ -575,12 +643,10 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
             }
         }
         // ---- renormalised softmax over the k picks
-        const float lmax = __shfl(wl, 0);
-        const float pj = (lane < k) ? expf(wl - lmax) : 0.0f;
-        const float sum = wave_sum_f(pj);
+        const float wk = topk_weight(wl, k);
         if (lane < k) {
             ids[(size_t)t * k + lane] = my_pick;
-            tw[(size_t)t * k + lane] = pj / sum;
+            tw[(size_t)t * k + lane] = wk;
             sid[tl][lane] = my_pick;
             atomicOr(&mask[my_pick], 1u << tl);
         }

@@ -102,6 +102,36 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float = TOL):
     return err / rms
 
 
+_ORACLE_CACHE = {}
+
+
+def oracle_tokens(inp, tokens, key=None):
+    """oracle.Layer(inp).tokens(tokens), memoised under `key` (e.g. the seed and shape of a
+    workload that several tests compare against)."""
+    import oracle
+    tokens = list(tokens)
+    if key is not None:
+        k = (key, tuple(tokens))
+        if k not in _ORACLE_CACHE:
+            _ORACLE_CACHE[k] = oracle.Layer(inp).tokens(tokens)
+        return _ORACLE_CACHE[k]
+    return oracle.Layer(inp).tokens(tokens)
+
+
+def check_topk_weights(w_gpu: np.ndarray, w_ref: np.ndarray, ulps: float = 1.0):
+    """Routing weights against the oracle's float64 values: within `ulps` units in the last
+    place of the float32 value (the kernels evaluate the renormalised softmax in float64 from
+    the fixed-order logits and round once), and every token's weights sum to 1 within 1e-6."""
+    w_gpu = np.asarray(w_gpu, np.float32)
+    ref32 = np.abs(w_ref).astype(np.float32)
+    ulp = np.maximum(np.spacing(ref32), np.spacing(np.nextafter(ref32, np.float32(0))))
+    err = np.abs(w_gpu.astype(np.float64) - w_ref)
+    worst = float(np.max(err / ulp)) if err.size else 0.0
+    assert worst <= ulps, f"routing weight off by {worst:.3g} ulp (limit {ulps})"
+    assert np.all(np.abs(w_gpu.astype(np.float64).sum(axis=-1) - 1.0) <= 1e-6)
+    return worst
+
+
 def asymmetric_bias(inp, seed):
     """Biases b = bf16(-8 s + d) with d ~ U(-2s, 2s) in a random half of the groups
     (the rest keep b = -8 s), so the GEMMs' rank-G bias term is exercised."""

@@ -1,7 +1,7 @@
 """Chunked prefill (moe_layer_chunked): the layer over consecutive token chunks with a
 workspace sized by the chunk.  Every token's routing and output depend on that token
 alone, so the chunked layer must equal the single-call layer bit for bit; it is also
-held to the oracle on sampled tokens."""
+held to the oracle on every token."""
 import numpy as np
 import pytest
 import torch
@@ -31,10 +31,8 @@ def test_chunked_equals_single_call_and_oracle(T, H, I, chunk, zipf, seed):
     moe.moe_layer_chunked(sh, run.x, run.w, y, chunk, ws)
     torch.cuda.synchronize()
     assert torch.equal(y, run.y), "chunked layer differs from the single call"
-    rng = np.random.default_rng(seed)
-    toks = sorted(set(rng.choice(T, size=min(T, 40), replace=False).tolist()) | {0, T - 1})
-    y_ref, _, _ = oracle.Layer(inp).tokens(toks)
-    ratio = check_y(y.cpu().numpy()[toks], y_ref)
+    y_ref, _, _ = oracle.Layer(inp).tokens(range(T))
+    ratio = check_y(y.cpu().numpy(), y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)
 
 
@@ -70,7 +68,6 @@ def test_chunked_asymmetric_bias():
     moe.moe_layer_chunked(sh, run.x, run.w, y, chunk, ws)
     torch.cuda.synchronize()
     assert torch.equal(y, run.y), "chunked layer differs from the single call"
-    toks = [0, 1, 191, 192, 383, 384, 499]
-    y_ref, _, _ = oracle.Layer(inp).tokens(toks)
-    ratio = check_y(y.cpu().numpy()[toks], y_ref)
+    y_ref, _, _ = oracle.Layer(inp).tokens(range(T))
+    ratio = check_y(y.cpu().numpy(), y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)

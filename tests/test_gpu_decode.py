@@ -6,7 +6,7 @@ import torch
 import bit_quantized_expert_top_amd as moe
 import oracle
 from synth import make_layer
-from moe_case import LayerRun, asymmetric_bias, check_y, device, shape_of, upload, x_dev
+from moe_case import LayerRun, asymmetric_bias, check_topk_weights, check_y, device, shape_of, upload, x_dev
 from synth.inputs import bf16_bits_to_f32
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,7 @@ def test_decode_matches_oracle(seed):
     ids, tw, y = run_decode(inp)
     y_ref, ids_ref, w_ref = oracle.Layer(inp).tokens([0])
     np.testing.assert_array_equal(ids, ids_ref[0])
-    np.testing.assert_allclose(tw, w_ref[0], rtol=2e-5, atol=2e-7)
+    check_topk_weights(tw, w_ref[0])
     ratio = check_y(y[None, :], y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)
 
@@ -127,7 +127,7 @@ def test_small_batch_decode_matches_oracle(T, seed, zipf):
     ids, tw, y = run_decode(inp)
     y_ref, ids_ref, w_ref = oracle.Layer(inp).tokens(range(T))
     np.testing.assert_array_equal(ids, ids_ref)
-    np.testing.assert_allclose(tw, w_ref, rtol=2e-5, atol=2e-7)
+    check_topk_weights(tw, w_ref)
     ratio = check_y(y, y_ref)
     print(f"  max err / rms = {ratio:.4g}, distinct experts = {len(set(ids.ravel().tolist()))}",
           flush=True)
@@ -145,7 +145,7 @@ def test_decode_asymmetric_bias(T, seed):
     if T == 1:
         ids, tw, y = ids[None], tw[None], y[None]
     np.testing.assert_array_equal(ids, ids_ref)
-    np.testing.assert_allclose(tw, w_ref, rtol=2e-5, atol=2e-7)
+    check_topk_weights(tw, w_ref)
     ratio = check_y(y, y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)
 

@@ -6,7 +6,8 @@ import torch
 import bit_quantized_expert_top_amd as moe
 import oracle
 from synth import make_layer
-from moe_case import LayerRun, asymmetric_bias, check_y, device, f16_np, unpermute_cols, upload
+from moe_case import (LayerRun, asymmetric_bias, check_topk_weights, check_y, device, f16_np,
+                      oracle_tokens, unpermute_cols, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,33 +21,80 @@ def sample_tokens(T, n, seed):
 
 
 CASES = [
-    ("tiny", dict(T=32, H=512, I=128), 1000, 32),
-    ("tiny_zipf", dict(T=32, H=512, I=128, zipf_s=1.1), 1001, 32),
-    ("ragged129", dict(T=129, H=512, I=128, zipf_s=1.1), 1003, 129),
-    ("T1_prefill_path", dict(T=1, H=2048, I=512), 2001, 1),
-    ("prefill512", dict(T=512, H=2048, I=512), 3000, 40),
-    ("prefill2048_zipf", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4000, 40),
+    ("tiny", dict(T=32, H=512, I=128), 1000),
+    ("tiny_zipf", dict(T=32, H=512, I=128, zipf_s=1.1), 1001),
+    ("ragged129", dict(T=129, H=512, I=128, zipf_s=1.1), 1003),
+    ("T1_prefill_path", dict(T=1, H=2048, I=512), 2001),
+    ("prefill512", dict(T=512, H=2048, I=512), 3000),
+    ("prefill2048_zipf", dict(T=2048, H=2048, I=512, zipf_s=1.1), 4000),
     # one layer of the 40-layer stack workload (T=4096, random router)
-    ("stack_layer_T4096", dict(T=4096, H=2048, I=512), 5000, 40),
+    ("stack_layer_T4096", dict(T=4096, H=2048, I=512), 5000),
     # narrow H (one router chunk per K quarter, one down tile), wide I, ragged T
-    ("narrowH_wideI", dict(T=77, H=256, I=1024), 4200, 40),
+    ("narrowH_wideI", dict(T=77, H=256, I=1024), 4200),
     # H not a power of two, I = 3 x 128
-    ("H768_I384", dict(T=200, H=768, I=384, zipf_s=1.1), 4201, 40),
+    ("H768_I384", dict(T=200, H=768, I=384, zipf_s=1.1), 4201),
 ]
 
 
-@pytest.mark.parametrize("name,kw,seed,nsamp", CASES, ids=[c[0] for c in CASES])
-def test_layer_matches_oracle(name, kw, seed, nsamp):
+@pytest.mark.parametrize("name,kw,seed", CASES, ids=[c[0] for c in CASES])
+def test_layer_matches_oracle(name, kw, seed):
+    """Every output of the layer (all T x H values) against the oracle."""
     print(f"[layer] {name} seed={seed} {kw}", flush=True)
     inp = make_layer(seed, **kw)
     run = LayerRun(inp).layer().sync()
     y = run.y.cpu().numpy()
-    toks = sample_tokens(inp.T, nsamp, seed)
-    y_ref, ids_ref, _ = oracle.Layer(inp).tokens(toks)
+    y_ref, ids_ref, w_ref = oracle_tokens(inp, range(inp.T), key=(seed, name))
     got = run.routing_np()
-    np.testing.assert_array_equal(got["ids"][toks], ids_ref)
-    ratio = check_y(y[toks], y_ref)
+    np.testing.assert_array_equal(got["ids"], ids_ref)
+    check_topk_weights(got["w"], w_ref)
+    ratio = check_y(y, y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)
+
+
+def test_prefill_graph_replays_two_weight_sets():
+    """The timed form of the prefill step: two layers with independently seeded weights share
+    the routing buffers, the workspace and h, captured together in one HIP graph.  Each of three
+    replays reproduces the eager outputs bit for bit (the GEMM work-queue counters re-arm
+    between launches), and the outputs match the oracle on every token."""
+    kw = dict(T=2048, H=2048, I=512, zipf_s=1.1)
+    print(f"[graph] prefill2048_zipf, weight sets 4000 and 4100", flush=True)
+    inp_a = make_layer(4000, **kw)
+    inp_b = make_layer(4100, **kw)
+    inp_b.x = inp_a.x
+    dev = device()
+    wa, wb = upload(inp_a, dev), upload(inp_b, dev)
+    run = LayerRun(inp_a, w=wa)
+    ya = torch.zeros_like(run.y)
+    yb = torch.zeros_like(run.y)
+
+    def step(w, y):
+        moe.moe_layer(run.shape, run.x, w, run.r, run.h, y, run.ws)
+
+    step(wa, ya)
+    step(wb, yb)
+    torch.cuda.synchronize()
+    ya_e, yb_e = ya.clone(), yb.clone()
+    routing_b = run.routing_np()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(wa, ya)
+        step(wb, yb)
+    for rep in range(3):
+        ya.zero_()
+        yb.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ya, ya_e) and torch.equal(yb, yb_e), f"replay {rep} differs from eager"
+        got = run.routing_np()
+        for key in ("ids", "w", "row_token", "tok_row", "blocks"):
+            np.testing.assert_array_equal(got[key], routing_b[key], err_msg=key)
+    del g
+    for inp, y, name in ((inp_a, ya_e, "a"), (inp_b, yb_e, "b")):
+        y_ref, _, _ = oracle_tokens(inp, range(inp.T),
+                                    key=(4000, "prefill2048_zipf") if name == "a" else None)
+        ratio = check_y(y.cpu().numpy(), y_ref)
+        print(f"  set {name}: max err / rms = {ratio:.4g}", flush=True)
 
 
 def test_largest_shape_prefill_and_decode():
@@ -58,7 +106,7 @@ def test_largest_shape_prefill_and_decode():
     dev = device()
     w = upload(inp, dev)
     run = LayerRun(inp, w=w).layer().sync()
-    toks = sample_tokens(T, 10, seed)
+    toks = list(range(T))
     L = oracle.Layer(inp)
     y_ref, ids_ref, w_ref = L.tokens(toks)
     got = run.routing_np()
@@ -74,7 +122,7 @@ def test_largest_shape_prefill_and_decode():
     torch.cuda.synchronize()
     i0 = toks.index(0)
     np.testing.assert_array_equal(ids.cpu().numpy()[0], ids_ref[i0])
-    np.testing.assert_allclose(tw.cpu().numpy()[0], w_ref[i0], rtol=2e-5, atol=2e-7)
+    check_topk_weights(tw.cpu().numpy()[0], w_ref[i0])
     ratio = check_y(y1.cpu().numpy(), y_ref[i0:i0 + 1])
     print(f"  decode max err / rms = {ratio:.4g}", flush=True)
 
@@ -127,7 +175,7 @@ def test_layer_all_tokens_one_expert_set():
     run = LayerRun(inp).layer().sync()
     got = run.routing_np()
     assert got["num_blocks"] == 8 * 3
-    toks = sample_tokens(inp.T, 60, 1)
+    toks = list(range(inp.T))
     y_ref, _, _ = oracle.Layer(inp).tokens(toks)
     check_y(run.y.cpu().numpy()[toks], y_ref)
 
@@ -153,7 +201,7 @@ def test_layer_asymmetric_bias(name, kw, seed):
     inp = make_layer(seed, **kw)
     asymmetric_bias(inp, seed)
     run = LayerRun(inp).route().gemm().down().sync()
-    toks = sample_tokens(inp.T, 32, seed)
+    toks = list(range(inp.T))
     y_ref, ids_ref, _ = oracle.Layer(inp).tokens(toks)
     got = run.routing_np()
     np.testing.assert_array_equal(got["ids"][toks], ids_ref)

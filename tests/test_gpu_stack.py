@@ -15,7 +15,12 @@ from synth.inputs import bf16_bits_to_f32
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,H,I,layers,nsamp", [(64, 512, 128, 4, 64), (256, 2048, 512, 3, 48)])
+@pytest.mark.parametrize("T,H,I,layers,nsamp", [
+    (64, 512, 128, 4, 64),
+    (256, 2048, 512, 3, 256),
+    # the stack workload's own shape (T=4096), three layers, a quarter of the tokens each
+    (4096, 2048, 512, 3, 1024),
+])
 def test_stack_teacher_forced(T, H, I, layers, nsamp):
     print(f"[stack] T={T} H={H} I={I} layers={layers}", flush=True)
     dev = device()

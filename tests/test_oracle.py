@@ -457,3 +457,40 @@ def test_rmsnorm_closed_form():
     np.testing.assert_allclose((uf ** 2).mean(axis=1), ms / (ms + eps), rtol=2 ** -7)
     ref = r_out / np.sqrt(ms + eps)[:, None]
     assert np.all(np.abs(uf - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+def _bf16_rne_direct(v):
+    """float64 -> nearest bfloat16 value (8 significant bits), ties to even, written from the
+    format's definition: v = m 2^e with m in [0.5, 1), kept as round_half_even(m 2^8) 2^(e-8).
+    Also returns the distance of m 2^8 from the nearest tie, to flag near-ties."""
+    m, e = np.frexp(v)
+    scaled = m * 256.0
+    k = np.rint(scaled)                                   # numpy rounds halves to even
+    frac = np.abs(scaled - np.floor(scaled) - 0.5)
+    return np.ldexp(k, e - 8), frac
+
+
+@pytest.mark.parametrize("H,eps", [(2048, 1e-6), (64, 1e-6), (512, 0.25), (96, 3.0)])
+def test_rmsnorm_bit_exact_direct_rounding(H, eps):
+    """u bit for bit against the definition r/sqrt(mean(r^2) + eps) evaluated in float64 and
+    rounded once to bfloat16 (the oracle rounds through float32 first, which can only differ at
+    near-ties, skipped here).  A large eps and a short row make eps and the 1/H of the mean
+    visible in most roundings (a missing eps or a mean over H - 1 fails)."""
+    rng = np.random.default_rng(H + 7)
+    T = 16
+    r = rng.standard_normal((T, H)) * 1.5
+    y = rng.standard_normal((T, H)) * 0.5
+    r_out, u = oracle.rmsnorm_residual(r, y, eps)
+    s = r + y
+    ms = np.array([sum(float(v) * float(v) for v in row) for row in s]) / H
+    ref, frac = _bf16_rne_direct(s / np.sqrt(ms + eps)[:, None])
+    got = bf16_bits_to_f32(u).astype(np.float64)
+    near_tie = frac < 1e-9
+    assert near_tie.mean() < 1e-3
+    np.testing.assert_array_equal(got[~near_tie], ref[~near_tie])
+    # the rounding really depends on eps and on the 1/H of the mean
+    alt, _ = _bf16_rne_direct(s / np.sqrt(ms * H / (H - 1) + eps)[:, None])
+    assert np.mean(alt != ref) > 0.005
+    if eps > 1e-3:
+        alt, _ = _bf16_rne_direct(s / np.sqrt(ms)[:, None])
+        assert np.mean(alt != ref) > 0.05
