@@ -55,6 +55,7 @@ _SIGS = {
     "moe_layer_chunked": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, i32, P, C.c_size_t, P],
                           i32),
     "moe_decode": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, P, P, P, C.c_size_t, P], i32),
+    "moe_decode_static": ([C.POINTER(_Shape), P, C.POINTER(_Weights), P, P, P, P], i32),
     "moe_decode_residual": ([C.POINTER(_Shape), P, P, C.c_float, P, C.POINTER(_Weights), P, P, P, P,
                              C.c_size_t, P], i32),
     "moe_rmsnorm_residual": ([i32, i32, C.c_float, P, P, P, P], i32),
@@ -334,6 +335,21 @@ def moe_decode(shape: Shape, x: torch.Tensor, w: DeviceLayer, ids: torch.Tensor,
     _check(lib().moe_decode(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
                             _ptr(ids, _I32, "ids"), _ptr(tw, _F32, "topk_w"), _ptr(y, _F32, "y"),
                             _ptr(ws, None, "ws"), ws.numel(), _stream(stream)), "moe_decode")
+
+
+def moe_decode_static(shape: Shape, x: torch.Tensor, w: DeviceLayer, ids: torch.Tensor,
+                      tw: torch.Tensor, y: torch.Tensor, stream=None):
+    """moe_decode without a workspace: the library's own per-GPU scratch array (calls that
+    overlap on one GPU race)."""
+    T, H, k = shape.T, shape.H, shape.top_k
+    _args(shape, w)
+    _need(x, T * H, "x")
+    _need(ids, T * k, "ids")
+    _need(tw, T * k, "topk_w")
+    _need(y, T * H, "y")
+    _check(lib().moe_decode_static(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
+                                   _ptr(ids, _I32, "ids"), _ptr(tw, _F32, "topk_w"),
+                                   _ptr(y, _F32, "y"), _stream(stream)), "moe_decode_static")
 
 
 def moe_decode_residual(shape: Shape, r: torch.Tensor, y_prev: torch.Tensor, eps: float,

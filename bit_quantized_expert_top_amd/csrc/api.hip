@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -328,6 +329,52 @@ moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weigh
     MOE_TRY(check_ws(shape, ws, ws_bytes));
     const WsLayout L = ws_layout(shape->T, shape->H, shape->I, shape->E, shape->top_k);
     launch_decode(*shape, x, *w, topk_ids, topk_w, y, (char *)ws + L.dec, (hipStream_t)stream);
+    return launched();
+}
+
+}  // extern "C"
+
+// ---- decode without a caller workspace ----
+// The decode kernels' scratch (each token's router logits and its nine h rows) in a
+// file-scope device array, sized for the largest decode call the API admits (8 tokens,
+// H = I = 2048).  Each GPU holds its own copy until the process ends.  Host code never
+// passes the array's name to a kernel: it is a host-side stand-in for the symbol.  The
+// device address is looked up once per device (with that device current) and cached.
+namespace {
+constexpr size_t kStaticScratchBytes = 303104;     // decode_scratch_bytes(8, 2048, 2048, 8)
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+moe_status static_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_static(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                             int32_t *topk_ids, float *topk_w, float *y, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (shape->T > kDecodeMaxT) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(topk_ids) || !aligned(topk_w) || !aligned(y))
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, true, true, true));
+    if (decode_scratch_bytes(shape->T, shape->H, shape->I, shape->top_k) > kStaticScratchBytes)
+        return MOE_ERR_WORKSPACE;
+    void *sp = nullptr;
+    MOE_TRY(static_scratch(&sp));
+    launch_decode(*shape, x, *w, topk_ids, topk_w, y, sp, (hipStream_t)stream);
     return launched();
 }
 

@@ -49,10 +49,11 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
  *     only ENQUEUES work on `stream`; none synchronises or copies
  *     device->host.  The caller owns every buffer; the library never
- *     allocates, frees or caches device memory and keeps no global state,
- *     so calls on different streams are independent as long as they use
- *     different workspaces (a workspace holds a call's scratch rows and the
- *     GEMMs' work-queue counters: two calls in flight on one workspace race).
+ *     allocates, frees or caches device memory, so calls on different streams
+ *     are independent as long as they use different workspaces (a workspace
+ *     holds a call's scratch rows and the GEMMs' work-queue counters: two
+ *     calls in flight on one workspace race).  The only global state is the
+ *     per-GPU scratch array of moe_decode_static (see there).
  *   - Errors: arguments are validated on the host before anything is
  *     enqueued; a call that returns an error has enqueued nothing.
  *     MOE_ERR_INVALID_ARG: NULL or misaligned pointer, T < 1, bad sizes.
@@ -220,6 +221,20 @@ moe_status moe_layer_chunked(const moe_shape *shape, const uint16_t *x, const mo
 moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                       int32_t *topk_ids, float *topk_w, float *y, void *ws, size_t ws_bytes,
                       void *stream);
+
+/* moe_decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  It takes no
+ * workspace; the decode scratch (each token's 256 router logits and its nine h rows,
+ * at most 303104 bytes for 8 tokens at H = I = 2048) lives in a device array inside
+ * the library, one per GPU, held until the process ends.  Arguments, layout and
+ * results are those of moe_decode, bit for bit.  The call allocates nothing; its first
+ * call on a device looks up that device's array address (hipGetSymbolAddress) once.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (several streams, or several host threads) race and must be serialised by the
+ * caller.  MOE_ERR_INVALID_ARG for T > 8 (and as moe_decode otherwise); MOE_ERR_HIP
+ * if the array's address cannot be obtained. */
+moe_status moe_decode_static(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                             int32_t *topk_ids, float *topk_w, float *y, void *stream);
 
 /* One layer of a decode stack after the first (the stacked-layer workload: a
  * residual add and RMSNorm with unit weight between MoE layers), with the add

@@ -155,6 +155,19 @@ def test_decode_token_limit():
                         need3, None) == INVALID
 
 
+def test_decode_static_validation_before_launch():
+    """moe_decode_static refuses what moe_decode refuses, before it looks up its scratch."""
+    L = B.lib()
+    assert L.moe_decode_static(C.byref(shape(T=9)), FAKE, C.byref(_weights()), FAKE, FAKE, FAKE,
+                               None) == INVALID
+    assert L.moe_decode_static(C.byref(shape(T=1, bits=8)), FAKE, C.byref(_weights()), FAKE, FAKE,
+                               FAKE, None) == UNSUP
+    assert L.moe_decode_static(C.byref(shape(T=1)), FAKE, C.byref(_weights("null_packed")), FAKE,
+                               FAKE, FAKE, None) == INVALID
+    assert L.moe_decode_static(C.byref(shape(T=1)), None, C.byref(_weights()), FAKE, FAKE, FAKE,
+                               None) == INVALID
+
+
 def test_misc_validation():
     L = B.lib()
     assert L.moe_rmsnorm_residual(0, 2048, 1e-6, FAKE, FAKE, FAKE, None) == INVALID
