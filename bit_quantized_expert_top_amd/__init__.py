@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     MoeError,
     Routing,
     Shape,
+    UnsupportedWeights,
     lib,
     moe_decode,
     moe_decode_residual,

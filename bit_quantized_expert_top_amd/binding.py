@@ -42,7 +42,7 @@ _lib = None
 _SIGS = {
     "moe_query": ([C.POINTER(_Shape), C.POINTER(C.c_size_t), C.POINTER(i32), C.POINTER(i32)], i32),
     "moe_packed_bytes": ([C.POINTER(_Shape), C.POINTER(C.c_size_t)], i32),
-    "moe_pack_weights": ([C.POINTER(_Shape), C.POINTER(_Weights), P, C.c_size_t, P], i32),
+    "moe_pack_weights": ([C.POINTER(_Shape), C.POINTER(_Weights), P, C.c_size_t, P, P], i32),
     "moe_route": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, C.c_size_t,
                    P], i32),
     "moe_expert_gemm_q4": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P,
@@ -84,6 +84,21 @@ class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {moe_status_str(status)} ({status})")
+
+
+PACK_FLAGS = {1: "a scale or bias is NaN or infinite",
+              2: "a row's nonzero scales span more than 2^23",
+              4: "a bias times the row's power-of-two scale leaves the bf16 range"}
+
+
+class UnsupportedWeights(MoeError):
+    """moe_pack_weights refused the weights (its status word is nonzero)."""
+
+    def __init__(self, flags: int):
+        self.flags = flags
+        why = "; ".join(t for b, t in PACK_FLAGS.items() if flags & b) or f"flags {flags}"
+        RuntimeError.__init__(self, f"moe_pack_weights: unsupported weights ({why})")
+        self.status = -2
 
 
 def moe_status_str(status: int) -> str:
@@ -219,9 +234,14 @@ class DeviceLayer:
         self.packed = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         off = (-self.packed.data_ptr()) % 256               # 256-byte aligned start
         self.packed = self.packed[off:off + nbytes]
+        status = torch.full((1,), -1, dtype=torch.int32, device=device)
         _check(lib().moe_pack_weights(C.byref(self.shape.c()), C.byref(self.c()),
-                                      self.packed.data_ptr(), nbytes, _stream(None)),
-               "moe_pack_weights")
+                                      self.packed.data_ptr(), nbytes, status.data_ptr(),
+                                      _stream(None)), "moe_pack_weights")
+        # the format is validated at load: refuse weights the kernels cannot take as documented
+        self.status = int(status.cpu()[0])
+        if self.status != 0:
+            raise UnsupportedWeights(self.status)
         if not keep_rows:
             torch.cuda.current_stream().synchronize()
             self.t = None

@@ -40,6 +40,9 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.lrank = take((size_t)T * k * 4);
     L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
     L.qctl = take((size_t)QCTL_WORDS * 4);
+    L.xmx = take((size_t)T * (H / 64) * 4);
+    L.tok = take((size_t)T * 2 * 4);
+    L.hexp = take((size_t)(T * k + T) * 4);
     L.dec = take(T <= kDecodeMaxT ? decode_scratch_bytes(T, H, I, k) : 0);
     L.total = off;
     return L;
@@ -152,17 +155,22 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
     int32_t *lrank = (int32_t *)(ws + L.lrank);
     float *xsq = (float *)(ws + L.xsq);
     if (r->logits) {
-        launch_prep_act(x, s->T, s->H, (uint16_t *)(ws + L.xp), (float *)(ws + L.xsum), xsq, st);
+        launch_prep_act(x, s->T, s->H, (uint16_t *)(ws + L.xp), (float *)(ws + L.xsum), xsq,
+                        (float *)(ws + L.xmx), st);
         // every logit requested: compute them all in the fixed order, select on them directly
         launch_router_logits(x, w->router_wt, w->router_bias, s->T, s->H, s->E, r->logits, st);
         launch_route_select(nullptr, r->logits, xsq, nullptr, w->router_bias, x, w->router_wt,
-                            s->T, s->H, s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank, st);
+                            s->T, s->H, s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank,
+                            (const float *)(ws + L.xmx), (uint16_t *)(ws + L.xp),
+                            (float *)(ws + L.xsum), (float *)(ws + L.tok), st);
     } else {
         float *part = (float *)(ws + L.part), *wn2 = (float *)(ws + L.wn2);
         launch_router_fast(x, w->router_wt, s->T, s->H, s->E, part, wn2, (uint16_t *)(ws + L.xp),
-                           (float *)(ws + L.xsum), xsq, st);
+                           (float *)(ws + L.xsum), xsq, (float *)(ws + L.xmx), st);
         launch_route_select(part, nullptr, xsq, wn2, w->router_bias, x, w->router_wt, s->T, s->H,
-                            s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank, st);
+                            s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank,
+                            (const float *)(ws + L.xmx), (uint16_t *)(ws + L.xp),
+                            (float *)(ws + L.xsum), (float *)(ws + L.tok), st);
     }
     launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, lrank, s->T, s->E, s->top_k, kBM,
                         r->counts, r->offsets, r->row_token, r->tok_row, r->row_w, r->blocks,
@@ -173,12 +181,13 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
 moe_status enqueue_gateup(const moe_shape *s, const uint16_t *x, const moe_weights *w,
                           const moe_routing *r, uint16_t *h, char *ws, hipStream_t st) {
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
-    (void)x;
-    const PackLayout P = pack_layout(s->H, s->I, s->E);
-    const uint8_t *pk = (const uint8_t *)w->packed;
-    launch_gateup(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum), pk + P.gu,
-                  pk + P.sh_gu, r->blocks, r->num_blocks, (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
-                  max_blocks_for(s->T, s->E, s->top_k), r->row_token, h, (float *)(ws + L.hsum), st);
+    (void)x;   // the GEMM reads moe_route's prepared copy of x in the workspace
+    const GemmWeights gw = gemm_weights(w->packed, s->H, s->I, s->E, true);
+    launch_gateup(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum),
+                  (const float *)(ws + L.tok), gw, r->blocks, r->num_blocks,
+                  (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
+                  max_blocks_for(s->T, s->E, s->top_k), r->row_token, h, (float *)(ws + L.hsum),
+                  (float *)(ws + L.hexp), st);
     return launched();
 }
 
@@ -187,10 +196,10 @@ moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
     // group sums of h: left in the workspace by the gate/up pass
     const float *hsum = (const float *)(ws + L.hsum);
-    const PackLayout P = pack_layout(s->H, s->I, s->E);
-    const uint8_t *pk = (const uint8_t *)w->packed;
-    launch_down(*s, h, hsum, pk + P.down, pk + P.sh_down, r->blocks, r->num_blocks,
-                (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl), max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
+    const GemmWeights gw = gemm_weights(w->packed, s->H, s->I, s->E, false);
+    launch_down(*s, h, hsum, (const float *)(ws + L.hexp), gw, r->blocks, r->num_blocks,
+                (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
+                max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
                 (uint16_t *)(ws + L.stage), y, st);
     return launched();
 }
@@ -217,7 +226,7 @@ moe_status moe_packed_bytes(const moe_shape *shape, size_t *packed_bytes) {
 }
 
 moe_status moe_pack_weights(const moe_shape *shape, const moe_weights *w, void *packed,
-                            size_t packed_bytes, void *stream) {
+                            size_t packed_bytes, int32_t *status, void *stream) {
     MOE_TRY(check_shape(shape));
     if (!w || !(q4_ok(w->gate) && q4_ok(w->up) && q4_ok(w->down) && q4_ok(w->sh_gate) &&
                 q4_ok(w->sh_up) && q4_ok(w->sh_down)))
@@ -225,7 +234,8 @@ moe_status moe_pack_weights(const moe_shape *shape, const moe_weights *w, void *
     if (!packed || (((uintptr_t)packed) & 255u) != 0 ||
         packed_bytes < pack_layout(shape->H, shape->I, shape->E).total)
         return MOE_ERR_INVALID_ARG;
-    launch_pack(*shape, *w, (uint8_t *)packed, (hipStream_t)stream);
+    if (status && (((uintptr_t)status) & 3u) != 0) return MOE_ERR_INVALID_ARG;
+    launch_pack(*shape, *w, (uint8_t *)packed, status, (hipStream_t)stream);
     return launched();
 }
 
@@ -341,7 +351,7 @@ moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weigh
 // passes the array's name to a kernel: it is a host-side stand-in for the symbol.  The
 // device address is looked up once per device (with that device current) and cached.
 namespace {
-constexpr size_t kStaticScratchBytes = 303104;     // decode_scratch_bytes(8, 2048, 2048, 8)
+constexpr size_t kStaticScratchBytes = decode_scratch_size(kDecodeMaxT, 2048, 8);   // 303616
 constexpr int kMaxDevices = 64;
 __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 std::mutex g_scratch_mu;

@@ -23,6 +23,14 @@ constexpr int kBM = 128;        // rows per routing block (GEMM M tile)
 constexpr int kTB = 8;          // tokens per routing token block (one wave each)
 constexpr int kDecodeMaxT = 8;  // moe_decode: tokens per call (each an independent GEMV problem)
 
+// Decode scratch for T tokens (E = 256 experts, k + 1 slots): the router logits, the h
+// rows and the per-slot h factors, each part rounded up to 256 bytes.
+constexpr size_t decode_scratch_size(int T, int I, int k) {
+    return (((size_t)T * 256 * 4 + 255) & ~(size_t)255) +
+           (((size_t)T * (k + 1) * I * 2 + 255) & ~(size_t)255) +
+           (((size_t)T * (k + 1) * 4 + 255) & ~(size_t)255);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -201,6 +209,14 @@ __device__ __forceinline__ float group_sum_dpp(float v, int n) {
     return v;
 }
 
+// Maximum over aligned groups of 8 lanes with DPP; every lane of a group ends with it.
+__device__ __forceinline__ float group_max_dpp8(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    return v;
+}
+
 // Activations enter the GEMMs with every 8-column block stored in the order
 // (0,4,1,5,2,6,3,7), matching the pair order in which 4-bit codes unpack.
 // Position of column `col` in that storage.
@@ -223,13 +239,33 @@ constexpr int QCTL_WORDS = 4 * QCTL_LINE;
 // with moe_pack_weights).
 constexpr int PK_BLOCK = 9216;
 constexpr int PK_CODES = 8192;      // byte offset of the scales; biases at +512
+// Per projection row (one GEMM column), two power-of-two factors written at load time:
+//  colk = 2^-k: the block holds scale and bias times 2^k, with k chosen so that the
+//         row's largest |scale| times 2^k lies in [2^10, 2^11); the rebuilt fp16
+//         weights (q - 8) s 2^k are then exact whenever the row's nonzero scales span
+//         at most 2^23, whatever their absolute size; results are multiplied by colk;
+//  colc = 2^-sigma: scale of c = (b + 8 s) 2^k in the rank-G bias pass, so that every
+//         |c| colc < 2^14 (its fp16 hi/lo split cannot overflow).
+// They are stored per tile: [colk of the 256 columns][colc of the 256 columns].
+constexpr int PK_COLF = 512;        // floats of column factors per tile
+// Load-time validation flags (the status word of the meta section)
+constexpr int PK_BAD_NONFINITE = 1;     // a scale or bias is NaN or infinite
+constexpr int PK_BAD_SCALE_SPAN = 2;    // a row's nonzero scales span more than 2^23
+constexpr int PK_BAD_BIAS_RANGE = 4;    // a bias times 2^k leaves the bf16 range
+constexpr int PK_EMETA = 4;         // floats per expert slot in the meta section
 struct PackLayout {
-    size_t gu, sh_gu, down, sh_down, total;   // byte offsets of the four sections
+    size_t gu, sh_gu, down, sh_down;        // tile-layout blocks of the four sections
+    size_t status;                          // int32 validation flags (one 256-byte line)
+    size_t emeta;                           // float [E+1][PK_EMETA]: [0] bounds the L2 norm
+                                            // of every gate and up row of the expert slot
+    size_t cgu, csh_gu, cdown, csh_down;    // column factors, per tile [PK_COLF] floats
+    size_t total;
 };
 PackLayout pack_layout(int H, int I, int E);
 // column c of a gate/up block of tile j: projection (c >> 5) & 1 (0 gate,
 // 1 up), row 128 j + 32 (c >> 6) + (c & 31); of a down block: row 256 j + c
-void launch_pack(const moe_shape &sh, const moe_weights &w, uint8_t *dst, hipStream_t s);
+void launch_pack(const moe_shape &sh, const moe_weights &w, uint8_t *dst, int32_t *status,
+                 hipStream_t s);
 
 // Workspace layout (byte offsets), shared by route/gemm/decode.  All host-known.
 struct WsLayout {
@@ -245,6 +281,9 @@ struct WsLayout {
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
     size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (by cost class)
     size_t qctl;        // int32 [64]             GEMM work-queue counters and class counts
+    size_t xmx;         // fp32 [T][H/64]         group maxima of |x|
+    size_t tok;         // fp32 [T][2]            per token: 2^e (x enters the GEMM as x 2^-e), ||x||
+    size_t hexp;        // fp32 [T*k + T]         per h row: 2^f (h is stored as h 2^-f)
     size_t dec;         // decode scratch
     size_t total;
 };
@@ -256,18 +295,20 @@ int max_blocks_for(int T, int E, int k);
 void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *bias, int T, int H,
                           int E, float *logits, hipStream_t s);
 void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
-                        float *wn2part, uint16_t *xp, float *xsum, float *xsq, hipStream_t s);
+                        float *wn2part, uint16_t *xp, float *xsum, float *xsq, float *xmx,
+                        hipStream_t s);
 void launch_route_select(const float *part, const float *exact, const float *xsq,
                          const float *wn2, const float *bias, const uint16_t *x,
                          const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,
-                         int32_t *blk_cnt, int32_t *lrank, hipStream_t s);
+                         int32_t *blk_cnt, int32_t *lrank, const float *xmx, uint16_t *xp,
+                         float *xsum, float *tok, hipStream_t s);
 void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
                          int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
                          int32_t *blocks, int32_t *num_blocks, int32_t *sched, int32_t *qctl,
                          hipStream_t s);
 void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
-                     hipStream_t s);
+                     float *xmx, hipStream_t s);
 
 struct GemmProj {
     const uint32_t *q;
@@ -275,15 +316,67 @@ struct GemmProj {
     const uint16_t *b;
 };
 
-void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum,
-                   const uint8_t *pk, const uint8_t *pk_sh, const int32_t *blocks,
-                   const int32_t *num_blocks, const int32_t *sched, int32_t *qctl, int max_blocks,
-                   const int32_t *row_token, uint16_t *h, float *hsum, hipStream_t s);
-void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const uint8_t *pk,
-                 const uint8_t *pk_sh, const int32_t *blocks, const int32_t *num_blocks,
+// The expert weights of one GEMM: tile-layout blocks and column factors of the routed
+// experts and of the shared expert, and the per-expert meta (gate/up only).
+struct GemmWeights {
+    const uint8_t *pk, *pk_sh;
+    const float *colf, *colf_sh;
+    const float *emeta;
+};
+GemmWeights gemm_weights(const void *packed, int H, int I, int E, bool gateup);
+
+void launch_gateup(const moe_shape &sh, const uint16_t *x, const float *xsum, const float *tok,
+                   const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
+                   const int32_t *sched, int32_t *qctl, int max_blocks, const int32_t *row_token,
+                   uint16_t *h, float *hsum, float *hexp, hipStream_t s);
+void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const float *hexp,
+                 const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
                  const int32_t *sched, int32_t *qctl, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  uint16_t *stage, float *y, hipStream_t s);
+
+// Power-of-two helpers for the range normalisation: 2^n as a float (n clamped to the
+// normal range), and floor(log2 |v|) of a finite nonzero float.
+__host__ __device__ inline float exp2i(int n) {
+    n = n < -126 ? -126 : (n > 127 ? 127 : n);
+    union { uint32_t u; float f; } c;
+    c.u = (uint32_t)(n + 127) << 23;
+    return c.f;
+}
+__device__ inline int ilog2f(float v) {
+    const uint32_t u = __float_as_uint(v) & 0x7fffffffu;
+    if (u >= 0x00800000u) return (int)(u >> 23) - 127;
+    return -127 - __builtin_clz(u) + 9;        // subnormal: 2^-149 .. 2^-127
+}
+
+// Exponent f of the power of two that brings h = silu(g) u into the fp16 range: with
+// |g|, |u| <= nw ||x|| (Cauchy-Schwarz, nw bounding the L2 norm of every gate and up row)
+// and |silu(g)| <= |g|, |h| <= B = (nw ||x||)^2.  f = 0 while B lies in [2^-2, 2^15);
+// otherwise f is the exponent with B 2^-f in [2^14, 2^15) (up to rounding), so h 2^-f
+// stays below 65504 and its bulk above the fp16 subnormals.
+__device__ inline int h_exponent(float nw, float nx) {
+    if (!(nw > 0.0f) || !(nx > 0.0f)) return 0;
+    const int a = ilog2f(nw) + ilog2f(nx);              // nw nx in [2^a, 2^(a+2))
+    int eb;                                             // B < 2^eb
+    if (a > 60 || a < -60) {
+        eb = 2 * a + 4;
+    } else {
+        const float p = nw * nx;                        // no overflow or underflow here
+        const float B = p * p;
+        if (B >= 0.25f && B < 32768.0f) return 0;
+        eb = ilog2f(B) + 1;
+    }
+    const int f = eb - 15;
+    return f < -100 ? -100 : (f > 100 ? 100 : f);
+}
+
+// Exponent e of the power of two that brings a token's activations into the fp16 range
+// of the expert GEMM: 0 while max |x| lies in [2^-6, 2^14) (bf16 values down to 2^-17
+// convert exactly), otherwise the e with max |x| 2^-e in [2^13, 2^14).
+__device__ inline int x_exponent(float xmax) {
+    if (!(xmax > 0.0f) || (xmax >= 0x1p-6f && xmax < 16384.0f)) return 0;
+    return ilog2f(xmax) - 13;
+}
 
 // res == NULL: decode x.  Otherwise x is ignored and the input is bf16(RMSNorm(res + yprev)),
 // written to u_out; res <- res + yprev (a decode stack's residual step).

@@ -137,8 +137,10 @@ __device__ void select_topk(const float *__restrict__ logits, int E, int k, int 
     pick_l = lane < k ? key_to_float(pkey) : 0.0f;
 }
 
-// scratch: the logits of every token, 256-byte aligned
+// scratch: the logits of every token, then the h rows and the h factors of every token's
+// nine slots, each part 256-byte aligned (decode_scratch_size)
 static size_t logits_bytes(int T, int E) { return ((size_t)T * E * 4 + 255) & ~(size_t)255; }
+static size_t hbuf_bytes(int T, int I, int k) { return ((size_t)T * (k + 1) * I * 2 + 255) & ~(size_t)255; }
 
 // 1b. (decode of two or more tokens) the top-k and weights of token blockIdx.x,
 // once per token, for the gate/up and down workgroups to read.
@@ -186,10 +188,11 @@ __device__ __forceinline__ float pair_sum(float v) {
 // after it, all at once.
 __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
-    const uint8_t *__restrict__ pk, const uint8_t *__restrict__ pk_sh, int32_t *__restrict__ ids_out,
-    float *__restrict__ tw_out, uint16_t *__restrict__ hbuf, bool picks_given,
+    GemmWeights gw, int32_t *__restrict__ ids_out, float *__restrict__ tw_out,
+    uint16_t *__restrict__ hbuf, float *__restrict__ hfac, bool picks_given,
     float *__restrict__ res, const float *__restrict__ yprev) {
     __shared__ float red[DW][4][DOUT][2];
+    __shared__ float xss[DW];
     __shared__ uint32_t selw[DW][32];
     __shared__ u32x4 xs[256];                                     // the token's x, H <= 2048
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -206,6 +209,7 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
         ids_out += t * k;
         tw_out += t * k;
         hbuf += t * NSLOT * I;
+        hfac += t * NSLOT;
         // decode stack: the residual add the router kernel folded into this layer's input
         // is committed here, once every router wave has read res and yprev
         if (res != nullptr && blockIdx.x == 0)
@@ -245,8 +249,12 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
             }
         }
     }
-    const uint8_t *tile = slot == k ? pk_sh + (size_t)j * G * PK_BLOCK
-                                    : pk + ((size_t)ex * JT + j) * G * PK_BLOCK;
+    const uint8_t *tile = slot == k ? gw.pk_sh + (size_t)j * G * PK_BLOCK
+                                    : gw.pk + ((size_t)ex * JT + j) * G * PK_BLOCK;
+    const float *tcf = slot == k ? gw.colf_sh + (size_t)j * PK_COLF
+                                 : gw.colf + ((size_t)ex * JT + j) * PK_COLF;
+    const float kg = tcf[tcg], ku = tcf[tcg + 32];              // 2^-k of my two columns
+    const float nw = gw.emeta[(size_t)(slot == k ? E : ex) * PK_EMETA];
     u32x4 cw[2];
     uint16_t sv[2], bv[2];
     {
@@ -260,6 +268,17 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
         }
     }
     if ((int)threadIdx.x < H / 8) xs[threadIdx.x] = xl;
+    {   // ||x||^2 of the token (bf16 squares are exact in fp32)
+        float q2 = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            q2 = __builtin_fmaf(bf16_lo(xl[r]), bf16_lo(xl[r]), q2);
+            q2 = __builtin_fmaf(bf16_hi(xl[r]), bf16_hi(xl[r]), q2);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) q2 += __shfl_xor(q2, off);
+        if (lane == 0) xss[wave] = q2;
+    }
     __syncthreads();
     u32x4 xv[4];
 #pragma unroll
@@ -290,8 +309,9 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
                                                         __builtin_bit_cast(bf16x2, xp[4 * qq + p]), d, false);
                 }
             // sum_k x_k (q_k s + b) = s (sum x (128 + q) - 128 sum x) + b sum x
+            // (the block holds s and b times 2^k; the column factor 2^-k undoes it exactly)
             const float val = bf16_to_f32(sv[r]) * (d - 128.0f * sx) + bf16_to_f32(bv[r]) * sx;
-            if (r == 0) ag += val; else au += val;
+            if (r == 0) ag += val * kg; else au += val * ku;
         }
     }
     ag = pair_sum(ag);
@@ -311,7 +331,14 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
                 gs += red[w][q][m][0];
                 us += red[w][q][m][1];
             }
-        hbuf[(size_t)slot * I + DOUT * o + m] = f32_to_f16(gs / (1.0f + expf(-gs)) * us);
+        // h is kept as h 2^-f in fp16, f from the bound (row norm x ||x||)^2 on |h| (0 in
+        // the usual range); every workgroup of the slot takes the same f, the first records 2^f
+        float x2 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < DW; ++w) x2 += xss[w];
+        const int f = h_exponent(nw, sqrtf(x2));
+        hbuf[(size_t)slot * I + DOUT * o + m] = f32_to_f16(gs / (1.0f + expf(-gs)) * (us * exp2i(-f)));
+        if (o == 0 && m == 0) hfac[slot] = exp2i(f);
     }
 }
 
@@ -322,9 +349,9 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
 // are added per output in a fixed order: groups, then slots in pick order with
 // their routing weights, then the shared expert.
 __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
-    const uint16_t *__restrict__ hbuf, int H, int I, const int32_t *__restrict__ ids,
-    const float *__restrict__ tw, int k, int E, const uint8_t *__restrict__ pk,
-    const uint8_t *__restrict__ pk_sh, float *__restrict__ y) {
+    const uint16_t *__restrict__ hbuf, const float *__restrict__ hfac, int H, int I,
+    const int32_t *__restrict__ ids, const float *__restrict__ tw, int k, int E, GemmWeights gw,
+    float *__restrict__ y) {
     __shared__ float part[DN_MAXP][DOUT];
     extern __shared__ u32x4 hsh[];                                // the token's h block, (k+1) I fp16
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
@@ -332,6 +359,7 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     {   // token blockIdx.y: its h block, picks and output row
         const size_t t = blockIdx.y;
         hbuf += t * NSLOT * I;
+        hfac += t * NSLOT;
         ids += t * k;
         tw += t * k;
         y += t * H;
@@ -364,6 +392,7 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     for (int it0 = 0; it0 < npass; it0 += DN_BATCH) {
         u32x4 cw[DN_BATCH], hv[DN_BATCH][4];
         uint16_t sv[DN_BATCH], bv[DN_BATCH];
+        float kf[DN_BATCH];
         int pp[DN_BATCH], hcs[DN_BATCH];
 #pragma unroll
         for (int b = 0; b < DN_BATCH; ++b) {
@@ -375,9 +404,11 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
 #pragma unroll
             for (int r = 0; r < NSLOT; ++r)
                 if (r == s) e = sid[r];
-            const uint8_t *blk = (s == k ? pk_sh + (size_t)j * G * PK_BLOCK
-                                         : pk + ((size_t)e * JD + j) * G * PK_BLOCK) +
+            const uint8_t *blk = (s == k ? gw.pk_sh + (size_t)j * G * PK_BLOCK
+                                         : gw.pk + ((size_t)e * JD + j) * G * PK_BLOCK) +
                                  (size_t)g * PK_BLOCK;
+            kf[b] = (s == k ? gw.colf_sh + (size_t)j * PK_COLF
+                            : gw.colf + ((size_t)e * JD + j) * PK_COLF)[tc];
             // pairs past the end load the last pair again (unconditional loads are
             // issued together) and are skipped below
             cw[b] = *(const u32x4 *)(blk + 32 * tc + 16 * ph);
@@ -417,17 +448,18 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
                                                d, false);
                 }
             // sum_i h_i (q_i s + b) = s (sum h (1024 + q) - 1024 sum h) + b sum h
-            const float val = pair_sum(bf16_to_f32(sv[b]) * (d - 1024.0f * shs) + bf16_to_f32(bv[b]) * shs);
+            const float val = pair_sum((bf16_to_f32(sv[b]) * (d - 1024.0f * shs) + bf16_to_f32(bv[b]) * shs) * kf[b]);
             if (ph == 0) part[pp[b]][cc] = val;
         }
     }
     __syncthreads();
     if (tid < DOUT) {
+        // each slot's h was kept as h 2^-f: its weight (1 for the shared expert) times 2^f
         float sum = 0.0f;
         for (int s = 0; s <= k; ++s) {
             float a = 0.0f;
             for (int g = 0; g < G; ++g) a += part[s * G + g][tid];
-            sum = s < k ? __builtin_fmaf(tw[s], a, sum) : sum + a;
+            sum = s < k ? __builtin_fmaf(tw[s] * hfac[s], a, sum) : __builtin_fmaf(hfac[s], a, sum);
         }
         y[256 * j + DOUT * v + tid] = sum;
     }
@@ -440,10 +472,11 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     char *p = (char *)scratch;
     float *logits = (float *)p;                                   // [T][E]
     uint16_t *hbuf = (uint16_t *)(p + logits_bytes(T, E));        // fp16 [T][k+1][I]
+    float *hfac = (float *)(p + logits_bytes(T, E) + hbuf_bytes(T, I, k));   // [T][k+1]
     // the API admits top_k = 8, E <= 256, H <= 2048 (G <= 32), I <= 2048, T <= kDecodeMaxT
     if (k + 1 != NSLOT || E > 256 || H > 2048 || I > 2048 || T < 1 || T > kDecodeMaxT) return;
-    const PackLayout P = pack_layout(H, I, E);
-    const uint8_t *pk = (const uint8_t *)w.packed;
+    const GemmWeights gu = gemm_weights(w.packed, H, I, E, true);
+    const GemmWeights dn = gemm_weights(w.packed, H, I, E, false);
     // with a residual the router kernel makes the layer input and writes it to u_out
     const uint16_t *xin = res ? u_out : x;
     // every kernel takes token t = blockIdx.y; the tokens are independent problems
@@ -455,15 +488,14 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     if (picks_given)
         hipLaunchKernelGGL(decode_select_kernel, dim3(T), dim3(64), 0, s, logits, E, k, ids, tw);
     hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT), T), dim3(64 * DW), 0, s, xin,
-                       logits, H, I, k, E, pk + P.gu, pk + P.sh_gu, ids, tw, hbuf, picks_given, res,
-                       yprev);
+                       logits, H, I, k, E, gu, ids, tw, hbuf, hfac, picks_given, res, yprev);
     hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT, T), dim3(64 * DW), (size_t)(k + 1) * I * 2, s,
-                       hbuf, H, I, ids, tw, k, E, pk + P.down, pk + P.sh_down, y);
+                       hbuf, hfac, H, I, ids, tw, k, E, dn, y);
 }
 
 size_t decode_scratch_bytes(int T, int H, int I, int k) {
     (void)H;
-    return logits_bytes(T, 256) + (size_t)T * (k + 1) * I * 2;
+    return decode_scratch_size(T, I, k);
 }
 
 }  // namespace moe

@@ -76,6 +76,11 @@ struct GemmArgs {
     int N;                 // rows of one projection: I (gate/up) or H (down)
     const uint8_t *pk;     // routed experts' tile-layout blocks [E][n_tiles][G]
     const uint8_t *pk_sh;  // the shared expert's [n_tiles][G]
+    const float *colf;     // routed experts' column factors [E][n_tiles][PK_COLF]
+    const float *colf_sh;  // the shared expert's [n_tiles][PK_COLF]
+    const float *emeta;    // per expert slot: [0] bounds the L2 norm of its gate and up rows
+    const float *tok;      // gate/up: per token {2^e, ||x||} (x enters as fp16 x 2^-e)
+    float *hexp;           // per h row 2^f (h stored as h 2^-f): gate/up writes, down reads
     const int32_t *blocks;
     const int32_t *num_blocks;
     const int32_t *sched;  // routed blocks by cost class (4, 3, 2, 1 M tiles), then expert
@@ -177,9 +182,20 @@ __device__ __forceinline__ int src_row(const GemmArgs &a, const Tile &t, int m) 
 
 // One tile.  Thread 0 also takes the workgroup's next work item from the queue
 // head during the main loop and leaves it in *s_next.
+// Per-item values that the epilogue reads from LDS, copied in by DMA at the item's start:
+// the 256 columns' 2^-k factors, two per-row values (gate/up: 2^e of the row's token and
+// its ||x||; down: the routing weight and 2^f of the row's h), and the expert slot's
+// row-norm bound (gate/up).
+struct ItemLds {
+    float *colk;   // [256]
+    float *ra;     // [kBM]
+    float *rb;     // [kBM]
+    float *ne;     // [64], all equal
+};
+
 template <int MODE, int MT>
 __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *s_next,
-                          float *s_roww) {
+                          const ItemLds &il) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));              // recomputed per item: nothing lane-dependent is hoisted
@@ -222,14 +238,29 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     };
     // RG::PER copies per thread and stage, completing in order: stage c is in
     // once at most (stages issued after it) * PER copies are outstanding.
-    // routing weights of the tile's rows (down, routed): copied into LDS by DMA
-    // before the stage copies (so older than all of them) and complete with the
-    // main loop's last wait.  A plain load would be waited for in the epilogue
-    // behind the epilogue's own stores.
-    if (MODE == 1 && !t.shared && wave < 2) {
-        const uint32_t lw = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)s_roww;
-        const int m = min(64 * wave + lane, t.nrows - 1);
-        dma4(a.row_w + t.r0 + m, lw + (uint32_t)(256 * wave));
+    // The epilogue's per-item values (ItemLds) are copied into LDS by DMA before the
+    // stage copies (so older than all of them) and complete with the main loop's last
+    // wait.  Plain loads would be waited for in the epilogue behind its own stores.
+    const float *tcolf = t.shared ? a.colf_sh + (size_t)t.ntile * PK_COLF
+                                  : a.colf + ((size_t)t.e * a.n_tiles + t.ntile) * PK_COLF;
+    {
+        auto lds_of = [](const float *p) {
+            return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+        };
+        dma4(tcolf + tid, lds_of(il.colk) + (uint32_t)(256 * wave));
+        if (wave < 2) {
+            const int m = min(64 * wave + lane, t.nrows - 1);
+            if (MODE == 0) {
+                const int tok = src_row<MODE>(a, t, m);
+                dma4(a.tok + 2 * (size_t)tok, lds_of(il.ra) + (uint32_t)(256 * wave));
+                dma4(a.tok + 2 * (size_t)tok + 1, lds_of(il.rb) + (uint32_t)(256 * wave));
+            } else {
+                if (!t.shared) dma4(a.row_w + t.r0 + m, lds_of(il.ra) + (uint32_t)(256 * wave));
+                dma4(a.hexp + t.r0 + m, lds_of(il.rb) + (uint32_t)(256 * wave));
+            }
+        } else if (MODE == 0 && wave == 2) {
+            dma4(a.emeta + (size_t)(t.shared ? a.E : t.e) * PK_EMETA, lds_of(il.ne));
+        }
     }
     static_for<RG::AHEAD>([&](auto P) {
         if (decltype(P)::value < nch) issue(decltype(P)::value, P);
@@ -320,14 +351,29 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     if (tid == 0) *s_next = next;                // read after the caller's next barrier
     // ---- rank-G term for groups whose bias is not -8 s (none for symmetric codes)
     if (__any(nz)) {
+        // The term is added at a reduced scale so that no fp16 operand overflows: the group
+        // sums enter as xs 2^-6 (|x| < 2^14 and |h| < 2^15 keep |xs| 2^-6 < 2^15) and each
+        // column's c as c colc (|c colc| < 2^14); the accumulators are brought to that scale
+        // first and back afterwards (powers of two: exact).
         const int K3 = 3 * G;
         int srcr[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) srcr[mt] = src_row<MODE>(a, t, 32 * mt + l32);
         // scale and bias of my columns, group g: tile block g, bytes PK_CODES + 2 c
         const uint8_t *cs[2];
+        float ccol[2], rsc[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) cs[nt] = tb + PK_CODES + 2 * (64 * wave + 32 * nt + l32);
+        for (int nt = 0; nt < 2; ++nt) {
+            cs[nt] = tb + PK_CODES + 2 * (64 * wave + 32 * nt + l32);
+            ccol[nt] = tcolf[256 + 64 * wave + 32 * nt + l32];
+            rsc[nt] = ccol[nt] * 0x1p-6f;
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= rsc[nt];
         for (int j3 = 0; j3 < (K3 + 15) / 16; ++j3) {
             uint32_t bw[2][4], aw[MT][4];
 #pragma unroll
@@ -343,8 +389,8 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                         float v = 0.0f;
                         if (tau < 3) {
                             const uint8_t *sp = cs[nt] + (size_t)g * PK_BLOCK;
-                            const float cf = bf16_to_f32(*(const uint16_t *)(sp + 512)) +
-                                             8.0f * bf16_to_f32(*(const uint16_t *)sp);
+                            const float cf = (bf16_to_f32(*(const uint16_t *)(sp + 512)) +
+                                              8.0f * bf16_to_f32(*(const uint16_t *)sp)) * ccol[nt];
                             const float hi = (float)(_Float16)cf;
                             v = tau < 2 ? hi : (float)(_Float16)(cf - hi);
                         }
@@ -354,7 +400,7 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                     for (int mt = 0; mt < MT; ++mt) {
                         float v = 0.0f;
                         if (tau < 3) {
-                            const float xs = a.Asum[(size_t)srcr[mt] * G + g];
+                            const float xs = a.Asum[(size_t)srcr[mt] * G + g] * 0x1p-6f;
                             const float hi = (float)(_Float16)xs;
                             v = tau == 1 ? (float)(_Float16)(xs - hi) : hi;
                         }
@@ -377,21 +423,40 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 }
             }
         }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) rsc[nt] = 1.0f / rsc[nt];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= rsc[nt];
     }
 
     // ---- epilogue.  Accumulator element i of lane (l32, gg) is row
     // 8*(i/4) + 4*gg + i%4 of its 32-row tile, column l32 of the wave's n-tile.
     __syncthreads();                             // every wave is done with the ring
     if (MODE == 0) {
+        // per row: the token's 2^e undoes the activation scale; h is stored as h 2^-f, f from
+        // the bound (expert row norm x ||x||)^2 on |h| (0 in the usual range); 2^f is kept
+        // per row for the down GEMM
+        if (tid < kBM) {
+            const int f = h_exponent(il.ne[0], il.rb[tid]);
+            il.rb[tid] = exp2i(-f);
+            if (t.ntile == 0 && tid < t.nrows) a.hexp[t.r0 + tid] = exp2i(f);
+        }
+        __syncthreads();
         // SwiGLU -> fp16 h tile in LDS [128 rows][128 columns], columns permuted
         const int pc = perm_pos(32 * wave + l32);
+        const float kg = il.colk[64 * wave + l32], ku = il.colk[64 * wave + 32 + l32];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = 32 * mt + 8 * (i >> 2) + 4 * gg + (i & 3);
-                const float g = acc[mt][0][i], u = acc[mt][1][i];
-                const float hv = __fdividef(g, 1.0f + __expf(-g)) * u;
+                const float al = il.ra[row];
+                const float g = acc[mt][0][i] * (al * kg), u = acc[mt][1][i] * (al * ku);
+                const float hv = __fdividef(g, 1.0f + __expf(-g)) * (u * il.rb[row]);
                 *(uint16_t *)(smem + row * HS_LD + 2 * pc) = f32_to_f16(hv);
             }
         __syncthreads();
@@ -439,19 +504,21 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 if (mt < MT && row < t.nrows) {
                     const uint8_t *src = smem + rr * YS_LD + seg * 128;
                     const int col = t.ntile * 256 + seg * 32;
+                    const floatx4 *kcp = (const floatx4 *)(il.colk + seg * 32);   // 2^-k per column
                     if (t.shared) {
                         float *dst = a.y + (size_t)(t.r0 - Trk + row) * a.N + col;
+                        const float hx = il.rb[row];
 #pragma unroll
                         for (int q = 0; q < 8; ++q)
-                            *(floatx4 *)(dst + 4 * q) = *(const floatx4 *)(src + 16 * q);
+                            *(floatx4 *)(dst + 4 * q) = *(const floatx4 *)(src + 16 * q) * (kcp[q] * hx);
                     } else {
                         // routed row: weighted output staged in bf16 (fp32 range; the combine adds in fp32)
                         uint16_t *dst = a.stage + (size_t)(t.r0 + row) * a.N + col;
-                        const float wr = s_roww[row];
+                        const float wr = il.ra[row] * il.rb[row];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const floatx4 v0 = *(const floatx4 *)(src + 32 * q);
-                            const floatx4 v1 = *(const floatx4 *)(src + 32 * q + 16);
+                            const floatx4 v0 = *(const floatx4 *)(src + 32 * q) * kcp[2 * q];
+                            const floatx4 v1 = *(const floatx4 *)(src + 32 * q + 16) * kcp[2 * q + 1];
                             u32x4 o;
                             o.x = pack_bf16x2(wr * v0[0], wr * v0[1]);
                             o.y = pack_bf16x2(wr * v0[2], wr * v0[3]);
@@ -477,7 +544,9 @@ template <int MODE>
 __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     __shared__ int s_next;
-    __shared__ float s_roww[kBM];
+    __shared__ __attribute__((aligned(16))) float s_colk[256];
+    __shared__ float s_ra[kBM], s_rb[kBM], s_ne[64];
+    const ItemLds il{s_colk, s_ra, s_rb, s_ne};
     const int nb = min(max(a.num_blocks[0], 0), a.max_blocks);
     const int n_items = (a.n_shared + nb) * a.n_tiles;
     // an item that turns out empty still takes the next one from the head
@@ -511,10 +580,10 @@ __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
             skip();
         } else {
             switch ((t.nrows + 31) >> 5) {
-                case 1: gemm_tile<MODE, 1>(a, t, smem, &s_next, s_roww); break;
-                case 2: gemm_tile<MODE, 2>(a, t, smem, &s_next, s_roww); break;
-                case 3: gemm_tile<MODE, 3>(a, t, smem, &s_next, s_roww); break;
-                default: gemm_tile<MODE, 4>(a, t, smem, &s_next, s_roww); break;
+                case 1: gemm_tile<MODE, 1>(a, t, smem, &s_next, il); break;
+                case 2: gemm_tile<MODE, 2>(a, t, smem, &s_next, il); break;
+                case 3: gemm_tile<MODE, 3>(a, t, smem, &s_next, il); break;
+                default: gemm_tile<MODE, 4>(a, t, smem, &s_next, il); break;
             }
         }
         __syncthreads();                         // s_next written; the tile is done with the LDS
@@ -548,18 +617,23 @@ static void allow_lds() {
     }
 }
 
-void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum,
-                   const uint8_t *pk, const uint8_t *pk_sh, const int32_t *blocks,
-                   const int32_t *num_blocks, const int32_t *sched, int32_t *qctl, int max_blocks,
-                   const int32_t *row_token, uint16_t *h, float *hsum, hipStream_t s) {
+void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, const float *tok,
+                   const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
+                   const int32_t *sched, int32_t *qctl, int max_blocks, const int32_t *row_token,
+                   uint16_t *h, float *hsum, float *hexp, hipStream_t s) {
     GemmArgs a{};
     a.A = xp;
     a.Asum = xsum;
     a.K = sh.H;
     a.G = sh.H / 64;
     a.N = sh.I;
-    a.pk = pk;
-    a.pk_sh = pk_sh;
+    a.pk = gw.pk;
+    a.pk_sh = gw.pk_sh;
+    a.colf = gw.colf;
+    a.colf_sh = gw.colf_sh;
+    a.emeta = gw.emeta;
+    a.tok = tok;
+    a.hexp = hexp;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.sched = sched;
@@ -613,8 +687,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     *(float4 *)(y + t * H + n + 4) = a1;
 }
 
-void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const uint8_t *pk,
-                 const uint8_t *pk_sh, const int32_t *blocks, const int32_t *num_blocks,
+void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const float *hexp,
+                 const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
                  const int32_t *sched, int32_t *qctl, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  uint16_t *stage, float *y, hipStream_t s) {
@@ -624,8 +698,12 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
     a.K = sh.I;
     a.G = sh.I / 64;
     a.N = sh.H;
-    a.pk = pk;
-    a.pk_sh = pk_sh;
+    a.pk = gw.pk;
+    a.pk_sh = gw.pk_sh;
+    a.colf = gw.colf;
+    a.colf_sh = gw.colf_sh;
+    a.emeta = gw.emeta;
+    a.hexp = (float *)hexp;
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.sched = sched;

@@ -176,7 +176,7 @@ __device__ __forceinline__ void rdma16(const void *g, uint32_t lds) {
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int H, int E, int S,
     float *__restrict__ part, uint16_t *__restrict__ xp, float *__restrict__ xsum,
-    float *__restrict__ xsq, float *__restrict__ wn2part) {
+    float *__restrict__ xsq, float *__restrict__ wn2part, float *__restrict__ xmx) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t rsm[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)rsm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // would count against the DMA waits (one vmcnt for loads and stores)
     constexpr int MAXCH = 8;                       // H <= 2048, four K ranges
     u32x4 xpv[MAXCH];
-    float s1v[MAXCH], s2v[MAXCH];
+    float s1v[MAXCH], s2v[MAXCH], mxv[MAXCH];
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c) {
         if (c >= nch) break;
@@ -241,15 +241,17 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         {
             const int row = tid >> 3, sg = tid & 7;
             const u32x4 v = *(const u32x4 *)(sx + row * 128 + 16 * (sg ^ (row & 7)));
-            float s1 = 0.0f, s2 = 0.0f;
+            float s1 = 0.0f, s2 = 0.0f, mx = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 s1 += bf16_lo(v[q]) + bf16_hi(v[q]);
                 s2 = __builtin_fmaf(bf16_lo(v[q]), bf16_lo(v[q]), s2);
                 s2 = __builtin_fmaf(bf16_hi(v[q]), bf16_hi(v[q]), s2);
+                mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[q])), fabsf(bf16_hi(v[q]))));
             }
             s1v[c] = group_sum_dpp(s1, 8);
             s2v[c] = group_sum_dpp(s2, 8);
+            mxv[c] = group_max_dpp8(mx);
             xpv[c] = permute_to_f16(v);
         }
         if (do_norm) {                             // thread tid = router row tid
@@ -278,6 +280,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                     const size_t gi = (size_t)(t0 + row) * G + kbeg / 64 + c;
                     xsum[gi] = s1v[c];
                     xsq[gi] = s2v[c];
+                    xmx[gi] = mxv[c];
                 }
             }
         }
@@ -425,7 +428,9 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     const float *__restrict__ xsq, int G, const float *__restrict__ wn2,
     const float *__restrict__ bias, const uint16_t *__restrict__ x,
     const uint16_t *__restrict__ wr, int T, int H, int E, int k, int32_t *__restrict__ ids,
-    float *__restrict__ tw, int32_t *__restrict__ blk_cnt, int32_t *__restrict__ lrank) {
+    float *__restrict__ tw, int32_t *__restrict__ blk_cnt, int32_t *__restrict__ lrank,
+    const float *__restrict__ xmx, uint16_t *__restrict__ xp, float *__restrict__ xsum,
+    float *__restrict__ tok) {
     __shared__ uint32_t mask[256];
     __shared__ int32_t sid[TB][8];
     __shared__ uint32_t cand_e[TB][256];
@@ -441,7 +446,11 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
         // every load of this phase goes out before the first wait: the token's
         // sums of squares, all RS_SPLIT partials and norms, and the biases
         float ss = 0.0f, bv[4], pv[4][RS_SPLIT], wv[4][RS_SPLIT];
-        if (!exact && lane < G) ss = xsq[(size_t)t * G + lane];
+        float xm = 0.0f;
+        if (lane < G) {
+            ss = xsq[(size_t)t * G + lane];
+            xm = xmx[(size_t)t * G + lane];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane + 64 * j;
@@ -458,7 +467,7 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
             }
         }
         if (!exact) {
-            const float nx = sqrtf(wave_sum_f(ss));
+            const float nx = sqrtf(wave_sum_f(ss));   // ||x||
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float v = pv[j][0], w2 = wv[j][0];
@@ -650,6 +659,34 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
             sid[tl][lane] = my_pick;
             atomicOr(&mask[my_pick], 1u << tl);
         }
+        // ---- the token's range for the expert GEMM: x enters it as fp16 x 2^-e, with e = 0
+        // unless max |x| is outside [2^-6, 2^14); then the fp16 copy and the group sums that
+        // the router pass wrote are redone with the token's power of two (exact)
+        const float xmax = key_to_float(wave_umax(ordered_key(xm)));
+        const int e = x_exponent(xmax);
+        if (e != 0) {
+            const float sc = exp2i(-e);
+            if (lane < G) {
+                const u32x4 *src = (const u32x4 *)(x + (size_t)t * H + 64 * lane);
+                u32x4 *dst = (u32x4 *)(xp + (size_t)t * H + 64 * lane);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const u32x4 v = src[q];
+                    u32x4 o;
+                    o.x = pack_f16x2(bf16_lo(v.x) * sc, bf16_lo(v.z) * sc);
+                    o.y = pack_f16x2(bf16_hi(v.x) * sc, bf16_hi(v.z) * sc);
+                    o.z = pack_f16x2(bf16_lo(v.y) * sc, bf16_lo(v.w) * sc);
+                    o.w = pack_f16x2(bf16_hi(v.y) * sc, bf16_hi(v.w) * sc);
+                    dst[q] = o;
+                }
+                xsum[(size_t)t * G + lane] *= sc;
+            }
+        }
+        const float nxt = sqrtf(wave_sum_f(ss));
+        if (lane == 0) {
+            tok[2 * (size_t)t] = exp2i(e);
+            tok[2 * (size_t)t + 1] = nxt;
+        }
     }
     __syncthreads();
     if (tid < 256) blk_cnt[(size_t)blockIdx.x * E + tid] = __popc(mask[tid]);
@@ -664,7 +701,8 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
 }
 
 void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
-                        float *wn2part, uint16_t *xp, float *xsum, float *xsq, hipStream_t s) {
+                        float *wn2part, uint16_t *xp, float *xsum, float *xsq, float *xmx,
+                        hipStream_t s) {
     const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
     static bool lds_set = false;
     if (!lds_set) {
@@ -673,16 +711,18 @@ void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int
         lds_set = true;
     }
     hipLaunchKernelGGL(router_mfma_kernel, dim3((T + RT_TOK - 1) / RT_TOK, S), dim3(256),
-                       R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq, wn2part);
+                       R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq, wn2part, xmx);
 }
 
 void launch_route_select(const float *part, const float *exact, const float *xsq,
                          const float *wn2, const float *bias, const uint16_t *x,
                          const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,
-                         int32_t *blk_cnt, int32_t *lrank, hipStream_t s) {
+                         int32_t *blk_cnt, int32_t *lrank, const float *xmx, uint16_t *xp,
+                         float *xsum, float *tok, hipStream_t s) {
     const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
     hipLaunchKernelGGL(route_select_kernel, dim3((T + TB - 1) / TB), dim3(64 * TB), 0, s, part, S,
-                       exact, xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank);
+                       exact, xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank,
+                       xmx, xp, xsum, tok);
 }
 
 // ---------------------------------------------------------------------------
@@ -820,14 +860,15 @@ void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
 __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restrict__ x, int rows,
                                                        int K, uint16_t *__restrict__ xp,
                                                        float *__restrict__ out,
-                                                       float *__restrict__ sq) {
+                                                       float *__restrict__ sq,
+                                                       float *__restrict__ mxo) {
     const int G = K / 64;
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (size_t)rows * G) return;
     const size_t r = i / G, g = i % G;
     const u32x4 *p = (const u32x4 *)(x + r * K + g * 64);
     u32x4 *q = (u32x4 *)(xp + r * K + g * 64);
-    float s = 0.0f, s2 = 0.0f;
+    float s = 0.0f, s2 = 0.0f, mx = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const u32x4 v = p[j];
@@ -837,19 +878,21 @@ __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restric
         for (int q = 0; q < 4; ++q) {
             s2 = __builtin_fmaf(bf16_lo(v[q]), bf16_lo(v[q]), s2);
             s2 = __builtin_fmaf(bf16_hi(v[q]), bf16_hi(v[q]), s2);
+            mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[q])), fabsf(bf16_hi(v[q]))));
         }
         q[j] = permute_to_f16(v);
     }
     out[i] = s;
     if (sq) sq[i] = s2;
+    if (mxo) mxo[i] = mx;
 }
 
 void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
-                     hipStream_t s) {
+                     float *xmx, hipStream_t s) {
     const size_t n = (size_t)rows * (K / 64);
     if (n == 0) return;
     hipLaunchKernelGGL(prep_act_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, rows,
-                       K, xp, xsum, xsq);
+                       K, xp, xsum, xsq, xmx);
 }
 
 }  // namespace moe

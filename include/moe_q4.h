@@ -133,21 +133,40 @@ moe_status moe_query(const moe_shape *shape, size_t *workspace_bytes, int32_t *m
 /* Host only.  Bytes of the tile-layout buffer for `shape`. */
 moe_status moe_packed_bytes(const moe_shape *shape, size_t *packed_bytes);
 
-/* Regroup the six row-layout projections of w into the tile layout (a pure
- * permutation of bytes, done once when the weights are loaded).  packed:
- * device buffer of at least moe_packed_bytes bytes, 256-byte aligned, not
- * overlapping the sources; w->packed is not read.  MOE_ERR_INVALID_ARG for a
- * NULL or misaligned pointer or a short buffer. */
+/* Load the six row-layout projections of w into the tile layout, once, when the
+ * weights are loaded; the pages' engine validates the checkpoint format at load and
+ * refuses every other (greatopti.com, "Une spécialisation assumée").
+ * The codes move unchanged.  Each projection row's scales and biases are stored times
+ * a power of two 2^k that puts the row's largest |scale| in [2^10, 2^11), with 2^-k
+ * kept per row in a meta section after the blocks; the kernels undo it exactly.  The
+ * meta section also holds per expert a bound on the L2 norm of its gate and up rows
+ * (used to keep the hidden activations in range) and a status word of validation
+ * flags, copied to *status (device int32, may be NULL) when the pack completes:
+ *   0  supported: the layer calls compute on these weights as documented;
+ *   1  a scale or bias is NaN or infinite;
+ *   2  a row's nonzero |scales| span more than 2^23 (its rebuilt fp16 weights would
+ *      not be exact);
+ *   4  a bias times the row's 2^k leaves the bf16 range.
+ * A nonzero status means the weights are refused: the layer calls must not be used
+ * with this buffer (their results would not be those documented).  The caller reads
+ * *status once the stream has reached it.
+ * packed: device buffer of at least moe_packed_bytes bytes, 256-byte aligned, not
+ * overlapping the sources; w->packed is not read.  MOE_ERR_INVALID_ARG for a NULL or
+ * misaligned pointer or a short buffer. */
 moe_status moe_pack_weights(const moe_shape *shape, const moe_weights *w, void *packed,
-                            size_t packed_bytes, void *stream);
+                            size_t packed_bytes, int32_t *status, void *stream);
 
 /* Router and routing (the pages' "histogram, prefix scan, scatter and block
  * map in one GPU command buffer", mechatronicstore.cl "Prefill: ...").
- * x: bf16 [T][H].  Logits are float32 in a fixed order (within each chunk
+ * x: bf16 [T][H], finite.  Logits are float32 in a fixed order (within each chunk
  * of 64 inputs a sequential sum from the chunk's first product, then a
  * sequential sum over chunks, then + bias), so routing is reproducible bit
- * for bit.  Also fills the workspace's group sums of x used by
- * moe_expert_gemm_q4. */
+ * for bit.  topk_w: the softmax over all experts renormalised over the picks,
+ * from the picks' fixed-order logits, evaluated in fp64 and rounded once.
+ * Also prepares x for moe_expert_gemm_q4 in the workspace: an fp16 copy of
+ * each token's row times 2^-e (e = 0 while max |x| lies in [2^-6, 2^14),
+ * otherwise the power of two that puts it in [2^13, 2^14): exact), its group
+ * sums, 2^e and ||x||. */
 moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                      const moe_routing *r, void *ws, size_t ws_bytes, void *stream);
 
@@ -155,16 +174,22 @@ moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weight
  * 4-bit codes directly (mechatronicstore.cl "Prefill: ...": weights rebuilt
  * tile by tile inside the grouped GEMM, FP32 accumulation), with the SwiGLU
  * epilogue h = silu(W_gate x) * (W_up x).
+ * x is not read: the GEMM reads the fp16 copy of x that moe_route prepared in
+ * the workspace (the argument is kept for symmetry with the other calls).
  * h: fp16 [T*top_k + T][I] (bits as uint16_t); rows 0..T*top_k-1 follow
  * routing order, row T*top_k + t is the shared expert of token t.  Within each
  * row, every block of 8 consecutive columns is stored in the order
- * 0,4,1,5,2,6,3,7 (the order in which the down GEMM consumes it).  Needs
- * moe_route's outputs and workspace; leaves the group sums of h in the
- * workspace for moe_down_combine.
+ * 0,4,1,5,2,6,3,7 (the order in which the down GEMM consumes it).  A row is
+ * stored as h 2^-f with f = 0 unless the bound (L2 norm of the expert's rows x
+ * ||x||)^2 on |h| leaves [2^-2, 2^15); the workspace keeps 2^f per row.  Needs
+ * moe_route's outputs and workspace; leaves the group sums of h and the row
+ * factors in the workspace for moe_down_combine.
  * Reads the expert weights from w->packed (tile layout).
- * Weights are rebuilt exactly as (q - 8) * scale in fp16 plus an fp32 term for
- * bias + 8 * scale; the activations enter the matrix cores in fp16.  Exact for
- * |scale| in [2^-13, 2^12] and |x| below 65504 (larger x overflows). */
+ * Weights are rebuilt exactly as (q - 8) * scale * 2^k in fp16 plus an fp32-accurate
+ * term for bias + 8 * scale; the activations enter the matrix cores in fp16 at the
+ * token's power of two.  So for weights that moe_pack_weights accepted and finite
+ * x, the only roundings are those of fp32 accumulation and of h to fp16 (as long as
+ * the values stay in the fp32 range). */
 moe_status moe_expert_gemm_q4(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                               const moe_routing *r, uint16_t *h, void *ws, size_t ws_bytes,
                               void *stream);
@@ -225,7 +250,7 @@ moe_status moe_decode(const moe_shape *shape, const uint16_t *x, const moe_weigh
 /* moe_decode for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, and harnesses that forbid hipMalloc.  It takes no
  * workspace; the decode scratch (each token's 256 router logits and its nine h rows,
- * at most 303104 bytes for 8 tokens at H = I = 2048) lives in a device array inside
+ * at most 303616 bytes for 8 tokens at H = I = 2048) lives in a device array inside
  * the library, one per GPU, held until the process ends.  Arguments, layout and
  * results are those of moe_decode, bit for bit.  The call allocates nothing; its first
  * call on a device looks up that device's array address (hipGetSymbolAddress) once.

@@ -192,27 +192,32 @@ def test_python_binding_checks_tensors():
 
 
 def test_packed_bytes_and_pack_validation():
-    """The tile layout holds exactly the row layout's bytes (four sections, each
-    rounded up to 256 bytes); moe_pack_weights validates before any launch."""
+    """The tile layout holds the row layout's bytes (four sections, each rounded up to
+    256 bytes), then the meta section: a 256-byte status line, 16 bytes per expert slot
+    and 2 KB of column factors per 256-column tile; moe_pack_weights validates its
+    arguments before any launch."""
     L = B.lib()
     for H, I in [(2048, 512), (512, 128), (1024, 256)]:
         s = shape(T=1, H=H, I=I)
         n = C.c_size_t()
         assert L.moe_packed_bytes(C.byref(s), C.byref(n)) == OK
         per_expert = 3 * H * I // 2 + 3 * 2 * 2 * H * I // 64     # codes + scales + biases
-        assert n.value >= 257 * per_expert and n.value < 257 * per_expert + 4 * 256
+        tiles = 257 * (I // 128 + H // 256)
+        meta = 256 + 257 * 16 + tiles * 2048
+        assert n.value >= 257 * per_expert + meta and n.value < 257 * per_expert + meta + 10 * 256
         assert n.value % 256 == 0
     s = shape(T=1)
     n = C.c_size_t()
     assert L.moe_packed_bytes(C.byref(s), C.byref(n)) == OK
     w = _weights()
-    assert L.moe_pack_weights(C.byref(s), C.byref(w), FAKE + 16, n.value, None) == INVALID
-    assert L.moe_pack_weights(C.byref(s), C.byref(w), FAKE, n.value - 1, None) == INVALID
-    assert L.moe_pack_weights(C.byref(s), C.byref(w), None, n.value, None) == INVALID
+    assert L.moe_pack_weights(C.byref(s), C.byref(w), FAKE + 16, n.value, None, None) == INVALID
+    assert L.moe_pack_weights(C.byref(s), C.byref(w), FAKE, n.value - 1, None, None) == INVALID
+    assert L.moe_pack_weights(C.byref(s), C.byref(w), None, n.value, None, None) == INVALID
+    assert L.moe_pack_weights(C.byref(s), C.byref(w), FAKE, n.value, FAKE + 2, None) == INVALID
     assert L.moe_pack_weights(C.byref(s), C.byref(_weights("misaligned_rows")), FAKE, n.value,
-                              None) == INVALID
+                              None, None) == INVALID
     assert L.moe_pack_weights(C.byref(shape(T=1, bits=8)), C.byref(w), FAKE, n.value,
-                              None) == UNSUP
+                              None, None) == UNSUP
     assert L.moe_packed_bytes(C.byref(s), None) == INVALID
 
 

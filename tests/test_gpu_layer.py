@@ -218,11 +218,12 @@ def test_layer_asymmetric_bias(name, kw, seed):
             assert np.all(np.abs(h[r] - a) <= bound), (t, j, e, np.max(np.abs(h[r] - a) - bound))
 
 
-@pytest.mark.parametrize("lo,hi", [(-13, -9), (8, 12)], ids=["small", "large"])
+@pytest.mark.parametrize("lo,hi", [(-13, -9), (8, 12), (-40, -36)], ids=["small", "large", "tiny"])
 def test_hidden_rows_scale_extremes(lo, hi):
-    """Scales at both ends of the range where the rebuilt fp16 weights are exact
-    ([2^-13, 2^12]; at the low end s / 16 is an fp16 subnormal): h still matches
-    the oracle to the fp16 storage bound."""
+    """Scales far from the usual ones (each weight row is rebuilt at its own power of two,
+    so the fp16 weights are exact at any magnitude): h matches the oracle to the fp16
+    storage bound.  x is chosen so that the bound (row norm x ||x||)^2 on |h| stays in
+    the range where h is stored unscaled (larger h: test_gpu_range)."""
     from synth.inputs import f32_to_bf16_bits
     print(f"[scale-extremes] 2^{lo} .. 2^{hi}", flush=True)
     inp = make_layer(4100 + lo, T=64, H=512, I=128)
@@ -233,9 +234,11 @@ def test_hidden_rows_scale_extremes(lo, hi):
         s = (m * 2.0 ** e).astype(np.float32)
         p.scale[...] = f32_to_bf16_bits(s)
         p.bias[...] = f32_to_bf16_bits(-8.0 * s)
-    # |x| in [2^-14, 2^-13) (large scales) or [1, 2) (small ones): fp16 normal
-    # values, and h stays well inside the fp16 range
-    mag = rng.uniform(1.0, 2.0, size=inp.x.shape) * (2.0 ** -14 if hi > 0 else 1.0)
+    # |x| in [2^-19, 2^-18) for the large scales (the activations then enter the GEMM
+    # at a token power of two), [1, 2) for the small ones, [2^30, 2^31) for the tiny ones
+    xmag = {"large": 2.0 ** -19, "small": 1.0, "tiny": 2.0 ** 30}[
+        "large" if hi > 0 else ("tiny" if lo < -20 else "small")]
+    mag = rng.uniform(1.0, 2.0, size=inp.x.shape) * xmag
     sign = np.where(rng.random(size=inp.x.shape) < 0.5, -1.0, 1.0)
     inp.x[...] = f32_to_bf16_bits((sign * mag).astype(np.float32))
     run = LayerRun(inp).route().gemm().sync()

@@ -1,15 +1,31 @@
 """moe_pack_weights against a numpy rendering of the tile layout that
-include/moe_q4.h documents: every byte of the packed buffer is checked."""
+include/moe_q4.h documents: every byte of the blocks is checked (codes unchanged, each
+row's scales and biases times its power of two 2^k), and the meta section's status,
+column factors and per-expert row-norm bounds."""
 import numpy as np
 import pytest
 
 import bit_quantized_expert_top_amd as moe
 from moe_case import device, upload
-from synth import make_layer
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, make_layer
 
 pytestmark = pytest.mark.gpu
 
 BLOCK, CODES = 9216, 8192
+
+
+def _row_shift(s_bits):
+    """k per row: the power of two that puts the row's largest |scale| in [2^10, 2^11)."""
+    sf = np.abs(bf16_bits_to_f32(s_bits)).astype(np.float64)
+    smax = sf.max(axis=-1)
+    _, e = np.frexp(smax)                    # smax = m 2^e, m in [0.5, 1)
+    return np.where(smax > 0, 10 - (e - 1), 0)
+
+
+def _shifted(bits, k):
+    """bf16 values times 2^k (exact), as bf16 bits."""
+    return f32_to_bf16_bits(np.ldexp(bf16_bits_to_f32(bits).astype(np.float64), k[..., None])
+                            .astype(np.float32))
 
 
 def _blocks(q, s, b, rows_of_col):
@@ -69,17 +85,51 @@ def test_pack_matches_documented_layout(H, I):
     def dn_cols(j):
         return [(0, 256 * j + c) for c in range(256)]
 
-    sections = []
+    def shifted(p):
+        q, s_, b_ = p
+        k = _row_shift(s_)
+        return q, _shifted(s_, k), _shifted(b_, k), k
+
+    sections, colk = [], []
     for shared in (False, True):
-        g, u = proj("sh_gate" if shared else "gate", shared), proj("sh_up" if shared else "up", shared)
+        g = shifted(proj("sh_gate" if shared else "gate", shared))
+        u = shifted(proj("sh_up" if shared else "up", shared))
         sections.append(_blocks([g[0], u[0]], [g[1], u[1]], [g[2], u[2]],
                                 _Cols(range(I // 128), gu_cols)))
+        # column factors 2^-k in the blocks' column order: [n_exp][tile][256]
+        colk.append(np.stack([np.ldexp(1.0, -np.array([(g[3], u[3])[p][:, n] for p, n in gu_cols(j)]).T)
+                              for j in range(I // 128)], axis=1))
     for shared in (False, True):
-        d = proj("sh_down" if shared else "down", shared)
+        d = shifted(proj("sh_down" if shared else "down", shared))
         sections.append(_blocks([d[0]], [d[1]], [d[2]], _Cols(range(H // 256), dn_cols)))
+        colk.append(np.stack([np.ldexp(1.0, -d[3][:, 256 * j:256 * j + 256])
+                              for j in range(H // 256)], axis=1))
     off = 0
     for sec in sections:
         flat = sec.reshape(-1)
         np.testing.assert_array_equal(got[off:off + flat.size], flat)
         off = (off + flat.size + 255) // 256 * 256
+    # meta: status line, per-expert bounds, then the column factors of the four sections
+    assert got[off:off + 4].view(np.int32)[0] == 0 and w.status == 0
+    off += 256
+    emeta = got[off:off + 257 * 16].view(np.float32).reshape(257, 4)
+    off = (off + 257 * 16 + 255) // 256 * 256
+    for ck in colk:
+        n = ck.size * 2 * 4
+        cf = got[off:off + n].view(np.float32).reshape(ck.shape[0], ck.shape[1], 2, 256)
+        np.testing.assert_array_equal(cf[:, :, 0, :], ck.astype(np.float32))
+        np.testing.assert_array_equal(cf[:, :, 1, :], 1.0)      # b = -8 s: no rank-G scale
+        off = (off + n + 255) // 256 * 256
     assert off == got.size == moe.moe_packed_bytes(moe.Shape(T=1, H=H, I=I, E=E))
+    # the bound on the L2 norm of every gate and up row of each expert slot
+    import oracle
+    for e in list(range(0, E, 37)) + [E]:
+        names = ("sh_gate", "sh_up") if e == E else ("gate", "up")
+        norms = []
+        for nm in names:
+            p = getattr(inp, nm)
+            q, s_, b_ = (p.q, p.scale, p.bias) if e == E else (p.q[e], p.scale[e], p.bias[e])
+            wd = oracle.dequant(q, s_, b_, I, H)
+            norms.append(np.sqrt((wd ** 2).sum(axis=1)).max())
+        nb = max(norms)
+        assert nb <= emeta[e, 0] <= nb * 1.002, (e, nb, emeta[e, 0])
