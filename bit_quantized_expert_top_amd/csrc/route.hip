@@ -414,9 +414,21 @@ __device__ float exact_logits8(const uint32_t *elist, int n, const uint16_t *__r
     __builtin_amdgcn_wave_barrier();
     float L = 0.0f;
     if (lane < n) {
-        const float *pp = part + 32 * lane;
-        L = pp[0];
-        for (int q = 1; q < nch; ++q) L = L + pp[q];
+        // the 32 partials in one batch of LDS reads, then added in chunk order
+        const float4 *pp = (const float4 *)(part + 32 * lane);
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float4 f = pp[q];
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
+        }
+        L = v[0];
+#pragma unroll
+        for (int q = 1; q < 32; ++q)
+            if (q < nch) L = L + v[q];
         if (bias) L = L + bias[elist[lane]];
     }
     __builtin_amdgcn_wave_barrier();
@@ -434,7 +446,7 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     __shared__ uint32_t mask[256];
     __shared__ int32_t sid[TB][8];
     __shared__ uint32_t cand_e[TB][256];
-    __shared__ float cand_l[TB][256];
+    __shared__ __attribute__((aligned(16))) float cand_l[TB][256];
     __shared__ float scr[TB][64];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int tl = wave, t = blockIdx.x * TB + tl;
