@@ -89,6 +89,8 @@ def main():
                     help="layers of the T=4096 stack leg (0: skip it)")
     ap.add_argument("--chunked-tokens", type=int, default=16384,
                     help="prompt length of the chunked-prefill leg (0 skips it)")
+    ap.add_argument("--affine-sets", type=int, default=4,
+                    help="weight sets of the affine-bias prefill leg (0: skip it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -164,30 +166,41 @@ def main():
     gateup_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     down_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
 
-    # throughput: the layer steps captured once in a HIP graph (one step per weight
-    # set), replayed so that exactly K steps run between the two events
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for w in sets:
-            step(w)
-    graph.replay()
+    # throughput: the layer steps captured in HIP graphs (one step per weight set, and
+    # the K mod sets remaining steps), replayed so that exactly K steps run between the
+    # first and the last event; an event between replays gives each replay's time
+    def capture(ws_):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for w in ws_:
+                step(w)
+        g.replay()
+        return g
+
+    graph = capture(sets)
+    reps, rem = divmod(K, len(sets))
+    graph_rem = capture(sets[:rem]) if rem else None
     torch.cuda.synchronize()
-    reps = max(1, K // len(sets))
-    K = reps * len(sets)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
     wall0 = time.perf_counter()
-    t_start.record()
-    for _ in range(reps):
+    evs[0].record()
+    for i in range(reps):
         graph.replay()
-    t_end.record()
+        evs[i + 1].record()
+    if graph_rem is not None:
+        graph_rem.replay()
+    evs[-1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = evs[0].elapsed_time(evs[-1])
     ms_step = total_ms / K
-    del graph
+    rep_step_us = sorted(evs[i].elapsed_time(evs[i + 1]) / len(sets) * 1e3 for i in range(reps))
+    step_stats = ({"mean": round(ms_step * 1e3, 2), "median": round(rep_step_us[len(rep_step_us) // 2], 2),
+                   "min": round(rep_step_us[0], 2), "replays": reps, "steps_per_replay": len(sets)}
+                  if reps else {"mean": round(ms_step * 1e3, 2)})
+    del graph, graph_rem
 
+    print(f"[bench] prefill {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     rows = T * K_TOP + T
     flops_gateup = 2.0 * rows * (2 * I) * H
     flops_down = 2.0 * rows * I * H
@@ -195,14 +208,56 @@ def main():
     gateup_tflops = flops_gateup / (gateup_ms * 1e-3) / 1e12
     layer_mfma_frac = (flops_gateup + flops_down) / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
+    # ---------------- the same workload with biases b != -8 s in every group ----------------
+    # (the general affine format: the GEMMs add the rank-G bias term in every item)
+    affine = None
+    if args.affine_sets:
+        print(f"[bench] affine biases, {args.affine_sets} weight sets", file=sys.stderr, flush=True)
+        del sets
+        torch.cuda.empty_cache()
+        asets = [device_layer(make_layer_device(SEED_PREFILL + 100 * s, T, H, I, E, zipf_s=ZIPF_S,
+                                                device=dev, with_x=False, affine=True))
+                 for s in range(args.affine_sets)]
+        for w in asets:
+            step(w)
+        torch.cuda.synchronize()
+        aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(len(asets))]
+        for i, w in enumerate(asets):
+            moe.moe_route(shape, x, w, r, ws)
+            aev[i][0].record()
+            moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
+            aev[i][1].record()
+            moe.moe_down_combine(shape, h, w, r, y, ws)
+        torch.cuda.synchronize()
+        a_gateup_us = sum(e[0].elapsed_time(e[1]) for e in aev) / len(aev) * 1e3
+        ag = capture(asets)
+        torch.cuda.synchronize()
+        areps = 4
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(areps):
+            ag.replay()
+        a1.record()
+        torch.cuda.synchronize()
+        a_us = a0.elapsed_time(a1) / (areps * len(asets)) * 1e3
+        affine = {"workload": "prefill2048_zipf_affine: the headline layer with every group's bias "
+                              "b = -8 s + d, d ~ U(-2 s, 2 s) (rank-G bias term in every GEMM item)",
+                  "us_per_step": round(a_us, 2), "tokens_per_s": round(T / (a_us * 1e-6), 1),
+                  "gateup_us": round(a_gateup_us, 2),
+                  "gateup_mfma_frac": round(flops_gateup / (a_gateup_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                  "weight_sets": len(asets)}
+        del ag, asets
+        torch.cuda.empty_cache()
+    else:
+        del sets
+
     # ---------------- decode: T=1 ----------------
     # One weight set per layer of a 40-layer decode stack.  (i) decode-path bandwidth: one
     # moe_decode per layer on that layer's own token, independent calls in one HIP graph;
     # (ii) the chained stack: every layer decodes the previous layer's output after the
     # residual add and RMSNorm, 40 layers in one HIP graph with no host synchronisation.
-    print(f"[bench] prefill {ms_step * 1e3:.1f} us/step; decode with {args.decode_sets} weight sets",
-          file=sys.stderr, flush=True)
-    del sets
+    print(f"[bench] decode with {args.decode_sets} weight sets", file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
     dshape = moe.Shape(T=1, H=H, I=I, E=E, top_k=K_TOP)
     dsets = []
@@ -479,10 +534,19 @@ def main():
         t0 = time.perf_counter()
         L.tokens(toks)
         dt = time.perf_counter() - t0
+        # one thread, on a sample of about a sixth of that time
+        oracle.set_threads(1)
+        n1 = max(1, min(n, int(n / cores * 2)))
+        t0 = time.perf_counter()
+        L.tokens(toks[:n1])
+        dt1 = time.perf_counter() - t0
+        oracle.set_threads(cores)
         cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                "sample": f"{n} of the {T} tokens of the same layer (weight set 0), full per-token "
                          f"path: router over 256 experts, top-8, 9 SwiGLU experts in float64; "
-                         f"{dt:.1f} s wall"}
+                         f"{dt:.1f} s wall",
+               "single_thread": {"value": round(n1 / dt1, 3), "unit": "tokens/s", "cores": 1,
+                                 "sample": f"the first {n1} of those tokens, {dt1:.1f} s wall"}}
 
     out = {
         "metric": METRIC,
@@ -492,6 +556,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_us": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -513,6 +578,7 @@ def main():
         "phase_us": {"route": round(route_ms * 1e3, 2), "gateup": round(gateup_ms * 1e3, 2),
                      "down_combine": round(down_ms * 1e3, 2)},
         "wall_s": round(wall, 3),
+        "prefill2048_zipf_affine": affine,
         "decode": {"metric": "T=1 decode HBM GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
                    "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(dec_us, 2),
                    "bytes_per_call": dec_bytes, "weight_sets": args.decode_sets},

@@ -239,15 +239,16 @@ constexpr int QCTL_WORDS = 4 * QCTL_LINE;
 // with moe_pack_weights).
 constexpr int PK_BLOCK = 9216;
 constexpr int PK_CODES = 8192;      // byte offset of the scales; biases at +512
-// Per projection row (one GEMM column), two power-of-two factors written at load time:
+// Per projection row (one GEMM column), a power-of-two factor written at load time:
 //  colk = 2^-k: the block holds scale and bias times 2^k, with k chosen so that the
 //         row's largest |scale| times 2^k lies in [2^10, 2^11); the rebuilt fp16
 //         weights (q - 8) s 2^k are then exact whenever the row's nonzero scales span
-//         at most 2^23, whatever their absolute size; results are multiplied by colk;
-//  colc = 2^-sigma: scale of c = (b + 8 s) 2^k in the rank-G bias pass, so that every
-//         |c| colc < 2^14 (its fp16 hi/lo split cannot overflow).
-// They are stored per tile: [colk of the 256 columns][colc of the 256 columns].
-constexpr int PK_COLF = 512;        // floats of column factors per tile
+//         at most 2^23, whatever their absolute size; results are multiplied by colk.
+// They are stored per tile: [colk of the 256 columns][flags], the flags word (int32 at
+// float index PK_TFLAG) nonzero when some column of the tile has a group with b != -8 s
+// (the tile needs the rank-G bias term).
+constexpr int PK_COLF = 260;        // floats of column factors and flags per tile (16-byte multiple)
+constexpr int PK_TFLAG = 256;
 // Load-time validation flags (the status word of the meta section)
 constexpr int PK_BAD_NONFINITE = 1;     // a scale or bias is NaN or infinite
 constexpr int PK_BAD_SCALE_SPAN = 2;    // a row's nonzero scales span more than 2^23

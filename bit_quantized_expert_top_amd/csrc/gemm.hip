@@ -135,6 +135,10 @@ __device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
+}
 
 // The same copies with a wave-uniform base address in SGPRs and a per-lane
 // 32-bit byte offset: the per-lane offsets stay fixed over the K loop and each
@@ -236,13 +240,75 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
         dma16s(blk + 4096, boff, lds0 + base + (uint32_t)(RG::A_BYTES + (256 + wave * 64) * 16));
         dma4s(blk, soff, lds0 + base + (uint32_t)(RG::A_BYTES + B_BYTES + wave * 256));
     };
+    floatx16 acc[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mt][0][i] = acc[mt][1][i] = 0.0f;
+
+    const float *tcolf = t.shared ? a.colf_sh + (size_t)t.ntile * PK_COLF
+                                  : a.colf + ((size_t)t.e * a.n_tiles + t.ntile) * PK_COLF;
+    // ---- rank-G term, for tiles with some group whose bias is not -8 s (a flag set at load
+    // time; none for symmetric codes): sum_g c_g xs_g, with c = b + 8 s per column and group
+    // (from the block's values, so at the column's 2^k like the main loop's weights) and xs
+    // the rows' group sums.  It runs before the main loop, in the (still free) ring: the G
+    // blocks' scale/bias sections (1 KB each) and the rows' group sums are copied in by DMA in
+    // one round trip, then fp32 MFMA steps (32 x 32 x 2, fp32 operands: no rounding of c or xs,
+    // no range limit) start the accumulators.
+    if (__builtin_amdgcn_readfirstlane(((const int *)tcolf)[PK_TFLAG])) {
+        // thread (row 32 i + tid / 8, p = tid % 8) copies the row's group sums g = p + 8 u
+        const int per = (G + 7) / 8;
+        const uint32_t sb0 = lds0, xs0 = lds0 + (uint32_t)(G * 1024);
+        for (int g = wave; g < G; g += NW)
+            dma16(tb + (size_t)g * PK_BLOCK + PK_CODES + 16 * lane, sb0 + (uint32_t)(1024 * g));
+        {
+            const int p = tid & 7;
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                // row 32 i + tid / 8 of the tile: its source row (gate/up: the token, read back
+                // from the A copy offsets instead of reloading row_token)
+                const int srow = MODE == 0 ? (int)((aoff[i] >> 1) / (uint32_t)K)
+                                           : src_row<MODE>(a, t, 32 * i + (tid >> 3));
+                for (int u = 0; u < per; ++u) {
+                    const int g = p + 8 * u;
+                    if (g < G)
+                        dma4(a.Asum + (size_t)srow * G + g,
+                             xs0 + (uint32_t)(4 * ((i * per + u) * 256 + 64 * wave)));
+                }
+            }
+        }
+        wait_vm<0>();
+        __syncthreads();
+        const uint8_t *sbl = smem;
+        const float *xsl = (const float *)(smem + G * 1024);
+        // k step j: groups 2 j and 2 j + 1; lane (l32, gg) supplies group 2 j + gg of row l32
+        // (A) and of column l32 (B)
+        for (int j = 0; j < (G + 1) / 2; ++j) {
+            const int g = 2 * j + gg;
+            float bv[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const uint8_t *sp = sbl + 1024 * min(g, G - 1) + 2 * (64 * wave + 32 * nt + l32);
+                const float cf = __builtin_fmaf(8.0f, bf16_to_f32(*(const uint16_t *)sp),
+                                                bf16_to_f32(*(const uint16_t *)(sp + 512)));
+                bv[nt] = g < G ? cf : 0.0f;
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float xs = g < G ? xsl[(mt * per + (g >> 3)) * 256 + 8 * l32 + (g & 7)] : 0.0f;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(xs, bv[nt], acc[mt][nt], 0, 0, 0);
+            }
+        }
+        __syncthreads();                         // the staged operands are no longer read
+    }
+
     // RG::PER copies per thread and stage, completing in order: stage c is in
     // once at most (stages issued after it) * PER copies are outstanding.
     // The epilogue's per-item values (ItemLds) are copied into LDS by DMA before the
     // stage copies (so older than all of them) and complete with the main loop's last
     // wait.  Plain loads would be waited for in the epilogue behind its own stores.
-    const float *tcolf = t.shared ? a.colf_sh + (size_t)t.ntile * PK_COLF
-                                  : a.colf + ((size_t)t.e * a.n_tiles + t.ntile) * PK_COLF;
     {
         auto lds_of = [](const float *p) {
             return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
@@ -266,19 +332,12 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
         if (decltype(P)::value < nch) issue(decltype(P)::value, P);
     });
 
-    floatx16 acc[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mt][0][i] = acc[mt][1][i] = 0.0f;
-
     uint32_t cM = 0x000F000Fu, cM2 = 0x00F000F0u, cC = 0x64006400u;
     asm volatile("" : "+v"(cM), "+v"(cM2), "+v"(cC));   // keep the unpack constants in VGPRs
     const f16x2 m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const f16x2 m1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     const int sw = (l32 >> 1) & 7;
     const int swb = (l32 >> 3) & 1;
-    bool nz = false;                             // any group with b != -8 s in my columns
     int next = 0;
 
     // K loop unrolled by the ring depth, so that stage c's ring slot (c % NST)
@@ -312,7 +371,6 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 wq[nt] = *(const u32x4 *)(sb + RG::A_BYTES + bc * 32 + 16 * (gg ^ swb));
                 const uint8_t *pr = sb + RG::A_BYTES + B_BYTES + bc * 2;
                 const float sf = bf16_to_f32(*(const uint16_t *)pr);
-                nz |= bf16_to_f32(*(const uint16_t *)(pr + 512)) != -8.0f * sf;
                 const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
                 ss[nt] = f16x2{sh, sh};
                 ss16[nt] = f16x2{sh16, sh16};
@@ -349,90 +407,6 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     }
 
     if (tid == 0) *s_next = next;                // read after the caller's next barrier
-    // ---- rank-G term for groups whose bias is not -8 s (none for symmetric codes)
-    if (__any(nz)) {
-        // The term is added at a reduced scale so that no fp16 operand overflows: the group
-        // sums enter as xs 2^-6 (|x| < 2^14 and |h| < 2^15 keep |xs| 2^-6 < 2^15) and each
-        // column's c as c colc (|c colc| < 2^14); the accumulators are brought to that scale
-        // first and back afterwards (powers of two: exact).
-        const int K3 = 3 * G;
-        int srcr[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) srcr[mt] = src_row<MODE>(a, t, 32 * mt + l32);
-        // scale and bias of my columns, group g: tile block g, bytes PK_CODES + 2 c
-        const uint8_t *cs[2];
-        float ccol[2], rsc[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            cs[nt] = tb + PK_CODES + 2 * (64 * wave + 32 * nt + l32);
-            ccol[nt] = tcolf[256 + 64 * wave + 32 * nt + l32];
-            rsc[nt] = ccol[nt] * 0x1p-6f;
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= rsc[nt];
-        for (int j3 = 0; j3 < (K3 + 15) / 16; ++j3) {
-            uint32_t bw[2][4], aw[MT][4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                float bvals[2][2], avals[MT][2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    // operand slot k'' = 16 j3 + 8 gg + 2 e2 + hh: term tau, group g
-                    const int kk = 16 * j3 + 8 * gg + 2 * e2 + hh;
-                    const int tau = kk / G, g = kk - tau * G;
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        float v = 0.0f;
-                        if (tau < 3) {
-                            const uint8_t *sp = cs[nt] + (size_t)g * PK_BLOCK;
-                            const float cf = (bf16_to_f32(*(const uint16_t *)(sp + 512)) +
-                                              8.0f * bf16_to_f32(*(const uint16_t *)sp)) * ccol[nt];
-                            const float hi = (float)(_Float16)cf;
-                            v = tau < 2 ? hi : (float)(_Float16)(cf - hi);
-                        }
-                        bvals[nt][hh] = v;
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        float v = 0.0f;
-                        if (tau < 3) {
-                            const float xs = a.Asum[(size_t)srcr[mt] * G + g] * 0x1p-6f;
-                            const float hi = (float)(_Float16)xs;
-                            v = tau == 1 ? (float)(_Float16)(xs - hi) : hi;
-                        }
-                        avals[mt][hh] = v;
-                    }
-                }
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) bw[nt][e2] = pack_f16x2(bvals[nt][0], bvals[nt][1]);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) aw[mt][e2] = pack_f16x2(avals[mt][0], avals[mt][1]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const u32x4 av = {aw[mt][0], aw[mt][1], aw[mt][2], aw[mt][3]};
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const u32x4 bv = {bw[nt][0], bw[nt][1], bw[nt][2], bw[nt][3]};
-                    acc[mt][nt] = mfma16(__builtin_bit_cast(f16x8, av),
-                                         __builtin_bit_cast(f16x8, bv), acc[mt][nt]);
-                }
-            }
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) rsc[nt] = 1.0f / rsc[nt];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= rsc[nt];
-    }
-
     // ---- epilogue.  Accumulator element i of lane (l32, gg) is row
     // 8*(i/4) + 4*gg + i%4 of its 32-row tile, column l32 of the wave's n-tile.
     __syncthreads();                             // every wave is done with the ring

@@ -70,10 +70,11 @@ __host__ __device__ inline void row_to_col(int gu, int proj, int n, int &j, int 
 }
 
 // Load-time statistics, one wave per projection row (expert e, projection proj, row n):
-// the power-of-two shift k of the row's scales, the rank-G scale sigma, the row's L2
+// the power-of-two shift k of the row's scales, whether its tile needs the rank-G bias
+// term, the row's L2
 // norm (gate and up rows: folded into the expert slot's bound by an atomic max on the
 // float's bits, which orders like the value for non-negative floats) and the validation
-// flags.  meta must hold zeros in the status line and the expert bounds beforehand.
+// flags.  The meta section must hold zeros beforehand.
 __global__ __launch_bounds__(256) void pack_stats_kernel(PackSrc src, int nexp, int N, int K, int gu,
                                                         int slot0, float *__restrict__ colf,
                                                         float *__restrict__ emeta,
@@ -108,19 +109,15 @@ __global__ __launch_bounds__(256) void pack_stats_kernel(PackSrc src, int nexp, 
     const bool bad_span = smax > 0.0f && smin * kmul < 0x1p-13f;
     const float bk = bv * kmul;
     const bool bad_bias = lane < G && __builtin_isfinite(bv) && !(fabsf(bk) < 0x1.fep127f);
-    // c = (b + 8 s) 2^k from the bf16 values the blocks will hold
-    const float ck = lane < G ? fabsf(bf16_to_f32(f32_to_bf16(bk)) + 8.0f * bf16_to_f32(f32_to_bf16(sv * kmul))) : 0.0f;
-    float cmax = __builtin_isfinite(ck) ? ck : 0.0f;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
-    const int sigma = cmax >= 16384.0f ? ilog2f(cmax) - 13 : 0;
+    // a group with b != -8 s: the row's tile needs the rank-G bias term
+    const bool affine = __any(lane < G && bv != -8.0f * sv);
     if (lane == 0) {
         int j, c;
         row_to_col(gu, proj, n, j, c);
         const int JT = gu ? N / 128 : N / 256;
         float *cf = colf + ((size_t)e * JT + j) * PK_COLF;
         cf[c] = exp2i(-k);
-        cf[256 + c] = exp2i(-sigma);
+        if (affine) atomicOr((int *)(cf + PK_TFLAG), 1);
     }
     const int flags = (__any(bad_nf) ? PK_BAD_NONFINITE : 0) | (bad_span ? PK_BAD_SCALE_SPAN : 0) |
                       (__any(bad_bias) ? PK_BAD_BIAS_RANGE : 0);
@@ -205,8 +202,9 @@ void launch_pack(const moe_shape &sh, const moe_weights &w, uint8_t *dst, int32_
     auto gp = [](const moe_q4 &p) { return GemmProj{p.q, p.scale, p.bias}; };
     int32_t *st = (int32_t *)(dst + L.status);
     float *emeta = (float *)(dst + L.emeta);
-    // the status line and the expert bounds start at zero (a fill kernel, not a memset)
-    const size_t nz = (L.cgu - L.status) / 4;
+    // the meta section starts at zero: status, expert bounds, tile flags (a fill kernel,
+    // not a memset)
+    const size_t nz = (L.total - L.status) / 4;
     hipLaunchKernelGGL(pack_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s,
                        (uint32_t *)st, nz);
     auto stats = [&](PackSrc src, int nexp, int N, int K, int gu, int slot0, size_t coff) {

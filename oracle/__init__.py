@@ -66,8 +66,14 @@ def lib():
         L.oracle_expert_down.argtypes = [C.POINTER(_Layer), i32, P, P]
         L.oracle_moe_tokens.argtypes = [C.POINTER(_Layer), P, i32, P, P, P]
         L.oracle_rmsnorm_residual.argtypes = [i32, i32, C.c_double, P, P, P, P]
+        L.oracle_set_threads.argtypes = [i32]
         _lib = L
     return _lib
+
+
+def set_threads(n: int):
+    """Threads of the oracle's OpenMP loops (for timing the CPU baseline)."""
+    lib().oracle_set_threads(int(n))
 
 
 def _p(a: Optional[np.ndarray]):

@@ -28,9 +28,16 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no -ffast-math).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the OpenMP loops below (timing the CPU baseline at one thread and at all). */
+void oracle_set_threads(int32_t n)
+{
+    if (n > 0) omp_set_num_threads(n);
+}
 
 typedef struct {
     const uint32_t *q;   /* codes [N][K/8], 8 per word, low nibble first   */

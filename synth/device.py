@@ -17,18 +17,23 @@ def _bf16_bits(t: torch.Tensor) -> torch.Tensor:
     return t.to(torch.bfloat16).view(torch.int16)      # round to nearest even
 
 
-def _proj(g: torch.Generator, lead, N, K, dev):
+def _proj(g: torch.Generator, lead, N, K, dev, affine: bool = False):
     q = torch.randint(-2 ** 31, 2 ** 31, lead + (N, K // PACK), generator=g, device=dev,
                       dtype=torch.int64).to(torch.int32)
     s = torch.empty(lead + (N, K // GROUP), device=dev, dtype=torch.float32).uniform_(
         0.002, 0.02, generator=g).to(torch.bfloat16)
-    b = (-8.0 * s.float()).to(torch.bfloat16)           # exact: -8 only moves the exponent
-    return q, s.view(torch.int16), b.view(torch.int16)
+    b = -8.0 * s.float()                                # exact: -8 only moves the exponent
+    if affine:
+        # the general affine case: every group's bias off -8 s by d ~ U(-2 s, 2 s)
+        d = torch.empty_like(b).uniform_(-2.0, 2.0, generator=g) * s.float()
+        b = b + d
+    return q, s.view(torch.int16), b.to(torch.bfloat16).view(torch.int16)
 
 
 def make_layer_device(seed: int, T: int, H: int, I: int, E: int = 256, zipf_s=None,
-                      device="cuda", with_x: bool = True) -> dict:
-    """Dict of device tensors: x, router_wt, router_bias and the six projections."""
+                      device="cuda", with_x: bool = True, affine: bool = False) -> dict:
+    """Dict of device tensors: x, router_wt, router_bias and the six projections
+    (affine=True: biases b != -8 s in every group)."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
@@ -38,12 +43,12 @@ def make_layer_device(seed: int, T: int, H: int, I: int, E: int = 256, zipf_s=No
     out["router_wt"] = _bf16_bits(torch.randn((E, H), generator=g, device=dev) / float(np.sqrt(H)))
     out["router_bias"] = (None if zipf_s is None else
                           torch.from_numpy(zipf_bias(E, zipf_s)).to(dev))
-    out["gate"] = _proj(g, (E,), I, H, dev)
-    out["up"] = _proj(g, (E,), I, H, dev)
-    out["down"] = _proj(g, (E,), H, I, dev)
-    out["sh_gate"] = _proj(g, (), I, H, dev)
-    out["sh_up"] = _proj(g, (), I, H, dev)
-    out["sh_down"] = _proj(g, (), H, I, dev)
+    out["gate"] = _proj(g, (E,), I, H, dev, affine)
+    out["up"] = _proj(g, (E,), I, H, dev, affine)
+    out["down"] = _proj(g, (E,), H, I, dev, affine)
+    out["sh_gate"] = _proj(g, (), I, H, dev, affine)
+    out["sh_up"] = _proj(g, (), I, H, dev, affine)
+    out["sh_down"] = _proj(g, (), H, I, dev, affine)
     return out
 
 

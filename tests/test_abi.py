@@ -194,7 +194,7 @@ def test_python_binding_checks_tensors():
 def test_packed_bytes_and_pack_validation():
     """The tile layout holds the row layout's bytes (four sections, each rounded up to
     256 bytes), then the meta section: a 256-byte status line, 16 bytes per expert slot
-    and 2 KB of column factors per 256-column tile; moe_pack_weights validates its
+    and 1040 bytes of column factors and flags per 256-column tile; moe_pack_weights validates its
     arguments before any launch."""
     L = B.lib()
     for H, I in [(2048, 512), (512, 128), (1024, 256)]:
@@ -203,7 +203,7 @@ def test_packed_bytes_and_pack_validation():
         assert L.moe_packed_bytes(C.byref(s), C.byref(n)) == OK
         per_expert = 3 * H * I // 2 + 3 * 2 * 2 * H * I // 64     # codes + scales + biases
         tiles = 257 * (I // 128 + H // 256)
-        meta = 256 + 257 * 16 + tiles * 2048
+        meta = 256 + 257 * 16 + tiles * 1040
         assert n.value >= 257 * per_expert + meta and n.value < 257 * per_expert + meta + 10 * 256
         assert n.value % 256 == 0
     s = shape(T=1)

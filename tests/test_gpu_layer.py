@@ -195,6 +195,8 @@ def test_layer_repeat_bit_identical():
 @pytest.mark.parametrize("name,kw,seed", [
     ("tiny", dict(T=32, H=512, I=128), 1100),
     ("medium_zipf", dict(T=256, H=2048, I=512, zipf_s=1.1), 1101),
+    # 12 groups along H and 6 along I: group counts that are not multiples of 8
+    ("H768_I384", dict(T=150, H=768, I=384, zipf_s=1.1), 1102),
 ])
 def test_layer_asymmetric_bias(name, kw, seed):
     print(f"[layer-bias] {name} seed={seed} {kw}", flush=True)

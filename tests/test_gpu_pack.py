@@ -115,10 +115,11 @@ def test_pack_matches_documented_layout(H, I):
     emeta = got[off:off + 257 * 16].view(np.float32).reshape(257, 4)
     off = (off + 257 * 16 + 255) // 256 * 256
     for ck in colk:
-        n = ck.size * 2 * 4
-        cf = got[off:off + n].view(np.float32).reshape(ck.shape[0], ck.shape[1], 2, 256)
-        np.testing.assert_array_equal(cf[:, :, 0, :], ck.astype(np.float32))
-        np.testing.assert_array_equal(cf[:, :, 1, :], 1.0)      # b = -8 s: no rank-G scale
+        # per tile: 2^-k of the 256 columns, a flags word, padding
+        n = ck.shape[0] * ck.shape[1] * 260 * 4
+        cf = got[off:off + n].view(np.float32).reshape(ck.shape[0], ck.shape[1], 260)
+        np.testing.assert_array_equal(cf[:, :, :256], ck.astype(np.float32))
+        assert np.all(cf[:, :, 256:].view(np.int32) == 0)       # b = -8 s: no rank-G term
         off = (off + n + 255) // 256 * 256
     assert off == got.size == moe.moe_packed_bytes(moe.Shape(T=1, H=H, I=I, E=E))
     # the bound on the L2 norm of every gate and up row of each expert slot
