@@ -380,10 +380,12 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     for (int q = 0; q < HCH; ++q)
         if (tid + 64 * DW * q < nh) hl[q] = ((const u32x4 *)hbuf)[tid + 64 * DW * q];
     int sid[NSLOT];
+    float sfac[NSLOT];     // per slot: routing weight (1 for the shared expert) times 2^f of its h
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
         const int e = s < k ? ids[s] : 0;
         sid[s] = (e < 0 || e >= E) ? 0 : e;
+        sfac[s] = (s < k ? tw[s] : 1.0f) * hfac[s];
     }
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     uint32_t cM = 0x000F000Fu, cC = 0x64006400u;
@@ -456,10 +458,11 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     if (tid < DOUT) {
         // each slot's h was kept as h 2^-f: its weight (1 for the shared expert) times 2^f
         float sum = 0.0f;
-        for (int s = 0; s <= k; ++s) {
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s) {
             float a = 0.0f;
             for (int g = 0; g < G; ++g) a += part[s * G + g][tid];
-            sum = s < k ? __builtin_fmaf(tw[s] * hfac[s], a, sum) : __builtin_fmaf(hfac[s], a, sum);
+            sum = __builtin_fmaf(sfac[s], a, sum);
         }
         y[256 * j + DOUT * v + tid] = sum;
     }
