@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     lib,
     moe_decode,
     moe_decode_residual,
+    moe_debug_status,
     moe_decode_static,
     moe_dequant_q4,
     moe_down_combine,

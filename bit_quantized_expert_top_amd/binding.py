@@ -10,7 +10,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoeq4.so")
+# MOE_Q4_LIB selects another build of the library (the MOE_DEBUG build, say)
+LIB_PATH = os.environ.get("MOE_Q4_LIB") or os.path.join(_HERE, "libmoeq4.so")
 
 P = C.c_void_p
 i32 = C.c_int32
@@ -60,6 +61,7 @@ _SIGS = {
                              C.c_size_t, P], i32),
     "moe_rmsnorm_residual": ([i32, i32, C.c_float, P, P, P, P], i32),
     "moe_dequant_q4": ([C.POINTER(_Q4), i32, i32, P, P], i32),
+    "moe_debug_status": ([C.POINTER(C.c_uint32), i32], i32),
     "moe_status_str": ([i32], C.c_char_p),
 }
 
@@ -103,6 +105,17 @@ class UnsupportedWeights(MoeError):
 
 def moe_status_str(status: int) -> str:
     return lib().moe_status_str(status).decode()
+
+
+def moe_debug_status(clear: bool = True):
+    """Index checks recorded by a MOE_DEBUG build (synchronises the device), or None when the
+    loaded library is a regular build."""
+    v = C.c_uint32(0)
+    st = lib().moe_debug_status(C.byref(v), 1 if clear else 0)
+    if st == -2:
+        return None
+    _check(st, "moe_debug_status")
+    return v.value
 
 
 def _check(status: int, where: str):

@@ -37,11 +37,26 @@ ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 PER_SOURCE = {"gemm.hip": ILP, "route.hip": ILP}
 
 
-def build(verbose: bool = False) -> str:
+# Host code checked by AddressSanitizer and UndefinedBehaviorSanitizer (the GPU code is
+# built as usual): every sanitizer flag is restricted to the host pass.  The library
+# leaves the sanitizer runtime to the executable that loads it.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
+# Device-side index checks that record what they catch in a status word (moe_debug_status)
+DEBUG = ["-DMOE_DEBUG"]
+
+
+def build(verbose: bool = False, sanitize: bool = False, debug: bool = False,
+          out: str = None) -> str:
+    """Compile every source and link the library (default: libmoeq4.so next to this file).
+    sanitize: host code with ASan + UBSan; debug: device index checks (MOE_DEBUG)."""
+    lib = out or LIB
+    extra = (SANITIZE if sanitize else []) + (DEBUG if debug else [])
     with tempfile.TemporaryDirectory(prefix="moeq4_") as tmpdir:
         def compile_one(src):
             obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
-            cmd = [HIPCC, *FLAGS, *PER_SOURCE.get(src, []), "-c", "-o", obj,
+            cmd = [HIPCC, *FLAGS, *PER_SOURCE.get(src, []), *extra, "-c", "-o", obj,
                    os.path.join(CSRC, src)]
             if verbose:
                 print(" ".join(cmd), flush=True)
@@ -50,13 +65,13 @@ def build(verbose: bool = False) -> str:
 
         with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as pool:
             objs = list(pool.map(compile_one, SOURCES))
-        tmp = LIB + ".tmp"
+        tmp = lib + ".tmp"
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -421,7 +421,22 @@ moe_status moe_dequant_q4(const moe_q4 *p, int32_t N, int32_t K, uint16_t *out, 
     return launched();
 }
 
-const char *moe_status_str(moe_status s) {
+moe_status moe_debug_status(uint32_t *flags, int32_t clear) {
+    if (!flags) return MOE_ERR_INVALID_ARG;
+#ifdef MOE_DEBUG
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+    const uint32_t v = dbg_read_route(clear != 0) | dbg_read_gemm(clear != 0) |
+                       dbg_read_decode(clear != 0);
+    *flags = v;
+    return (v & 0x80000000u) ? MOE_ERR_HIP : MOE_OK;
+#else
+    (void)clear;
+    *flags = 0;
+    return MOE_ERR_UNSUPPORTED;
+#endif
+}
+
+const char *moe_status_str(int32_t s) {
     switch (s) {
         case MOE_OK: return "ok";
         case MOE_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer or bad size)";

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe_q4.h"
 
 namespace moe {
@@ -267,6 +269,61 @@ PackLayout pack_layout(int H, int I, int E);
 // 1 up), row 128 j + 32 (c >> 6) + (c & 31); of a down block: row 256 j + c
 void launch_pack(const moe_shape &sh, const moe_weights &w, uint8_t *dst, int32_t *status,
                  hipStream_t s);
+
+// Device index checks of the MOE_DEBUG build.  Wherever a kernel meets an index that the
+// routing structures should never hold (an expert id, row, token or block out of range) it
+// already clamps or skips it; the debug build also records what it met in a status word of
+// the translation unit (moe_debug_status reads and clears them all).  Vector atomics only.
+constexpr uint32_t DBG_ROUTE_INDEX = 1;     // scatter: pick expert or row out of range
+constexpr uint32_t DBG_GEMM_BLOCK = 2;      // grouped GEMM: malformed block map entry
+constexpr uint32_t DBG_GEMM_TOKEN = 4;      // grouped GEMM: row token out of range
+constexpr uint32_t DBG_COMBINE_ROW = 8;     // combine: a pick's row out of range
+constexpr uint32_t DBG_DECODE_ID = 16;      // decode: a pick's expert id out of range
+#ifdef MOE_DEBUG
+static __device__ uint32_t dbg_word;
+#define MOE_DBG(cond, bit)                           \
+    do {                                             \
+        if (!(cond)) atomicOr(&dbg_word, (bit));     \
+    } while (0)
+// host: read (and clear) this translation unit's status word
+#define MOE_DBG_READER(name)                                                          \
+    uint32_t name(bool clear) {                                                       \
+        uint32_t v = 0;                                                               \
+        if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(dbg_word), sizeof v, 0,                \
+                                hipMemcpyDeviceToHost) != hipSuccess)                 \
+            return 0x80000000u;                                                       \
+        if (clear) {                                                                  \
+            const uint32_t z = 0;                                                     \
+            (void)hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &z, sizeof z, 0,            \
+                                    hipMemcpyHostToDevice);                           \
+        }                                                                             \
+        return v;                                                                     \
+    }
+#else
+#define MOE_DBG(cond, bit) ((void)0)
+#define MOE_DBG_READER(name) \
+    uint32_t name(bool) { return 0; }
+#endif
+uint32_t dbg_read_route(bool clear);
+uint32_t dbg_read_gemm(bool clear);
+uint32_t dbg_read_decode(bool clear);
+
+// A kernel's dynamic-LDS limit raised once per device (thread-safe: a host thread's
+// first launch on a device sets it, concurrent first launches wait for that).
+struct LdsLimit {
+    static constexpr int kMaxDevices = 64;
+    std::once_flag once[kMaxDevices];
+    void ensure(const void *fn, int bytes) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+            (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+            return;
+        }
+        std::call_once(once[dev], [&] {
+            (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        });
+    }
+};
 
 // Workspace layout (byte offsets), shared by route/gemm/decode.  All host-known.
 struct WsLayout {

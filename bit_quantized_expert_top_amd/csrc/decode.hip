@@ -234,12 +234,14 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     int ex = 0;
     if (slot < k && picks_given) {
         ex = ids_out[slot];                                       // written by decode_select_kernel
+        MOE_DBG(ex >= 0 && ex < E, DBG_DECODE_ID);
         ex = (ex < 0 || ex >= E) ? 0 : ex;
     } else if (slot < k) {
         int pe;
         float pl;
         select_topk(logits, E, k, pe, pl, selw[wave]);
         ex = __builtin_amdgcn_readlane(pe, slot);
+        MOE_DBG(ex >= 0 && ex < E, DBG_DECODE_ID);
         ex = (ex < 0 || ex >= E) ? 0 : ex;
         if (blockIdx.x == 0 && wave == 0) {
             const float wv = topk_weight(pl, k);
@@ -384,6 +386,7 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
         const int e = s < k ? ids[s] : 0;
+        MOE_DBG(e >= 0 && e < E, DBG_DECODE_ID);
         sid[s] = (e < 0 || e >= E) ? 0 : e;
         sfac[s] = (s < k ? tw[s] : 1.0f) * hfac[s];
     }
@@ -500,5 +503,7 @@ size_t decode_scratch_bytes(int T, int H, int I, int k) {
     (void)H;
     return decode_scratch_size(T, I, k);
 }
+
+MOE_DBG_READER(dbg_read_decode)
 
 }  // namespace moe

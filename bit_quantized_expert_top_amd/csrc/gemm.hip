@@ -179,6 +179,7 @@ __device__ __forceinline__ int src_row(const GemmArgs &a, const Tile &t, int m) 
     const int mm = m < t.nrows ? m : 0;
     if (MODE == 0) {
         const int tok = t.shared ? (t.r0 - a.T * a.topk + mm) : a.row_token[t.r0 + mm];
+        MOE_DBG(tok >= 0 && tok < a.T, DBG_GEMM_TOKEN);
         return (tok >= 0 && tok < a.T) ? tok : 0;
     }
     return t.r0 + mm;
@@ -546,6 +547,7 @@ __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
                 ok = !(t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
                        t.r0 + t.nrows > a.T * a.topk);
             }
+            if (threadIdx.x == 0) MOE_DBG(ok, DBG_GEMM_BLOCK);
         } else {
             t.r0 = a.T * a.topk + slot * kBM;
             t.nrows = min(kBM, a.T - slot * kBM);
@@ -583,12 +585,8 @@ static unsigned grid_for(int n_shared, int max_blocks, int n_tiles) {
 // the GEMM needs more dynamic LDS than the default launch limit
 template <int MODE>
 static void allow_lds() {
-    static bool done = false;
-    if (!done) {
-        (void)hipFuncSetAttribute((const void *)q4_gemm_kernel<MODE>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, L_TOTAL);
-        done = true;
-    }
+    static LdsLimit lim;
+    lim.ensure((const void *)q4_gemm_kernel<MODE>, L_TOTAL);
 }
 
 void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, const float *tok,
@@ -644,7 +642,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     u32x4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
+    {
+        MOE_DBG(j >= k || (rows[j] >= 0 && rows[j] < T * k), DBG_COMBINE_ROW);
         if (rows[j] >= 0 && rows[j] < T * k) v[j] = *(const u32x4 *)(stage + (size_t)rows[j] * H + n);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (rows[j] < 0 || rows[j] >= T * k) continue;
@@ -701,5 +702,7 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, stage,
                        tok_row, sh.T, sh.H, sh.top_k, y);
 }
+
+MOE_DBG_READER(dbg_read_gemm)
 
 }  // namespace moe

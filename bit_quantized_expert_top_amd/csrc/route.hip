@@ -716,12 +716,8 @@ void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int
                         float *wn2part, uint16_t *xp, float *xsum, float *xsq, float *xmx,
                         hipStream_t s) {
     const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
-    static bool lds_set = false;
-    if (!lds_set) {
-        (void)hipFuncSetAttribute((const void *)router_mfma_kernel,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, R_NST * R_STAGE);
-        lds_set = true;
-    }
+    static LdsLimit lim;
+    lim.ensure((const void *)router_mfma_kernel, R_NST * R_STAGE);
     hipLaunchKernelGGL(router_mfma_kernel, dim3((T + RT_TOK - 1) / RT_TOK, S), dim3(256),
                        R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq, wn2part, xmx);
 }
@@ -847,8 +843,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     if (idx >= T * k) return;
     const int t = idx / k;
     const int e = ids[idx];
+    MOE_DBG(e >= 0 && e < E, DBG_ROUTE_INDEX);
     if (e < 0 || e >= E) return;
     const int r = s_off[e] + blk_base[(size_t)(t / TB) * E + e] + lrank[idx];
+    MOE_DBG(r >= 0 && r < T * k, DBG_ROUTE_INDEX);
     if (r < 0 || r >= T * k) return;
     row_token[r] = t;
     tok_row[idx] = r;
@@ -906,5 +904,7 @@ void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xs
     hipLaunchKernelGGL(prep_act_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, rows,
                        K, xp, xsum, xsq, xmx);
 }
+
+MOE_DBG_READER(dbg_read_route)
 
 }  // namespace moe

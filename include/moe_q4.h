@@ -53,7 +53,8 @@
  *     are independent as long as they use different workspaces (a workspace
  *     holds a call's scratch rows and the GEMMs' work-queue counters: two
  *     calls in flight on one workspace race).  The only global state is the
- *     per-GPU scratch array of moe_decode_static (see there).
+ *     per-GPU scratch array of moe_decode_static (see there) and the kernels'
+ *     dynamic-LDS limits, raised once per device on first use (thread-safe).
  *   - Errors: arguments are validated on the host before anything is
  *     enqueued; a call that returns an error has enqueued nothing.
  *     MOE_ERR_INVALID_ARG: NULL or misaligned pointer, T < 1, bad sizes.
@@ -285,8 +286,18 @@ moe_status moe_rmsnorm_residual(int32_t T, int32_t H, float eps, float *r, const
  * bf16_round_nearest_even(fp32 fma(code, scale, bias)).  out: bf16 [N][K]. */
 moe_status moe_dequant_q4(const moe_q4 *p, int32_t N, int32_t K, uint16_t *out, void *stream);
 
-/* Static string for a status code. */
-const char *moe_status_str(moe_status s);
+/* Device index checks of a MOE_DEBUG build of the library (build.py debug=True).  Where a
+ * kernel meets an index that valid routing structures never hold (an expert id, row, token
+ * or block map entry out of range) it skips or clamps it in every build; the debug build
+ * also records it.  This call waits for the device (hipDeviceSynchronize: it is the one
+ * call that synchronises) and stores in *flags (host) the OR of what the kernels recorded
+ * since the last clear: 1 scatter index, 2 block map entry, 4 row token, 8 combine row,
+ * 16 decode expert id; clear != 0 resets the record.  MOE_ERR_UNSUPPORTED (and *flags = 0)
+ * in a regular build; MOE_ERR_HIP if the device or the record cannot be read. */
+moe_status moe_debug_status(uint32_t *flags, int32_t clear);
+
+/* Static string for a status code (any value: unknown codes get a generic string). */
+const char *moe_status_str(int32_t status);
 
 #ifdef __cplusplus
 }
