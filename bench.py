@@ -48,10 +48,10 @@ SEED_STACK = 5000
 # 131085.4 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
 # source these counters were taken on; otherwise the JSON reports null.
 GATEUP_TRAFFIC = {
-    "gemm_src_sha256": "172ea8df7e208c2b8649635765940d580a2ea501a7d92c7024179f9df6cc98d4",
-    "fetch_kib": 160964.9, "fetch_scale": 2.0,
-    "write_kib": 20704.8, "write_scale": 1.0,
-    "profile": "profiles/q4_gemm_gateup_prefill2048_zipf_hbm_traffic.md",
+    "gemm_src_sha256": "611b8adba533a7bebf5a206de05ea08461b81d4a2291fa9acf726b3f46b0be22",
+    "fetch_kib": 159201.9, "fetch_scale": 2.0,
+    "write_kib": 20748.0, "write_scale": 1.0,
+    "profile": "profiles/moe_layer_prefill2048_zipf_hbm_traffic.md",
 }
 
 
