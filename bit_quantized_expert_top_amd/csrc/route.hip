@@ -126,12 +126,13 @@ void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *
 //    quantity, so every approximate logit lies within
 //        delta = 2^-16 (||x|| ||w|| + |b|)  (+ a denormal guard)
 //    of the fixed-order logit (Cauchy-Schwarz bounds sum|x_k w_k|).
-// 2. route_select (one wave per token): the top-8 by approximate logits is
-//    accepted as is when the 8 intervals are disjoint and no other expert's
-//    interval reaches the lowest of them; otherwise the fixed-order logits of
-//    every candidate that might belong to the top-8 are recomputed exactly
-//    (same order as router_logits) and the top-8 is taken from those.  Either
-//    way the ids equal those of the fixed-order logits, bit for bit.
+// 2. route_select (one wave per token): the top-8 by approximate logits, and
+//    every other expert whose interval reaches the lowest lower bound of those
+//    8, are the only experts that can hold a top-8 fixed-order logit.  Their
+//    fixed-order logits are recomputed exactly (same order as router_logits)
+//    and the top-8 is taken from those, so the ids equal those of the
+//    fixed-order logits bit for bit, and the routing weights are computed from
+//    the exact logits of the picks.
 // ---------------------------------------------------------------------------
 constexpr int TB = kTB;           // tokens per routing block (one wave each)
 constexpr int RS_SPLIT = 4;       // K splits of the approximate router
@@ -295,146 +296,124 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         }
 }
 
-// Fixed-order logit of one expert row for the half-wave `half` (lanes
-// 32*half .. +31): lane c computes chunk c sequentially from its first product
-// (xv: the token's 64 inputs of chunk c, wv: the expert's, both already in
-// registers); the chunk partials go through LDS (scratch: 64 floats for the
-// wave) and the first lane of each half adds them in chunk order, then the
-// bias.  Called by the whole wave; the result is valid in lanes 0 (half 0) and
-// 32 (half 1).
-__device__ float canon_logit_half(const u32x4 (&xv)[8], const u32x4 (&wv)[8], bool live, int H,
-                                  float bias_e, int lane, float *scratch) {
-    const int c = lane & 31, nch = H / 64;
-    float part = 0.0f;
-    if (c < nch && live) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (q == 0 && r == 0)
-                    part = bf16_lo(xv[0][0]) * bf16_lo(wv[0][0]);
-                else
-                    part = __builtin_fmaf(bf16_lo(xv[q][r]), bf16_lo(wv[q][r]), part);
-                part = __builtin_fmaf(bf16_hi(xv[q][r]), bf16_hi(wv[q][r]), part);
-            }
-        }
-    }
-    scratch[lane] = part;
-    __builtin_amdgcn_wave_barrier();
-    float total = 0.0f;
-    if (c == 0) {
-        const float *ps = scratch + lane;
-        float v[32];
-#pragma unroll
-        for (int q = 0; q < 32; ++q) v[q] = ps[q];
-        total = v[0];
-#pragma unroll
-        for (int q = 1; q < 32; ++q)
-            if (q < nch) total = total + v[q];
-        total = total + bias_e;
-    }
-    __builtin_amdgcn_wave_barrier();
-    return total;
-}
-
-// Fixed-order logits of the nc experts cand_e[0..nc) of token row xr into
-// cand_l, two per step (one per half-wave); the next step's router rows are
-// loaded while the current step is summed.
-__device__ void recompute_candidates(const uint32_t *cand_e, float *cand_l, int nc,
-                                     const uint16_t *__restrict__ xr,
-                                     const uint16_t *__restrict__ wr, const float *__restrict__ bias,
-                                     int H, int lane, float *scratch) {
-    const int c = lane & 31;
-    const bool has_chunk = c < H / 64;
-    u32x4 xv[8], wv[8], wn[8];
-    if (has_chunk) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xv[q] = ((const u32x4 *)(xr + 64 * c))[q];
-    }
-    auto load = [&](int c0, u32x4 (&dst)[8]) {
-        const int ci = c0 + (lane >> 5);
-        const int e = ci < nc ? (int)cand_e[ci] : -1;
-        if (has_chunk && e >= 0) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) dst[q] = ((const u32x4 *)(wr + (size_t)e * H + 64 * c))[q];
-        }
-    };
-    load(0, wv);
-    for (int c0 = 0; c0 < nc; c0 += 2) {
-        if (c0 + 2 < nc) load(c0 + 2, wn);
-        const int ci = c0 + (lane >> 5);
-        const int e = ci < nc ? (int)cand_e[ci] : -1;
-        const float b = (e >= 0 && bias) ? bias[e] : 0.0f;
-        const float L = canon_logit_half(xv, wv, e >= 0, H, b, lane, scratch);
-        if (c == 0 && ci < nc) cand_l[ci] = L;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) wv[q] = wn[q];
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0..12
+__device__ __forceinline__ void wait_vm_upto12(int n) {
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
     }
 }
 
-// Fixed-order logits of up to 8 experts elist[0..n) of token row xr, with every
-// router row load of the four passes issued at once (a single round trip): half
-// h of the wave takes experts h, 2 + h, 4 + h, 6 + h, lane c of a half chunk c.
-// The chunk partials meet in wave-local LDS (part: 256 floats) and lane i < n
-// adds expert i's in chunk order, then its bias; lane i returns that logit.
-__device__ float exact_logits8(const uint32_t *elist, int n, const uint16_t *__restrict__ xr,
-                               const uint16_t *__restrict__ wr, const float *__restrict__ bias,
-                               int H, int lane, float *part) {
+// Per-wave LDS stage of the exact recompute: four 4 KB slots, one router row
+// (or the token's x row) each, in 128-byte chunks of 64 inputs; 16-byte slot s
+// of chunk c holds segment s ^ (c & 7) of the chunk, so that the 32 lanes
+// reading one chunk each hit distinct banks.
+constexpr int XS_SLOT = 4096;
+constexpr int XS_WAVE = 4 * XS_SLOT;
+
+// DMA of one row of H bf16 values into a 4 KB stage slot (LDS address dst) in the
+// swizzled chunk layout: instruction j copies chunks 8 j .. 8 j + 7, lane l
+// filling slot l & 7 of chunk 8 j + (l >> 3) (a chunk past the row: any valid one).
+__device__ __forceinline__ void stage_row(const uint16_t *row, int H, int lane, uint32_t dst) {
+    const int nch = H / 64, ipr = (nch + 7) >> 3;
+    const int dch = lane >> 3, dseg = (lane & 7) ^ dch;
+    for (int j = 0; j < ipr; ++j) {
+        const int cc = 8 * j + dch < nch ? 8 * j + dch : 0;
+        rdma16(row + 64 * cc + 8 * dseg, dst + (uint32_t)(1024 * j));
+    }
+}
+
+// Fixed-order logits of the n experts elist[0..n) (n <= 256) of one token: on
+// entry out[i] holds the bias of elist[i], on exit its logit (wave-local LDS).
+// The token's x row is already in slot 3 of the wave's stage (stage /
+// stage_lds: its generic and LDS addresses).  The router rows travel by DMA
+// into slots 0-2 at once, into slot 3 once x is in registers, and then each
+// round refills the two slots it has read with the rows two rounds ahead.  In
+// round r half h of the wave takes row 2 r + h, lane c of the half chunk c,
+// summed sequentially from its first product; the chunk partials meet in scr
+// (64 floats) and lanes 0 and 32 add them in chunk order, then the bias.
+__device__ void exact_logits(const uint32_t *elist, int n, float *out,
+                             const uint16_t *__restrict__ wr, int H, int lane, float *scr,
+                             const uint8_t *stage, uint32_t stage_lds) {
     const int c = lane & 31, hh = lane >> 5, nch = H / 64;
-    const bool has_chunk = c < nch;
-    u32x4 xv[8], wv[4][8];
-    if (has_chunk) {
+    const int ipr = (nch + 7) >> 3;               // DMA instructions per row (1 KB each)
+    auto issue = [&](int i) {
+        stage_row(wr + (size_t)elist[i] * H, H, lane, stage_lds + (uint32_t)(XS_SLOT * (i & 3)));
+    };
+    // vmcnt(0), in the form the compiler's own wait bookkeeping sees: x has landed,
+    // and no load of the caller is in flight from here on, so the compiler adds no
+    // waits of its own between the copies below and the explicit waits for them
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    const int pre = n < 3 ? n : 3;
+    for (int i = 0; i < pre; ++i) issue(i);
+    u32x4 xv[8];
+    if (c < nch) {
+        const uint8_t *xs = stage + 3 * XS_SLOT + 128 * c;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) xv[q] = ((const u32x4 *)(xr + 64 * c))[q];
+        for (int q = 0; q < 8; ++q) xv[q] = *(const u32x4 *)(xs + 16 * (q ^ (c & 7)));
     }
-    int ev[4];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot 3 is refilled next
+    int next = pre;
+    if (next < n) issue(next++);
+    for (int r = 0; 2 * r < n; ++r) {
+        const int need = 2 * r + 2 < n ? 2 * r + 2 : n;
+        wait_vm_upto12((next - need) * ipr);
+        const int i = 2 * r + hh;
+        float s = 0.0f;
+        if (c < nch && i < n) {
+            const uint8_t *ws = stage + XS_SLOT * (i & 3) + 128 * c;
+            u32x4 wv[8];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int ci = 2 * p + hh;
-        ev[p] = ci < n ? (int)elist[ci] : -1;
-        if (has_chunk && ev[p] >= 0) {
+            for (int q = 0; q < 8; ++q) wv[q] = *(const u32x4 *)(ws + 16 * (q ^ (c & 7)));
+            // sequential within the chunk, from its first product (each fma adds one exact product)
+            s = bf16_lo(xv[0][0]) * bf16_lo(wv[0][0]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) wv[p][q] = ((const u32x4 *)(wr + (size_t)ev[p] * H + 64 * c))[q];
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (q > 0 || u > 0) s = __builtin_fmaf(bf16_lo(xv[q][u]), bf16_lo(wv[q][u]), s);
+                    s = __builtin_fmaf(bf16_hi(xv[q][u]), bf16_hi(wv[q][u]), s);
+                }
         }
-    }
+        scr[lane] = s;
+        __builtin_amdgcn_wave_barrier();
+        if (c == 0 && i < n) {
+            // the 32 partials in one batch of LDS reads, then added in chunk order
+            const float4 *pp = (const float4 *)(scr + 32 * hh);
+            float v[32];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        if (!has_chunk || ev[p] < 0) continue;
-        // sequential within the chunk, from its first product (each fma adds one exact product)
-        float s = bf16_lo(xv[0][0]) * bf16_lo(wv[p][0][0]);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (q > 0 || r > 0) s = __builtin_fmaf(bf16_lo(xv[q][r]), bf16_lo(wv[p][q][r]), s);
-                s = __builtin_fmaf(bf16_hi(xv[q][r]), bf16_hi(wv[p][q][r]), s);
+            for (int q = 0; q < 8; ++q) {
+                const float4 f = pp[q];
+                v[4 * q] = f.x;
+                v[4 * q + 1] = f.y;
+                v[4 * q + 2] = f.z;
+                v[4 * q + 3] = f.w;
             }
-        part[32 * (2 * p + hh) + c] = s;
-    }
-    __builtin_amdgcn_wave_barrier();
-    float L = 0.0f;
-    if (lane < n) {
-        // the 32 partials in one batch of LDS reads, then added in chunk order
-        const float4 *pp = (const float4 *)(part + 32 * lane);
-        float v[32];
+            float L = v[0];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float4 f = pp[q];
-            v[4 * q] = f.x;
-            v[4 * q + 1] = f.y;
-            v[4 * q + 2] = f.z;
-            v[4 * q + 3] = f.w;
+            for (int q = 1; q < 32; ++q)
+                if (q < nch) L = L + v[q];
+            out[i] = L + out[i];
         }
-        L = v[0];
-#pragma unroll
-        for (int q = 1; q < 32; ++q)
-            if (q < nch) L = L + v[q];
-        if (bias) L = L + bias[elist[lane]];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this round's slots are refilled next
+        __builtin_amdgcn_wave_barrier();
+        for (int u = 0; u < 2 && next < n; ++u) issue(next++);
     }
-    __builtin_amdgcn_wave_barrier();
-    return L;
 }
 
+// EXACT: every logit given in `exact` (fixed order); else the approximate partials.
+template <bool EXACT>
 __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     const float *__restrict__ part, int S, const float *__restrict__ exact,
     const float *__restrict__ xsq, int G, const float *__restrict__ wn2,
@@ -447,41 +426,61 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     __shared__ int32_t sid[TB][8];
     __shared__ uint32_t cand_e[TB][256];
     __shared__ __attribute__((aligned(16))) float cand_l[TB][256];
-    __shared__ float scr[TB][64];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ __attribute__((aligned(16))) float scr[TB][64];
+    extern __shared__ __attribute__((aligned(1024))) uint8_t xstage[];   // [TB][XS_WAVE]
+    const uint32_t xstage_lds =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)xstage;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tl = wave, t = blockIdx.x * TB + tl;
     if (tid < 256) mask[tid] = 0u;
     __syncthreads();
+    const uint8_t *stage = xstage + XS_WAVE * tl;
+    const uint32_t stage_lds = xstage_lds + (uint32_t)(XS_WAVE * tl);
     if (t < T) {
+        // the token's x row, for the fixed-order logits below, goes to slot 3 of the
+        // wave's stage now, ahead of everything else
+        if (!EXACT) stage_row(x + (size_t)t * H, H, lane, stage_lds + 3 * XS_SLOT);
         // ---- logits (approximate or exact) and their error radius
         float lt[4], dl[4];
         // every load of this phase goes out before the first wait: the token's
-        // sums of squares, all RS_SPLIT partials and norms, and the biases
-        float ss = 0.0f, bv[4], pv[4][RS_SPLIT], wv[4][RS_SPLIT];
-        float xm = 0.0f;
-        if (lane < G) {
-            ss = xsq[(size_t)t * G + lane];
-            xm = xmx[(size_t)t * G + lane];
-        }
+        // sums of squares and group maxima, all RS_SPLIT partials and norms (or
+        // the exact logits), and the biases.  No load sits under a branch (a
+        // branch between loads makes the compiler wait at it): out-of-range
+        // lanes and a missing bias read a valid address and discard the value.
+        float bv[4];
+        const int gi = lane < G ? lane : 0;
+        float ss = xsq[(size_t)t * G + gi];
+        float xm = xmx[(size_t)t * G + gi];
+        const float *bsrc = bias ? bias : (exact ? exact : wn2);   // >= E floats each
+        if (EXACT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane + 64 * j;
-            bv[j] = bias ? bias[e] : 0.0f;
-            if (exact) {
+            for (int j = 0; j < 4; ++j) {
+                const int e = lane + 64 * j;
+                bv[j] = bsrc[e];
                 lt[j] = exact[(size_t)t * E + e];
                 dl[j] = 0.0f;
-            } else {
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!bias) bv[j] = 0.0f;
+        } else {
+            float pv[4][RS_SPLIT], wv[4][RS_SPLIT];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = lane + 64 * j;
+                bv[j] = bsrc[e];
 #pragma unroll
                 for (int sp = 0; sp < RS_SPLIT; ++sp) {
                     pv[j][sp] = part[((size_t)sp * T + t) * E + e];
                     wv[j][sp] = wn2[(size_t)sp * E + e];
                 }
             }
-        }
-        if (!exact) {
+            if (lane >= G) ss = 0.0f;
             const float nx = sqrtf(wave_sum_f(ss));   // ||x||
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                if (!bias) bv[j] = 0.0f;
                 float v = pv[j][0], w2 = wv[j][0];
 #pragma unroll
                 for (int sp = 1; sp < RS_SPLIT; ++sp) {
@@ -492,79 +491,42 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 dl[j] = 0x1p-16f * (sqrtf(w2) * nx * 1.001f + fabsf(bv[j])) + 0x1p-100f;
             }
         }
-        // ---- top-k by the (approximate) logits, ties to the lower index, then the
-        // certificate.  Up to two rounds: if the first fails, only the experts in
-        // ambiguous clusters (adjacent picks whose intervals overlap, plus the
-        // boundary between the k-th pick and the rest) get their fixed-order
-        // logit, with a zero radius, and the selection is certified again.
+        if (lane >= G) {
+            ss = 0.0f;
+            xm = 0.0f;
+        }
+        // ---- top-k of the (approximate) logits, ties to the lower index
         bool taken[4];
-        int my_pick = -1;
-        float my_l = 0.0f, my_lb = 0.0f, my_ub = 0.0f, my_d = 0.0f;
-        float m8 = INFINITY;
-        bool certified = false;
-        for (int round = 0; round < 2; ++round) {
-            uint32_t key[4];
+        uint32_t key[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            key[j] = ordered_key(lt[j]);
+            taken[j] = false;
+        }
+        int pe;
+        uint32_t pkey;
+        wave_topk_radix(key, k, taken, pe, pkey, (uint32_t *)scr[tl]);
+        int my_pick = lane < k ? pe : -1;
+        float wl = lane < k ? key_to_float(pkey) : 0.0f;   // the pick's logit (lanes < k)
+        if (!EXACT) {
+            // Every exact logit lies within d of its approximation.  An expert whose
+            // interval [l - d, l + d] ends below m8, the lowest lower bound of the picks,
+            // has an exact logit below every pick's, so the exact top-k lies among the
+            // picks and the experts whose intervals reach m8.  Those candidates get their
+            // fixed-order logits, and the top-k is taken among the exact values.
+            const int pl = lane < k ? pe : 0;
+            float pd = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                key[j] = ordered_key(lt[j]);
-                taken[j] = false;
+                const float dj = __shfl(dl[j], pl & 63);
+                if ((pl >> 6) == j) pd = dj;
             }
-            // the picks, then each pick's logit and radius from wave-local LDS
-            // (cand_l / cand_e are free between recompute rounds)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                cand_l[tl][lane + 64 * j] = lt[j];
-                cand_e[tl][lane + 64 * j] = __float_as_uint(dl[j]);
-            }
-            {
-                int pe;
-                uint32_t pkey;
-                wave_topk_radix(key, k, taken, pe, pkey, (uint32_t *)scr[tl]);
-                if (lane < k) {
-                    const float l = cand_l[tl][pe], d = __uint_as_float(cand_e[tl][pe]);
-                    my_pick = pe;
-                    my_l = key_to_float(pkey);
-                    my_d = d;
-                    my_lb = l - d;
-                    my_ub = l + d;
-                }
-                __builtin_amdgcn_wave_barrier();
-            }
-            // certificate: disjoint intervals in rank order, nothing else reaching the k-th
-            m8 = INFINITY;
+            const float lb = lane < k ? wl - pd : INFINITY;
+            float m8 = INFINITY;
             for (int p = 0; p < k; ++p)
-                m8 = fminf(m8, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_lb), p)));
-            // lane p < k-1 compares its lower bound with the upper bound of pick p+1
-            float next_ub = 0.0f, prev_lb = INFINITY;
-            for (int p = 0; p + 1 < k; ++p) {
-                const float nu = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ub), p + 1));
-                const float pl = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_lb), p));
-                if (lane == p) next_ub = nu;
-                if (lane == p + 1) prev_lb = pl;
-            }
-            const bool pair_ok = (lane >= k - 1) || (my_lb > next_ub);
-            bool extra = false;
-            float extra_ub = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (!taken[j] && lt[j] + dl[j] >= m8) {
-                    extra = true;
-                    extra_ub = fmaxf(extra_ub, lt[j] + dl[j]);
-                }
-            certified = __all(pair_ok) && !__any(extra);
-            if (certified || round == 1) break;
-
-            // ---- cluster recompute: the ambiguous picks and the extras
-            const float max_xub = key_to_float(wave_umax(ordered_key(extra_ub)));
-            const bool amb_pick = lane < k && ((lane + 1 < k && my_lb <= next_ub) ||
-                                               (lane > 0 && prev_lb <= my_ub) || my_lb <= max_xub);
-            int nc = 0;
-            {
-                const uint64_t bal = __ballot(amb_pick);
-                const int pos = (int)__popcll(bal & ((1ull << lane) - 1ull));
-                if (amb_pick) cand_e[tl][pos] = my_pick;
-                nc = (int)__popcll(bal);
-            }
+                m8 = fminf(m8, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lb), p)));
+            if (lane < k) cand_e[tl][lane] = (uint32_t)pe;
+            int nc = k;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool c = !taken[j] && lt[j] + dl[j] >= m8;
@@ -574,92 +536,75 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 nc += (int)__popcll(bal);
             }
             __builtin_amdgcn_wave_barrier();
-            recompute_candidates(cand_e[tl], cand_l[tl], nc, x + (size_t)t * H, wr, bias, H, lane,
-                                 scr[tl]);
-            __builtin_amdgcn_wave_barrier();
-            for (int ci = 0; ci < nc; ++ci) {
-                const int e = (int)cand_e[tl][ci];
-                const float L = cand_l[tl][ci];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (lane + 64 * j == e) {
-                        lt[j] = L;
-                        dl[j] = 0.0f;
-                    }
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
-        float wl = my_l;   // logit used for the weights (lanes < k)
-        if (certified) {
-            // the weights come from the picks' fixed-order logits: those that still carry
-            // an approximate logit (nonzero radius) are recomputed, 8 rows at most
-            const bool need = lane < k && my_d != 0.0f;
-            const uint64_t bal = __ballot(need);
-            const int pos = (int)__popcll(bal & ((1ull << lane) - 1ull));
-            if (need) cand_e[tl][pos] = (uint32_t)my_pick;
-            const int nc = (int)__popcll(bal);
-            __builtin_amdgcn_wave_barrier();
-            if (nc > 0) {
-                const float L = exact_logits8(cand_e[tl], nc, x + (size_t)t * H, wr, bias, H, lane,
-                                              cand_l[tl]);
-                const float Lp = __shfl(L, pos);
-                if (need) wl = Lp;
-            }
-        }
-        if (!certified) {
-            // candidates: every expert whose interval reaches m8 (includes the k picks);
-            // those not yet exact first (they are recomputed), then the exact ones
-            int nc = 0;
-            for (int pass = 0; pass < 2; ++pass) {
+            // the candidates' biases (expert e's sits in lane e & 63, slot e >> 6)
+            for (int g = 0; g < nc; g += 64) {
+                const int ci = g + lane;
+                const int ee = ci < nc ? (int)cand_e[tl][ci] : 0;
+                float b = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const bool c = (taken[j] || (lt[j] + dl[j] >= m8)) &&
-                                   ((dl[j] == 0.0f) == (pass == 1));
-                    const uint64_t bal = __ballot(c);
-                    const int pos = nc + (int)__popcll(bal & ((1ull << lane) - 1ull));
-                    if (c) {
-                        cand_e[tl][pos] = lane + 64 * j;
-                        if (pass == 1) cand_l[tl][pos] = lt[j];
-                    }
-                    nc += (int)__popcll(bal);
+                    const float bj = __shfl(bv[j], ee & 63);
+                    if ((ee >> 6) == j) b = bj;
                 }
-                if (pass == 0) {
-                    __builtin_amdgcn_wave_barrier();
-                    recompute_candidates(cand_e[tl], cand_l[tl], nc, x + (size_t)t * H, wr, bias, H,
-                                         lane, scr[tl]);
-                }
+                if (ci < nc) cand_l[tl][ci] = b;
             }
             __builtin_amdgcn_wave_barrier();
-            // top-k among the candidates by the exact logits (ties to the lower index)
-            uint32_t ck[4];
-            bool gone[4];
+            exact_logits(cand_e[tl], nc, cand_l[tl], wr, H, lane, scr[tl], stage, stage_lds);
+            __builtin_amdgcn_wave_barrier();
+            if (nc <= 64) {
+                // rank of candidate `lane` by (exact logit desc, index asc)
+                const bool live = lane < nc;
+                const uint32_t ce = live ? cand_e[tl][lane] : 0xffffffffu;
+                const float cl = live ? cand_l[tl][lane] : 0.0f;
+                const uint32_t ck = live ? ordered_key(cl) : 0u;
+                int rank = 0;
+                for (int j = 0; j < nc; ++j) {
+                    const uint32_t kj = __builtin_amdgcn_readlane(ck, j);
+                    const uint32_t ej = __builtin_amdgcn_readlane(ce, j);
+                    rank += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
+                }
+                if (live && rank < k) {
+                    ((uint32_t *)scr[tl])[rank] = ce;
+                    scr[tl][8 + rank] = cl;
+                }
+                __builtin_amdgcn_wave_barrier();
+                if (lane < k) {
+                    my_pick = (int)((const uint32_t *)scr[tl])[lane];
+                    wl = scr[tl][8 + lane];
+                }
+                __builtin_amdgcn_wave_barrier();
+            } else {
+                // more than 64 candidates: k rounds of a wave arg-max over them
+                uint32_t ck[4];
+                bool gone[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int ci = lane + 64 * j;
-                gone[j] = ci >= nc;
-                ck[j] = gone[j] ? 0u : ordered_key(cand_l[tl][ci]);
-            }
-            for (int p = 0; p < k; ++p) {
-                uint32_t m = 0;
+                for (int j = 0; j < 4; ++j) {
+                    const int ci = lane + 64 * j;
+                    gone[j] = ci >= nc;
+                    ck[j] = gone[j] ? 0u : ordered_key(cand_l[tl][ci]);
+                }
+                for (int p = 0; p < k; ++p) {
+                    uint32_t m = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (!gone[j] && ck[j] > m) m = ck[j];
-                m = wave_umax(m);
-                // among the candidates holding the max key, the lowest expert index
-                uint32_t emin = 0xffffffffu;
+                    for (int j = 0; j < 4; ++j)
+                        if (!gone[j] && ck[j] > m) m = ck[j];
+                    m = wave_umax(m);
+                    // among the candidates holding the max key, the lowest expert index
+                    uint32_t emin = 0xffffffffu;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (!gone[j] && ck[j] == m) {
-                        const uint32_t ee = cand_e[tl][lane + 64 * j];
-                        emin = ee < emin ? ee : emin;
+                    for (int j = 0; j < 4; ++j)
+                        if (!gone[j] && ck[j] == m) {
+                            const uint32_t ee = cand_e[tl][lane + 64 * j];
+                            emin = ee < emin ? ee : emin;
+                        }
+                    emin = ~wave_umax(~emin);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (!gone[j] && ck[j] == m && cand_e[tl][lane + 64 * j] == emin) gone[j] = true;
+                    if (lane == p) {
+                        my_pick = (int)emin;
+                        wl = key_to_float(m);
                     }
-                emin = ~wave_umax(~emin);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (!gone[j] && ck[j] == m && cand_e[tl][lane + 64 * j] == emin) gone[j] = true;
-                if (lane == p) {
-                    my_pick = (int)emin;
-                    wl = key_to_float(m);
                 }
             }
         }
@@ -728,9 +673,17 @@ void launch_route_select(const float *part, const float *exact, const float *xsq
                          int32_t *blk_cnt, int32_t *lrank, const float *xmx, uint16_t *xp,
                          float *xsum, float *tok, hipStream_t s) {
     const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
-    hipLaunchKernelGGL(route_select_kernel, dim3((T + TB - 1) / TB), dim3(64 * TB), 0, s, part, S,
-                       exact, xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank,
-                       xmx, xp, xsum, tok);
+    const dim3 grid((T + TB - 1) / TB), block(64 * TB);
+    if (exact) {
+        hipLaunchKernelGGL(route_select_kernel<true>, grid, block, 0, s, part, S, exact, xsq, H / 64,
+                           wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank, xmx, xp, xsum, tok);
+    } else {
+        static LdsLimit lim;
+        lim.ensure((const void *)route_select_kernel<false>, TB * XS_WAVE);
+        hipLaunchKernelGGL(route_select_kernel<false>, grid, block, TB * XS_WAVE, s, part, S, exact,
+                           xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank, xmx,
+                           xp, xsum, tok);
+    }
 }
 
 // ---------------------------------------------------------------------------
