@@ -38,6 +38,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.stage = take((size_t)T * k * H * 2);
     L.blk_cnt = take(nTB * E * 4);
     L.lrank = take((size_t)T * k * 4);
+    L.sup = take(nTB <= (size_t)kSupBlk * kSupMax ? (nTB + kSupBlk - 1) / kSupBlk * E * 4 : 0);
     L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
     L.qctl = take((size_t)QCTL_WORDS * 4);
     L.xmx = take((size_t)T * (H / 64) * 4);
@@ -154,25 +155,31 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
     int32_t *blk_cnt = (int32_t *)(ws + L.blk_cnt);
     int32_t *lrank = (int32_t *)(ws + L.lrank);
     float *xsq = (float *)(ws + L.xsq);
+    // superblock counts of the single-pass routing structures (T <= 4096): zeroed by the
+    // router pass, accumulated by the select kernel
+    const int nTB = (s->T + kTB - 1) / kTB;
+    const int nsup = nTB <= kSupBlk * kSupMax ? (nTB + kSupBlk - 1) / kSupBlk * s->E : 0;
+    int32_t *sup = nsup ? (int32_t *)(ws + L.sup) : nullptr;
     if (r->logits) {
         launch_prep_act(x, s->T, s->H, (uint16_t *)(ws + L.xp), (float *)(ws + L.xsum), xsq,
                         (float *)(ws + L.xmx), st);
+        if (sup) launch_zero_i32(sup, nsup, st);
         // every logit requested: compute them all in the fixed order, select on them directly
         launch_router_logits(x, w->router_wt, w->router_bias, s->T, s->H, s->E, r->logits, st);
         launch_route_select(nullptr, r->logits, xsq, nullptr, w->router_bias, x, w->router_wt,
                             s->T, s->H, s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank,
-                            (const float *)(ws + L.xmx), (uint16_t *)(ws + L.xp),
+                            sup, (const float *)(ws + L.xmx), (uint16_t *)(ws + L.xp),
                             (float *)(ws + L.xsum), (float *)(ws + L.tok), st);
     } else {
         float *part = (float *)(ws + L.part), *wn2 = (float *)(ws + L.wn2);
         launch_router_fast(x, w->router_wt, s->T, s->H, s->E, part, wn2, (uint16_t *)(ws + L.xp),
-                           (float *)(ws + L.xsum), xsq, (float *)(ws + L.xmx), st);
+                           (float *)(ws + L.xsum), xsq, (float *)(ws + L.xmx), sup, nsup, st);
         launch_route_select(part, nullptr, xsq, wn2, w->router_bias, x, w->router_wt, s->T, s->H,
-                            s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank,
+                            s->E, s->top_k, r->topk_ids, r->topk_w, blk_cnt, lrank, sup,
                             (const float *)(ws + L.xmx), (uint16_t *)(ws + L.xp),
                             (float *)(ws + L.xsum), (float *)(ws + L.tok), st);
     }
-    launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, lrank, s->T, s->E, s->top_k, kBM,
+    launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, sup, lrank, s->T, s->E, s->top_k, kBM,
                         r->counts, r->offsets, r->row_token, r->tok_row, r->row_w, r->blocks,
                         r->num_blocks, (int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl), st);
     return launched();

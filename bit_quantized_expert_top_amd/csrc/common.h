@@ -23,6 +23,8 @@ constexpr int kWave = 64;
 constexpr int kGroup = 64;      // quantisation group along K
 constexpr int kBM = 128;        // rows per routing block (GEMM M tile)
 constexpr int kTB = 8;          // tokens per routing token block (one wave each)
+constexpr int kSupBlk = 16;      // token blocks per superblock of the single-pass routing scan
+constexpr int kSupMax = 32;      // superblocks of the single-pass scan (T <= 4096)
 constexpr int kDecodeMaxT = 8;  // moe_decode: tokens per call (each an independent GEMV problem)
 
 // Decode scratch for T tokens (E = 256 experts, k + 1 slots): the router logits, the h
@@ -337,6 +339,7 @@ struct WsLayout {
     size_t stage;       // bf16 [T*k][H]          routed down outputs times routing weight
     size_t blk_cnt;     // int32 [T/kTB][E]       per token-block expert counts / bases
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
+    size_t sup;         // int32 [T/(kTB kSupBlk)][E] per superblock expert counts (T <= 4096)
     size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (by cost class)
     size_t qctl;        // int32 [64]             GEMM work-queue counters and class counts
     size_t xmx;         // fp32 [T][H/64]         group maxima of |x|
@@ -354,17 +357,20 @@ void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *
                           int E, float *logits, hipStream_t s);
 void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
                         float *wn2part, uint16_t *xp, float *xsum, float *xsq, float *xmx,
-                        hipStream_t s);
+                        int32_t *zero, int nzero, hipStream_t s);
 void launch_route_select(const float *part, const float *exact, const float *xsq,
                          const float *wn2, const float *bias, const uint16_t *x,
                          const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,
-                         int32_t *blk_cnt, int32_t *lrank, const float *xmx, uint16_t *xp,
-                         float *xsum, float *tok, hipStream_t s);
+                         int32_t *blk_cnt, int32_t *lrank, int32_t *sup, const float *xmx,
+                         uint16_t *xp, float *xsum, float *tok, hipStream_t s);
+// sup != NULL (T <= 4096): one kernel from the superblock counts; else a per-expert
+// scan kernel, then the scatter
 void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
-                         const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
-                         int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
-                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, int32_t *qctl,
-                         hipStream_t s);
+                         const int32_t *sup, const int32_t *lrank, int T, int E, int k, int BM,
+                         int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
+                         float *row_w, int32_t *blocks, int32_t *num_blocks, int32_t *sched,
+                         int32_t *qctl, hipStream_t s);
+void launch_zero_i32(int32_t *p, int n, hipStream_t s);
 void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
                      float *xmx, hipStream_t s);
 

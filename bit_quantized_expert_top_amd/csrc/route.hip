@@ -177,7 +177,8 @@ __device__ __forceinline__ void rdma16(const void *g, uint32_t lds) {
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int H, int E, int S,
     float *__restrict__ part, uint16_t *__restrict__ xp, float *__restrict__ xsum,
-    float *__restrict__ xsq, float *__restrict__ wn2part, float *__restrict__ xmx) {
+    float *__restrict__ xsq, float *__restrict__ wn2part, float *__restrict__ xmx,
+    int32_t *__restrict__ zbuf, int nzero) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t rsm[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)rsm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -270,6 +271,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         }
     }
     if (do_norm) wn2part[(size_t)sp * E + tid] = wsq;
+    // the select kernel's superblock counters start at zero (stored after the
+    // loop, like every store of this kernel)
+    if (blockIdx.x == 0 && sp == 0)
+        for (int i = tid; i < nzero; i += 256) zbuf[i] = 0;
     {
         const int row = tid >> 3, sg = tid & 7;
         if (t0 + row < T) {
@@ -420,8 +425,8 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     const float *__restrict__ bias, const uint16_t *__restrict__ x,
     const uint16_t *__restrict__ wr, int T, int H, int E, int k, int32_t *__restrict__ ids,
     float *__restrict__ tw, int32_t *__restrict__ blk_cnt, int32_t *__restrict__ lrank,
-    const float *__restrict__ xmx, uint16_t *__restrict__ xp, float *__restrict__ xsum,
-    float *__restrict__ tok) {
+    int32_t *__restrict__ sup, const float *__restrict__ xmx, uint16_t *__restrict__ xp,
+    float *__restrict__ xsum, float *__restrict__ tok) {
     __shared__ uint32_t mask[256];
     __shared__ int32_t sid[TB][8];
     __shared__ uint32_t cand_e[TB][256];
@@ -646,7 +651,12 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
         }
     }
     __syncthreads();
-    if (tid < 256) blk_cnt[(size_t)blockIdx.x * E + tid] = __popc(mask[tid]);
+    if (tid < 256) {
+        const int c = __popc(mask[tid]);
+        blk_cnt[(size_t)blockIdx.x * E + tid] = c;
+        // the block's counts into its superblock's (integer sums: order-independent)
+        if (sup && c) atomicAdd(sup + (size_t)(blockIdx.x / kSupBlk) * E + tid, c);
+    }
     if (tid < TB * k) {
         const int tl2 = tid / k, j = tid % k;
         const int t2 = blockIdx.x * TB + tl2;
@@ -659,30 +669,32 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
 
 void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int E, float *part,
                         float *wn2part, uint16_t *xp, float *xsum, float *xsq, float *xmx,
-                        hipStream_t s) {
+                        int32_t *zero, int nzero, hipStream_t s) {
     const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
     static LdsLimit lim;
     lim.ensure((const void *)router_mfma_kernel, R_NST * R_STAGE);
     hipLaunchKernelGGL(router_mfma_kernel, dim3((T + RT_TOK - 1) / RT_TOK, S), dim3(256),
-                       R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq, wn2part, xmx);
+                       R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq, wn2part, xmx,
+                       zero, nzero);
 }
 
 void launch_route_select(const float *part, const float *exact, const float *xsq,
                          const float *wn2, const float *bias, const uint16_t *x,
                          const uint16_t *wr, int T, int H, int E, int k, int32_t *ids, float *w,
-                         int32_t *blk_cnt, int32_t *lrank, const float *xmx, uint16_t *xp,
-                         float *xsum, float *tok, hipStream_t s) {
+                         int32_t *blk_cnt, int32_t *lrank, int32_t *sup, const float *xmx,
+                         uint16_t *xp, float *xsum, float *tok, hipStream_t s) {
     const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
     const dim3 grid((T + TB - 1) / TB), block(64 * TB);
     if (exact) {
         hipLaunchKernelGGL(route_select_kernel<true>, grid, block, 0, s, part, S, exact, xsq, H / 64,
-                           wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank, xmx, xp, xsum, tok);
+                           wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank, sup, xmx, xp, xsum,
+                           tok);
     } else {
         static LdsLimit lim;
         lim.ensure((const void *)route_select_kernel<false>, TB * XS_WAVE);
         hipLaunchKernelGGL(route_select_kernel<false>, grid, block, TB * XS_WAVE, s, part, S, exact,
-                           xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank, xmx,
-                           xp, xsum, tok);
+                           xsq, H / 64, wn2, bias, x, wr, T, H, E, k, ids, w, blk_cnt, lrank, sup,
+                           xmx, xp, xsum, tok);
     }
 }
 
@@ -693,27 +705,85 @@ void launch_route_select(const float *part, const float *exact, const float *xsq
 // row = offsets[e] + block_base[b][e] + rank, which orders rows by expert,
 // then token.
 // ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 256 threads of a workgroup (4 waves): a shuffle
+// scan inside each wave, then the wave totals through LDS (wt: 4 entries); *total
+// receives the sum over all threads.  Called by the whole workgroup.
+__device__ unsigned long long block_scan_u64(unsigned long long v, int tid, unsigned long long *wt,
+                                             unsigned long long *total) {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) wt[wave] = v;
+    __syncthreads();
+    unsigned long long add = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) add += wt[w];
+        tot += wt[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return v + add;
+}
+
 __global__ __launch_bounds__(256) void scan_experts_kernel(int32_t *__restrict__ blk_cnt, int nTB,
                                                            int E, int32_t *__restrict__ counts) {
-    __shared__ int tmp[256];
+    __shared__ unsigned long long wt[4];
     const int e = blockIdx.x, tid = threadIdx.x;
     int run = 0;
     for (int b0 = 0; b0 < nTB; b0 += 256) {
         const int b = b0 + tid;
         const int v = b < nTB ? blk_cnt[(size_t)b * E + e] : 0;
-        tmp[tid] = v;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            const int a = tid >= o ? tmp[tid - o] : 0;
-            __syncthreads();
-            tmp[tid] += a;
-            __syncthreads();
-        }
-        if (b < nTB) blk_cnt[(size_t)b * E + e] = run + tmp[tid] - v;
-        run += tmp[255];
-        __syncthreads();
+        unsigned long long tot;
+        const int inc = (int)block_scan_u64((unsigned long long)v, tid, wt, &tot);
+        if (b < nTB) blk_cnt[(size_t)b * E + e] = run + inc - v;
+        run += (int)tot;
     }
     if (tid == 0) counts[e] = run;
+}
+
+// Workgroup 0 of the scatter: expert offsets, the block map of at most BM rows per
+// block, its size, and the GEMM schedule (thread tid = expert tid with cnt rows from
+// row off; wt: the block scan's LDS scratch).  Called by the whole workgroup.
+__device__ void publish_blocks(int tid, int cnt, int off, int BM, unsigned long long *wt,
+                               int32_t *__restrict__ offsets, int32_t *__restrict__ blocks,
+                               int32_t *__restrict__ num_blocks, int32_t *__restrict__ sched,
+                               int32_t *__restrict__ qctl) {
+    const int nblk = (cnt + BM - 1) / BM;
+    // GEMM schedule: blocks by cost class (32-row M tiles: 4, 3, 2, 1), then by
+    // expert.  Four 16-bit class counters per expert are scanned as one word.
+    const int last_rows = nblk ? cnt - (nblk - 1) * BM : 0;
+    const int last_cls = nblk ? 4 - min(4, (last_rows + 31) >> 5) : 0;   // 0 = 4 tiles
+    unsigned long long mine = 0;
+    if (nblk) mine = (unsigned long long)(nblk - 1) + (1ull << (16 * last_cls));
+    unsigned long long ntot, tot;
+    const int bstart = (int)block_scan_u64((unsigned long long)nblk, tid, wt, &ntot) - nblk;
+    const unsigned long long pre = block_scan_u64(mine, tid, wt, &tot) - mine;
+    offsets[tid] = off;
+    if (tid == 255) {
+        offsets[256] = off + cnt;
+        num_blocks[0] = bstart + nblk;
+    }
+    for (int i = 0; i < nblk; ++i) {
+        int32_t *bp = blocks + 3 * (size_t)(bstart + i);
+        bp[0] = tid;
+        bp[1] = off + i * BM;
+        bp[2] = min(BM, cnt - i * BM);
+    }
+    // the GEMMs' queue counters start at zero
+    if (tid < 4) qctl[tid * QCTL_LINE] = 0;
+    int base[4];
+    base[0] = 0;
+    for (int c = 1; c < 4; ++c) base[c] = base[c - 1] + (int)((tot >> (16 * (c - 1))) & 0xFFFF);
+    int p0 = base[0] + (int)(pre & 0xFFFF);
+    for (int i = 0; i + 1 < nblk; ++i) sched[p0++] = bstart + i;
+    if (nblk) {
+        const int pl = last_cls == 0 ? p0 : base[last_cls] + (int)((pre >> (16 * last_cls)) & 0xFFFF);
+        sched[pl] = bstart + nblk - 1;
+    }
 }
 
 // Every workgroup scans the expert counts itself (256 values) to get the
@@ -726,71 +796,14 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     int32_t *__restrict__ offsets, int32_t *__restrict__ blocks, int32_t *__restrict__ num_blocks,
     int32_t *__restrict__ row_token, int32_t *__restrict__ tok_row, float *__restrict__ row_w,
     int32_t *__restrict__ sched, int32_t *__restrict__ qctl) {
-    __shared__ int tmp[256];
     __shared__ int s_off[256];
-    __shared__ unsigned long long cls_scan[256];
+    __shared__ unsigned long long wt[4];
     const int tid = threadIdx.x;
     const int cnt = counts[tid];
-    tmp[tid] = cnt;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int a = tid >= o ? tmp[tid - o] : 0;
-        __syncthreads();
-        tmp[tid] += a;
-        __syncthreads();
-    }
-    const int off = tmp[tid] - cnt;
+    unsigned long long tot;
+    const int off = (int)block_scan_u64((unsigned long long)cnt, tid, wt, &tot) - cnt;
     s_off[tid] = off;
-    if (blockIdx.x == 0) {
-        const int nblk = (cnt + BM - 1) / BM;
-        __syncthreads();
-        tmp[tid] = nblk;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            const int a = tid >= o ? tmp[tid - o] : 0;
-            __syncthreads();
-            tmp[tid] += a;
-            __syncthreads();
-        }
-        const int bstart = tmp[tid] - nblk;
-        offsets[tid] = off;
-        if (tid == 255) {
-            offsets[256] = off + cnt;
-            num_blocks[0] = bstart + nblk;
-        }
-        for (int i = 0; i < nblk; ++i) {
-            int32_t *bp = blocks + 3 * (size_t)(bstart + i);
-            bp[0] = tid;
-            bp[1] = off + i * BM;
-            bp[2] = min(BM, cnt - i * BM);
-        }
-        // GEMM schedule: blocks by cost class (32-row M tiles: 4, 3, 2, 1), then by
-        // expert.  Four 16-bit class counters per expert are scanned as one word.
-        const int last_rows = nblk ? cnt - (nblk - 1) * BM : 0;
-        const int last_cls = nblk ? 4 - min(4, (last_rows + 31) >> 5) : 0;   // 0 = 4 tiles
-        unsigned long long mine = 0;
-        if (nblk) mine = (unsigned long long)(nblk - 1) + (1ull << (16 * last_cls));
-        cls_scan[tid] = mine;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            const unsigned long long a = tid >= o ? cls_scan[tid - o] : 0ull;
-            __syncthreads();
-            cls_scan[tid] += a;
-            __syncthreads();
-        }
-        const unsigned long long tot = cls_scan[255], pre = cls_scan[tid] - mine;
-        // the GEMMs' queue counters start at zero
-        if (tid < 4) qctl[tid * QCTL_LINE] = 0;
-        int base[4];
-        base[0] = 0;
-        for (int c = 1; c < 4; ++c) base[c] = base[c - 1] + (int)((tot >> (16 * (c - 1))) & 0xFFFF);
-        int p0 = base[0] + (int)(pre & 0xFFFF);
-        for (int i = 0; i + 1 < nblk; ++i) sched[p0++] = bstart + i;
-        if (nblk) {
-            const int pl = last_cls == 0 ? p0 : base[last_cls] + (int)((pre >> (16 * last_cls)) & 0xFFFF);
-            sched[pl] = bstart + nblk - 1;
-        }
-    }
+    if (blockIdx.x == 0) publish_blocks(tid, cnt, off, BM, wt, offsets, blocks, num_blocks, sched, qctl);
     __syncthreads();
     const int idx = blockIdx.x * 256 + tid;
     if (idx >= T * k) return;
@@ -806,16 +819,102 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     row_w[r] = tw[idx];
 }
 
+// The routing structures in one kernel for T <= 4096, one workgroup per 32 tokens
+// (4 token blocks; 256 picks, one per thread), thread e standing for expert e in
+// the scans.  route_select has added every token block's expert counts into the
+// row of its superblock (kSupBlk consecutive blocks) in sup, so the base of
+// expert e in block b is the sum of sup over the superblocks before b's plus
+// blk_cnt over the blocks of b's superblock before b, and the expert counts are
+// the column sums of sup: one batch of loads, then the same LDS scans as
+// scatter_kernel.  Workgroup 0 also publishes counts, offsets, the block map
+// and the GEMM schedule.
+__global__ __launch_bounds__(256) void scatter1_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ tw,
+    const int32_t *__restrict__ blk_cnt, const int32_t *__restrict__ sup,
+    const int32_t *__restrict__ lrank, int T, int E, int k, int BM,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ blocks,
+    int32_t *__restrict__ num_blocks, int32_t *__restrict__ row_token,
+    int32_t *__restrict__ tok_row, float *__restrict__ row_w, int32_t *__restrict__ sched,
+    int32_t *__restrict__ qctl) {
+    __shared__ int s_off[256];
+    __shared__ int s_base[4][256];
+    __shared__ unsigned long long wt[4];
+    const int tid = threadIdx.x, e = tid;
+    const int nTB = (T + TB - 1) / TB, nS = (nTB + kSupBlk - 1) / kSupBlk;
+    const int b0 = blockIdx.x * 4, s0 = b0 / kSupBlk;
+    // every load at once, none under a branch: rows past the end read a valid row
+    // and are discarded
+    const int idx = blockIdx.x * 256 + tid;
+    const bool has = idx < T * k;
+    const int ic = has ? idx : 0;
+    const int pe = ids[ic], prk = lrank[ic];
+    const float pw = tw[ic];
+    int sv[kSupMax], iv[kSupBlk];
+#pragma unroll
+    for (int q = 0; q < kSupMax; ++q) sv[q] = sup[(size_t)(q < nS ? q : nS - 1) * E + e];
+#pragma unroll
+    for (int q = 0; q < kSupBlk; ++q) {
+        const int b = s0 * kSupBlk + q;
+        iv[q] = blk_cnt[(size_t)(b < nTB ? b : nTB - 1) * E + e];
+    }
+    int cnt = 0, run = 0;
+#pragma unroll
+    for (int q = 0; q < kSupMax; ++q) {
+        const int v = q < nS ? sv[q] : 0;
+        cnt += v;
+        if (q < s0) run += v;
+    }
+#pragma unroll
+    for (int q = 0; q < kSupBlk; ++q) {
+        const int b = s0 * kSupBlk + q;
+        if (b >= b0 && b < b0 + 4) s_base[b - b0][e] = run;
+        if (b < b0 + 4 && b < nTB) run += iv[q];
+    }
+    unsigned long long tot;
+    const int off = (int)block_scan_u64((unsigned long long)cnt, tid, wt, &tot) - cnt;
+    s_off[tid] = off;
+    if (blockIdx.x == 0) {
+        counts[tid] = cnt;
+        publish_blocks(tid, cnt, off, BM, wt, offsets, blocks, num_blocks, sched, qctl);
+    }
+    __syncthreads();
+    if (!has) return;
+    const int t = idx / k;
+    MOE_DBG(pe >= 0 && pe < E, DBG_ROUTE_INDEX);
+    if (pe < 0 || pe >= E) return;
+    const int r = s_off[pe] + s_base[t / TB - b0][pe] + prk;
+    MOE_DBG(r >= 0 && r < T * k, DBG_ROUTE_INDEX);
+    if (r < 0 || r >= T * k) return;
+    row_token[r] = t;
+    tok_row[idx] = r;
+    row_w[r] = pw;
+}
+
 void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
-                         const int32_t *lrank, int T, int E, int k, int BM, int32_t *counts,
-                         int32_t *offsets, int32_t *row_token, int32_t *tok_row, float *row_w,
-                         int32_t *blocks, int32_t *num_blocks, int32_t *sched, int32_t *qctl,
-                         hipStream_t s) {
+                         const int32_t *sup, const int32_t *lrank, int T, int E, int k, int BM,
+                         int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
+                         float *row_w, int32_t *blocks, int32_t *num_blocks, int32_t *sched,
+                         int32_t *qctl, hipStream_t s) {
     const int nTB = (T + TB - 1) / TB;
+    if (sup) {
+        hipLaunchKernelGGL(scatter1_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w,
+                           blk_cnt, sup, lrank, T, E, k, BM, counts, offsets, blocks, num_blocks,
+                           row_token, tok_row, row_w, sched, qctl);
+        return;
+    }
     hipLaunchKernelGGL(scan_experts_kernel, dim3(E), dim3(256), 0, s, blk_cnt, nTB, E, counts);
     hipLaunchKernelGGL(scatter_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w, blk_cnt,
                        lrank, counts, T, E, k, BM, offsets, blocks, num_blocks, row_token,
                        tok_row, row_w, sched, qctl);
+}
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *__restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+void launch_zero_i32(int32_t *p, int n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
 }
 
 // Activation preparation for the GEMM: fp16 copy with the 8-block permutation
