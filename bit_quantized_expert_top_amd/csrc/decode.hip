@@ -186,7 +186,9 @@ __device__ __forceinline__ float pair_sum(float v) {
 // of group 4 w + gi (+ 32 per further pass), so one load instruction of a wave
 // covers four groups.  x is loaded before the selection, the weights right
 // after it, all at once.
-__global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
+// at most 64 VGPRs: 8 waves per SIMD, so that four workgroups share a CU (small batches
+// launch T x 576 workgroups)
+__global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
     GemmWeights gw, int32_t *__restrict__ ids_out, float *__restrict__ tw_out,
     uint16_t *__restrict__ hbuf, float *__restrict__ hfac, bool picks_given,
@@ -326,7 +328,9 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(
     if (threadIdx.x < DOUT) {
         const int m = threadIdx.x;
         float gs = 0.0f, us = 0.0f;
-#pragma unroll
+        // (four waves' partials per batch of LDS reads: all 64 at once would exceed the
+        // kernel's 64 registers)
+#pragma unroll 4
         for (int w = 0; w < DW; ++w)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
