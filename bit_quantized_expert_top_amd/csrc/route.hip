@@ -343,13 +343,15 @@ __device__ __forceinline__ void stage_row(const uint16_t *row, int H, int lane, 
 // entry out[i] holds the bias of elist[i], on exit its logit (wave-local LDS).
 // The token's x row is already in slot 3 of the wave's stage (stage /
 // stage_lds: its generic and LDS addresses).  The router rows travel by DMA
-// into slots 0-2 at once, into slot 3 once x is in registers, and then each
-// round refills the two slots it has read with the rows two rounds ahead.  In
-// round r half h of the wave takes row 2 r + h, lane c of the half chunk c,
-// summed sequentially from its first product; the chunk partials meet in scr
-// (64 floats) and lanes 0 and 32 add them in chunk order, then the bias.
+// into slots 0-2 at once and into slot 3 once x is in registers; round r takes
+// rows 4 r .. 4 r + 3 (slots 0-3) and then refills all four slots with the next
+// round's rows.  Half h of the wave takes rows 4 r + h and 4 r + 2 + h, lane c
+// of the half chunk c of both, each summed sequentially from its first product
+// (two independent chains per lane).  The chunk partials of 8 rows collect in
+// part (256 floats); after every second round lanes 0-7 add one row's 32
+// partials each in chunk order, then its bias.
 __device__ void exact_logits(const uint32_t *elist, int n, float *out,
-                             const uint16_t *__restrict__ wr, int H, int lane, float *scr,
+                             const uint16_t *__restrict__ wr, int H, int lane, float *part,
                              const uint8_t *stage, uint32_t stage_lds) {
     const int c = lane & 31, hh = lane >> 5, nch = H / 64;
     const int ipr = (nch + 7) >> 3;               // DMA instructions per row (1 KB each)
@@ -371,49 +373,63 @@ __device__ void exact_logits(const uint32_t *elist, int n, float *out,
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot 3 is refilled next
     int next = pre;
     if (next < n) issue(next++);
-    for (int r = 0; 2 * r < n; ++r) {
-        const int need = 2 * r + 2 < n ? 2 * r + 2 : n;
+    for (int r = 0; 4 * r < n; ++r) {
+        const int need = 4 * r + 4 < n ? 4 * r + 4 : n;
         wait_vm_upto12((next - need) * ipr);
-        const int i = 2 * r + hh;
-        float s = 0.0f;
-        if (c < nch && i < n) {
-            const uint8_t *ws = stage + XS_SLOT * (i & 3) + 128 * c;
-            u32x4 wv[8];
+        const int ia = 4 * r + hh, ib = ia + 2;
+        if (c < nch) {
+            const uint8_t *wa = stage + XS_SLOT * hh + 128 * c;
+            const uint8_t *wb = stage + XS_SLOT * (2 + hh) + 128 * c;
+            u32x4 va[8], vb[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) wv[q] = *(const u32x4 *)(ws + 16 * (q ^ (c & 7)));
-            // sequential within the chunk, from its first product (each fma adds one exact product)
-            s = bf16_lo(xv[0][0]) * bf16_lo(wv[0][0]);
+            for (int q = 0; q < 8; ++q) {
+                va[q] = *(const u32x4 *)(wa + 16 * (q ^ (c & 7)));
+                vb[q] = *(const u32x4 *)(wb + 16 * (q ^ (c & 7)));
+            }
+            // sequential within the chunk, from its first product (each fma adds one exact
+            // product); rows past n read a stale slot and are never used
+            float sa = bf16_lo(xv[0][0]) * bf16_lo(va[0][0]);
+            float sb = bf16_lo(xv[0][0]) * bf16_lo(vb[0][0]);
 #pragma unroll
             for (int q = 0; q < 8; ++q)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    if (q > 0 || u > 0) s = __builtin_fmaf(bf16_lo(xv[q][u]), bf16_lo(wv[q][u]), s);
-                    s = __builtin_fmaf(bf16_hi(xv[q][u]), bf16_hi(wv[q][u]), s);
+                    if (q > 0 || u > 0) {
+                        sa = __builtin_fmaf(bf16_lo(xv[q][u]), bf16_lo(va[q][u]), sa);
+                        sb = __builtin_fmaf(bf16_lo(xv[q][u]), bf16_lo(vb[q][u]), sb);
+                    }
+                    sa = __builtin_fmaf(bf16_hi(xv[q][u]), bf16_hi(va[q][u]), sa);
+                    sb = __builtin_fmaf(bf16_hi(xv[q][u]), bf16_hi(vb[q][u]), sb);
                 }
-        }
-        scr[lane] = s;
-        __builtin_amdgcn_wave_barrier();
-        if (c == 0 && i < n) {
-            // the 32 partials in one batch of LDS reads, then added in chunk order
-            const float4 *pp = (const float4 *)(scr + 32 * hh);
-            float v[32];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 f = pp[q];
-                v[4 * q] = f.x;
-                v[4 * q + 1] = f.y;
-                v[4 * q + 2] = f.z;
-                v[4 * q + 3] = f.w;
-            }
-            float L = v[0];
-#pragma unroll
-            for (int q = 1; q < 32; ++q)
-                if (q < nch) L = L + v[q];
-            out[i] = L + out[i];
+            part[32 * (ia & 7) + c] = sa;
+            part[32 * (ib & 7) + c] = sb;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this round's slots are refilled next
         __builtin_amdgcn_wave_barrier();
-        for (int u = 0; u < 2 && next < n; ++u) issue(next++);
+        for (int u = 0; u < 4 && next < n; ++u) issue(next++);
+        if ((r & 1) || 4 * r + 4 >= n) {
+            // rows 8 g .. 8 g + 7 complete: lane l adds row 8 g + l's partials in chunk order
+            const int i = 8 * (r >> 1) + lane;
+            if (lane < 8 && i < n) {
+                const float4 *pp = (const float4 *)(part + 32 * lane);
+                float v[32];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float4 f = pp[q];
+                    v[4 * q] = f.x;
+                    v[4 * q + 1] = f.y;
+                    v[4 * q + 2] = f.z;
+                    v[4 * q + 3] = f.w;
+                }
+                float L = v[0];
+#pragma unroll
+                for (int q = 1; q < 32; ++q)
+                    if (q < nch) L = L + v[q];
+                out[i] = L + out[i];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_wave_barrier();
+        }
     }
 }
 
@@ -432,6 +448,7 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
     __shared__ uint32_t cand_e[TB][256];
     __shared__ __attribute__((aligned(16))) float cand_l[TB][256];
     __shared__ __attribute__((aligned(16))) float scr[TB][64];
+    __shared__ __attribute__((aligned(16))) float xpart[TB][256];   // exact recompute: 8 rows' chunk partials
     extern __shared__ __attribute__((aligned(1024))) uint8_t xstage[];   // [TB][XS_WAVE]
     const uint32_t xstage_lds =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)xstage;
@@ -554,7 +571,7 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 if (ci < nc) cand_l[tl][ci] = b;
             }
             __builtin_amdgcn_wave_barrier();
-            exact_logits(cand_e[tl], nc, cand_l[tl], wr, H, lane, scr[tl], stage, stage_lds);
+            exact_logits(cand_e[tl], nc, cand_l[tl], wr, H, lane, xpart[tl], stage, stage_lds);
             __builtin_amdgcn_wave_barrier();
             if (nc <= 64) {
                 // rank of candidate `lane` by (exact logit desc, index asc)
