@@ -485,8 +485,9 @@ def main():
             for w in layers:
                 moe.moe_route(sshape, u, w, sr, sws)
                 moe.moe_expert_gemm_q4(sshape, u, w, sr, sh_, sws)
-                moe.moe_down_combine(sshape, sh_, w, sr, sy, sws)
-                moe.moe_rmsnorm_residual(Ts, H, 1e-6, res, sy, u)
+                # down GEMM, combine, residual add and RMSNorm: the combined rows are added
+                # to the residual as they are formed (y holds only the shared part)
+                moe.moe_down_combine_residual(sshape, sh_, w, sr, sy, res, 1e-6, u, sws)
 
         stack_pass()
         torch.cuda.synchronize()

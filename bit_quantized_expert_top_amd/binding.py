@@ -50,6 +50,8 @@ _SIGS = {
                             C.c_size_t, P], i32),
     "moe_down_combine": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P,
                           C.c_size_t, P], i32),
+    "moe_down_combine_residual": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing),
+                                   P, P, C.c_float, P, P, C.c_size_t, P], i32),
     "moe_layer": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P, P,
                    C.c_size_t, P], i32),
     "moe_query_chunked": ([C.POINTER(_Shape), i32, C.POINTER(C.c_size_t)], i32),
@@ -323,6 +325,21 @@ def moe_down_combine(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing, 
     _check(lib().moe_down_combine(C.byref(shape.c()), _ptr(h, _H16, "h"), C.byref(w.c()),
                                   C.byref(r.c()), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
                                   ws.numel(), _stream(stream)), "moe_down_combine")
+
+
+def moe_down_combine_residual(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing,
+                              y: torch.Tensor, res: torch.Tensor, eps: float, u: torch.Tensor,
+                              ws: torch.Tensor, stream=None):
+    """Down GEMM + combine fused with the residual add and RMSNorm of a stack: res += y_layer,
+    u = bf16(RMSNorm(res)); y is scratch (the shared expert's part only on return)."""
+    _args(shape, w, r, h=h, y=y)
+    _need(res, shape.T * shape.H, "res")
+    _need(u, shape.T * shape.H, "u")
+    _check(lib().moe_down_combine_residual(C.byref(shape.c()), _ptr(h, _H16, "h"), C.byref(w.c()),
+                                           C.byref(r.c()), _ptr(y, _F32, "y"),
+                                           _ptr(res, _F32, "res"), eps, _ptr(u, _B16, "u"),
+                                           _ptr(ws, None, "ws"), ws.numel(), _stream(stream)),
+           "moe_down_combine_residual")
 
 
 def moe_layer(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,

@@ -199,7 +199,8 @@ moe_status enqueue_gateup(const moe_shape *s, const uint16_t *x, const moe_weigh
 }
 
 moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights *w,
-                        const moe_routing *r, float *y, char *ws, hipStream_t st) {
+                        const moe_routing *r, float *y, char *ws, hipStream_t st,
+                        bool combine = true) {
     const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
     // group sums of h: left in the workspace by the gate/up pass
     const float *hsum = (const float *)(ws + L.hsum);
@@ -207,7 +208,7 @@ moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights
     launch_down(*s, h, hsum, (const float *)(ws + L.hexp), gw, r->blocks, r->num_blocks,
                 (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
                 max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
-                (uint16_t *)(ws + L.stage), y, st);
+                (uint16_t *)(ws + L.stage), y, combine, st);
     return launched();
 }
 
@@ -276,6 +277,27 @@ moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe
     MOE_TRY(check_routing(r));
     MOE_TRY(check_ws(shape, ws, ws_bytes));
     return enqueue_down(shape, h, w, r, y, (char *)ws, (hipStream_t)stream);
+}
+
+moe_status moe_down_combine_residual(const moe_shape *shape, const uint16_t *h,
+                                     const moe_weights *w, const moe_routing *r, float *y,
+                                     float *res, float eps, uint16_t *u, void *ws,
+                                     size_t ws_bytes, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(h) || !aligned(y) || !aligned(res) || !aligned(u) || !(eps >= 0.0f))
+        return MOE_ERR_INVALID_ARG;
+    if ((const void *)res == (const void *)y || (const void *)u == (const void *)res ||
+        (const void *)u == (const void *)y)
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, false, false, true));
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY(enqueue_down(shape, h, w, r, y, (char *)ws, st, false));
+    const WsLayout L = ws_layout(shape->T, shape->H, shape->I, shape->E, shape->top_k);
+    launch_combine_residual_norm(shape->T, shape->H, shape->top_k, eps, res, y,
+                                 (const uint16_t *)((char *)ws + L.stage), r->tok_row, u, st);
+    return launched();
 }
 
 moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
@@ -433,7 +455,7 @@ moe_status moe_debug_status(uint32_t *flags, int32_t clear) {
 #ifdef MOE_DEBUG
     if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
     const uint32_t v = dbg_read_route(clear != 0) | dbg_read_gemm(clear != 0) |
-                       dbg_read_decode(clear != 0);
+                       dbg_read_decode(clear != 0) | dbg_read_misc(clear != 0);
     *flags = v;
     return (v & 0x80000000u) ? MOE_ERR_HIP : MOE_OK;
 #else

@@ -309,6 +309,7 @@ static __device__ uint32_t dbg_word;
 uint32_t dbg_read_route(bool clear);
 uint32_t dbg_read_gemm(bool clear);
 uint32_t dbg_read_decode(bool clear);
+uint32_t dbg_read_misc(bool clear);
 
 // A kernel's dynamic-LDS limit raised once per device (thread-safe: a host thread's
 // first launch on a device sets it, concurrent first launches wait for that).
@@ -397,7 +398,11 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
                  const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
                  const int32_t *sched, int32_t *qctl, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
-                 uint16_t *stage, float *y, hipStream_t s);
+                 uint16_t *stage, float *y, bool combine, hipStream_t s);
+// r += (y + the k staging rows of each token, in pick order); u = bf16(RMSNorm(r))
+void launch_combine_residual_norm(int T, int H, int k, float eps, float *r, const float *y,
+                                  const uint16_t *stage, const int32_t *tok_row, uint16_t *u,
+                                  hipStream_t s);
 
 // Power-of-two helpers for the range normalisation: 2^n as a float (n clamped to the
 // normal range), and floor(log2 |v|) of a finite nonzero float.

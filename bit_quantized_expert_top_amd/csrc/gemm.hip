@@ -666,7 +666,7 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
                  const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
                  const int32_t *sched, int32_t *qctl, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
-                 uint16_t *stage, float *y, hipStream_t s) {
+                 uint16_t *stage, float *y, bool combine, hipStream_t s) {
     GemmArgs a{};
     a.A = h;
     a.Asum = hsum;
@@ -697,7 +697,8 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
     // shared-expert blocks write y, routed blocks their weighted staging rows ...
     hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(grid_for(a.n_shared, max_blocks, a.n_tiles)),
                        dim3(NTHR), L_TOTAL, s, a);
-    // ... then each token adds its eight routed rows
+    // ... then each token adds its eight routed rows (unless the caller's next kernel does)
+    if (!combine) return;
     const size_t n8 = (size_t)sh.T * sh.H / 8;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, stage,
                        tok_row, sh.T, sh.H, sh.top_k, y);

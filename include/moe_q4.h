@@ -207,6 +207,21 @@ moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe
                             const moe_routing *r, float *y, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* moe_down_combine fused with the residual add and RMSNorm that follow it in a stack of
+ * layers (moe_rmsnorm_residual): with y_layer the output moe_down_combine would write,
+ *   res <- res + y_layer,   u = bf16(res / sqrt(mean(res^2) + eps))   (unit weight),
+ * bit for bit as moe_down_combine followed by moe_rmsnorm_residual (the same operations in
+ * the same order: the eight routed rows are added to the shared expert's row in pick
+ * order, in fp32, while the residual row is read).  y_layer is never stored, which saves
+ * writing and re-reading T*H*4 bytes: y is scratch and holds only the shared expert's part
+ * on return.  res, y: fp32 [T][H]; u: bf16 [T][H]; h, weights, routing and workspace as
+ * for moe_down_combine.  MOE_ERR_INVALID_ARG if res, y and u overlap pairwise (by start
+ * address) or eps < 0. */
+moe_status moe_down_combine_residual(const moe_shape *shape, const uint16_t *h,
+                                     const moe_weights *w, const moe_routing *r, float *y,
+                                     float *res, float eps, uint16_t *u, void *ws,
+                                     size_t ws_bytes, void *stream);
+
 /* The whole layer: moe_route, moe_expert_gemm_q4, moe_down_combine. */
 moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                      const moe_routing *r, uint16_t *h, float *y, void *ws, size_t ws_bytes,

@@ -46,6 +46,9 @@ int main(void)
             EXPECT(moe_route(&s, fake, &w, &r, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
             EXPECT(moe_expert_gemm_q4(&s, fake, &w, &r, fake, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
             EXPECT(moe_down_combine(&s, fake, &w, &r, fake, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
+            EXPECT(moe_down_combine_residual(&s, fake, &w, &r, (float *)fake, (float *)fake + 64,
+                                             1e-6f, (uint16_t *)fake + 4096, fake, ws - 1, NULL),
+                   MOE_ERR_WORKSPACE);
             EXPECT(moe_layer(&s, fake, &w, &r, fake, fake, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
             EXPECT(moe_layer_chunked(&s, fake, &w, fake, 64, fake, cws - 1, NULL), MOE_ERR_WORKSPACE);
             if (s.T <= 8) {

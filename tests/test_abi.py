@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ("moe_query", "moe_route", "moe_expert_gemm_q4", "moe_down_combine", "moe_layer",
+    for n in ("moe_query", "moe_route", "moe_expert_gemm_q4", "moe_down_combine",
+              "moe_down_combine_residual", "moe_layer",
               "moe_query_chunked", "moe_layer_chunked", "moe_decode", "moe_rmsnorm_residual",
               "moe_dequant_q4", "moe_status_str"):
         assert n in names
@@ -127,6 +128,20 @@ def test_gemm_and_down_validation_before_launch():
     assert L.moe_down_combine(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), FAKE, FAKE, 0,
                               None) == WS
     assert L.moe_layer(C.byref(s), FAKE, None, C.byref(r), FAKE, FAKE, FAKE, need, None) == INVALID
+    # the fused down + residual + norm: the same checks, plus its three fp32/bf16 row buffers
+    # must be distinct and eps >= 0
+    Y, R, U = FAKE + 4096, FAKE + 8192, FAKE + 12288
+    fused = L.moe_down_combine_residual
+    assert fused(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), Y, R, 1e-6, U, FAKE, 0,
+                 None) == WS
+    assert fused(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), Y, Y, 1e-6, U, FAKE, need,
+                 None) == INVALID
+    assert fused(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), Y, R, 1e-6, R, FAKE, need,
+                 None) == INVALID
+    assert fused(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), Y, R, -1.0, U, FAKE, need,
+                 None) == INVALID
+    assert fused(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), Y + 8, R, 1e-6, U, FAKE, need,
+                 None) == INVALID
 
 
 def test_decode_token_limit():

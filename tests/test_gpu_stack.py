@@ -48,3 +48,30 @@ def test_stack_teacher_forced(T, H, I, layers, nsamp):
         ur = bf16_bits_to_f32(u_ref).astype(np.float64)
         # the oracle adds in fp64, the GPU in fp32: at most one bf16 ulp apart
         assert np.all(np.abs(ug - ur) <= 2.0 ** -7 * np.abs(ur) + 1e-30), layer
+
+
+@pytest.mark.parametrize("T,H,I", [(64, 512, 128), (333, 768, 384), (4096, 2048, 512)])
+def test_fused_down_residual_norm_is_bit_identical(T, H, I):
+    """moe_down_combine_residual gives exactly the residual and the next layer's input that
+    moe_down_combine followed by moe_rmsnorm_residual give (ragged T, another H, the stack
+    workload's T), on every element."""
+    print(f"[stack] fused down + residual + norm, T={T} H={H} I={I}", flush=True)
+    dev = device()
+    inp = make_layer(5100 + T, T=T, H=H, I=I)
+    run = LayerRun(inp).route().gemm().sync()
+    g = torch.Generator(device="cpu").manual_seed(T)
+    r0 = (torch.randn((T, H), generator=g) * 3.0).to(dev)
+    # unfused: y, then r += y and u = norm(r)
+    run.down().sync()
+    r_a = r0.clone()
+    u_a = torch.empty((T, H), dtype=torch.int16, device=dev)
+    moe.moe_rmsnorm_residual(T, H, 1e-6, r_a, run.y, u_a)
+    # fused (y is scratch there)
+    r_b = r0.clone()
+    u_b = torch.empty((T, H), dtype=torch.int16, device=dev)
+    y_b = torch.empty((T, H), dtype=torch.float32, device=dev)
+    moe.moe_down_combine_residual(run.shape, run.h, run.w, run.r, y_b, r_b, 1e-6, u_b, run.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(r_a, r_b)
+    assert torch.equal(u_a, u_b)
+    assert torch.all(torch.isfinite(r_b))
