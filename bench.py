@@ -48,9 +48,9 @@ SEED_STACK = 5000
 # 131085.4 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
 # source these counters were taken on; otherwise the JSON reports null.
 GATEUP_TRAFFIC = {
-    "gemm_src_sha256": "611b8adba533a7bebf5a206de05ea08461b81d4a2291fa9acf726b3f46b0be22",
-    "fetch_kib": 159201.9, "fetch_scale": 2.0,
-    "write_kib": 20748.0, "write_scale": 1.0,
+    "gemm_src_sha256": "1416c5d7ae83c7ad2f2dc794938cb757ef7feae9aaf0a6342575b81fec133340",
+    "fetch_kib": 159765.9, "fetch_scale": 2.0,
+    "write_kib": 20741.6, "write_scale": 1.0,
     "profile": "profiles/moe_layer_prefill2048_zipf_hbm_traffic.md",
 }
 
