@@ -28,11 +28,12 @@ constexpr int kSupMax = 32;      // superblocks of the single-pass scan (T <= 40
 constexpr int kDecodeMaxT = 8;  // moe_decode: tokens per call (each an independent GEMV problem)
 
 // Decode scratch for T tokens (E = 256 experts, k + 1 slots): the router logits, the h
-// rows and the per-slot h factors, each part rounded up to 256 bytes.
+// rows, and the per-slot h factors followed by each token's ||x||^2, each part rounded
+// up to 256 bytes.
 constexpr size_t decode_scratch_size(int T, int I, int k) {
     return (((size_t)T * 256 * 4 + 255) & ~(size_t)255) +
            (((size_t)T * (k + 1) * I * 2 + 255) & ~(size_t)255) +
-           (((size_t)T * (k + 1) * 4 + 255) & ~(size_t)255);
+           (((size_t)T * (k + 2) * 4 + 255) & ~(size_t)255);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }

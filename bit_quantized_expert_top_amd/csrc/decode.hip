@@ -54,7 +54,8 @@ __global__ __launch_bounds__(64) void decode_router_kernel(const uint16_t *__res
                                                            float *__restrict__ logits,
                                                            const float *__restrict__ res,
                                                            const float *__restrict__ yprev, float eps,
-                                                           uint16_t *__restrict__ u_out) {
+                                                           uint16_t *__restrict__ u_out,
+                                                           float *__restrict__ xn2) {
     const int lane = threadIdx.x;
     const int e = blockIdx.x;
     const int E = gridDim.x;
@@ -99,6 +100,23 @@ __global__ __launch_bounds__(64) void decode_router_kernel(const uint16_t *__res
 #pragma unroll
             for (int j = 0; j < 8; ++j) pu[j] = xv[j];
         }
+    }
+    if (e == 0) {
+        // the token's ||x||^2 for the gate/up kernel's h range bound (bf16 squares are
+        // exact in fp32): off that kernel's latency chain
+        float q2 = 0.0f;
+        if (lane < G) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    q2 = __builtin_fmaf(bf16_lo(xv[j][r]), bf16_lo(xv[j][r]), q2);
+                    q2 = __builtin_fmaf(bf16_hi(xv[j][r]), bf16_hi(xv[j][r]), q2);
+                }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) q2 += __shfl_xor(q2, off);
+        if (lane == 0) xn2[t] = q2;
     }
     float P = 0.0f;
     if (lane < G) {
@@ -191,10 +209,9 @@ __device__ __forceinline__ float pair_sum(float v) {
 __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, int H, int I, int k, int E,
     GemmWeights gw, int32_t *__restrict__ ids_out, float *__restrict__ tw_out,
-    uint16_t *__restrict__ hbuf, float *__restrict__ hfac, bool picks_given,
-    float *__restrict__ res, const float *__restrict__ yprev) {
+    uint16_t *__restrict__ hbuf, float *__restrict__ hfac, const float *__restrict__ xn2,
+    bool picks_given, float *__restrict__ res, const float *__restrict__ yprev) {
     __shared__ float red[DW][4][DOUT][2];
-    __shared__ float xss[DW];
     __shared__ uint32_t selw[DW][32];
     __shared__ u32x4 xs[256];                                     // the token's x, H <= 2048
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -233,6 +250,7 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
     const int gc = min(g, G - 1);
     u32x4 xl = {0u, 0u, 0u, 0u};
     if ((int)threadIdx.x < H / 8) xl = *(const u32x4 *)(x + 8 * threadIdx.x);
+    const float x2 = xn2[blockIdx.y];                             // ||x||^2 (router kernel)
     int ex = 0;
     if (slot < k && picks_given) {
         ex = ids_out[slot];                                       // written by decode_select_kernel
@@ -272,17 +290,6 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
         }
     }
     if ((int)threadIdx.x < H / 8) xs[threadIdx.x] = xl;
-    {   // ||x||^2 of the token (bf16 squares are exact in fp32)
-        float q2 = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            q2 = __builtin_fmaf(bf16_lo(xl[r]), bf16_lo(xl[r]), q2);
-            q2 = __builtin_fmaf(bf16_hi(xl[r]), bf16_hi(xl[r]), q2);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) q2 += __shfl_xor(q2, off);
-        if (lane == 0) xss[wave] = q2;
-    }
     __syncthreads();
     u32x4 xv[4];
 #pragma unroll
@@ -339,9 +346,6 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
             }
         // h is kept as h 2^-f in fp16, f from the bound (row norm x ||x||)^2 on |h| (0 in
         // the usual range); every workgroup of the slot takes the same f, the first records 2^f
-        float x2 = 0.0f;
-#pragma unroll
-        for (int w = 0; w < DW; ++w) x2 += xss[w];
         const int f = h_exponent(nw, sqrtf(x2));
         hbuf[(size_t)slot * I + DOUT * o + m] = f32_to_f16(gs / (1.0f + expf(-gs)) * (us * exp2i(-f)));
         if (o == 0 && m == 0) hfac[slot] = exp2i(f);
@@ -483,6 +487,7 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     float *logits = (float *)p;                                   // [T][E]
     uint16_t *hbuf = (uint16_t *)(p + logits_bytes(T, E));        // fp16 [T][k+1][I]
     float *hfac = (float *)(p + logits_bytes(T, E) + hbuf_bytes(T, I, k));   // [T][k+1]
+    float *xn2 = hfac + (size_t)T * (k + 1);                                  // [T]
     // the API admits top_k = 8, E <= 256, H <= 2048 (G <= 32), I <= 2048, T <= kDecodeMaxT
     if (k + 1 != NSLOT || E > 256 || H > 2048 || I > 2048 || T < 1 || T > kDecodeMaxT) return;
     const GemmWeights gu = gemm_weights(w.packed, H, I, E, true);
@@ -491,14 +496,14 @@ void launch_decode(const moe_shape &sh, const uint16_t *x, const moe_weights &w,
     const uint16_t *xin = res ? u_out : x;
     // every kernel takes token t = blockIdx.y; the tokens are independent problems
     hipLaunchKernelGGL(decode_router_kernel, dim3(E, T), dim3(64), 0, s, x, w.router_wt, w.router_bias,
-                       H, logits, res, yprev, eps, u_out);
+                       H, logits, res, yprev, eps, u_out, xn2);
     // one token: every gate/up wave takes the top-k itself (no extra launch on the
     // latency chain); more tokens: the picks are taken once per token
     const bool picks_given = T > 1;
     if (picks_given)
         hipLaunchKernelGGL(decode_select_kernel, dim3(T), dim3(64), 0, s, logits, E, k, ids, tw);
     hipLaunchKernelGGL(decode_gateup_kernel, dim3((k + 1) * (I / DOUT), T), dim3(64 * DW), 0, s, xin,
-                       logits, H, I, k, E, gu, ids, tw, hbuf, hfac, picks_given, res, yprev);
+                       logits, H, I, k, E, gu, ids, tw, hbuf, hfac, xn2, picks_given, res, yprev);
     hipLaunchKernelGGL(decode_down_kernel, dim3(H / DOUT, T), dim3(64 * DW), (size_t)(k + 1) * I * 2, s,
                        hbuf, hfac, H, I, ids, tw, k, E, dn, y);
 }
