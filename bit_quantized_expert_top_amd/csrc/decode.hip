@@ -275,8 +275,16 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
                                     : gw.pk + ((size_t)ex * JT + j) * G * PK_BLOCK;
     const float *tcf = slot == k ? gw.colf_sh + (size_t)j * PK_COLF
                                  : gw.colf + ((size_t)ex * JT + j) * PK_COLF;
-    const float kg = tcf[tcg], ku = tcf[tcg + 32];              // 2^-k of my two columns
-    const float nw = gw.emeta[(size_t)(slot == k ? E : ex) * PK_EMETA];
+    // the columns' 2^-k and the expert's row-norm bound, for the eight output threads only
+    // (lanes 0-7 of wave 0, output m = lane): the factor is a power of two, so applying it
+    // to the reduced sums gives the same bits as applying it to every partial
+    float kg = 1.0f, ku = 1.0f, nw = 0.0f;
+    if (wave == 0) {
+        const int tc = 64 * u + 8 * v + (lane & 7);
+        kg = tcf[tc];
+        ku = tcf[tc + 32];
+        nw = gw.emeta[(size_t)(slot == k ? E : ex) * PK_EMETA];
+    }
     u32x4 cw[2];
     uint16_t sv[2], bv[2];
     {
@@ -320,9 +328,10 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
                                                         __builtin_bit_cast(bf16x2, xp[4 * qq + p]), d, false);
                 }
             // sum_k x_k (q_k s + b) = s (sum x (128 + q) - 128 sum x) + b sum x
-            // (the block holds s and b times 2^k; the column factor 2^-k undoes it exactly)
+            // (the block holds s and b times 2^k; the column factor 2^-k undoes it exactly,
+            // after the reduction)
             const float val = bf16_to_f32(sv[r]) * (d - 128.0f * sx) + bf16_to_f32(bv[r]) * sx;
-            if (r == 0) ag += val * kg; else au += val * ku;
+            if (r == 0) ag += val; else au += val;
         }
     }
     ag = pair_sum(ag);
@@ -344,6 +353,8 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
                 gs += red[w][q][m][0];
                 us += red[w][q][m][1];
             }
+        gs *= kg;
+        us *= ku;
         // h is kept as h 2^-f in fp16, f from the bound (row norm x ||x||)^2 on |h| (0 in
         // the usual range); every workgroup of the slot takes the same f, the first records 2^f
         const int f = h_exponent(nw, sqrtf(x2));
@@ -363,6 +374,7 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ tw, int k, int E, GemmWeights gw,
     float *__restrict__ y) {
     __shared__ float part[DN_MAXP][DOUT];
+    __shared__ float slot_sum[NSLOT][DOUT];
     extern __shared__ u32x4 hsh[];                                // the token's h block, (k+1) I fp16
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
     const int G = I / 64, JD = H / 256, NPAIR = (k + 1) * G;
@@ -398,6 +410,19 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
         sid[s] = (e < 0 || e >= E) ? 0 : e;
         sfac[s] = (s < k ? tw[s] : 1.0f) * hfac[s];
     }
+    // thread (slot tid / 8, output tid % 8), tid < 72: that slot's column factor 2^-k of the
+    // output, applied to the slot's reduced sum (a power of two: the same bits as applying it
+    // to every partial), loaded now and used at the end
+    float kfm = 1.0f;
+    if (tid < NSLOT * DOUT) {
+        const int s = tid >> 3;
+        int e = 0;
+#pragma unroll
+        for (int r = 0; r < NSLOT; ++r)
+            if (r == s) e = sid[r];
+        kfm = (s == k ? gw.colf_sh + (size_t)j * PK_COLF
+                      : gw.colf + ((size_t)e * JD + j) * PK_COLF)[8 * v + (tid & 7)];
+    }
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     uint32_t cM = 0x000F000Fu, cC = 0x64006400u;
     asm volatile("" : "+v"(cM), "+v"(cC));
@@ -405,7 +430,6 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
     for (int it0 = 0; it0 < npass; it0 += DN_BATCH) {
         u32x4 cw[DN_BATCH], hv[DN_BATCH][4];
         uint16_t sv[DN_BATCH], bv[DN_BATCH];
-        float kf[DN_BATCH];
         int pp[DN_BATCH], hcs[DN_BATCH];
 #pragma unroll
         for (int b = 0; b < DN_BATCH; ++b) {
@@ -420,8 +444,6 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
             const uint8_t *blk = (s == k ? gw.pk_sh + (size_t)j * G * PK_BLOCK
                                          : gw.pk + ((size_t)e * JD + j) * G * PK_BLOCK) +
                                  (size_t)g * PK_BLOCK;
-            kf[b] = (s == k ? gw.colf_sh + (size_t)j * PK_COLF
-                            : gw.colf + ((size_t)e * JD + j) * PK_COLF)[tc];
             // pairs past the end load the last pair again (unconditional loads are
             // issued together) and are skipped below
             cw[b] = *(const u32x4 *)(blk + 32 * tc + 16 * ph);
@@ -461,20 +483,24 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
                                                d, false);
                 }
             // sum_i h_i (q_i s + b) = s (sum h (1024 + q) - 1024 sum h) + b sum h
-            const float val = pair_sum((bf16_to_f32(sv[b]) * (d - 1024.0f * shs) + bf16_to_f32(bv[b]) * shs) * kf[b]);
+            const float val = pair_sum(bf16_to_f32(sv[b]) * (d - 1024.0f * shs) + bf16_to_f32(bv[b]) * shs);
             if (ph == 0) part[pp[b]][cc] = val;
         }
+    }
+    __syncthreads();
+    if (tid < NSLOT * DOUT) {
+        // each slot's sum over its groups, in group order, times its column factor
+        const int s = tid >> 3, m = tid & 7;
+        float a = 0.0f;
+        for (int g = 0; g < G; ++g) a += part[s * G + g][m];
+        slot_sum[s][m] = a * kfm;
     }
     __syncthreads();
     if (tid < DOUT) {
         // each slot's h was kept as h 2^-f: its weight (1 for the shared expert) times 2^f
         float sum = 0.0f;
 #pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
-            float a = 0.0f;
-            for (int g = 0; g < G; ++g) a += part[s * G + g][tid];
-            sum = __builtin_fmaf(sfac[s], a, sum);
-        }
+        for (int s = 0; s < NSLOT; ++s) sum = __builtin_fmaf(sfac[s], slot_sum[s][tid], sum);
         y[256 * j + DOUT * v + tid] = sum;
     }
 }
