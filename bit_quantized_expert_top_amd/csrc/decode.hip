@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
     GemmWeights gw, int32_t *__restrict__ ids_out, float *__restrict__ tw_out,
     uint16_t *__restrict__ hbuf, float *__restrict__ hfac, const float *__restrict__ xn2,
     bool picks_given, float *__restrict__ res, const float *__restrict__ yprev) {
-    __shared__ float red[DW][4][DOUT][2];
+    __shared__ float red[DW][DOUT][2];
     __shared__ uint32_t selw[DW][32];
     __shared__ u32x4 xs[256];                                     // the token's x, H <= 2048
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -334,25 +334,27 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
             if (r == 0) ag += val; else au += val;
         }
     }
+    // sums over the two physical halves (lane bit 0) and the wave's four groups (lane bits
+    // 4-5), then over the eight waves in wave order by the output lanes
     ag = pair_sum(ag);
     au = pair_sum(au);
-    if (ph == 0) {
-        red[wave][gi][cc][0] = ag;
-        red[wave][gi][cc][1] = au;
+    ag += __shfl_xor(ag, 16);
+    au += __shfl_xor(au, 16);
+    ag += __shfl_xor(ag, 32);
+    au += __shfl_xor(au, 32);
+    if (lane < 16 && ph == 0) {
+        red[wave][cc][0] = ag;
+        red[wave][cc][1] = au;
     }
     __syncthreads();
     if (threadIdx.x < DOUT) {
         const int m = threadIdx.x;
         float gs = 0.0f, us = 0.0f;
-        // (four waves' partials per batch of LDS reads: all 64 at once would exceed the
-        // kernel's 64 registers)
-#pragma unroll 4
-        for (int w = 0; w < DW; ++w)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                gs += red[w][q][m][0];
-                us += red[w][q][m][1];
-            }
+        for (int w = 0; w < DW; ++w) {
+            gs += red[w][m][0];
+            us += red[w][m][1];
+        }
         gs *= kg;
         us *= ku;
         // h is kept as h 2^-f in fp16, f from the bound (row norm x ||x||)^2 on |h| (0 in
