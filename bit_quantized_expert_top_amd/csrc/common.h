@@ -121,10 +121,10 @@ __device__ __forceinline__ int wave_argmax4(const uint32_t (&key)[4], const bool
 // ties to the lower expert index.  A bitwise search from the top bit finds the
 // k-th largest key value T (stopping early once exactly k keys reach the
 // candidate); the picks are the keys above T and the lowest-index keys equal to
-// T.  They are then ranked by (key desc, index asc) through wave-local LDS (wl:
-// 32 words).  Lane p < k ends with pick p; taken[j] marks the picks.
-__device__ inline void wave_topk_radix(const uint32_t (&key)[4], int k, bool (&taken)[4], int &pick_e,
-                                uint32_t &pick_key, uint32_t *wl) {
+// T.  wave_topk_set marks them in taken[j]; wave_topk_radix also ranks them by
+// (key desc, index asc) through wave-local LDS (wl: 32 words), so that lane p < k
+// ends with pick p.
+__device__ inline void wave_topk_set(const uint32_t (&key)[4], int k, bool (&taken)[4]) {
     const int lane = threadIdx.x & 63;
     const uint64_t below = (1ull << lane) - 1ull;
     uint32_t lo = 0;                     // #(key >= lo) >= k throughout
@@ -159,6 +159,13 @@ __device__ inline void wave_topk_radix(const uint32_t (&key)[4], int k, bool (&t
             need -= min((int)__popcll(eq), max(need, 0));
         }
     }
+}
+
+__device__ inline void wave_topk_radix(const uint32_t (&key)[4], int k, bool (&taken)[4], int &pick_e,
+                                uint32_t &pick_key, uint32_t *wl) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    wave_topk_set(key, k, taken);
     // compact the picks (any order), then rank them
     int base = 0;
 #pragma unroll

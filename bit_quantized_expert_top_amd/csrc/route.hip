@@ -339,8 +339,9 @@ __device__ __forceinline__ void stage_row(const uint16_t *row, int H, int lane, 
     }
 }
 
-// Fixed-order logits of the n experts elist[0..n) (n <= 256) of one token: on
-// entry out[i] holds the bias of elist[i], on exit its logit (wave-local LDS).
+// Fixed-order logits of the n experts elist[0..n) (n <= 256) of one token into
+// out[0..n) (wave-local LDS); bv holds every expert's bias (expert e in lane e & 63,
+// slot e >> 6).
 // The token's x row is already in slot 3 of the wave's stage (stage /
 // stage_lds: its generic and LDS addresses).  The router rows travel by DMA
 // into slots 0-2 at once and into slot 3 once x is in registers; round r takes
@@ -350,7 +351,7 @@ __device__ __forceinline__ void stage_row(const uint16_t *row, int H, int lane, 
 // (two independent chains per lane).  The chunk partials of 8 rows collect in
 // part (256 floats); after every second round lanes 0-7 add one row's 32
 // partials each in chunk order, then its bias.
-__device__ void exact_logits(const uint32_t *elist, int n, float *out,
+__device__ void exact_logits(const uint32_t *elist, int n, float *out, const float (&bv)[4],
                              const uint16_t *__restrict__ wr, int H, int lane, float *part,
                              const uint8_t *stage, uint32_t stage_lds) {
     const int c = lane & 31, hh = lane >> 5, nch = H / 64;
@@ -364,6 +365,19 @@ __device__ void exact_logits(const uint32_t *elist, int n, float *out,
     __builtin_amdgcn_s_waitcnt(0x0F70);
     const int pre = n < 3 ? n : 3;
     for (int i = 0; i < pre; ++i) issue(i);
+    // while they travel: out[i] = the bias of elist[i] (expert e's sits in lane e & 63 of
+    // bv, slot e >> 6)
+    for (int g = 0; g < n; g += 64) {
+        const int ci = g + lane;
+        const int ee = ci < n ? (int)elist[ci] : 0;
+        float b = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float bj = __shfl(bv[j], ee & 63);
+            if ((ee >> 6) == j) b = bj;
+        }
+        if (ci < n) out[ci] = b;
+    }
     u32x4 xv[8];
     if (c < nch) {
         const uint8_t *xs = stage + 3 * XS_SLOT + 128 * c;
@@ -525,53 +539,40 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
             key[j] = ordered_key(lt[j]);
             taken[j] = false;
         }
-        int pe;
-        uint32_t pkey;
-        wave_topk_radix(key, k, taken, pe, pkey, (uint32_t *)scr[tl]);
-        int my_pick = lane < k ? pe : -1;
-        float wl = lane < k ? key_to_float(pkey) : 0.0f;   // the pick's logit (lanes < k)
-        if (!EXACT) {
+        int my_pick = -1;
+        float wl = 0.0f;   // the pick's logit (lanes < k)
+        if (EXACT) {
+            int pe;
+            uint32_t pkey;
+            wave_topk_radix(key, k, taken, pe, pkey, (uint32_t *)scr[tl]);
+            my_pick = lane < k ? pe : -1;
+            wl = lane < k ? key_to_float(pkey) : 0.0f;
+        } else {
             // Every exact logit lies within d of its approximation.  An expert whose
-            // interval [l - d, l + d] ends below m8, the lowest lower bound of the picks,
-            // has an exact logit below every pick's, so the exact top-k lies among the
-            // picks and the experts whose intervals reach m8.  Those candidates get their
-            // fixed-order logits, and the top-k is taken among the exact values.
-            const int pl = lane < k ? pe : 0;
-            float pd = 0.0f;
+            // interval [l - d, l + d] ends below m8, the lowest lower bound of the k
+            // largest approximations, has an exact logit below all of theirs, so the
+            // exact top-k lies among those k and the experts whose intervals reach m8.
+            // These candidates get their fixed-order logits, and the top-k is taken
+            // among the exact values (their order here does not matter).
+            wave_topk_set(key, k, taken);
+            uint32_t nk = 0u;   // max of ~key(l - d) over the k: ~key of the lowest bound
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float dj = __shfl(dl[j], pl & 63);
-                if ((pl >> 6) == j) pd = dj;
+                const uint32_t v = taken[j] ? ~ordered_key(lt[j] - dl[j]) : 0u;
+                nk = v > nk ? v : nk;
             }
-            const float lb = lane < k ? wl - pd : INFINITY;
-            float m8 = INFINITY;
-            for (int p = 0; p < k; ++p)
-                m8 = fminf(m8, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lb), p)));
-            if (lane < k) cand_e[tl][lane] = (uint32_t)pe;
-            int nc = k;
+            const float m8 = key_to_float(~wave_umax(nk));
+            int nc = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bool c = !taken[j] && lt[j] + dl[j] >= m8;
+                const bool c = taken[j] || lt[j] + dl[j] >= m8;
                 const uint64_t bal = __ballot(c);
                 const int pos = nc + (int)__popcll(bal & ((1ull << lane) - 1ull));
                 if (c) cand_e[tl][pos] = lane + 64 * j;
                 nc += (int)__popcll(bal);
             }
             __builtin_amdgcn_wave_barrier();
-            // the candidates' biases (expert e's sits in lane e & 63, slot e >> 6)
-            for (int g = 0; g < nc; g += 64) {
-                const int ci = g + lane;
-                const int ee = ci < nc ? (int)cand_e[tl][ci] : 0;
-                float b = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float bj = __shfl(bv[j], ee & 63);
-                    if ((ee >> 6) == j) b = bj;
-                }
-                if (ci < nc) cand_l[tl][ci] = b;
-            }
-            __builtin_amdgcn_wave_barrier();
-            exact_logits(cand_e[tl], nc, cand_l[tl], wr, H, lane, xpart[tl], stage, stage_lds);
+            exact_logits(cand_e[tl], nc, cand_l[tl], bv, wr, H, lane, xpart[tl], stage, stage_lds);
             __builtin_amdgcn_wave_barrier();
             if (nc <= 64) {
                 // rank of candidate `lane` by (exact logit desc, index asc)
