@@ -155,26 +155,30 @@ __device__ __forceinline__ u32x4 permute_to_f16(u32x4 v) {
 }
 
 // Approximate logits (no bias), partial over K range s: part[s][t][e].  A
-// workgroup takes 32 tokens x all 256 experts x one K range: per 64-wide
-// chunk the x rows (4 KB) and the router rows (32 KB) are copied into an LDS
-// ring by whole-line DMA (16-byte slots XOR-swizzled by row so that the MFMA
-// operand reads are free of bank conflicts), and wave w computes experts
-// 64 w .. 64 w + 63.  The same pass prepares x for the expert GEMM from the
-// staged chunk (fp16 with the 8-block permutation (0,4,1,5,2,6,3,7), and per
-// group of 64 the sum and the sum of squares), and the workgroups of token
-// tile 0 the squared norms of the router rows per K range.
+// workgroup takes 32 tokens x one half of the 256 experts x one K range: per
+// 64-wide chunk the x rows (4 KB) and the half's router rows (16 KB) are copied
+// into a 4-stage LDS ring by whole-line DMA (16-byte slots XOR-swizzled by row,
+// so that the MFMA operand reads are free of bank conflicts), three chunks
+// ahead, and wave w computes experts 128 h + 32 w .. + 31.  The ring is 80 KB, so
+// two workgroups share a CU.  The expert-half-0 workgroups also prepare x for
+// the expert GEMM from the staged chunk (fp16 with the 8-block permutation
+// (0,4,1,5,2,6,3,7), and per group of 64 the sum, the sum of squares and the
+// largest magnitude), and the workgroups of token tile 0 the squared norms of
+// their router rows per K range.
 constexpr int RT_TOK = 32;
+constexpr int RT_EH = 128;                        // experts per workgroup (half of 256)
 constexpr int RX_BYTES = RT_TOK * 128;            // x chunk [32 rows][8 x 16 B]
-constexpr int RW_BYTES = 256 * 128;               // router chunk [256 rows][8 x 16 B]
+constexpr int RW_BYTES = RT_EH * 128;             // router chunk [128 rows][8 x 16 B]
 constexpr int R_STAGE = RX_BYTES + RW_BYTES;
-constexpr int R_NST = 3;
+constexpr int R_NST = 4;
+constexpr int R_PER = 1 + RT_EH / 32;             // copies per thread and chunk
 
 __device__ __forceinline__ void rdma16(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
 
-__global__ __launch_bounds__(256) void router_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int H, int E, int S,
     float *__restrict__ part, uint16_t *__restrict__ xp, float *__restrict__ xsum,
     float *__restrict__ xsq, float *__restrict__ wn2part, float *__restrict__ xmx,
@@ -184,28 +188,30 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, gg = lane >> 5;
-    const int t0 = blockIdx.x * RT_TOK, sp = blockIdx.y;
+    const int t0 = blockIdx.x * RT_TOK, sp = blockIdx.y, e0 = blockIdx.z * RT_EH;
     const int klen = H / S, kbeg = sp * klen, nch = klen / 64, G = H / 64;
+    const bool do_prep = blockIdx.z == 0;          // x preparation: one expert half only
     // DMA: thread tid copies slot tid&7 of row tid/8 (x) and of rows 32 i + tid/8
     // (router); the slot holds segment slot ^ (row & 7) of the row's 128 bytes
     const int seg = (tid & 7) ^ ((tid >> 3) & 7);
     const uint16_t *xsrc = x + (size_t)min(t0 + (tid >> 3), T - 1) * H + kbeg + 8 * seg;
-    const uint16_t *wsrc = wr + (size_t)(tid >> 3) * H + kbeg + 8 * seg;
+    const uint16_t *wsrc = wr + (size_t)(e0 + (tid >> 3)) * H + kbeg + 8 * seg;
     auto issue = [&](int c) {
         const uint32_t base = lds0 + (uint32_t)((c % R_NST) * R_STAGE);
         rdma16(xsrc + 64 * c, base + (uint32_t)(wave * 1024));
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < RT_EH / 32; ++i)
             rdma16(wsrc + (size_t)32 * i * H + 64 * c, base + (uint32_t)(RX_BYTES + 4096 * i + wave * 1024));
     };
-    issue(0);
-    if (nch > 1) issue(1);
-    floatx16 tot[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tot[0][i] = tot[1][i] = 0.0f;
+    for (int c = 0; c < R_NST - 1; ++c)
+        if (c < nch) issue(c);
+    floatx16 tot;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot[i] = 0.0f;
     const floatx16 zero = {};
     float wsq = 0.0f;
-    const bool do_norm = blockIdx.x == 0;
+    const bool do_norm = blockIdx.x == 0 && tid < RT_EH;
     // x preparation results, stored after the loop: a store issued inside it
     // would count against the DMA waits (one vmcnt for loads and stores)
     constexpr int MAXCH = 8;                       // H <= 2048, four K ranges
@@ -214,33 +220,32 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c) {
         if (c >= nch) break;
-        if (c + 1 < nch)
-            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        // chunks issued after c: min(R_NST - 2, nch - 1 - c), R_PER copies each
+        const int after = min(R_NST - 2, nch - 1 - c);
+        if (after >= 2)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * R_PER) : "memory");
+        else if (after == 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(R_PER) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();                           // chunk c in; chunk c-1 no longer read
-        if (c + 2 < nch) issue(c + 2);
+        if (c + R_NST - 1 < nch) issue(c + R_NST - 1);
         const uint8_t *sx = rsm + (c % R_NST) * R_STAGE;
         const uint8_t *sw = sx + RX_BYTES;
-        // 32 x 64 experts: per 16-wide k step j, segment 2 j + gg of the rows
-        floatx16 p[2];
+        // 32 tokens x 32 experts per wave: per 16-wide k step j, segment 2 j + gg of the rows
+        floatx16 p;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int sg = 2 * j + gg;
             const bf16x8 av = *(const bf16x8 *)(sx + l32 * 128 + 16 * (sg ^ (l32 & 7)));
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int e = 64 * wave + 32 * nt + l32;
-                const bf16x8 bv = *(const bf16x8 *)(sw + e * 128 + 16 * (sg ^ (e & 7)));
-                p[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, j == 0 ? zero : p[nt], 0, 0, 0);
-            }
+            const int el = 32 * wave + l32;
+            const bf16x8 bv = *(const bf16x8 *)(sw + el * 128 + 16 * (sg ^ (el & 7)));
+            p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, j == 0 ? zero : p, 0, 0, 0);
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) tot[nt][i] += p[nt][i];
+        for (int i = 0; i < 16; ++i) tot[i] += p[i];
         // x preparation: thread -> row tid/8, 16-byte segment tid&7 of the chunk
-        {
+        if (do_prep) {
             const int row = tid >> 3, sg = tid & 7;
             const u32x4 v = *(const u32x4 *)(sx + row * 128 + 16 * (sg ^ (row & 7)));
             float s1 = 0.0f, s2 = 0.0f, mx = 0.0f;
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             mxv[c] = group_max_dpp8(mx);
             xpv[c] = permute_to_f16(v);
         }
-        if (do_norm) {                             // thread tid = router row tid
+        if (do_norm) {                             // thread tid = router row e0 + tid
             const uint8_t *rw = sw + tid * 128;
 #pragma unroll
             for (int sg = 0; sg < 8; ++sg) {
@@ -270,12 +275,12 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             }
         }
     }
-    if (do_norm) wn2part[(size_t)sp * E + tid] = wsq;
+    if (do_norm) wn2part[(size_t)sp * E + e0 + tid] = wsq;
     // the select kernel's superblock counters start at zero (stored after the
     // loop, like every store of this kernel)
-    if (blockIdx.x == 0 && sp == 0)
+    if (blockIdx.x == 0 && sp == 0 && blockIdx.z == 0)
         for (int i = tid; i < nzero; i += 256) zbuf[i] = 0;
-    {
+    if (do_prep) {
         const int row = tid >> 3, sg = tid & 7;
         if (t0 + row < T) {
 #pragma unroll
@@ -293,12 +298,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     }
     float *out = part + (size_t)sp * T * E;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = t0 + 8 * (i >> 2) + 4 * gg + (i & 3);
-            if (t < T) out[(size_t)t * E + 64 * wave + 32 * nt + l32] = tot[nt][i];
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int t = t0 + 8 * (i >> 2) + 4 * gg + (i & 3);
+        if (t < T) out[(size_t)t * E + e0 + 32 * wave + l32] = tot[i];
+    }
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in 0..12
@@ -691,9 +694,9 @@ void launch_router_fast(const uint16_t *x, const uint16_t *wr, int T, int H, int
     const int S = RS_SPLIT;       // H >= 256: every split holds at least one chunk
     static LdsLimit lim;
     lim.ensure((const void *)router_mfma_kernel, R_NST * R_STAGE);
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + RT_TOK - 1) / RT_TOK, S), dim3(256),
-                       R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq, wn2part, xmx,
-                       zero, nzero);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + RT_TOK - 1) / RT_TOK, S, 256 / RT_EH),
+                       dim3(256), R_NST * R_STAGE, s, x, wr, T, H, E, S, part, xp, xsum, xsq,
+                       wn2part, xmx, zero, nzero);
 }
 
 void launch_route_select(const float *part, const float *exact, const float *xsq,
