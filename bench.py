@@ -38,6 +38,7 @@ ZIPF_S = 1.1
 SEED_PREFILL = 4000
 SEED_DECODE = 2000
 SEED_UNIFORM = 3000
+SEED_EP_SHARE = 6000
 SEED_STACK = 5000
 
 
@@ -83,6 +84,9 @@ def main():
     ap.add_argument("--decode-sets", type=int, default=40,
                     help="T=1 layers (independent weights): decode calls and the chained stack")
     ap.add_argument("--decode-steps", type=int, default=400)
+    ap.add_argument("--ep-share-sets", type=int, default=4,
+                    help="weight sets of the T=2048 leg whose picks stay on one GPU's expert-parallel "
+                         "share (32 of 256 experts); 0 skips it")
     ap.add_argument("--uniform-sets", type=int, default=4,
                     help="weight sets of the T=512 uniform-routing leg (0: skip it)")
     ap.add_argument("--stack-layers", type=int, default=40,
@@ -364,6 +368,86 @@ def main():
     del dsets, dres, du
     torch.cuda.empty_cache()
 
+    # ---------------- prefill T=2048 on one GPU's expert-parallel share ----------------
+    # Under expert parallelism over 8 GPUs each GPU owns 32 experts and, after the dispatch
+    # all-to-all, runs their rows: 8 GPUs x 2048 tokens x 8 picks x 32/256 = 16384 rows, 512 per
+    # expert.  Here 2048 tokens pick among 32 experts only (router bias), which gives each of
+    # them the same 512 rows; the shared expert runs the GPU's own 2048 tokens, as it would.
+    ep = None
+    if args.ep_share_sets:
+        print(f"[bench] T={T} expert-parallel share (32 experts), {args.ep_share_sets} weight sets",
+              file=sys.stderr, flush=True)
+        raw = make_layer_device(SEED_EP_SHARE, T, H, I, E, device=dev, ep_share=8)
+        xe = raw["x"]
+        esets = [device_layer(raw)]
+        del raw
+        for s_ in range(1, args.ep_share_sets):
+            esets.append(device_layer(make_layer_device(SEED_EP_SHARE + 100 * s_, T, H, I, E, device=dev,
+                                                        with_x=False, ep_share=8)))
+
+        def estep(w):
+            moe.moe_route(shape, xe, w, r, ws)
+            moe.moe_expert_gemm_q4(shape, xe, w, r, h, ws)
+            moe.moe_down_combine(shape, h, w, r, y, ws)
+
+        for w in esets:
+            estep(w)
+        torch.cuda.synchronize()
+        e_active = int((r.counts > 0).sum().item())
+        e_max = int(r.counts.max().item())
+        EK = 12
+        eev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(EK)]
+        for s_ in range(EK):
+            w = esets[s_ % len(esets)]
+            eev[s_][0].record()
+            moe.moe_route(shape, xe, w, r, ws)
+            moe.moe_expert_gemm_q4(shape, xe, w, r, h, ws)
+            eev[s_][1].record()
+            moe.moe_down_combine(shape, h, w, r, y, ws)
+            eev[s_][2].record()
+        torch.cuda.synchronize()
+        # gate/up alone: its own events around the launch
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(EK)]
+        for s_ in range(EK):
+            w = esets[s_ % len(esets)]
+            moe.moe_route(shape, xe, w, r, ws)
+            gev[s_][0].record()
+            moe.moe_expert_gemm_q4(shape, xe, w, r, h, ws)
+            gev[s_][1].record()
+            moe.moe_down_combine(shape, h, w, r, y, ws)
+        torch.cuda.synchronize()
+        e_gateup_ms = sum(g_[0].elapsed_time(g_[1]) for g_ in gev) / EK
+        e_down_ms = sum(e_[1].elapsed_time(e_[2]) for e_ in eev) / EK
+        eg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(eg):
+            for w in esets:
+                estep(w)
+        eg.replay()
+        torch.cuda.synchronize()
+        ereps = max(1, 24 // len(esets))
+        a_ = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a_.record()
+        for _ in range(ereps):
+            eg.replay()
+        b_.record()
+        torch.cuda.synchronize()
+        e_us = a_.elapsed_time(b_) / (ereps * len(esets)) * 1e3
+        erows = T * K_TOP + T
+        e_fl_gu = 2.0 * erows * (2 * I) * H
+        e_fl_dn = 2.0 * erows * I * H
+        ep = {"workload": f"prefill{T}_ep8_share: one GPU's share under expert parallelism over 8 GPUs, "
+                          f"T={T} tokens picking among 32 experts (router bias), {erows - T} routed rows, "
+                          f"{e_active} experts active, at most {e_max} rows per expert",
+              "us_per_step": round(e_us, 2), "tokens_per_s": round(T / (e_us * 1e-6), 1),
+              "gateup_us": round(e_gateup_ms * 1e3, 2),
+              "gateup_mfma_frac": round(e_fl_gu / (e_gateup_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+              "down_combine_us": round(e_down_ms * 1e3, 2),
+              "layer_mfma_frac": round((e_fl_gu + e_fl_dn) / (e_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 4),
+              "weight_sets": len(esets)}
+        del eg, esets, xe
+        torch.cuda.empty_cache()
+
     # ---------------- prefill T=512, uniform-ish routing: every expert is active ----------------
     uni = None
     if args.uniform_sets:
@@ -580,6 +664,7 @@ def main():
                      "down_combine": round(down_ms * 1e3, 2)},
         "wall_s": round(wall, 3),
         "prefill2048_zipf_affine": affine,
+        "prefill2048_ep8_share": ep,
         "decode": {"metric": "T=1 decode HBM GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
                    "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(dec_us, 2),
                    "bytes_per_call": dec_bytes, "weight_sets": args.decode_sets},

@@ -21,13 +21,16 @@ Distributions: x ~ N(0,1) rounded to bf16; router weight ~ N(0, sigma) with
 sigma = 1/sqrt(H), rounded to bf16; scale ~ U(0.002, 0.02) rounded to bf16;
 bias = -8 * scale (exact in bf16).  The skewed-routing workload adds a fixed
 per-expert logit bias b_e = -s * ln(e + 1), the log of an unnormalised Zipf(s)
-prior over expert rank e + 1.
+prior over expert rank e + 1.  The expert-parallel share workload biases every
+expert outside [0, E/n) by -32, so that the picks stay on one GPU's share of the
+experts under expert parallelism over n GPUs.
 """
 from .inputs import (  # noqa: F401
     LayerInputs,
     Projection,
     WORKLOADS,
     bf16_bits_to_f32,
+    ep_share_bias,
     f32_to_bf16_bits,
     make_layer,
     make_projection,

@@ -10,7 +10,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .inputs import GROUP, PACK, LayerInputs, Projection, zipf_bias
+from .inputs import GROUP, PACK, LayerInputs, Projection, ep_share_bias, zipf_bias
 
 
 def _bf16_bits(t: torch.Tensor) -> torch.Tensor:
@@ -31,9 +31,11 @@ def _proj(g: torch.Generator, lead, N, K, dev, affine: bool = False):
 
 
 def make_layer_device(seed: int, T: int, H: int, I: int, E: int = 256, zipf_s=None,
-                      device="cuda", with_x: bool = True, affine: bool = False) -> dict:
+                      device="cuda", with_x: bool = True, affine: bool = False,
+                      ep_share=None) -> dict:
     """Dict of device tensors: x, router_wt, router_bias and the six projections
-    (affine=True: biases b != -8 s in every group)."""
+    (affine=True: biases b != -8 s in every group; ep_share=n: the router bias keeps the
+    picks among one GPU's E/n experts)."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
@@ -43,6 +45,8 @@ def make_layer_device(seed: int, T: int, H: int, I: int, E: int = 256, zipf_s=No
     out["router_wt"] = _bf16_bits(torch.randn((E, H), generator=g, device=dev) / float(np.sqrt(H)))
     out["router_bias"] = (None if zipf_s is None else
                           torch.from_numpy(zipf_bias(E, zipf_s)).to(dev))
+    if ep_share is not None:
+        out["router_bias"] = torch.from_numpy(ep_share_bias(E, ep_share)).to(dev)
     out["gate"] = _proj(g, (E,), I, H, dev, affine)
     out["up"] = _proj(g, (E,), I, H, dev, affine)
     out["down"] = _proj(g, (E,), H, I, dev, affine)

@@ -69,8 +69,20 @@ def zipf_bias(E: int, s: float) -> np.ndarray:
     return (-s * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
 
 
+def ep_share_bias(E: int, n_gpus: int) -> np.ndarray:
+    """Router bias that keeps every pick among experts [0, E / n_gpus): one GPU's share of the
+    experts under expert parallelism over n_gpus GPUs (0 there, -32 elsewhere; the logits are
+    about N(0, 1), so no other expert reaches the top-k)."""
+    if E % n_gpus:
+        raise ValueError("E must be a multiple of n_gpus")
+    b = np.full(E, -32.0, np.float32)
+    b[: E // n_gpus] = 0.0
+    return b
+
+
 def make_layer(seed: int, T: int, H: int, I: int, E: int = 256, top_k: int = 8,
-               zipf_s: Optional[float] = None, with_x: bool = True) -> LayerInputs:
+               zipf_s: Optional[float] = None, with_x: bool = True,
+               ep_share: Optional[int] = None) -> LayerInputs:
     """Draw one layer in a fixed order: x, router weight, gate, up, down, shared gate/up/down."""
     rng = np.random.Generator(np.random.PCG64(seed))
     if with_x:
@@ -85,9 +97,11 @@ def make_layer(seed: int, T: int, H: int, I: int, E: int = 256, top_k: int = 8,
     sh_up = make_projection(rng, (), I, H)
     sh_down = make_projection(rng, (), H, I)
     bias = zipf_bias(E, zipf_s) if zipf_s is not None else None
+    if ep_share is not None:
+        bias = ep_share_bias(E, ep_share)
     return LayerInputs(T=T, H=H, I=I, E=E, top_k=top_k, x=x, router_wt=wr, router_bias=bias,
                        gate=gate, up=up, down=down, sh_gate=sh_gate, sh_up=sh_up,
-                       sh_down=sh_down, meta={"seed": seed, "zipf_s": zipf_s})
+                       sh_down=sh_down, meta={"seed": seed, "zipf_s": zipf_s, "ep_share": ep_share})
 
 
 # The workloads: shapes and routing recipes of the five synthetic layers.

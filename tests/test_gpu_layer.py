@@ -33,6 +33,9 @@ CASES = [
     ("narrowH_wideI", dict(T=77, H=256, I=1024), 4200),
     # H not a power of two, I = 3 x 128
     ("H768_I384", dict(T=200, H=768, I=384, zipf_s=1.1), 4201),
+    # one GPU's share under expert parallelism over 8 GPUs: every pick among experts 0-31
+    # (512 rows per expert, no small blocks)
+    ("ep8_share_T2048", dict(T=2048, H=2048, I=512, ep_share=8), 6000),
 ]
 
 
@@ -46,6 +49,8 @@ def test_layer_matches_oracle(name, kw, seed):
     y_ref, ids_ref, w_ref = oracle_tokens(inp, range(inp.T), key=(seed, name))
     got = run.routing_np()
     np.testing.assert_array_equal(got["ids"], ids_ref)
+    if "ep_share" in kw:
+        assert got["ids"].max() < inp.E // kw["ep_share"]
     check_topk_weights(got["w"], w_ref)
     ratio = check_y(y, y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)

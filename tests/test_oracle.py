@@ -206,6 +206,17 @@ def test_topk_textbook_sort(tiny):
         assert ids[t].tolist() == ref
 
 
+def test_ep_share_bias_keeps_picks_on_the_share():
+    """The expert-parallel share workload: with experts 32-255 biased by -32, every token's
+    top-8 lies in experts 0-31, and the routing covers only those experts."""
+    inp = make_layer(6000, T=64, H=512, I=128, ep_share=8)
+    l = oracle.router_logits(inp.x, inp.router_wt, inp.router_bias)
+    ids, _ = oracle.topk(l, 8)
+    assert ids.max() < 32 and ids.min() >= 0
+    r = oracle.routing(ids, inp.E, 128)
+    assert (np.asarray(r["counts"])[32:] == 0).all() and int(np.asarray(r["counts"]).sum()) == 64 * 8
+
+
 def test_topk_ties_lower_index():
     rng = np.random.default_rng(5)
     E = 256
