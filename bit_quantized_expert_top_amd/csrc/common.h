@@ -229,14 +229,6 @@ __device__ __forceinline__ float group_max_dpp8(float v) {
     return v;
 }
 
-// Activations enter the GEMMs with every 8-column block stored in the order
-// (0,4,1,5,2,6,3,7), matching the pair order in which 4-bit codes unpack.
-// Position of column `col` in that storage.
-__host__ __device__ __forceinline__ int perm_pos(int col) {
-    const int p = col & 7;
-    return (col & ~7) | ((p & 3) << 1) | (p >> 2);
-}
-
 // GEMM work queues (int32 words of the workspace's qctl area): per GEMM a
 // queue head and a finished-workgroup count.  The routing scatter zeroes
 // them; each GEMM launch's last workgroup zeroes its own again.  Every counter
@@ -340,7 +332,7 @@ struct LdsLimit {
 struct WsLayout {
     size_t logits;      // fp32 [T][E]            (used when routing.logits == NULL)
     size_t xsum;        // fp32 [T][H/64]         group sums of x
-    size_t xp;          // fp16 [T][H]            x in fp16, 8-blocks in the permuted order
+    size_t xp;          // fp16 [T][H]            x in fp16 (times the token's 2^-e)
     size_t xsq;         // fp32 [T][H/64]         group sums of x^2
     size_t part;        // fp32 [4][T][E]         K-split approximate router logits
     size_t wn2;         // fp32 [4][E]            squared norms of the router rows, per K split

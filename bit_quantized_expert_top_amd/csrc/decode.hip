@@ -183,14 +183,15 @@ constexpr int DOUT = 8;                // outputs per decode workgroup (gate/up 
 constexpr int DN_BATCH = 3;            // down: (slot, group) pairs per lane loaded at once
 constexpr int DN_MAXP = NSLOT * 32;    // down: (slot, group) pairs for I <= 2048
 
-// code pair p of word w as two 16-bit values q_p, q_{p+4} in a magic-number
-// format (and-or with C = 128.0 bf16 pairs or 1024.0 fp16 pairs)
-// x (or h) pairs in the same order: (v_p, v_{p+4}) of each 8-block
-__device__ __forceinline__ void pair_order(const u32x4 v, uint32_t *o) {
-    o[0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-    o[1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-    o[2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-    o[3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+// Nibble pair p (nibbles p and p + 4) of a tile-layout word holds the codes 2p and
+// 2p + 1 and unpacks as two 16-bit values in a magic-number format (and-or with
+// C = 128.0 bf16 pairs or 1024.0 fp16 pairs).  The matching x (or h) pair is word p
+// of the 8-block: the words go into a scalar array, which the dot products read.
+__device__ __forceinline__ void pair_words(const u32x4 v, uint32_t *o) {
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
 }
 
 // sum of lanes l and l ^ 1
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(8, 8)))
         float sx = 0.0f;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-            pair_order(xv[qq], xp + 4 * qq);
+            pair_words(xv[qq], xp + 4 * qq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sx += bf16_lo(xv[qq][r]) + bf16_hi(xv[qq][r]);
         }
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(
             float shs = 0.0f;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                pair_order(hv[b][qq], hp + 4 * qq);
+                pair_words(hv[b][qq], hp + 4 * qq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) shs += f16_lo(hv[b][qq][r]) + f16_hi(hv[b][qq][r]);
             }

@@ -20,13 +20,13 @@
 //  * the 32x32x16 fp16 MFMA accumulates straight into the fp32 result, so no
 //    per-group rescaling is left on the vector ALU;
 //  * the rank-G term sum_g c_g xs_g is zero whenever b = -8 s (the format's
-//    symmetric case); otherwise a wave adds it with a small MFMA pass over
-//    K = 3G of fp16 hi/lo splits: c_hi xs_hi + c_hi xs_lo + c_lo xs_hi.
+//    symmetric case); otherwise the item starts its accumulators with a small
+//    fp32 MFMA pass (32x32x2, no rounding of c or of the group sums xs).
 //
-// Element order: code pairs come out as k = (0,4), (1,5), (2,6), (3,7) of each
-// 8-block, so activations are stored with every 8-block permuted to
-// (0,4,1,5,2,6,3,7): x by the router's preparation pass, h by the gate/up
-// epilogue.
+// Element order: the tile layout keeps each word's even codes in its low
+// nibbles and its odd codes in the high ones, so the and-or pairs (p, p + 4)
+// are the code pairs (2p, 2p + 1) and the weights come out in natural order;
+// x and h are stored in natural order too.
 //
 // Tiles: a workgroup (4 waves) takes one routing block (up to 128 rows of one
 // expert) and 256 weight columns: gate/up takes 128 columns of I from both
@@ -70,7 +70,7 @@ constexpr int YS_LD = 1056;                  // epilogue y tile row stride (byte
 static_assert(kBM * HS_LD <= L_TOTAL && 64 * YS_LD <= L_TOTAL, "epilogue tiles fit the ring");
 
 struct GemmArgs {
-    const uint16_t *A;     // fp16 permuted activations: x [T][H] (gate/up) or h [rows][I] (down)
+    const uint16_t *A;     // fp16 activations: x [T][H] (gate/up) or h [rows][I] (down)
     const float *Asum;     // group sums of A rows: by token [T][G] or by row [rows][G]
     int K, G;
     int N;                 // rows of one projection: I (gate/up) or H (down)
@@ -103,9 +103,10 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
     return r;
 }
 
-// 8 codes of one word -> 8 fp16 weights (q - 8) * s, element order (0,4,1,5,2,6,3,7).
-// Even nibbles (mask M1 = 0x000F000F) land as 1024 + q, odd ones (M2 =
-// 0x00F000F0) as 1024 + 16 q; subtracting 1032 resp. 1152 leaves q - 8 resp.
+// 8 codes of one tile-layout word -> 8 fp16 weights (q - 8) * s in code order
+// (nibbles (0,4), (1,5), (2,6), (3,7) hold the code pairs (0,1), (2,3), (4,5), (6,7)).
+// Nibbles 0 and 4 of a byte pair (mask M1 = 0x000F000F) land as 1024 + q, nibbles
+// 1 and 5 (M2 = 0x00F000F0) as 1024 + 16 q; subtracting 1032 resp. 1152 leaves q - 8 resp.
 // 16 (q - 8), and the scale s resp. s / 16 (exact in fp16 for |s| >= 2^-13,
 // as a subnormal at worst) gives (q - 8) s exactly: 13 operations per word.
 __device__ __forceinline__ f16x8 rebuild8(uint32_t w, uint32_t M1, uint32_t M2, uint32_t C,
@@ -421,8 +422,8 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
             if (t.ntile == 0 && tid < t.nrows) a.hexp[t.r0 + tid] = exp2i(f);
         }
         __syncthreads();
-        // SwiGLU -> fp16 h tile in LDS [128 rows][128 columns], columns permuted
-        const int pc = perm_pos(32 * wave + l32);
+        // SwiGLU -> fp16 h tile in LDS [128 rows][128 columns]
+        const int pc = 32 * wave + l32;
         const float kg = il.colk[64 * wave + l32], ku = il.colk[64 * wave + 32 + l32];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)

@@ -6,7 +6,8 @@
 // few whole-line loads (the pages rebuild weights tile by tile in the grouped
 // GEMM and owe their decode bandwidth to coalesced reads: mechatronicstore.cl,
 // "Prefill: pesos comprimidos y enrutamiento en la GPU" and "Decode: mover
-// menos bytes por token").  The regrouping only moves bytes.
+// menos bytes por token").  The regrouping only moves bytes (and reorders the
+// codes inside each 32-bit word, below).
 #include "common.h"
 
 #include <algorithm>
@@ -147,6 +148,22 @@ __global__ __launch_bounds__(256) void pack_stats_kernel(PackSrc src, int nexp, 
     }
 }
 
+// Code order inside a tile-layout word: the even codes 0, 2, 4, 6 of the
+// checkpoint word go to nibbles 0-3 (the low half), the odd codes 1, 3, 5, 7 to
+// nibbles 4-7.  The kernels unpack a word as the nibble pairs (p, p + 4), p = 0..3
+// (one and-or with mask 0x000F000F per pair, shifted by 4 p), which in this order
+// are the code pairs (2p, 2p + 1): weights come out in natural order and meet
+// activations (x, h) stored in natural order.
+__device__ __forceinline__ uint32_t unzip_codes(uint32_t w) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        r |= ((w >> (8 * m)) & 0xFu) << (4 * m);             // code 2m   -> nibble m
+        r |= ((w >> (8 * m + 4)) & 0xFu) << (4 * m + 16);    // code 2m+1 -> nibble m + 4
+    }
+    return r;
+}
+
 // One thread per 16-byte piece of codes; the first 256 threads of a block
 // also move the block's scales and biases, times the column's 2^k.  Block b
 // of a section is (expert, tile j, group g) with g fastest; N = rows per
@@ -172,7 +189,12 @@ __global__ __launch_bounds__(256) void pack_kernel(PackSrc src, int nexp, int N,
             const int n = gu ? 128 * j + 32 * (c >> 6) + (c & 31) : 256 * j + c;
             const size_t row = (size_t)e * N + n;
             const u32x4 v = *(const u32x4 *)(q.q + row * (size_t)(K / 8) + 8 * g + 4 * (hh ^ ((c >> 3) & 1)));
-            *(u32x4 *)(blk + 16 * pp) = v;
+            u32x4 o;
+            o.x = unzip_codes(v.x);
+            o.y = unzip_codes(v.y);
+            o.z = unzip_codes(v.z);
+            o.w = unzip_codes(v.w);
+            *(u32x4 *)(blk + 16 * pp) = o;
         }
         if (pp < 256) {
             const int c = pp;

@@ -143,14 +143,14 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     return v;
 }
 
-// 8 bf16 values k = 0..7 -> fp16 in the GEMM operand order (0,4,1,5,2,6,3,7).
-// Exact for |x| in the fp16 normal range (bf16 has 8 significant bits, fp16 11).
-__device__ __forceinline__ u32x4 permute_to_f16(u32x4 v) {
+// 8 bf16 values -> fp16, in order.  Exact for |x| in the fp16 normal range (bf16 has
+// 8 significant bits, fp16 11).
+__device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
     u32x4 o;
-    o.x = pack_f16x2(bf16_lo(v.x), bf16_lo(v.z));
-    o.y = pack_f16x2(bf16_hi(v.x), bf16_hi(v.z));
-    o.z = pack_f16x2(bf16_lo(v.y), bf16_lo(v.w));
-    o.w = pack_f16x2(bf16_hi(v.y), bf16_hi(v.w));
+    o.x = pack_f16x2(bf16_lo(v.x), bf16_hi(v.x));
+    o.y = pack_f16x2(bf16_lo(v.y), bf16_hi(v.y));
+    o.z = pack_f16x2(bf16_lo(v.z), bf16_hi(v.z));
+    o.w = pack_f16x2(bf16_lo(v.w), bf16_hi(v.w));
     return o;
 }
 
@@ -161,10 +161,9 @@ __device__ __forceinline__ u32x4 permute_to_f16(u32x4 v) {
 // so that the MFMA operand reads are free of bank conflicts), three chunks
 // ahead, and wave w computes experts 128 h + 32 w .. + 31.  The ring is 80 KB, so
 // two workgroups share a CU.  The expert-half-0 workgroups also prepare x for
-// the expert GEMM from the staged chunk (fp16 with the 8-block permutation
-// (0,4,1,5,2,6,3,7), and per group of 64 the sum, the sum of squares and the
-// largest magnitude), and the workgroups of token tile 0 the squared norms of
-// their router rows per K range.
+// the expert GEMM from the staged chunk (fp16, and per group of 64 the sum, the
+// sum of squares and the largest magnitude), and the workgroups of token tile 0
+// the squared norms of their router rows per K range.
 constexpr int RT_TOK = 32;
 constexpr int RT_EH = 128;                        // experts per workgroup (half of 256)
 constexpr int RX_BYTES = RT_TOK * 128;            // x chunk [32 rows][8 x 16 B]
@@ -259,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
             s1v[c] = group_sum_dpp(s1, 8);
             s2v[c] = group_sum_dpp(s2, 8);
             mxv[c] = group_max_dpp8(mx);
-            xpv[c] = permute_to_f16(v);
+            xpv[c] = to_f16x8(v);
         }
         if (do_norm) {                             // thread tid = router row e0 + tid
             const uint8_t *rw = sw + tid * 128;
@@ -656,10 +655,10 @@ __global__ __launch_bounds__(64 * TB) void route_select_kernel(
                 for (int q = 0; q < 8; ++q) {
                     const u32x4 v = src[q];
                     u32x4 o;
-                    o.x = pack_f16x2(bf16_lo(v.x) * sc, bf16_lo(v.z) * sc);
-                    o.y = pack_f16x2(bf16_hi(v.x) * sc, bf16_hi(v.z) * sc);
-                    o.z = pack_f16x2(bf16_lo(v.y) * sc, bf16_lo(v.w) * sc);
-                    o.w = pack_f16x2(bf16_hi(v.y) * sc, bf16_hi(v.w) * sc);
+                    o.x = pack_f16x2(bf16_lo(v.x) * sc, bf16_hi(v.x) * sc);
+                    o.y = pack_f16x2(bf16_lo(v.y) * sc, bf16_hi(v.y) * sc);
+                    o.z = pack_f16x2(bf16_lo(v.z) * sc, bf16_hi(v.z) * sc);
+                    o.w = pack_f16x2(bf16_lo(v.w) * sc, bf16_hi(v.w) * sc);
                     dst[q] = o;
                 }
                 xsum[(size_t)t * G + lane] *= sc;
@@ -938,8 +937,8 @@ void launch_zero_i32(int32_t *p, int n, hipStream_t s) {
     if (n > 0) hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
 }
 
-// Activation preparation for the GEMM: fp16 copy with the 8-block permutation
-// (0,4,1,5,2,6,3,7) of every row plus the group sums, one thread per (row, group of 64).
+// Activation preparation for the GEMM: fp16 copy of every row plus the group sums, one
+// thread per (row, group of 64).
 __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restrict__ x, int rows,
                                                        int K, uint16_t *__restrict__ xp,
                                                        float *__restrict__ out,
@@ -963,7 +962,7 @@ __global__ __launch_bounds__(256) void prep_act_kernel(const uint16_t *__restric
             s2 = __builtin_fmaf(bf16_hi(v[q]), bf16_hi(v[q]), s2);
             mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[q])), fabsf(bf16_hi(v[q]))));
         }
-        q[j] = permute_to_f16(v);
+        q[j] = to_f16x8(v);
     }
     out[i] = s;
     if (sq) sq[i] = s2;

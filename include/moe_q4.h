@@ -28,14 +28,18 @@
  *     This row layout is the checkpoint format; moe_pack_weights turns it
  *     into the tile layout below, which is what the layer calls read.
  *   - Tile layout (the `packed` buffer, written by moe_pack_weights): the
- *     same bytes regrouped so that one 64-wide K step of one 256-column GEMM
+ *     same data regrouped so that one 64-wide K step of one 256-column GEMM
  *     tile is one contiguous 9216-byte block, read by a few whole-line copies
  *     (the pages rebuild weights tile by tile inside the grouped GEMM and get
  *     their decode bandwidth from coalesced reads: mechatronicstore.cl,
  *     "Prefill: ..." and "Decode: ...").  A block is
  *       bytes [0, 8192):     codes of 256 columns, 32 bytes each: 16-byte
  *                            half hh of column c holds code words
- *                            4 * (hh ^ ((c >> 3) & 1)) .. +3 of the group;
+ *                            4 * (hh ^ ((c >> 3) & 1)) .. +3 of the group,
+ *                            each word with its codes reordered: code 2m in
+ *                            nibble m, code 2m + 1 in nibble m + 4 (m = 0..3),
+ *                            so that the kernels unpack the nibble pairs
+ *                            (m, m + 4) as consecutive codes;
  *       bytes [8192, 8704):  bf16 scales of the 256 columns;
  *       bytes [8704, 9216):  bf16 biases of the 256 columns.
  *     Sections, in this order, each starting 256-byte aligned:
@@ -137,7 +141,7 @@ moe_status moe_packed_bytes(const moe_shape *shape, size_t *packed_bytes);
 /* Load the six row-layout projections of w into the tile layout, once, when the
  * weights are loaded; the pages' engine validates the checkpoint format at load and
  * refuses every other (greatopti.com, "Une spécialisation assumée").
- * The codes move unchanged.  Each projection row's scales and biases are stored times
+ * The codes move with the in-word reordering above.  Each projection row's scales and biases are stored times
  * a power of two 2^k that puts the row's largest |scale| in [2^10, 2^11), with 2^-k
  * kept per row in a meta section after the blocks; the kernels undo it exactly.  The
  * meta section also holds per expert a bound on the L2 norm of its gate and up rows
@@ -177,11 +181,9 @@ moe_status moe_route(const moe_shape *shape, const uint16_t *x, const moe_weight
  * epilogue h = silu(W_gate x) * (W_up x).
  * x is not read: the GEMM reads the fp16 copy of x that moe_route prepared in
  * the workspace (the argument is kept for symmetry with the other calls).
- * h: fp16 [T*top_k + T][I] (bits as uint16_t); rows 0..T*top_k-1 follow
- * routing order, row T*top_k + t is the shared expert of token t.  Within each
- * row, every block of 8 consecutive columns is stored in the order
- * 0,4,1,5,2,6,3,7 (the order in which the down GEMM consumes it).  A row is
- * stored as h 2^-f with f = 0 unless the bound (L2 norm of the expert's rows x
+ * h: fp16 [T*top_k + T][I] (bits as uint16_t), natural column order; rows
+ * 0..T*top_k-1 follow routing order, row T*top_k + t is the shared expert of
+ * token t.  A row is stored as h 2^-f with f = 0 unless the bound (L2 norm of the expert's rows x
  * ||x||)^2 on |h| leaves [2^-2, 2^15); the workspace keeps 2^f per row.  Needs
  * moe_route's outputs and workspace; leaves the group sums of h and the row
  * factors in the workspace for moe_down_combine.

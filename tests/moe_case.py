@@ -82,16 +82,6 @@ def f16_np(t: torch.Tensor) -> np.ndarray:
     return t.cpu().contiguous().view(torch.int16).numpy().view(np.float16).astype(np.float32)
 
 
-def perm_pos(col):
-    """Storage position of column `col` in the GEMM activation layout (8-blocks as 0,4,1,5,2,6,3,7)."""
-    col = np.asarray(col)
-    p = col & 7
-    return (col & ~7) | ((p & 3) << 1) | (p >> 2)
-
-
-def unpermute_cols(a: np.ndarray) -> np.ndarray:
-    """h as stored by moe_expert_gemm_q4 -> natural column order."""
-    return a[..., perm_pos(np.arange(a.shape[-1]))]
 
 
 def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float = TOL):

@@ -7,7 +7,7 @@ import bit_quantized_expert_top_amd as moe
 import oracle
 from synth import make_layer
 from moe_case import (LayerRun, asymmetric_bias, check_topk_weights, check_y, device, f16_np,
-                      oracle_tokens, unpermute_cols, upload)
+                      oracle_tokens, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,7 +142,7 @@ def test_hidden_rows_match_oracle():
     inp = make_layer(4000, T=2048, H=2048, I=512, zipf_s=1.1)
     run = LayerRun(inp).route().gemm().sync()
     got = run.routing_np()
-    h = unpermute_cols(f16_np(run.h))
+    h = f16_np(run.h)
     L = oracle.Layer(inp)
     T, k = inp.T, inp.top_k
     rng = np.random.default_rng(5)
@@ -214,7 +214,7 @@ def test_layer_asymmetric_bias(name, kw, seed):
     np.testing.assert_array_equal(got["ids"][toks], ids_ref)
     ratio = check_y(run.y.cpu().numpy()[toks], y_ref)
     print(f"  max err / rms = {ratio:.4g}", flush=True)
-    h = unpermute_cols(f16_np(run.h))
+    h = f16_np(run.h)
     L = oracle.Layer(inp)
     for t in toks[:6]:
         for j in (0, 7):
@@ -250,7 +250,7 @@ def test_hidden_rows_scale_extremes(lo, hi):
     inp.x[...] = f32_to_bf16_bits((sign * mag).astype(np.float32))
     run = LayerRun(inp).route().gemm().sync()
     got = run.routing_np()
-    h = unpermute_cols(f16_np(run.h))
+    h = f16_np(run.h)
     L = oracle.Layer(inp)
     T, k = inp.T, inp.top_k
     for t in range(0, T, 7):

@@ -1,7 +1,8 @@
 """moe_pack_weights against a numpy rendering of the tile layout that
-include/moe_q4.h documents: every byte of the blocks is checked (codes unchanged, each
-row's scales and biases times its power of two 2^k), and the meta section's status,
-column factors and per-expert row-norm bounds."""
+include/moe_q4.h documents: every byte of the blocks is checked (each code word's even
+codes in its low nibbles and odd codes in its high nibbles, each row's scales and biases
+times its power of two 2^k), and the meta section's status, column factors and
+per-expert row-norm bounds."""
 import numpy as np
 import pytest
 
@@ -28,6 +29,17 @@ def _shifted(bits, k):
                             .astype(np.float32))
 
 
+def _unzip(words):
+    """Checkpoint code words -> tile-layout words: code 2m to nibble m, code 2m+1 to
+    nibble m + 4 (m = 0..3)."""
+    w = words.astype(np.uint64)
+    r = np.zeros_like(w)
+    for m in range(4):
+        r |= ((w >> (8 * m)) & 0xF) << (4 * m)
+        r |= ((w >> (8 * m + 4)) & 0xF) << (4 * m + 16)
+    return r.astype(np.uint32)
+
+
 def _blocks(q, s, b, rows_of_col):
     """Tile-layout blocks of one stack of projections.
 
@@ -42,7 +54,7 @@ def _blocks(q, s, b, rows_of_col):
     for j in range(JT):
         cols = rows_of_col(j)
         for c, (p, n) in enumerate(cols):
-            words = q[p][:, n, :].reshape(n_exp, G, 8)           # [e][g][8 words]
+            words = _unzip(q[p][:, n, :]).reshape(n_exp, G, 8)   # [e][g][8 words]
             sw = (c >> 3) & 1
             for hh in range(2):
                 src = words[:, :, 4 * (hh ^ sw):4 * (hh ^ sw) + 4]
