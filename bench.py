@@ -49,9 +49,9 @@ SEED_STACK = 5000
 # 131085.4 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
 # source these counters were taken on; otherwise the JSON reports null.
 GATEUP_TRAFFIC = {
-    "gemm_src_sha256": "1416c5d7ae83c7ad2f2dc794938cb757ef7feae9aaf0a6342575b81fec133340",
-    "fetch_kib": 159765.9, "fetch_scale": 2.0,
-    "write_kib": 20741.6, "write_scale": 1.0,
+    "gemm_src_sha256": "101582eff3bf547315aae2bb4735897b54f8185fb1905cf7c813da0abfa4c8a4",
+    "fetch_kib": 159644.2, "fetch_scale": 2.0,
+    "write_kib": 20754.0, "write_scale": 1.0,
     "profile": "profiles/moe_layer_prefill2048_zipf_hbm_traffic.md",
 }
 
