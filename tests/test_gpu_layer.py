@@ -56,6 +56,31 @@ def test_layer_matches_oracle(name, kw, seed):
     print(f"  max err / rms = {ratio:.4g}", flush=True)
 
 
+def test_max_tokens_sampled():
+    """The largest T one call accepts (65536 tokens, 131 MB of x): routing takes the multi-pass
+    path (more than 32 superblocks of token blocks).  Given the GPU's picks, the expert counts,
+    offsets, scatter and block map of all 524288 picks equal the oracle's bit for bit; on
+    sampled tokens the picks, weights and outputs match the oracle; every output is finite."""
+    T = 65536
+    print(f"[layer] max tokens T={T}", flush=True)
+    inp = make_layer(7000, T=T, H=2048, I=512, zipf_s=1.1)
+    run = LayerRun(inp).layer().sync()
+    got = run.routing_np()
+    ref = oracle.routing(got["ids"], inp.E, 128)
+    for key in ("counts", "offsets", "row_token", "tok_row"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    assert got["num_blocks"] == ref["num_blocks"]
+    np.testing.assert_array_equal(got["blocks"], ref["blocks"])
+    y = run.y.cpu().numpy()
+    assert np.isfinite(y).all()
+    toks = sample_tokens(T, 16, 7000)
+    y_ref, ids_ref, w_ref = oracle_tokens(inp, toks)
+    np.testing.assert_array_equal(got["ids"][toks], ids_ref)
+    check_topk_weights(got["w"][toks], w_ref)
+    ratio = check_y(y[toks], y_ref)
+    print(f"  max err / rms = {ratio:.4g}", flush=True)
+
+
 def test_prefill_graph_replays_two_weight_sets():
     """The timed form of the prefill step: two layers with independently seeded weights share
     the routing buffers, the workspace and h, captured together in one HIP graph.  Each of three
