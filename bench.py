@@ -4,12 +4,14 @@
 Headline (the JSON line's `value`): prefill throughput in tokens/s of one MoE
 layer at T=2048 tokens with Zipf-skewed routing (H=2048, I=512, 256 experts,
 top-8 + shared expert, 4-bit affine g=64 weights), one step = moe_route +
-moe_expert_gemm_q4 + moe_down_combine on a batch already resident in HBM.
-Consecutive steps rotate over independently seeded weight sets (distinct
-layers) so that no step finds its weights in the 256 MB last-level cache.
+moe_expert_ffn_q4 (both expert GEMMs in one persistent launch, then the
+combine) on a batch already resident in HBM.  Consecutive steps rotate over
+independently seeded weight sets (distinct layers) so that no step finds its
+weights in the 256 MB last-level cache.
 
-Also reported: the gate/up GEMM kernel's MFMA roofline fraction (HIP events
-around its launch inside the timed loop), the batch-1 decode path's HBM
+Also reported: the one-launch GEMM kernel's MFMA roofline fraction (HIP events
+around its launch, timed per step), the same steps with the two GEMMs as two
+launches (moe_expert_gemm_q4 + moe_down_combine), the batch-1 decode path's HBM
 bandwidth (40 independently weighted layers, one call each) and the per-layer
 latency of the same 40 layers chained through the residual add and RMSNorm (one
 HIP graph, no host synchronisation), decode calls of 2, 4 and 8 tokens, a
@@ -42,29 +44,26 @@ SEED_EP_SHARE = 6000
 SEED_STACK = 5000
 
 
-# HBM traffic of the gate/up GEMM launch on this workload, from two rocprofv3 --pmc
-# runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean of 19
-# dispatches), each scaled by what the same counter reports for a plain 256 MiB
-# device-to-device copy (bench.py --copy-calibration 256: FETCH_SIZE reads
-# 131085.4 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM
-# source these counters were taken on; otherwise the JSON reports null.
-GATEUP_TRAFFIC = {
-    "gemm_src_sha256": "101582eff3bf547315aae2bb4735897b54f8185fb1905cf7c813da0abfa4c8a4",
-    "fetch_kib": 159644.2, "fetch_scale": 2.0,
-    "write_kib": 20754.0, "write_scale": 1.0,
-    "profile": "profiles/moe_layer_prefill2048_zipf_hbm_traffic.md",
-}
+# HBM traffic of the one-launch GEMM kernel (q4_ffn_kernel) on this workload, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean
+# over the dispatches), each scaled by what the same counter reports for a plain 256 MiB
+# device-to-device copy (bench.py --copy-calibration 256: FETCH_SIZE reads 131085.4 KiB ->
+# x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM source these counters were
+# taken on; otherwise (or before they are taken) the JSON reports null.
+FFN_TRAFFIC = None
 
 
-def gateup_traffic_bytes():
+def ffn_traffic_bytes():
     import hashlib
+    t = FFN_TRAFFIC
+    if t is None:
+        return None
     src = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                        "bit_quantized_expert_top_amd", "csrc", "gemm.hip")
     try:
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    t = GATEUP_TRAFFIC
     if h != t["gemm_src_sha256"]:
         return None
     return round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
@@ -78,8 +77,10 @@ def expert_bytes(H, I):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=120,
+                    help="untimed steps replayed back to back right before the timed ones (the "
+                         "clocks take about 60 steps of sustained load to settle)")
     ap.add_argument("--sets", type=int, default=6, help="weight sets rotated in the prefill loop")
     ap.add_argument("--decode-sets", type=int, default=40,
                     help="T=1 layers (independent weights): decode calls and the chained stack")
@@ -145,30 +146,31 @@ def main():
 
     def step(w):
         moe.moe_route(shape, x, w, r, ws)
-        moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
-        moe.moe_down_combine(shape, h, w, r, y, ws)
+        moe.moe_expert_ffn_q4(shape, x, w, r, h, y, ws)
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
+    def phases(step_inputs, xs, r_, ws_, h_, y_):
+        """Eager steps with HIP events on the launch stream between the routing, the one-launch
+        GEMM kernel (moe_expert_ffn_q4 without its combine) and the combine: mean ms of each."""
+        ev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in step_inputs]
+        for (w, shp), e in zip(step_inputs, ev_):
+            e[0].record()
+            moe.moe_route(shp, xs, w, r_, ws_)
+            e[1].record()
+            moe.moe_expert_ffn_q4(shp, xs, w, r_, h_, y_, ws_, combine=False)
+            e[2].record()
+            moe.moe_combine(shp, r_, y_, ws_)
+            e[3].record()
+        torch.cuda.synchronize()
+        n_ = len(ev_)
+        return [sum(e[i].elapsed_time(e[i + 1]) for e in ev_) / n_ for i in range(3)]
+
+    for w in sets:                                  # first touch of every set and buffer
+        step(w)
     torch.cuda.synchronize()
 
     K = args.steps
-    # per-phase timing (eager launches, HIP events on the launch stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for s in range(K):
-        w = sets[s % len(sets)]
-        e0, e1, e2, e3 = ev[s]
-        e0.record()
-        moe.moe_route(shape, x, w, r, ws)
-        e1.record()
-        moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
-        e2.record()
-        moe.moe_down_combine(shape, h, w, r, y, ws)
-        e3.record()
-    torch.cuda.synchronize()
-    route_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    gateup_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    down_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    route_ms, ffn_ms, comb_ms = phases([(sets[s % len(sets)], shape) for s in range(K)], x, r, ws,
+                                       h, y)
 
     # throughput: the layer steps captured in HIP graphs (one step per weight set, and
     # the K mod sets remaining steps), replayed so that exactly K steps run between the
@@ -184,7 +186,10 @@ def main():
     graph = capture(sets)
     reps, rem = divmod(K, len(sets))
     graph_rem = capture(sets[:rem]) if rem else None
-    torch.cuda.synchronize()
+    # the W warmup steps (rounded up to whole replays), back to back as the timed ones
+    warm_reps = -(-args.warmup // len(sets))
+    for _ in range(warm_reps):
+        graph.replay()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
     wall0 = time.perf_counter()
     evs[0].record()
@@ -208,9 +213,46 @@ def main():
     rows = T * K_TOP + T
     flops_gateup = 2.0 * rows * (2 * I) * H
     flops_down = 2.0 * rows * I * H
+    flops_ffn = flops_gateup + flops_down
     tok_s = T / (ms_step * 1e-3)
-    gateup_tflops = flops_gateup / (gateup_ms * 1e-3) / 1e12
-    layer_mfma_frac = (flops_gateup + flops_down) / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    ffn_tflops = flops_ffn / (ffn_ms * 1e-3) / 1e12
+    layer_mfma_frac = flops_ffn / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+
+    # the same steps with the GEMMs as two launches (moe_expert_gemm_q4, moe_down_combine)
+    def step2(w):
+        moe.moe_route(shape, x, w, r, ws)
+        moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
+        moe.moe_down_combine(shape, h, w, r, y, ws)
+
+    K2 = min(K, 2 * len(sets))
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K2)]
+    for s_ in range(K2):
+        w = sets[s_ % len(sets)]
+        moe.moe_route(shape, x, w, r, ws)
+        ev2[s_][0].record()
+        moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
+        ev2[s_][1].record()
+        moe.moe_down_combine(shape, h, w, r, y, ws)
+        ev2[s_][2].record()
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        for w in sets:
+            step2(w)
+    for _ in range(warm_reps + 1):                  # the same warmup as the timed steps
+        g2.replay()
+    t2a = torch.cuda.Event(enable_timing=True)
+    t2b = torch.cuda.Event(enable_timing=True)
+    reps2 = max(1, reps)
+    t2a.record()
+    for _ in range(reps2):
+        g2.replay()
+    t2b.record()
+    torch.cuda.synchronize()
+    two_launch = {"us_per_step": round(t2a.elapsed_time(t2b) / (reps2 * len(sets)) * 1e3, 2),
+                  "gateup_us": round(sum(e[0].elapsed_time(e[1]) for e in ev2) / K2 * 1e3, 2),
+                  "down_combine_us": round(sum(e[1].elapsed_time(e[2]) for e in ev2) / K2 * 1e3, 2)}
+    del g2
 
     # ---------------- the same workload with biases b != -8 s in every group ----------------
     # (the general affine format: the GEMMs add the rank-G bias term in every item)
@@ -225,17 +267,10 @@ def main():
         for w in asets:
             step(w)
         torch.cuda.synchronize()
-        aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(len(asets))]
-        for i, w in enumerate(asets):
-            moe.moe_route(shape, x, w, r, ws)
-            aev[i][0].record()
-            moe.moe_expert_gemm_q4(shape, x, w, r, h, ws)
-            aev[i][1].record()
-            moe.moe_down_combine(shape, h, w, r, y, ws)
-        torch.cuda.synchronize()
-        a_gateup_us = sum(e[0].elapsed_time(e[1]) for e in aev) / len(aev) * 1e3
+        a_ffn_us = phases([(w, shape) for w in asets], x, r, ws, h, y)[1] * 1e3
         ag = capture(asets)
-        torch.cuda.synchronize()
+        for _ in range(-(-60 // len(asets))):         # about 60 steps of warmup, back to back
+            ag.replay()
         areps = 4
         a0 = torch.cuda.Event(enable_timing=True)
         a1 = torch.cuda.Event(enable_timing=True)
@@ -248,8 +283,8 @@ def main():
         affine = {"workload": "prefill2048_zipf_affine: the headline layer with every group's bias "
                               "b = -8 s + d, d ~ U(-2 s, 2 s) (rank-G bias term in every GEMM item)",
                   "us_per_step": round(a_us, 2), "tokens_per_s": round(T / (a_us * 1e-6), 1),
-                  "gateup_us": round(a_gateup_us, 2),
-                  "gateup_mfma_frac": round(flops_gateup / (a_gateup_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                  "ffn_kernel_us": round(a_ffn_us, 2),
+                  "ffn_mfma_frac": round(flops_ffn / (a_ffn_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 4),
                   "weight_sets": len(asets)}
         del ag, asets
         torch.cuda.empty_cache()
@@ -387,8 +422,7 @@ def main():
 
         def estep(w):
             moe.moe_route(shape, xe, w, r, ws)
-            moe.moe_expert_gemm_q4(shape, xe, w, r, h, ws)
-            moe.moe_down_combine(shape, h, w, r, y, ws)
+            moe.moe_expert_ffn_q4(shape, xe, w, r, h, y, ws)
 
         for w in esets:
             estep(w)
@@ -396,34 +430,14 @@ def main():
         e_active = int((r.counts > 0).sum().item())
         e_max = int(r.counts.max().item())
         EK = 12
-        eev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(EK)]
-        for s_ in range(EK):
-            w = esets[s_ % len(esets)]
-            eev[s_][0].record()
-            moe.moe_route(shape, xe, w, r, ws)
-            moe.moe_expert_gemm_q4(shape, xe, w, r, h, ws)
-            eev[s_][1].record()
-            moe.moe_down_combine(shape, h, w, r, y, ws)
-            eev[s_][2].record()
-        torch.cuda.synchronize()
-        # gate/up alone: its own events around the launch
-        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(EK)]
-        for s_ in range(EK):
-            w = esets[s_ % len(esets)]
-            moe.moe_route(shape, xe, w, r, ws)
-            gev[s_][0].record()
-            moe.moe_expert_gemm_q4(shape, xe, w, r, h, ws)
-            gev[s_][1].record()
-            moe.moe_down_combine(shape, h, w, r, y, ws)
-        torch.cuda.synchronize()
-        e_gateup_ms = sum(g_[0].elapsed_time(g_[1]) for g_ in gev) / EK
-        e_down_ms = sum(e_[1].elapsed_time(e_[2]) for e_ in eev) / EK
+        _, e_ffn_ms, e_comb_ms = phases([(esets[s_ % len(esets)], shape) for s_ in range(EK)], xe, r,
+                                        ws, h, y)
         eg = torch.cuda.CUDAGraph()
         with torch.cuda.graph(eg):
             for w in esets:
                 estep(w)
-        eg.replay()
-        torch.cuda.synchronize()
+        for _ in range(-(-60 // len(esets))):         # about 60 steps of warmup, back to back
+            eg.replay()
         ereps = max(1, 24 // len(esets))
         a_ = torch.cuda.Event(enable_timing=True)
         b_ = torch.cuda.Event(enable_timing=True)
@@ -440,9 +454,9 @@ def main():
                           f"T={T} tokens picking among 32 experts (router bias), {erows - T} routed rows, "
                           f"{e_active} experts active, at most {e_max} rows per expert",
               "us_per_step": round(e_us, 2), "tokens_per_s": round(T / (e_us * 1e-6), 1),
-              "gateup_us": round(e_gateup_ms * 1e3, 2),
-              "gateup_mfma_frac": round(e_fl_gu / (e_gateup_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-              "down_combine_us": round(e_down_ms * 1e3, 2),
+              "ffn_kernel_us": round(e_ffn_ms * 1e3, 2),
+              "ffn_mfma_frac": round((e_fl_gu + e_fl_dn) / (e_ffn_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+              "combine_us": round(e_comb_ms * 1e3, 2),
               "layer_mfma_frac": round((e_fl_gu + e_fl_dn) / (e_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 4),
               "weight_sets": len(esets)}
         del eg, esets, xe
@@ -469,8 +483,7 @@ def main():
 
         def ustep(w):
             moe.moe_route(ushape, xu, w, ur, uws)
-            moe.moe_expert_gemm_q4(ushape, xu, w, ur, uh, uws)
-            moe.moe_down_combine(ushape, uh, w, ur, uy, uws)
+            moe.moe_expert_ffn_q4(ushape, xu, w, ur, uh, uy, uws)
 
         for w in usets:
             ustep(w)
@@ -480,8 +493,8 @@ def main():
         with torch.cuda.graph(ug):
             for w in usets:
                 ustep(w)
-        ug.replay()
-        torch.cuda.synchronize()
+        for _ in range(-(-60 // len(usets))):         # about 60 steps of warmup, back to back
+            ug.replay()
         ureps = max(1, 24 // len(usets))
         u0 = torch.cuda.Event(enable_timing=True)
         u1 = torch.cuda.Event(enable_timing=True)
@@ -568,10 +581,11 @@ def main():
             u.copy_(x0)
             for w in layers:
                 moe.moe_route(sshape, u, w, sr, sws)
-                moe.moe_expert_gemm_q4(sshape, u, w, sr, sh_, sws)
-                # down GEMM, combine, residual add and RMSNorm: the combined rows are added
-                # to the residual as they are formed (y holds only the shared part)
-                moe.moe_down_combine_residual(sshape, sh_, w, sr, sy, res, 1e-6, u, sws)
+                # both GEMMs in one launch (y: the shared expert's part), then the combine with
+                # the residual add and RMSNorm: the combined rows are added to the residual as
+                # they are formed
+                moe.moe_expert_ffn_q4(sshape, u, w, sr, sh_, sy, sws, combine=False)
+                moe.moe_combine_residual(sshape, sr, sy, res, 1e-6, u, sws)
 
         stack_pass()
         torch.cuda.synchronize()
@@ -580,6 +594,7 @@ def main():
             stack_pass()
         sg.replay()
         torch.cuda.synchronize()
+        sg.replay()                                    # a pass of warmup, back to back
         s0 = torch.cuda.Event(enable_timing=True)
         s1 = torch.cuda.Event(enable_timing=True)
         sreps = 3
@@ -654,14 +669,17 @@ def main():
                                "Zipf(1.1) router bias",
                    "T": T, "H": H, "I": I, "E": E, "top_k": K_TOP, "weight_sets": args.sets,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "q4_gemm_kernel<0> (gate/up + SwiGLU, fp16 MFMA)",
-                     "achieved": round(gateup_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gateup_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": gateup_traffic_bytes(), "avg_launch_us": round(gateup_ms * 1e3, 2),
-                     "flops_per_launch": flops_gateup},
+        "roofline": {"bound": "mfma",
+                     "kernel": "q4_ffn_kernel (gate/up + SwiGLU + down in one persistent launch, "
+                               "fp16 MFMA)",
+                     "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": ffn_traffic_bytes(), "avg_launch_us": round(ffn_ms * 1e3, 2),
+                     "flops_per_launch": flops_ffn},
         "layer_mfma_frac": round(layer_mfma_frac, 4),
-        "phase_us": {"route": round(route_ms * 1e3, 2), "gateup": round(gateup_ms * 1e3, 2),
-                     "down_combine": round(down_ms * 1e3, 2)},
+        "phase_us": {"route": round(route_ms * 1e3, 2), "ffn_kernel": round(ffn_ms * 1e3, 2),
+                     "combine": round(comb_ms * 1e3, 2)},
+        "two_launch": two_launch,
         "wall_s": round(wall, 3),
         "prefill2048_zipf_affine": affine,
         "prefill2048_ep8_share": ep,

@@ -52,6 +52,11 @@ _SIGS = {
                           C.c_size_t, P], i32),
     "moe_down_combine_residual": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing),
                                    P, P, C.c_float, P, P, C.c_size_t, P], i32),
+    "moe_expert_ffn_q4": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P,
+                           i32, P, C.c_size_t, P], i32),
+    "moe_combine": ([C.POINTER(_Shape), C.POINTER(_Routing), P, P, C.c_size_t, P], i32),
+    "moe_combine_residual": ([C.POINTER(_Shape), C.POINTER(_Routing), P, P, C.c_float, P, P,
+                              C.c_size_t, P], i32),
     "moe_layer": ([C.POINTER(_Shape), P, C.POINTER(_Weights), C.POINTER(_Routing), P, P, P,
                    C.c_size_t, P], i32),
     "moe_query_chunked": ([C.POINTER(_Shape), i32, C.POINTER(C.c_size_t)], i32),
@@ -325,6 +330,38 @@ def moe_down_combine(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing, 
     _check(lib().moe_down_combine(C.byref(shape.c()), _ptr(h, _H16, "h"), C.byref(w.c()),
                                   C.byref(r.c()), _ptr(y, _F32, "y"), _ptr(ws, None, "ws"),
                                   ws.numel(), _stream(stream)), "moe_down_combine")
+
+
+def moe_expert_ffn_q4(shape: Shape, x: torch.Tensor, w: DeviceLayer, r: Routing, h: torch.Tensor,
+                      y: torch.Tensor, ws: torch.Tensor, combine: bool = True, stream=None):
+    """moe_expert_gemm_q4 + moe_down_combine with both GEMMs in one launch (same h and y).
+    combine=False leaves y = the shared expert's part and the routed rows staged in ws for
+    moe_combine / moe_combine_residual."""
+    _args(shape, w, r, x=x, h=h, y=y)
+    _check(lib().moe_expert_ffn_q4(C.byref(shape.c()), _ptr(x, _B16, "x"), C.byref(w.c()),
+                                   C.byref(r.c()), _ptr(h, _H16, "h"), _ptr(y, _F32, "y"),
+                                   1 if combine else 0, _ptr(ws, None, "ws"), ws.numel(),
+                                   _stream(stream)), "moe_expert_ffn_q4")
+
+
+def moe_combine(shape: Shape, r: Routing, y: torch.Tensor, ws: torch.Tensor, stream=None):
+    """y += each token's staged routed rows in pick order (after moe_expert_ffn_q4(combine=False))."""
+    _need(y, shape.T * shape.H, "y")
+    _check(lib().moe_combine(C.byref(shape.c()), C.byref(r.c()), _ptr(y, _F32, "y"),
+                             _ptr(ws, None, "ws"), ws.numel(), _stream(stream)), "moe_combine")
+
+
+def moe_combine_residual(shape: Shape, r: Routing, y: torch.Tensor, res: torch.Tensor, eps: float,
+                         u: torch.Tensor, ws: torch.Tensor, stream=None):
+    """res += y + the staged routed rows; u = bf16(RMSNorm(res)) (after
+    moe_expert_ffn_q4(combine=False)); y is only read."""
+    _need(y, shape.T * shape.H, "y")
+    _need(res, shape.T * shape.H, "res")
+    _need(u, shape.T * shape.H, "u")
+    _check(lib().moe_combine_residual(C.byref(shape.c()), C.byref(r.c()), _ptr(y, _F32, "y"),
+                                      _ptr(res, _F32, "res"), eps, _ptr(u, _B16, "u"),
+                                      _ptr(ws, None, "ws"), ws.numel(), _stream(stream)),
+           "moe_combine_residual")
 
 
 def moe_down_combine_residual(shape: Shape, h: torch.Tensor, w: DeviceLayer, r: Routing,

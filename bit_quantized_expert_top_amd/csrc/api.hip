@@ -17,6 +17,8 @@ int max_blocks_for(int T, int E, int k) {
     return (rows + kBM - 1) / kBM + (rows < E ? rows : E);
 }
 
+int ffn_slots(int T, int E, int k) { return (T + kBM - 1) / kBM + max_blocks_for(T, E, k); }
+
 size_t decode_scratch_bytes(int T, int H, int I, int k);
 
 WsLayout ws_layout(int T, int H, int I, int E, int k) {
@@ -40,7 +42,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.lrank = take((size_t)T * k * 4);
     L.sup = take(nTB <= (size_t)kSupBlk * kSupMax ? (nTB + kSupBlk - 1) / kSupBlk * E * 4 : 0);
     L.sched = take((size_t)max_blocks_for(T, E, k) * 4);
-    L.qctl = take((size_t)QCTL_WORDS * 4);
+    L.qctl = take((size_t)(QCTL_WORDS + ffn_slots(T, E, k)) * 4);
     L.xmx = take((size_t)T * (H / 64) * 4);
     L.tok = take((size_t)T * 2 * 4);
     L.hexp = take((size_t)(T * k + T) * 4);
@@ -181,7 +183,8 @@ moe_status enqueue_route(const moe_shape *s, const uint16_t *x, const moe_weight
     }
     launch_scan_scatter(r->topk_ids, r->topk_w, blk_cnt, sup, lrank, s->T, s->E, s->top_k, kBM,
                         r->counts, r->offsets, r->row_token, r->tok_row, r->row_w, r->blocks,
-                        r->num_blocks, (int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl), st);
+                        r->num_blocks, (int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
+                        ffn_slots(s->T, s->E, s->top_k), st);
     return launched();
 }
 
@@ -209,6 +212,20 @@ moe_status enqueue_down(const moe_shape *s, const uint16_t *h, const moe_weights
                 (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
                 max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row,
                 (uint16_t *)(ws + L.stage), y, combine, st);
+    return launched();
+}
+
+// gate/up and down in one launch, then (combine) the combine
+moe_status enqueue_ffn(const moe_shape *s, const moe_weights *w, const moe_routing *r, uint16_t *h,
+                       float *y, bool combine, char *ws, hipStream_t st) {
+    const WsLayout L = ws_layout(s->T, s->H, s->I, s->E, s->top_k);
+    launch_ffn(*s, (const uint16_t *)(ws + L.xp), (const float *)(ws + L.xsum),
+               (const float *)(ws + L.tok), gemm_weights(w->packed, s->H, s->I, s->E, true),
+               gemm_weights(w->packed, s->H, s->I, s->E, false), r->blocks, r->num_blocks,
+               (const int32_t *)(ws + L.sched), (int32_t *)(ws + L.qctl),
+               max_blocks_for(s->T, s->E, s->top_k), r->row_token, r->row_w, r->tok_row, h,
+               (float *)(ws + L.hsum), (float *)(ws + L.hexp), (uint16_t *)(ws + L.stage), y,
+               combine, st);
     return launched();
 }
 
@@ -279,6 +296,46 @@ moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe
     return enqueue_down(shape, h, w, r, y, (char *)ws, (hipStream_t)stream);
 }
 
+moe_status moe_expert_ffn_q4(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                             const moe_routing *r, uint16_t *h, float *y, int32_t combine,
+                             void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(x) || !aligned(h) || !aligned(y)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_weights(w, false, true, true));
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    (void)x;   // the GEMMs read moe_route's prepared copy of x in the workspace
+    return enqueue_ffn(shape, w, r, h, y, combine != 0, (char *)ws, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_shape *shape, const moe_routing *r, float *y, void *ws,
+                       size_t ws_bytes, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(y)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(shape->T, shape->H, shape->I, shape->E, shape->top_k);
+    launch_combine(*shape, (const uint16_t *)((char *)ws + L.stage), r->tok_row, y,
+                   (hipStream_t)stream);
+    return launched();
+}
+
+moe_status moe_combine_residual(const moe_shape *shape, const moe_routing *r, float *y, float *res,
+                                float eps, uint16_t *u, void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_shape(shape));
+    if (!aligned(y) || !aligned(res) || !aligned(u) || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if ((const void *)res == (const void *)y || (const void *)u == (const void *)res ||
+        (const void *)u == (const void *)y)
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_routing(r));
+    MOE_TRY(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(shape->T, shape->H, shape->I, shape->E, shape->top_k);
+    launch_combine_residual_norm(shape->T, shape->H, shape->top_k, eps, res, y,
+                                 (const uint16_t *)((char *)ws + L.stage), r->tok_row, u,
+                                 (hipStream_t)stream);
+    return launched();
+}
+
 moe_status moe_down_combine_residual(const moe_shape *shape, const uint16_t *h,
                                      const moe_weights *w, const moe_routing *r, float *y,
                                      float *res, float eps, uint16_t *u, void *ws,
@@ -310,8 +367,7 @@ moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weight
     MOE_TRY(check_ws(shape, ws, ws_bytes));
     hipStream_t st = (hipStream_t)stream;
     MOE_TRY(enqueue_route(shape, x, w, r, (char *)ws, st));
-    MOE_TRY(enqueue_gateup(shape, x, w, r, h, (char *)ws, st));
-    return enqueue_down(shape, h, w, r, y, (char *)ws, st);
+    return enqueue_ffn(shape, w, r, h, y, true, (char *)ws, st);
 }
 
 moe_status moe_query_chunked(const moe_shape *shape, int32_t chunk, size_t *workspace_bytes) {
@@ -351,8 +407,7 @@ moe_status moe_layer_chunked(const moe_shape *shape, const uint16_t *x, const mo
         const uint16_t *xc = x + (size_t)c0 * H;
         float *yc = y + (size_t)c0 * H;
         MOE_TRY(enqueue_route(&sc, xc, w, &r, base, st));
-        MOE_TRY(enqueue_gateup(&sc, xc, w, &r, h, base, st));
-        MOE_TRY(enqueue_down(&sc, h, w, &r, yc, base, st));
+        MOE_TRY(enqueue_ffn(&sc, w, &r, h, yc, true, base, st));
     }
     return MOE_OK;
 }

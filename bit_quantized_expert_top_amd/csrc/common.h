@@ -229,14 +229,19 @@ __device__ __forceinline__ float group_max_dpp8(float v) {
     return v;
 }
 
-// GEMM work queues (int32 words of the workspace's qctl area): per GEMM a
-// queue head and a finished-workgroup count.  The routing scatter zeroes
-// them; each GEMM launch's last workgroup zeroes its own again.  Every counter
-// has a 128-byte line of its own (atomics on one shared line serialise).
+// GEMM work queues (int32 words of the workspace's qctl area): per GEMM launch a
+// queue head and a finished-workgroup count, then (one-launch FFN) a finished
+// gate/up item count per slot.  The routing scatter zeroes them all; each
+// launch's last workgroup zeroes its own again.  Every queue counter has a
+// 128-byte line of its own (atomics on one shared line serialise).
 constexpr int QCTL_LINE = 32;                       // words per counter
 constexpr int QCTL_GATEUP = 0;                      // head, then finished count
 constexpr int QCTL_DOWN = 2 * QCTL_LINE;            // same for the down GEMM
-constexpr int QCTL_WORDS = 4 * QCTL_LINE;
+constexpr int QCTL_FFN = 4 * QCTL_LINE;             // same for the one-launch FFN
+constexpr int QCTL_WORDS = 6 * QCTL_LINE;           // then the FFN's per-slot counts
+// bounded wait of a one-launch FFN down item for its slot's gate/up items (s_sleep 2 rounds,
+// each with a round trip to memory: about a second)
+constexpr int kFfnSpin = 1 << 20;
 
 // Tile layout of the expert weights: one block per (tile of 256 columns, group
 // of 64 inputs), codes then scales then biases (the block format is documented
@@ -281,6 +286,7 @@ constexpr uint32_t DBG_GEMM_BLOCK = 2;      // grouped GEMM: malformed block map
 constexpr uint32_t DBG_GEMM_TOKEN = 4;      // grouped GEMM: row token out of range
 constexpr uint32_t DBG_COMBINE_ROW = 8;     // combine: a pick's row out of range
 constexpr uint32_t DBG_DECODE_ID = 16;      // decode: a pick's expert id out of range
+constexpr uint32_t DBG_FFN_WAIT = 32;       // one-launch FFN: a down item's wait timed out
 #ifdef MOE_DEBUG
 static __device__ uint32_t dbg_word;
 #define MOE_DBG(cond, bit)                           \
@@ -342,7 +348,7 @@ struct WsLayout {
     size_t lrank;       // int32 [T][k]           rank of (t,j) inside its token block
     size_t sup;         // int32 [T/(kTB kSupBlk)][E] per superblock expert counts (T <= 4096)
     size_t sched;       // int32 [max_blocks]     GEMM order of the routed blocks (by cost class)
-    size_t qctl;        // int32 [64]             GEMM work-queue counters and class counts
+    size_t qctl;        // int32 [QCTL_WORDS + ffn_slots]  GEMM work-queue counters, FFN slot counts
     size_t xmx;         // fp32 [T][H/64]         group maxima of |x|
     size_t tok;         // fp32 [T][2]            per token: 2^e (x enters the GEMM as x 2^-e), ||x||
     size_t hexp;        // fp32 [T*k + T]         per h row: 2^f (h is stored as h 2^-f)
@@ -352,6 +358,8 @@ struct WsLayout {
 
 WsLayout ws_layout(int T, int H, int I, int E, int k);
 int max_blocks_for(int T, int E, int k);
+// work-item slots of the GEMMs: shared-expert blocks plus at most max_blocks_for routed blocks
+int ffn_slots(int T, int E, int k);
 
 // ---- launchers (defined in the .hip files; all asynchronous) ----
 void launch_router_logits(const uint16_t *x, const uint16_t *wr_t, const float *bias, int T, int H,
@@ -370,7 +378,7 @@ void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *sup, const int32_t *lrank, int T, int E, int k, int BM,
                          int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
                          float *row_w, int32_t *blocks, int32_t *num_blocks, int32_t *sched,
-                         int32_t *qctl, hipStream_t s);
+                         int32_t *qctl, int nslots, hipStream_t s);
 void launch_zero_i32(int32_t *p, int n, hipStream_t s);
 void launch_prep_act(const uint16_t *x, int rows, int K, uint16_t *xp, float *xsum, float *xsq,
                      float *xmx, hipStream_t s);
@@ -399,6 +407,15 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
                  const int32_t *sched, int32_t *qctl, int max_blocks,
                  const int32_t *row_token, const float *row_w, const int32_t *tok_row,
                  uint16_t *stage, float *y, bool combine, hipStream_t s);
+// gate/up and down in one persistent launch, then (combine) the combine
+void launch_ffn(const moe_shape &sh, const uint16_t *xp, const float *xsum, const float *tok,
+                const GemmWeights &gwg, const GemmWeights &gwd, const int32_t *blocks,
+                const int32_t *num_blocks, const int32_t *sched, int32_t *qctl, int max_blocks,
+                const int32_t *row_token, const float *row_w, const int32_t *tok_row, uint16_t *h,
+                float *hsum, float *hexp, uint16_t *stage, float *y, bool combine, hipStream_t s);
+// y[t] += the k staged routed rows of token t, in pick order (fp32)
+void launch_combine(const moe_shape &sh, const uint16_t *stage, const int32_t *tok_row, float *y,
+                    hipStream_t s);
 // r += (y + the k staging rows of each token, in pick order); u = bf16(RMSNorm(r))
 void launch_combine_residual_norm(int T, int H, int k, float eps, float *r, const float *y,
                                   const uint16_t *stage, const int32_t *tok_row, uint16_t *u,

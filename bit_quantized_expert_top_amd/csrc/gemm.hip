@@ -132,9 +132,15 @@ __device__ __forceinline__ floatx16 mfma16(f16x8 a, f16x8 b, floatx16 c) {
 // [lds + 16 i, +16) (dword form: [lds + 4 i, +4)).  Issued through inline assembly so that the compiler does not
 // wait for them before every LDS read; completion is awaited explicitly
 // (s_waitcnt vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
-                 : "memory", "m0");
+// COH: the copy carries the agent-scope cache policy (sc1), so it returns what an sc1 store
+// on another XCD wrote, even where this XCD's L2 holds an older copy of the line.
+template <bool COH = false> __device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+    if constexpr (COH)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off sc1" ::"v"(g), "s"(lds)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+                     : "memory", "m0");
 }
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
@@ -144,13 +150,35 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
 // The same copies with a wave-uniform base address in SGPRs and a per-lane
 // 32-bit byte offset: the per-lane offsets stay fixed over the K loop and each
 // K step only moves the scalar base.
+template <bool COH = false>
 __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
+    if constexpr (COH)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(sbase),
+                     "s"(lds)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                     "s"(lds)
+                     : "memory", "m0");
 }
 __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
+}
+
+// Vector stores of the gate/up outputs.  COH: agent-scope policy (sc1), the store is written
+// through to memory, where the sc1 copies of a down item on any XCD read it.
+template <bool COH> __device__ __forceinline__ void store16(void *p, u32x4 v) {
+    if constexpr (COH)
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+    else
+        *(u32x4 *)p = v;
+}
+template <bool COH> __device__ __forceinline__ void store4(float *p, float v) {
+    if constexpr (COH)
+        asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+    else
+        *p = v;
 }
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
@@ -199,9 +227,13 @@ struct ItemLds {
     float *ne;     // [64], all equal
 };
 
-template <int MODE, int MT>
+// COH (the one-launch FFN): h, its group sums and its row factors travel between XCDs, so the
+// gate/up pass stores them and the down pass copies them with the agent-scope policy.
+// pend >= 0: slot whose gate/up item this workgroup finished last and has not yet reported; its
+// stores are awaited with the first stage (s_waitcnt vmcnt(0)) and done[pend] incremented.
+template <int MODE, int MT, bool COH>
 __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *s_next,
-                          const ItemLds &il) {
+                          const ItemLds &il, int32_t *done, int pend) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));              // recomputed per item: nothing lane-dependent is hoisted
@@ -236,7 +268,8 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
         constexpr uint32_t base = (uint32_t)(decltype(SLOT)::value * RG::STAGE);
         const uint8_t *ag = (const uint8_t *)a.A + (size_t)c * (KC * 2);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) dma16s(ag, aoff[i], lds0 + base + (uint32_t)((i * 256 + wave * 64) * 16));
+        for (int i = 0; i < MT; ++i)
+            dma16s<COH && MODE == 1>(ag, aoff[i], lds0 + base + (uint32_t)((i * 256 + wave * 64) * 16));
         const uint8_t *blk = tb + (size_t)c * PK_BLOCK;
         dma16s(blk, boff, lds0 + base + (uint32_t)(RG::A_BYTES + wave * 64 * 16));
         dma16s(blk + 4096, boff, lds0 + base + (uint32_t)(RG::A_BYTES + (256 + wave * 64) * 16));
@@ -274,7 +307,7 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 for (int u = 0; u < per; ++u) {
                     const int g = p + 8 * u;
                     if (g < G)
-                        dma4(a.Asum + (size_t)srow * G + g,
+                        dma4<COH && MODE == 1>(a.Asum + (size_t)srow * G + g,
                              xs0 + (uint32_t)(4 * ((i * per + u) * 256 + 64 * wave)));
                 }
             }
@@ -324,7 +357,7 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 dma4(a.tok + 2 * (size_t)tok + 1, lds_of(il.rb) + (uint32_t)(256 * wave));
             } else {
                 if (!t.shared) dma4(a.row_w + t.r0 + m, lds_of(il.ra) + (uint32_t)(256 * wave));
-                dma4(a.hexp + t.r0 + m, lds_of(il.rb) + (uint32_t)(256 * wave));
+                dma4<COH>(a.hexp + t.r0 + m, lds_of(il.rb) + (uint32_t)(256 * wave));
             }
         } else if (MODE == 0 && wave == 2) {
             dma4(a.emeta + (size_t)(t.shared ? a.E : t.e) * PK_EMETA, lds_of(il.ne));
@@ -351,7 +384,8 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
             if (c >= nch) return;
             // stages issued after c: min(AHEAD - 1, nch - 1 - c)
             const int after = min(RG::AHEAD - 1, nch - 1 - c);
-            if (after <= 0)
+            const bool report = c == 0 && pend >= 0;   // also the last item's stores
+            if (after <= 0 || report)
                 wait_vm<0>();
             else if (after == 1)
                 wait_vm<RG::PER>();
@@ -360,6 +394,8 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
             else
                 wait_vm<(RG::AHEAD > 3 ? 3 : 0) * RG::PER>();
             __syncthreads();                     // stage c visible; stage c-1 no longer read
+            if (report && tid == 0)
+                __hip_atomic_fetch_add(done + pend, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (c + RG::AHEAD < nch)             // into the slot of stage c-1
                 issue(c + RG::AHEAD, std::integral_constant<int, (u + RG::AHEAD) % RG::NST>{});
             if (c == 1 && tid == 0) next = atomicAdd(&a.qctl[0], 1);   // overlaps the tile
@@ -419,7 +455,7 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
         if (tid < kBM) {
             const int f = h_exponent(il.ne[0], il.rb[tid]);
             il.rb[tid] = exp2i(-f);
-            if (t.ntile == 0 && tid < t.nrows) a.hexp[t.r0 + tid] = exp2i(f);
+            if (t.ntile == 0 && tid < t.nrows) store4<COH>(a.hexp + t.r0 + tid, exp2i(f));
         }
         __syncthreads();
         // SwiGLU -> fp16 h tile in LDS [128 rows][128 columns]
@@ -436,20 +472,29 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 *(uint16_t *)(smem + row * HS_LD + 2 * pc) = f32_to_f16(hv);
             }
         __syncthreads();
-        // thread: row tid/2, 64-column half tid&1 -> 128 B of h and one group sum
-        const int row = tid >> 1, half = tid & 1;
-        if (row < t.nrows) {
-            const uint8_t *src = smem + row * HS_LD + half * 128;
-            uint16_t *dst = a.h + (size_t)(t.r0 + row) * a.N + t.ntile * 128 + half * 64;
-            float sum = 0.0f;
+        // group sums: thread = row tid/2, 64-column half tid&1, summed in column order
+        {
+            const int row = tid >> 1, half = tid & 1;
+            if (row < t.nrows) {
+                const uint8_t *src = smem + row * HS_LD + half * 128;
+                float sum = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const u32x4 v = *(const u32x4 *)(src + 16 * q);
+                for (int q = 0; q < 8; ++q) {
+                    const u32x4 v = *(const u32x4 *)(src + 16 * q);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sum += f16_lo(v[r]) + f16_hi(v[r]);
-                *(u32x4 *)(dst + 8 * q) = v;
+                    for (int r = 0; r < 4; ++r) sum += f16_lo(v[r]) + f16_hi(v[r]);
+                }
+                store4<COH>(a.hsum + (size_t)(t.r0 + row) * (a.N / 64) + t.ntile * 2 + half, sum);
             }
-            a.hsum[(size_t)(t.r0 + row) * (a.N / 64) + t.ntile * 2 + half] = sum;
+        }
+        // h: 16 lanes per row, so that each store instruction writes whole 128-byte lines (the
+        // sc1 stores are written through line by line)
+#pragma unroll
+        for (int q = 0; q < kBM * 16 / NTHR; ++q) {
+            const int p = q * NTHR + tid, row = p >> 4, c16 = p & 15;
+            if (row < t.nrows)
+                store16<COH>(a.h + (size_t)(t.r0 + row) * a.N + t.ntile * 128 + 8 * c16,
+                             *(const u32x4 *)(smem + row * HS_LD + 16 * c16));
         }
     } else {
         const int Trk = a.T * a.topk;
@@ -509,6 +554,43 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
     }
 }
 
+// The tile of work item (slot, n-tile): slots are the shared-expert blocks, then the routed
+// blocks in the routing schedule's order.  False for a malformed block map entry, which
+// turns into a skipped item, never an out-of-bounds access.
+__device__ __forceinline__ bool item_tile(const GemmArgs &a, int slot, int ntile, int nb, Tile &t) {
+    t.ntile = ntile;
+    t.shared = slot < a.n_shared;
+    t.e = 0;
+    if (t.shared) {
+        t.r0 = a.T * a.topk + slot * kBM;
+        t.nrows = min(kBM, a.T - slot * kBM);
+        return true;
+    }
+    const int mb = a.sched[slot - a.n_shared];
+    bool ok = mb >= 0 && mb < nb;
+    if (ok) {
+        t.e = a.blocks[3 * mb];
+        t.r0 = a.blocks[3 * mb + 1];
+        t.nrows = a.blocks[3 * mb + 2];
+        ok = !(t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
+               t.r0 + t.nrows > a.T * a.topk);
+    }
+    if (threadIdx.x == 0) MOE_DBG(ok, DBG_GEMM_BLOCK);
+    return ok;
+}
+
+// one tile with the M-tile count of its rows
+template <int MODE, bool COH>
+__device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *s_next,
+                                         const ItemLds &il, int32_t *done, int pend) {
+    switch ((t.nrows + 31) >> 5) {
+        case 1: gemm_tile<MODE, 1, COH>(a, t, smem, s_next, il, done, pend); break;
+        case 2: gemm_tile<MODE, 2, COH>(a, t, smem, s_next, il, done, pend); break;
+        case 3: gemm_tile<MODE, 3, COH>(a, t, smem, s_next, il, done, pend); break;
+        default: gemm_tile<MODE, 4, COH>(a, t, smem, s_next, il, done, pend); break;
+    }
+}
+
 // Work items: (slot, n-tile) with the n-tile fastest, so the n-tiles of a
 // block (which read the same activation rows) run side by side; slots are the
 // shared-expert blocks, then the routed blocks in the routing schedule's order
@@ -525,50 +607,122 @@ __global__ __launch_bounds__(NTHR, 2) void q4_gemm_kernel(GemmArgs a) {
     const ItemLds il{s_colk, s_ra, s_rb, s_ne};
     const int nb = min(max(a.num_blocks[0], 0), a.max_blocks);
     const int n_items = (a.n_shared + nb) * a.n_tiles;
-    // an item that turns out empty still takes the next one from the head
-    auto skip = [&]() {
-        if (threadIdx.x == 0) s_next = atomicAdd(&a.qctl[0], 1);
-    };
     for (int k = blockIdx.x; k < n_items; k = (int)gridDim.x + s_next) {
         __syncthreads();                         // s_next has been read by every thread
         const int slot = k / a.n_tiles;
         Tile t;
-        t.ntile = k - slot * a.n_tiles;
-        t.shared = slot < a.n_shared;
-        t.e = 0;
-        bool ok = true;
-        if (!t.shared) {
-            const int mb = a.sched[slot - a.n_shared];
-            ok = mb >= 0 && mb < nb;
-            if (ok) {
-                t.e = a.blocks[3 * mb];
-                t.r0 = a.blocks[3 * mb + 1];
-                t.nrows = a.blocks[3 * mb + 2];
-                // a malformed block map turns into a no-op, never an out-of-bounds access
-                ok = !(t.e < 0 || t.e >= a.E || t.r0 < 0 || t.nrows < 1 || t.nrows > kBM ||
-                       t.r0 + t.nrows > a.T * a.topk);
-            }
-            if (threadIdx.x == 0) MOE_DBG(ok, DBG_GEMM_BLOCK);
-        } else {
-            t.r0 = a.T * a.topk + slot * kBM;
-            t.nrows = min(kBM, a.T - slot * kBM);
-        }
-        if (!ok) {
-            skip();
-        } else {
-            switch ((t.nrows + 31) >> 5) {
-                case 1: gemm_tile<MODE, 1>(a, t, smem, &s_next, il); break;
-                case 2: gemm_tile<MODE, 2>(a, t, smem, &s_next, il); break;
-                case 3: gemm_tile<MODE, 3>(a, t, smem, &s_next, il); break;
-                default: gemm_tile<MODE, 4>(a, t, smem, &s_next, il); break;
-            }
-        }
+        if (item_tile(a, slot, k - slot * a.n_tiles, nb, t))
+            run_tile<MODE, false>(a, t, smem, &s_next, il, nullptr, -1);
+        else if (threadIdx.x == 0)               // an empty item still takes the next one
+            s_next = atomicAdd(&a.qctl[0], 1);
         __syncthreads();                         // s_next written; the tile is done with the LDS
     }
     // the last workgroup out re-arms the head for the next launch
     if (threadIdx.x == 0 && atomicAdd(&a.qctl[QCTL_LINE], 1) == (int)gridDim.x - 1) {
         atomicExch(&a.qctl[0], 0);
         atomicExch(&a.qctl[QCTL_LINE], 0);
+    }
+}
+
+// Both GEMMs in one persistent launch.  One queue holds every gate/up item, then every down
+// item (each part longest first, as above), so that workgroups freed by the last, short
+// gate/up items start on the long down items instead of idling until the launch ends.
+//
+// A down item reads its block's h rows from all I/128 gate/up items of that slot, which may
+// have run on any XCD; each XCD has its own L2.  The gate/up items therefore store h, its group
+// sums and the row factors 2^f with the agent-scope policy (written through), the down items
+// copy them with that policy (never served from a stale L2 line), and done[slot] counts the
+// slot's finished gate/up items.  A workgroup reports a gate/up item once its stores are
+// complete: at the first stage wait of its next gate/up item (s_waitcnt vmcnt(0) there), or
+// before it takes a down item or leaves.  A down item's thread 0 then waits, with a bounded
+// spin, until done[slot] reaches I/128.
+//
+// The wait ends: the queue hands out items in index order, and every gate/up item precedes
+// every down item.  Of the unfinished items, the one with the lowest index waits for nothing
+// (its gate/up items are finished, or it is a gate/up item), and its workgroup is running it
+// or finishing an earlier item that also waits for nothing.  Workgroups start on static items
+// (item = workgroup index) only within the gate/up part; the others take their first item from
+// the head.
+//
+// done[] is zeroed by the routing pass and, for the next launch, by the last workgroup out.
+__global__ __launch_bounds__(NTHR, 2) void q4_ffn_kernel(GemmArgs ag, GemmArgs ad, int32_t *done) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    __shared__ int s_next, s_last;
+    __shared__ __attribute__((aligned(16))) float s_colk[256];
+    __shared__ float s_ra[kBM], s_rb[kBM], s_ne[64];
+    const ItemLds il{s_colk, s_ra, s_rb, s_ne};
+    const int tid = threadIdx.x;
+    const int nb = min(max(ag.num_blocks[0], 0), ag.max_blocks);
+    const int nslot = ag.n_shared + nb;
+    const int ng = nslot * ag.n_tiles, n_items = ng + nslot * ad.n_tiles;
+    const int nstatic = min((int)gridDim.x, ng);
+    int32_t *head = ag.qctl;                     // the same queue words in ad
+    auto report = [&](int slot) {
+        __hip_atomic_fetch_add(done + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    int pend = -1;                               // gate/up slot finished but not yet reported
+    auto flush = [&]() {                         // whole workgroup; pend is uniform
+        if (pend >= 0) {
+            wait_vm<0>();                        // this wave's h stores are complete
+            __syncthreads();                     // ... and every other wave's
+            if (tid == 0) report(pend);
+            pend = -1;
+        }
+    };
+    if ((int)blockIdx.x >= nstatic) {
+        if (tid == 0) s_next = atomicAdd(head, 1);
+        __syncthreads();
+    }
+    for (int k = (int)blockIdx.x < nstatic ? (int)blockIdx.x : nstatic + s_next; k < n_items;
+         k = nstatic + s_next) {
+        __syncthreads();                         // s_next has been read by every thread
+        Tile t;
+        if (k < ng) {
+            const int slot = k / ag.n_tiles;
+            if (item_tile(ag, slot, k - slot * ag.n_tiles, nb, t)) {
+                run_tile<0, true>(ag, t, smem, &s_next, il, done, pend);
+                pend = slot;
+            } else {
+                flush();
+                if (tid == 0) {
+                    report(slot);                // nothing stored: reported at once
+                    s_next = atomicAdd(head, 1);
+                }
+            }
+        } else {
+            const int kd = k - ng, slot = kd / ad.n_tiles;
+            const bool ok = item_tile(ad, slot, kd - slot * ad.n_tiles, nb, t);
+            flush();                             // never wait while holding a report
+            if (ok) {
+                if (tid == 0) {
+                    int it = 0;
+                    while (__hip_atomic_load(done + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                               ag.n_tiles &&
+                           it < kFfnSpin) {
+                        __builtin_amdgcn_s_sleep(2);
+                        ++it;
+                    }
+                    MOE_DBG(it < kFfnSpin, DBG_FFN_WAIT);
+                }
+                __syncthreads();                 // the slot's h is complete
+                run_tile<1, true>(ad, t, smem, &s_next, il, done, -1);
+            } else if (tid == 0) {
+                s_next = atomicAdd(head, 1);
+            }
+        }
+        __syncthreads();                         // s_next written; the tile is done with the LDS
+    }
+    flush();
+    // the last workgroup out zeroes the counters and re-arms the head for the next launch
+    if (tid == 0) s_last = atomicAdd(&head[QCTL_LINE], 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (s_last) {
+        for (int i = tid; i < nslot; i += NTHR)
+            __hip_atomic_store(done + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            atomicExch(&head[0], 0);
+            atomicExch(&head[QCTL_LINE], 0);
+        }
     }
 }
 
@@ -583,17 +737,20 @@ static unsigned grid_for(int n_shared, int max_blocks, int n_tiles) {
     return (unsigned)std::max<long>(1, std::min<long>(items, 2L * cus));
 }
 
-// the GEMM needs more dynamic LDS than the default launch limit
-template <int MODE>
+// the GEMMs need more dynamic LDS than the default launch limit
+template <const void *(*FN)()>
 static void allow_lds() {
     static LdsLimit lim;
-    lim.ensure((const void *)q4_gemm_kernel<MODE>, L_TOTAL);
+    lim.ensure(FN(), L_TOTAL);
 }
+template <int MODE> static const void *gemm_fn() { return (const void *)q4_gemm_kernel<MODE>; }
+static const void *ffn_fn() { return (const void *)q4_ffn_kernel; }
 
-void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, const float *tok,
-                   const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
-                   const int32_t *sched, int32_t *qctl, int max_blocks, const int32_t *row_token,
-                   uint16_t *h, float *hsum, float *hexp, hipStream_t s) {
+static GemmArgs gateup_args(const moe_shape &sh, const uint16_t *xp, const float *xsum,
+                            const float *tok, const GemmWeights &gw, const int32_t *blocks,
+                            const int32_t *num_blocks, const int32_t *sched, int32_t *qctl,
+                            int max_blocks, const int32_t *row_token, uint16_t *h, float *hsum,
+                            float *hexp) {
     GemmArgs a{};
     a.A = xp;
     a.Asum = xsum;
@@ -610,7 +767,7 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, c
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.sched = sched;
-    a.qctl = qctl + QCTL_GATEUP;
+    a.qctl = qctl;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.T = sh.T;
@@ -620,7 +777,16 @@ void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, c
     a.n_shared = shared_blocks(sh.T);
     a.h = h;
     a.hsum = hsum;
-    allow_lds<0>();
+    return a;
+}
+
+void launch_gateup(const moe_shape &sh, const uint16_t *xp, const float *xsum, const float *tok,
+                   const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
+                   const int32_t *sched, int32_t *qctl, int max_blocks, const int32_t *row_token,
+                   uint16_t *h, float *hsum, float *hexp, hipStream_t s) {
+    const GemmArgs a = gateup_args(sh, xp, xsum, tok, gw, blocks, num_blocks, sched,
+                                   qctl + QCTL_GATEUP, max_blocks, row_token, h, hsum, hexp);
+    allow_lds<gemm_fn<0>>();
     hipLaunchKernelGGL(q4_gemm_kernel<0>, dim3(grid_for(a.n_shared, max_blocks, a.n_tiles)),
                        dim3(NTHR), L_TOTAL, s, a);
 }
@@ -663,11 +829,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     *(float4 *)(y + t * H + n + 4) = a1;
 }
 
-void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const float *hexp,
-                 const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
-                 const int32_t *sched, int32_t *qctl, int max_blocks,
-                 const int32_t *row_token, const float *row_w, const int32_t *tok_row,
-                 uint16_t *stage, float *y, bool combine, hipStream_t s) {
+static GemmArgs down_args(const moe_shape &sh, const uint16_t *h, const float *hsum,
+                          const float *hexp, const GemmWeights &gw, const int32_t *blocks,
+                          const int32_t *num_blocks, const int32_t *sched, int32_t *qctl,
+                          int max_blocks, const int32_t *row_token, const float *row_w,
+                          uint16_t *stage, float *y) {
     GemmArgs a{};
     a.A = h;
     a.Asum = hsum;
@@ -683,7 +849,7 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
     a.blocks = blocks;
     a.num_blocks = num_blocks;
     a.sched = sched;
-    a.qctl = qctl + QCTL_DOWN;
+    a.qctl = qctl;
     a.max_blocks = max_blocks;
     a.row_token = row_token;
     a.row_w = row_w;
@@ -694,15 +860,45 @@ void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, cons
     a.n_shared = shared_blocks(sh.T);
     a.y = y;
     a.stage = stage;
-    allow_lds<1>();
+    return a;
+}
+
+// each token adds its k weighted routed rows to y
+void launch_combine(const moe_shape &sh, const uint16_t *stage, const int32_t *tok_row, float *y,
+                    hipStream_t s) {
+    const size_t n8 = (size_t)sh.T * sh.H / 8;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, stage,
+                       tok_row, sh.T, sh.H, sh.top_k, y);
+}
+
+void launch_down(const moe_shape &sh, const uint16_t *h, const float *hsum, const float *hexp,
+                 const GemmWeights &gw, const int32_t *blocks, const int32_t *num_blocks,
+                 const int32_t *sched, int32_t *qctl, int max_blocks,
+                 const int32_t *row_token, const float *row_w, const int32_t *tok_row,
+                 uint16_t *stage, float *y, bool combine, hipStream_t s) {
+    const GemmArgs a = down_args(sh, h, hsum, hexp, gw, blocks, num_blocks, sched,
+                                 qctl + QCTL_DOWN, max_blocks, row_token, row_w, stage, y);
+    allow_lds<gemm_fn<1>>();
     // shared-expert blocks write y, routed blocks their weighted staging rows ...
     hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(grid_for(a.n_shared, max_blocks, a.n_tiles)),
                        dim3(NTHR), L_TOTAL, s, a);
     // ... then each token adds its eight routed rows (unless the caller's next kernel does)
-    if (!combine) return;
-    const size_t n8 = (size_t)sh.T * sh.H / 8;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, stage,
-                       tok_row, sh.T, sh.H, sh.top_k, y);
+    if (combine) launch_combine(sh, stage, tok_row, y, s);
+}
+
+void launch_ffn(const moe_shape &sh, const uint16_t *xp, const float *xsum, const float *tok,
+                const GemmWeights &gwg, const GemmWeights &gwd, const int32_t *blocks,
+                const int32_t *num_blocks, const int32_t *sched, int32_t *qctl, int max_blocks,
+                const int32_t *row_token, const float *row_w, const int32_t *tok_row, uint16_t *h,
+                float *hsum, float *hexp, uint16_t *stage, float *y, bool combine, hipStream_t s) {
+    const GemmArgs ag = gateup_args(sh, xp, xsum, tok, gwg, blocks, num_blocks, sched,
+                                    qctl + QCTL_FFN, max_blocks, row_token, h, hsum, hexp);
+    const GemmArgs ad = down_args(sh, h, hsum, hexp, gwd, blocks, num_blocks, sched,
+                                  qctl + QCTL_FFN, max_blocks, row_token, row_w, stage, y);
+    allow_lds<ffn_fn>();
+    hipLaunchKernelGGL(q4_ffn_kernel, dim3(grid_for(ag.n_shared, max_blocks, ag.n_tiles + ad.n_tiles)),
+                       dim3(NTHR), L_TOTAL, s, ag, ad, qctl + QCTL_WORDS);
+    if (combine) launch_combine(sh, stage, tok_row, y, s);
 }
 
 MOE_DBG_READER(dbg_read_gemm)

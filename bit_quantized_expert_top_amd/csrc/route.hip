@@ -771,7 +771,7 @@ __global__ __launch_bounds__(256) void scan_experts_kernel(int32_t *__restrict__
 __device__ void publish_blocks(int tid, int cnt, int off, int BM, unsigned long long *wt,
                                int32_t *__restrict__ offsets, int32_t *__restrict__ blocks,
                                int32_t *__restrict__ num_blocks, int32_t *__restrict__ sched,
-                               int32_t *__restrict__ qctl) {
+                               int32_t *__restrict__ qctl, int nslots) {
     const int nblk = (cnt + BM - 1) / BM;
     // GEMM schedule: blocks by cost class (32-row M tiles: 4, 3, 2, 1), then by
     // expert.  Four 16-bit class counters per expert are scanned as one word.
@@ -793,8 +793,9 @@ __device__ void publish_blocks(int tid, int cnt, int off, int BM, unsigned long 
         bp[1] = off + i * BM;
         bp[2] = min(BM, cnt - i * BM);
     }
-    // the GEMMs' queue counters start at zero
-    if (tid < 4) qctl[tid * QCTL_LINE] = 0;
+    // the GEMMs' queue counters and the FFN's per-slot counts start at zero
+    if (tid < QCTL_WORDS / QCTL_LINE) qctl[tid * QCTL_LINE] = 0;
+    for (int i = tid; i < nslots; i += 256) qctl[QCTL_WORDS + i] = 0;
     int base[4];
     base[0] = 0;
     for (int c = 1; c < 4; ++c) base[c] = base[c - 1] + (int)((tot >> (16 * (c - 1))) & 0xFFFF);
@@ -815,7 +816,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t *__restrict__ counts, int T, int E, int k, int BM,
     int32_t *__restrict__ offsets, int32_t *__restrict__ blocks, int32_t *__restrict__ num_blocks,
     int32_t *__restrict__ row_token, int32_t *__restrict__ tok_row, float *__restrict__ row_w,
-    int32_t *__restrict__ sched, int32_t *__restrict__ qctl) {
+    int32_t *__restrict__ sched, int32_t *__restrict__ qctl, int nslots) {
     __shared__ int s_off[256];
     __shared__ unsigned long long wt[4];
     const int tid = threadIdx.x;
@@ -823,7 +824,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     unsigned long long tot;
     const int off = (int)block_scan_u64((unsigned long long)cnt, tid, wt, &tot) - cnt;
     s_off[tid] = off;
-    if (blockIdx.x == 0) publish_blocks(tid, cnt, off, BM, wt, offsets, blocks, num_blocks, sched, qctl);
+    if (blockIdx.x == 0)
+        publish_blocks(tid, cnt, off, BM, wt, offsets, blocks, num_blocks, sched, qctl, nslots);
     __syncthreads();
     const int idx = blockIdx.x * 256 + tid;
     if (idx >= T * k) return;
@@ -855,7 +857,7 @@ __global__ __launch_bounds__(256) void scatter1_kernel(
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ blocks,
     int32_t *__restrict__ num_blocks, int32_t *__restrict__ row_token,
     int32_t *__restrict__ tok_row, float *__restrict__ row_w, int32_t *__restrict__ sched,
-    int32_t *__restrict__ qctl) {
+    int32_t *__restrict__ qctl, int nslots) {
     __shared__ int s_off[256];
     __shared__ int s_base[4][256];
     __shared__ unsigned long long wt[4];
@@ -895,7 +897,7 @@ __global__ __launch_bounds__(256) void scatter1_kernel(
     s_off[tid] = off;
     if (blockIdx.x == 0) {
         counts[tid] = cnt;
-        publish_blocks(tid, cnt, off, BM, wt, offsets, blocks, num_blocks, sched, qctl);
+        publish_blocks(tid, cnt, off, BM, wt, offsets, blocks, num_blocks, sched, qctl, nslots);
     }
     __syncthreads();
     if (!has) return;
@@ -914,18 +916,18 @@ void launch_scan_scatter(const int32_t *ids, const float *w, int32_t *blk_cnt,
                          const int32_t *sup, const int32_t *lrank, int T, int E, int k, int BM,
                          int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *tok_row,
                          float *row_w, int32_t *blocks, int32_t *num_blocks, int32_t *sched,
-                         int32_t *qctl, hipStream_t s) {
+                         int32_t *qctl, int nslots, hipStream_t s) {
     const int nTB = (T + TB - 1) / TB;
     if (sup) {
         hipLaunchKernelGGL(scatter1_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w,
                            blk_cnt, sup, lrank, T, E, k, BM, counts, offsets, blocks, num_blocks,
-                           row_token, tok_row, row_w, sched, qctl);
+                           row_token, tok_row, row_w, sched, qctl, nslots);
         return;
     }
     hipLaunchKernelGGL(scan_experts_kernel, dim3(E), dim3(256), 0, s, blk_cnt, nTB, E, counts);
     hipLaunchKernelGGL(scatter_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, ids, w, blk_cnt,
                        lrank, counts, T, E, k, BM, offsets, blocks, num_blocks, row_token,
-                       tok_row, row_w, sched, qctl);
+                       tok_row, row_w, sched, qctl, nslots);
 }
 
 __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *__restrict__ p, int n) {

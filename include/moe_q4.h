@@ -209,6 +209,39 @@ moe_status moe_down_combine(const moe_shape *shape, const uint16_t *h, const moe
                             const moe_routing *r, float *y, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* moe_expert_gemm_q4 followed by moe_down_combine, with both GEMMs in one persistent
+ * launch (the same routing blocks, grouped GEMMs and combine as mechatronicstore.cl
+ * "Prefill: ...", scheduled as one queue: every gate/up tile, then every down tile).
+ * Workgroups freed by the last gate/up tiles start on down tiles while those finish; a down
+ * tile waits, inside the launch, for the gate/up tiles of its routing block.  h and y are
+ * bit for bit those of the two calls: every tile computes the same operations in the same
+ * order.  Arguments, layouts and preconditions as for the two calls: x is not read (the GEMMs
+ * read moe_route's prepared copy in the workspace); h fp16 [T*top_k + T][I] (written, as by
+ * moe_expert_gemm_q4); y fp32 [T][H] (overwritten).  Needs moe_route's outputs and workspace.
+ * combine != 0: each token then adds its top_k staged routed rows to y, as moe_down_combine
+ * does.  combine == 0: on return y holds the shared expert's output only and the routed rows'
+ * weighted outputs stay staged in the workspace, for moe_combine or moe_combine_residual.
+ * Calls that share a workspace must not overlap (the launch keeps its queue and per-block
+ * counters there and zeroes them again when it ends). */
+moe_status moe_expert_ffn_q4(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
+                             const moe_routing *r, uint16_t *h, float *y, int32_t combine,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* The combine that completes moe_expert_ffn_q4(combine = 0) on the same routing and
+ * workspace: y[t] += sum_j staged row tok_row[t][j], in pick order j = 0..top_k-1, in fp32
+ * (the combine of moe_down_combine).  y: fp32 [T][H]. */
+moe_status moe_combine(const moe_shape *shape, const moe_routing *r, float *y, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* The same combine fused with the residual add and RMSNorm of a stack of layers, after
+ * moe_expert_ffn_q4(combine = 0): with y_layer = y + the staged rows (what moe_combine would
+ * leave in y), res <- res + y_layer, u = bf16(res / sqrt(mean(res^2) + eps)), bit for bit
+ * as the combine of moe_down_combine_residual.  y is only read.  res, y fp32 [T][H]; u bf16
+ * [T][H].  MOE_ERR_INVALID_ARG if res, y and u overlap pairwise (by start address) or
+ * eps < 0. */
+moe_status moe_combine_residual(const moe_shape *shape, const moe_routing *r, float *y, float *res,
+                                float eps, uint16_t *u, void *ws, size_t ws_bytes, void *stream);
+
 /* moe_down_combine fused with the residual add and RMSNorm that follow it in a stack of
  * layers (moe_rmsnorm_residual): with y_layer the output moe_down_combine would write,
  *   res <- res + y_layer,   u = bf16(res / sqrt(mean(res^2) + eps))   (unit weight),
@@ -224,7 +257,8 @@ moe_status moe_down_combine_residual(const moe_shape *shape, const uint16_t *h,
                                      float *res, float eps, uint16_t *u, void *ws,
                                      size_t ws_bytes, void *stream);
 
-/* The whole layer: moe_route, moe_expert_gemm_q4, moe_down_combine. */
+/* The whole layer: moe_route, then moe_expert_ffn_q4 (the same h and y as moe_route,
+ * moe_expert_gemm_q4, moe_down_combine). */
 moe_status moe_layer(const moe_shape *shape, const uint16_t *x, const moe_weights *w,
                      const moe_routing *r, uint16_t *h, float *y, void *ws, size_t ws_bytes,
                      void *stream);
@@ -309,7 +343,9 @@ moe_status moe_dequant_q4(const moe_q4 *p, int32_t N, int32_t K, uint16_t *out, 
  * also records it.  This call waits for the device (hipDeviceSynchronize: it is the one
  * call that synchronises) and stores in *flags (host) the OR of what the kernels recorded
  * since the last clear: 1 scatter index, 2 block map entry, 4 row token, 8 combine row,
- * 16 decode expert id; clear != 0 resets the record.  MOE_ERR_UNSUPPORTED (and *flags = 0)
+ * 16 decode expert id, 32 a moe_expert_ffn_q4 down tile that gave up waiting for its block's
+ * gate/up tiles (about a second; never with the launch alone on the device); clear != 0
+ * resets the record.  MOE_ERR_UNSUPPORTED (and *flags = 0)
  * in a regular build; MOE_ERR_HIP if the device or the record cannot be read. */
 moe_status moe_debug_status(uint32_t *flags, int32_t clear);
 

@@ -46,6 +46,11 @@ int main(void)
             EXPECT(moe_route(&s, fake, &w, &r, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
             EXPECT(moe_expert_gemm_q4(&s, fake, &w, &r, fake, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
             EXPECT(moe_down_combine(&s, fake, &w, &r, fake, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
+            EXPECT(moe_expert_ffn_q4(&s, fake, &w, &r, fake, fake, 1, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
+            EXPECT(moe_combine(&s, &r, fake, fake, ws - 1, NULL), MOE_ERR_WORKSPACE);
+            EXPECT(moe_combine_residual(&s, &r, (float *)fake, (float *)fake + 64, 1e-6f,
+                                        (uint16_t *)fake + 4096, fake, ws - 1, NULL),
+                   MOE_ERR_WORKSPACE);
             EXPECT(moe_down_combine_residual(&s, fake, &w, &r, (float *)fake, (float *)fake + 64,
                                              1e-6f, (uint16_t *)fake + 4096, fake, ws - 1, NULL),
                    MOE_ERR_WORKSPACE);

@@ -24,6 +24,7 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("moe_query", "moe_route", "moe_expert_gemm_q4", "moe_down_combine",
+              "moe_expert_ffn_q4", "moe_combine", "moe_combine_residual",
               "moe_down_combine_residual", "moe_layer",
               "moe_query_chunked", "moe_layer_chunked", "moe_decode", "moe_rmsnorm_residual",
               "moe_dequant_q4", "moe_status_str"):
@@ -128,6 +129,30 @@ def test_gemm_and_down_validation_before_launch():
     assert L.moe_down_combine(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), FAKE, FAKE, 0,
                               None) == WS
     assert L.moe_layer(C.byref(s), FAKE, None, C.byref(r), FAKE, FAKE, FAKE, need, None) == INVALID
+    # both GEMMs in one launch: the checks of the two calls
+    ffn = L.moe_expert_ffn_q4
+    for comb in (0, 1):
+        assert ffn(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), FAKE, FAKE, comb, FAKE,
+                   need - 1, None) == WS
+        assert ffn(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), FAKE, FAKE + 8, comb, FAKE,
+                   need, None) == INVALID
+        assert ffn(C.byref(s), FAKE, C.byref(_weights()), C.byref(r), None, FAKE, comb, FAKE,
+                   need, None) == INVALID
+        assert ffn(C.byref(s), FAKE, C.byref(_weights("null_packed")), C.byref(r), FAKE, FAKE,
+                   comb, FAKE, need, None) == INVALID
+        assert ffn(C.byref(s), FAKE, C.byref(_weights()), None, FAKE, FAKE, comb, FAKE, need,
+                   None) == INVALID
+    # the combine that completes it, alone and with the residual add + RMSNorm
+    assert L.moe_combine(C.byref(s), C.byref(r), FAKE, FAKE, need - 1, None) == WS
+    assert L.moe_combine(C.byref(s), C.byref(r), FAKE + 8, FAKE, need, None) == INVALID
+    assert L.moe_combine(C.byref(s), None, FAKE, FAKE, need, None) == INVALID
+    cres = L.moe_combine_residual
+    Y2, R2, U2 = FAKE + 4096, FAKE + 8192, FAKE + 12288
+    assert cres(C.byref(s), C.byref(r), Y2, R2, 1e-6, U2, FAKE, need - 1, None) == WS
+    assert cres(C.byref(s), C.byref(r), Y2, Y2, 1e-6, U2, FAKE, need, None) == INVALID
+    assert cres(C.byref(s), C.byref(r), Y2, R2, 1e-6, R2, FAKE, need, None) == INVALID
+    assert cres(C.byref(s), C.byref(r), Y2, R2, -1.0, U2, FAKE, need, None) == INVALID
+    assert cres(C.byref(s), C.byref(r), Y2 + 8, R2, 1e-6, U2, FAKE, need, None) == INVALID
     # the fused down + residual + norm: the same checks, plus its three fp32/bf16 row buffers
     # must be distinct and eps >= 0
     Y, R, U = FAKE + 4096, FAKE + 8192, FAKE + 12288

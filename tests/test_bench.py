@@ -29,6 +29,6 @@ def test_decode_algorithmic_bytes():
 
 
 def test_traffic_is_tied_to_the_measured_source():
-    t = bench.gateup_traffic_bytes()
+    t = bench.ffn_traffic_bytes()
     # either the counters belong to this gemm.hip (a byte count) or they are withheld
     assert t is None or (isinstance(t, int) and t > 0)
