@@ -50,7 +50,12 @@ SEED_STACK = 5000
 # device-to-device copy (bench.py --copy-calibration 256: FETCH_SIZE reads 131085.4 KiB ->
 # x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM source these counters were
 # taken on; otherwise (or before they are taken) the JSON reports null.
-FFN_TRAFFIC = None
+FFN_TRAFFIC = {
+    "gemm_src_sha256": "7c495100e1af66b34a83db6b5e4e17bdf6d016271b043001f80e6697d12e864b",
+    "fetch_kib": 266696.8, "fetch_scale": 2.0,
+    "write_kib": 102900.7, "write_scale": 1.0,
+    "profile": "profiles/moe_layer_prefill2048_zipf_hbm_traffic.md",
+}
 
 
 def ffn_traffic_bytes():
