@@ -42,6 +42,7 @@ SEED_DECODE = 2000
 SEED_UNIFORM = 3000
 SEED_EP_SHARE = 6000
 SEED_STACK = 5000
+MIN_WARMUP = 60                # steps of sustained load before the clocks settle (measured)
 
 
 # HBM traffic of the one-launch GEMM kernel (q4_ffn_kernel) on this workload, from two
@@ -84,8 +85,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=120,
-                    help="untimed steps replayed back to back right before the timed ones (the "
-                         "clocks take about 60 steps of sustained load to settle)")
+                    help="untimed steps replayed back to back right before the timed ones; at "
+                         "least MIN_WARMUP are run (the clocks take about 60 steps of sustained "
+                         "load to settle), and the JSON reports the number run")
     ap.add_argument("--sets", type=int, default=6, help="weight sets rotated in the prefill loop")
     ap.add_argument("--decode-sets", type=int, default=40,
                     help="T=1 layers (independent weights): decode calls and the chained stack")
@@ -191,8 +193,10 @@ def main():
     graph = capture(sets)
     reps, rem = divmod(K, len(sets))
     graph_rem = capture(sets[:rem]) if rem else None
-    # the W warmup steps (rounded up to whole replays), back to back as the timed ones
-    warm_reps = -(-args.warmup // len(sets))
+    # the W warmup steps (at least MIN_WARMUP, rounded up to whole replays), back to back as
+    # the timed ones
+    warm_reps = -(-max(args.warmup, MIN_WARMUP) // len(sets))
+    warm_steps = warm_reps * len(sets)
     for _ in range(warm_reps):
         graph.replay()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
@@ -274,7 +278,7 @@ def main():
         torch.cuda.synchronize()
         a_ffn_us = phases([(w, shape) for w in asets], x, r, ws, h, y)[1] * 1e3
         ag = capture(asets)
-        for _ in range(-(-60 // len(asets))):         # about 60 steps of warmup, back to back
+        for _ in range(-(-MIN_WARMUP // len(asets))):  # MIN_WARMUP steps of warmup, back to back
             ag.replay()
         areps = 4
         a0 = torch.cuda.Event(enable_timing=True)
@@ -441,7 +445,7 @@ def main():
         with torch.cuda.graph(eg):
             for w in esets:
                 estep(w)
-        for _ in range(-(-60 // len(esets))):         # about 60 steps of warmup, back to back
+        for _ in range(-(-MIN_WARMUP // len(esets))):  # MIN_WARMUP steps of warmup, back to back
             eg.replay()
         ereps = max(1, 24 // len(esets))
         a_ = torch.cuda.Event(enable_timing=True)
@@ -498,7 +502,7 @@ def main():
         with torch.cuda.graph(ug):
             for w in usets:
                 ustep(w)
-        for _ in range(-(-60 // len(usets))):         # about 60 steps of warmup, back to back
+        for _ in range(-(-MIN_WARMUP // len(usets))):  # MIN_WARMUP steps of warmup, back to back
             ug.replay()
         ureps = max(1, 24 // len(usets))
         u0 = torch.cuda.Event(enable_timing=True)
@@ -659,7 +663,8 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warm_steps,
+        "warmup_requested": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "step_us": step_stats,
         "higher_is_better": True,
