@@ -52,9 +52,9 @@ MIN_WARMUP = 60                # steps of sustained load before the clocks settl
 # x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM source these counters were
 # taken on; otherwise (or before they are taken) the JSON reports null.
 FFN_TRAFFIC = {
-    "gemm_src_sha256": "7c495100e1af66b34a83db6b5e4e17bdf6d016271b043001f80e6697d12e864b",
-    "fetch_kib": 266696.8, "fetch_scale": 2.0,
-    "write_kib": 102900.7, "write_scale": 1.0,
+    "gemm_src_sha256": "078af5dbf1abc672b6e15ccbe6eb05157b2c482772b0f626167863a8bac38af2",
+    "fetch_kib": 262091.7, "fetch_scale": 2.0,
+    "write_kib": 102882.0, "write_scale": 1.0,
     "profile": "profiles/moe_layer_prefill2048_zipf_hbm_traffic.md",
 }
 

@@ -131,19 +131,21 @@ __device__ __forceinline__ floatx16 mfma16(f16x8 a, f16x8 b, floatx16 c) {
 // Asynchronous global->LDS copies.  Lane i of the wave writes LDS bytes
 // [lds + 16 i, +16) (dword form: [lds + 4 i, +4)).  Issued through inline assembly so that the compiler does not
 // wait for them before every LDS read; completion is awaited explicitly
-// (s_waitcnt vmcnt) before the barrier that publishes a stage.
+// (s_waitcnt vmcnt) before the barrier that publishes a stage.  The compiler does not see the
+// copy inside the asm, so the statement keeps the one wait state that gfx9 needs between an
+// SALU write of M0 and an LDS DMA that reads it.
 // COH: the copy carries the agent-scope cache policy (sc1), so it returns what an sc1 store
 // on another XCD wrote, even where this XCD's L2 holds an older copy of the line.
 template <bool COH = false> __device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
     if constexpr (COH)
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off sc1" ::"v"(g), "s"(lds)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off sc1" ::"v"(g), "s"(lds)
                      : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
                      : "memory", "m0");
 }
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
 
@@ -153,24 +155,28 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
 template <bool COH = false>
 __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
     if constexpr (COH)
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(sbase),
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(sbase),
                      "s"(lds)
                      : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                      "s"(lds)
                      : "memory", "m0");
 }
 __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
 }
 
-// Vector stores of the gate/up outputs.  COH: agent-scope policy (sc1), the store is written
-// through to memory, where the sc1 copies of a down item on any XCD read it.
+// Vector stores of the GEMM outputs.  COH: agent-scope policy (sc1), written through to
+// memory: where the sc1 copies of a down item on any XCD read h, and measured faster for the
+// down outputs of the one launch as well.  The compiler does not
+// see a store inside the asm, so the 16-byte form keeps the wait states itself: a store of more
+// than 8 bytes reads its data registers after it issues, and the next instructions must not
+// overwrite them (2 wait states on gfx940 and later).
 template <bool COH> __device__ __forceinline__ void store16(void *p, u32x4 v) {
     if constexpr (COH)
-        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+        asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 2" ::"v"(p), "v"(v) : "memory");
     else
         *(u32x4 *)p = v;
 }
@@ -498,6 +504,15 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
         }
     } else {
         const int Trk = a.T * a.topk;
+        // stores: 32 consecutive lanes write one row's 256 columns, so that every store
+        // instruction covers whole 128-byte lines.  Routed rows (bf16): lane c8 takes columns
+        // 8 c8 .. 8 c8 + 7, one 16-byte store.  Shared rows (fp32): columns 4 c8 .. 4 c8 + 3 and
+        // 128 + 4 c8 .. 128 + 4 c8 + 3, two 16-byte stores each covering 512 contiguous bytes.
+        const int c8 = tid & 31;
+        const int cA = t.shared ? 4 * c8 : 8 * c8, cB = t.shared ? 128 + 4 * c8 : 8 * c8 + 4;
+        const floatx4 k0 = *(const floatx4 *)(il.colk + cA);          // 2^-k per column
+        const floatx4 k1 = *(const floatx4 *)(il.colk + cB);
+        const int col0 = t.ntile * 256;
         // two m-tiles (64 rows) per pass through the LDS y tile
 #pragma unroll
         for (int p = 0; p < (MT + 1) / 2; ++p) {
@@ -516,37 +531,29 @@ __device__ void gemm_tile(const GemmArgs &a, const Tile &t, uint8_t *smem, int *
                 }
             }
             __syncthreads();
-            // thread: row tid/8 of each 32-row half, 32 columns from (tid&7)*32
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int mt = 2 * p + h2;
-                const int rr = 32 * h2 + (tid >> 3), seg = tid & 7;
-                const int row = 32 * mt + (tid >> 3);
-                if (mt < MT && row < t.nrows) {
-                    const uint8_t *src = smem + rr * YS_LD + seg * 128;
-                    const int col = t.ntile * 256 + seg * 32;
-                    const floatx4 *kcp = (const floatx4 *)(il.colk + seg * 32);   // 2^-k per column
+            for (int i = 0; i < 8; ++i) {
+                const int rr = (tid >> 5) + 8 * i;               // row of this pass's 64
+                const int row = 64 * p + rr;
+                if (2 * p + (rr >> 5) < MT && row < t.nrows) {
+                    const uint8_t *src = smem + rr * YS_LD;
+                    const floatx4 s0 = *(const floatx4 *)(src + 4 * cA);
+                    const floatx4 s1 = *(const floatx4 *)(src + 4 * cB);
                     if (t.shared) {
-                        float *dst = a.y + (size_t)(t.r0 - Trk + row) * a.N + col;
                         const float hx = il.rb[row];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            *(floatx4 *)(dst + 4 * q) = *(const floatx4 *)(src + 16 * q) * (kcp[q] * hx);
+                        float *dst = a.y + (size_t)(t.r0 - Trk + row) * a.N + col0;
+                        store16<COH>(dst + cA, __builtin_bit_cast(u32x4, s0 * (k0 * hx)));
+                        store16<COH>(dst + cB, __builtin_bit_cast(u32x4, s1 * (k1 * hx)));
                     } else {
                         // routed row: weighted output staged in bf16 (fp32 range; the combine adds in fp32)
-                        uint16_t *dst = a.stage + (size_t)(t.r0 + row) * a.N + col;
                         const float wr = il.ra[row] * il.rb[row];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const floatx4 v0 = *(const floatx4 *)(src + 32 * q) * kcp[2 * q];
-                            const floatx4 v1 = *(const floatx4 *)(src + 32 * q + 16) * kcp[2 * q + 1];
-                            u32x4 o;
-                            o.x = pack_bf16x2(wr * v0[0], wr * v0[1]);
-                            o.y = pack_bf16x2(wr * v0[2], wr * v0[3]);
-                            o.z = pack_bf16x2(wr * v1[0], wr * v1[1]);
-                            o.w = pack_bf16x2(wr * v1[2], wr * v1[3]);
-                            *(u32x4 *)(dst + 8 * q) = o;
-                        }
+                        const floatx4 v0 = s0 * k0, v1 = s1 * k1;
+                        u32x4 o;
+                        o.x = pack_bf16x2(wr * v0[0], wr * v0[1]);
+                        o.y = pack_bf16x2(wr * v0[2], wr * v0[3]);
+                        o.z = pack_bf16x2(wr * v1[0], wr * v1[1]);
+                        o.w = pack_bf16x2(wr * v1[2], wr * v1[3]);
+                        store16<COH>(a.stage + (size_t)(t.r0 + row) * a.N + col0 + cA, o);
                     }
                 }
             }

@@ -172,8 +172,10 @@ constexpr int R_STAGE = RX_BYTES + RW_BYTES;
 constexpr int R_NST = 4;
 constexpr int R_PER = 1 + RT_EH / 32;             // copies per thread and chunk
 
+// global->LDS copy of 16 B per lane (inline asm: the statement keeps the wait state that gfx9
+// needs between the M0 write and the LDS DMA reading it)
 __device__ __forceinline__ void rdma16(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
 
