@@ -151,20 +151,23 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
 
 // The same copies with a wave-uniform base address in SGPRs and a per-lane
 // 32-bit byte offset: the per-lane offsets stay fixed over the K loop and each
-// K step only moves the scalar base.
+// K step only moves the scalar base.  The base may have been written by a VALU
+// instruction just before (an SGPR reloaded from a spill lane); gfx9 needs 5 wait states
+// between that write and a vector memory instruction reading the SGPR, which the statement
+// keeps itself (s_nop 2, the M0 write, s_nop 0).
 template <bool COH = false>
 __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
     if constexpr (COH)
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(sbase),
+        asm volatile("s_nop 2\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(sbase),
                      "s"(lds)
                      : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+        asm volatile("s_nop 2\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                      "s"(lds)
                      : "memory", "m0");
 }
 __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+    asm volatile("s_nop 2\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
 }
 
