@@ -701,16 +701,19 @@ __global__ __launch_bounds__(NTHR, 2) void q4_ffn_kernel(GemmArgs ag, GemmArgs a
             }
         } else {
             const int kd = k - ng, slot = kd / ad.n_tiles;
+            // the slot's count is read while the block is decoded (counts only grow, and a count
+            // that is complete stays complete, so an early read is as good as a late one)
+            int seen = 0;
+            if (tid == 0) seen = __hip_atomic_load(done + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const bool ok = item_tile(ad, slot, kd - slot * ad.n_tiles, nb, t);
             flush();                             // never wait while holding a report
             if (ok) {
                 if (tid == 0) {
                     int it = 0;
-                    while (__hip_atomic_load(done + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                               ag.n_tiles &&
-                           it < kFfnSpin) {
+                    while (seen < ag.n_tiles && it < kFfnSpin) {
                         __builtin_amdgcn_s_sleep(2);
                         ++it;
+                        seen = __hip_atomic_load(done + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                     MOE_DBG(it < kFfnSpin, DBG_FFN_WAIT);
                 }
