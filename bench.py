@@ -52,9 +52,9 @@ MIN_WARMUP = 60                # steps of sustained load before the clocks settl
 # x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only for the GEMM source these counters were
 # taken on; otherwise (or before they are taken) the JSON reports null.
 FFN_TRAFFIC = {
-    "gemm_src_sha256": "8f509b85284c0b0c87347791ce3df8bb60e180c5d16139529673b7cf7ef28b28",
-    "fetch_kib": 265492.1, "fetch_scale": 2.0,
-    "write_kib": 102882.0, "write_scale": 1.0,
+    "gemm_src_sha256": "94aec9054e878f00509ce45aba73d258f3395060b565913175d1f27a70a7ea43",
+    "fetch_kib": 265492.1042, "fetch_scale": 2.0,
+    "write_kib": 102882.0104, "write_scale": 1.0,
     "profile": "profiles/moe_layer_prefill2048_zipf_hbm_traffic.md",
 }
 

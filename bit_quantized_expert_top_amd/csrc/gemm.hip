@@ -715,7 +715,7 @@ __global__ __launch_bounds__(NTHR, 2) void q4_ffn_kernel(GemmArgs ag, GemmArgs a
                         ++it;
                         seen = __hip_atomic_load(done + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
-                    MOE_DBG(it < kFfnSpin, DBG_FFN_WAIT);
+                    MOE_DBG(seen >= ag.n_tiles, DBG_FFN_WAIT);   // flagged only if it gave up
                 }
                 __syncthreads();                 // the slot's h is complete
                 run_tile<1, true>(ad, t, smem, &s_next, il, done, -1);
